@@ -1,0 +1,494 @@
+/*
+ * Plain, slow fp64 CPU oracle for the ATMA global-layer hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load
+ * this file: only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark use it.  It shares no code, header, table or helper with the HIP
+ * library; it reads fp64 arrays (inputs widened exactly from whatever precision the
+ * caller holds) and writes fp64 results.
+ *
+ * Sources (the ATMA paper, "ATMA: Long-Context Language Modeling via Polar Attention
+ * and Gated-Delta Compression Memory", arXiv 2606.25156):
+ *   - gated-delta memory: Section 3.3, the single displayed equation
+ *         M_t = gamma_t M_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  r_t = M_t q_t.
+ *     Here gamma_t is called alpha (per-token decay), M is called S (state, Dv x Dk),
+ *     r is called o.
+ *   - Polar attention: Section 3.2 equation (temperature t_i and null floor nu_i);
+ *     Appendix C.2 (one softmax over the masked real-key logits plus one virtual
+ *     null logit, channels computed from the resulting weights); Appendix A.2
+ *     (direction c_i = s_i / max(||s_i||, eps), magnitude mu_i = tanh(beta log(1+m_eff)));
+ *     Appendix C.3 and its Table 6 (streaming statistics M, L, Q2, S; n_eff = L^2/Q2,
+ *     m_eff = n_eff L / Z, direction = normalize(S + p_null v_null)).
+ *
+ * Readings taken where the pages are silent (each is listed with its reason in the
+ * repository's design notes):
+ *   - score scale: real logit = t_i * (q_i . k_j) / sqrt(D)  (standard scaled dot product);
+ *   - n_i = number of real keys visible to query i under the causal mask (i+1, 0-based i);
+ *   - natural logarithms; softplus(x) = log(1 + e^x);
+ *   - the null logit is t_i * nu_i (same temperature as the real logits);
+ *   - Z = real mass + null mass (the full partition of the single softmax);
+ *   - output o_i = mu_i * c_i;
+ *   - eps = caller-supplied (1e-12 by convention), applied to the Z-normalised s_i;
+ *   - parameters are per head; temp_raw and null_slope_raw pass through softplus.
+ *
+ * Every entry point parallelises only over independent (batch, head) pairs or query
+ * rows with plain pthreads; the arithmetic of one task is a straight loop.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------- */
+/* thread pool: run fn(task, ctx) for task = 0..ntasks-1 over nthreads threads  */
+/* ------------------------------------------------------------------------- */
+typedef void (*task_fn)(long task, void* ctx);
+typedef struct { task_fn fn; void* ctx; long ntasks; int tid, nthreads; } worker_arg;
+
+static void* worker_main(void* p) {
+    worker_arg* a = (worker_arg*)p;
+    for (long t = a->tid; t < a->ntasks; t += a->nthreads) a->fn(t, a->ctx);
+    return NULL;
+}
+
+static int resolve_threads(int nthreads, long ntasks) {
+    if (nthreads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = n > 0 ? (int)n : 1;
+    }
+    if (nthreads > ntasks) nthreads = (int)(ntasks > 0 ? ntasks : 1);
+    if (nthreads > 256) nthreads = 256;
+    return nthreads;
+}
+
+static void run_tasks(task_fn fn, void* ctx, long ntasks, int nthreads) {
+    nthreads = resolve_threads(nthreads, ntasks);
+    if (nthreads == 1) {
+        for (long t = 0; t < ntasks; ++t) fn(t, ctx);
+        return;
+    }
+    pthread_t th[256];
+    worker_arg args[256];
+    for (int i = 0; i < nthreads; ++i) {
+        args[i].fn = fn; args[i].ctx = ctx; args[i].ntasks = ntasks;
+        args[i].tid = i; args[i].nthreads = nthreads;
+        pthread_create(&th[i], NULL, worker_main, &args[i]);
+    }
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
+/* Number of threads the oracle would use for a given task count (reported by benchmarks). */
+int oracle_threads_used(int nthreads, long ntasks) { return resolve_threads(nthreads, ntasks); }
+
+/* ========================================================================= */
+/* Gated-delta memory, sequential definition (Section 3.3 equation)          */
+/* ========================================================================= */
+/* Layouts (row-major, last index fastest):
+ *   q, k  [B, T, H, Dk];  v [B, T, H, Dv];  alpha, beta [B, T, H];
+ *   init_state, final_state [B, H, Dv, Dk] (init may be NULL = zero state);
+ *   o [B, T, H, Dv];  states (optional, may be NULL) [B, T, H, Dv, Dk] = S_t after token t. */
+typedef struct {
+    int B, T, H, Dk, Dv;
+    const double *q, *k, *v, *alpha, *beta, *init;
+    double *o, *final_state, *states;
+} gdn_ctx;
+
+static void gdn_seq_task(long task, void* p) {
+    const gdn_ctx* c = (const gdn_ctx*)p;
+    const int b = (int)(task / c->H), h = (int)(task % c->H);
+    const int Dk = c->Dk, Dv = c->Dv, H = c->H;
+    double* S = (double*)calloc((size_t)Dv * Dk, sizeof(double));
+    double* u = (double*)malloc((size_t)Dv * sizeof(double));
+    if (c->init) memcpy(S, c->init + ((size_t)b * H + h) * Dv * Dk, sizeof(double) * Dv * Dk);
+    for (int t = 0; t < c->T; ++t) {
+        const size_t tok = ((size_t)b * c->T + t) * H + h;
+        const double* qt = c->q + tok * Dk;
+        const double* kt = c->k + tok * Dk;
+        const double* vt = c->v + tok * Dv;
+        const double a = c->alpha[tok], be = c->beta[tok];
+        /* u = S_{t-1} k_t */
+        for (int r = 0; r < Dv; ++r) {
+            double s = 0.0;
+            for (int j = 0; j < Dk; ++j) s += S[r * Dk + j] * kt[j];
+            u[r] = s;
+        }
+        /* S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+         *     = alpha_t (S_{t-1} - beta_t u k_t^T) + beta_t v_t k_t^T */
+        for (int r = 0; r < Dv; ++r)
+            for (int j = 0; j < Dk; ++j)
+                S[r * Dk + j] = a * (S[r * Dk + j] - be * u[r] * kt[j]) + be * vt[r] * kt[j];
+        /* o_t = S_t q_t */
+        double* ot = c->o + tok * Dv;
+        for (int r = 0; r < Dv; ++r) {
+            double s = 0.0;
+            for (int j = 0; j < Dk; ++j) s += S[r * Dk + j] * qt[j];
+            ot[r] = s;
+        }
+        if (c->states) memcpy(c->states + tok * Dv * Dk, S, sizeof(double) * Dv * Dk);
+    }
+    if (c->final_state) memcpy(c->final_state + ((size_t)b * H + h) * Dv * Dk, S, sizeof(double) * Dv * Dk);
+    free(S);
+    free(u);
+}
+
+int oracle_gdn_sequential(int B, int T, int H, int Dk, int Dv,
+                          const double* q, const double* k, const double* v,
+                          const double* alpha, const double* beta, const double* init_state,
+                          double* o, double* final_state, double* states, int nthreads) {
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || !q || !k || !v || !alpha || !beta || !o) return -1;
+    gdn_ctx c = {B, T, H, Dk, Dv, q, k, v, alpha, beta, init_state, o, final_state, states};
+    run_tasks(gdn_seq_task, &c, (long)B * H, nthreads);
+    return 0;
+}
+
+/* ========================================================================= */
+/* Gated-delta memory, chunked form (exact algebraic rewrite of Section 3.3)  */
+/* ========================================================================= */
+/* Writing S_t = alpha_t S_{t-1} + delta_t k_t^T with
+ * delta_t = beta_t (v_t - alpha_t S_{t-1} k_t) and unrolling inside a chunk of n tokens
+ * that starts from state S_in (g_r = sum_{s<=r} log alpha_s, r = 0..n-1):
+ *   A[r][s] = beta_r exp(g_r - g_s) (k_r . k_s)            for s < r, else 0
+ *   T = (I + A)^{-1}                                        (unit lower triangular)
+ *   W = T diag(beta * exp(g)) K,   U = T diag(beta) V
+ *   Delta = U - W S_in^T                                    (row r = delta_r)
+ *   O = diag(exp(g)) Q S_in^T + lower_incl(Q K^T * exp(g_r - g_s)) Delta
+ *   S_out = exp(g_{n-1}) S_in + Delta^T diag(exp(g_{n-1} - g)) K
+ * Each step below is one of these lines, computed with plain loops. */
+typedef struct { gdn_ctx g; int C; } gdn_chunk_ctx;
+
+static void gdn_chunk_task(long task, void* p) {
+    const gdn_chunk_ctx* cc = (const gdn_chunk_ctx*)p;
+    const gdn_ctx* c = &cc->g;
+    const int b = (int)(task / c->H), h = (int)(task % c->H);
+    const int Dk = c->Dk, Dv = c->Dv, H = c->H, C = cc->C;
+    double* S = (double*)calloc((size_t)Dv * Dk, sizeof(double));
+    double* g = (double*)malloc(sizeof(double) * C);
+    double* A = (double*)malloc(sizeof(double) * C * C);
+    double* Ti = (double*)malloc(sizeof(double) * C * C);
+    double* W = (double*)malloc(sizeof(double) * C * Dk);
+    double* U = (double*)malloc(sizeof(double) * C * Dv);
+    double* Dl = (double*)malloc(sizeof(double) * C * Dv);
+    double* Sn = (double*)malloc(sizeof(double) * Dv * Dk);
+    if (c->init) memcpy(S, c->init + ((size_t)b * H + h) * Dv * Dk, sizeof(double) * Dv * Dk);
+#define TOK(t) (((size_t)b * c->T + (t)) * H + h)
+    for (int t0 = 0; t0 < c->T; t0 += C) {
+        const int n = (c->T - t0 < C) ? c->T - t0 : C;
+        /* g_r: cumulative log-decay inside the chunk */
+        double acc = 0.0;
+        for (int r = 0; r < n; ++r) { acc += log(c->alpha[TOK(t0 + r)]); g[r] = acc; }
+        /* A (strictly lower) */
+        for (int r = 0; r < n; ++r)
+            for (int s = 0; s < n; ++s) {
+                double val = 0.0;
+                if (s < r) {
+                    const double* kr = c->k + TOK(t0 + r) * Dk;
+                    const double* ks = c->k + TOK(t0 + s) * Dk;
+                    double d = 0.0;
+                    for (int j = 0; j < Dk; ++j) d += kr[j] * ks[j];
+                    val = c->beta[TOK(t0 + r)] * exp(g[r] - g[s]) * d;
+                }
+                A[r * n + s] = val;
+            }
+        /* T = (I + A)^{-1} by forward substitution, column by column:
+         * T[r][j] = [r==j] - sum_{s<r} A[r][s] T[s][j] */
+        for (int j = 0; j < n; ++j)
+            for (int r = 0; r < n; ++r) {
+                double val = (r == j) ? 1.0 : 0.0;
+                for (int s = 0; s < r; ++s) val -= A[r * n + s] * Ti[s * n + j];
+                Ti[r * n + j] = val;
+            }
+        /* W = T diag(beta e^g) K ;  U = T diag(beta) V */
+        for (int r = 0; r < n; ++r) {
+            for (int j = 0; j < Dk; ++j) {
+                double s_ = 0.0;
+                for (int s = 0; s < n; ++s)
+                    s_ += Ti[r * n + s] * c->beta[TOK(t0 + s)] * exp(g[s]) * c->k[TOK(t0 + s) * Dk + j];
+                W[r * Dk + j] = s_;
+            }
+            for (int j = 0; j < Dv; ++j) {
+                double s_ = 0.0;
+                for (int s = 0; s < n; ++s)
+                    s_ += Ti[r * n + s] * c->beta[TOK(t0 + s)] * c->v[TOK(t0 + s) * Dv + j];
+                U[r * Dv + j] = s_;
+            }
+        }
+        /* Delta = U - W S_in^T */
+        for (int r = 0; r < n; ++r)
+            for (int i = 0; i < Dv; ++i) {
+                double s_ = 0.0;
+                for (int j = 0; j < Dk; ++j) s_ += W[r * Dk + j] * S[i * Dk + j];
+                Dl[r * Dv + i] = U[r * Dv + i] - s_;
+            }
+        /* O = diag(e^g) Q S_in^T + lower_incl(Q K^T * e^{g_r - g_s}) Delta */
+        for (int r = 0; r < n; ++r) {
+            const double* qr = c->q + TOK(t0 + r) * Dk;
+            double* orow = c->o + TOK(t0 + r) * Dv;
+            for (int i = 0; i < Dv; ++i) {
+                double s_ = 0.0;
+                for (int j = 0; j < Dk; ++j) s_ += qr[j] * S[i * Dk + j];
+                orow[i] = exp(g[r]) * s_;
+            }
+            for (int s = 0; s <= r; ++s) {
+                const double* ks = c->k + TOK(t0 + s) * Dk;
+                double d = 0.0;
+                for (int j = 0; j < Dk; ++j) d += qr[j] * ks[j];
+                const double pw = d * exp(g[r] - g[s]);
+                for (int i = 0; i < Dv; ++i) orow[i] += pw * Dl[s * Dv + i];
+            }
+        }
+        /* S_out = e^{g_{n-1}} S_in + Delta^T diag(e^{g_{n-1} - g}) K */
+        for (int i = 0; i < Dv; ++i)
+            for (int j = 0; j < Dk; ++j) {
+                double s_ = exp(g[n - 1]) * S[i * Dk + j];
+                for (int r = 0; r < n; ++r)
+                    s_ += Dl[r * Dv + i] * exp(g[n - 1] - g[r]) * c->k[TOK(t0 + r) * Dk + j];
+                Sn[i * Dk + j] = s_;
+            }
+        memcpy(S, Sn, sizeof(double) * Dv * Dk);
+    }
+#undef TOK
+    if (c->final_state) memcpy(c->final_state + ((size_t)b * H + h) * Dv * Dk, S, sizeof(double) * Dv * Dk);
+    free(S); free(g); free(A); free(Ti); free(W); free(U); free(Dl); free(Sn);
+}
+
+int oracle_gdn_chunked(int B, int T, int H, int Dk, int Dv, int C,
+                       const double* q, const double* k, const double* v,
+                       const double* alpha, const double* beta, const double* init_state,
+                       double* o, double* final_state, int nthreads) {
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || C < 1 || !q || !k || !v || !alpha || !beta || !o) return -1;
+    gdn_chunk_ctx cc = {{B, T, H, Dk, Dv, q, k, v, alpha, beta, init_state, o, final_state, NULL}, C};
+    run_tasks(gdn_chunk_task, &cc, (long)B * H, nthreads);
+    return 0;
+}
+
+/* ========================================================================= */
+/* Polar attention                                                             */
+/* ========================================================================= */
+/* Per-head parameters, each [Hq] except v_null [Hq, D]:
+ *   temp_raw (alpha in Section 3.2), null_slope_raw (gamma in Section 3.2),
+ *   null_bias (b in Section 3.2), mag_beta (beta in Appendix A.2), v_null (Appendix C.3). */
+typedef struct {
+    const double *temp_raw, *null_slope_raw, *null_bias, *mag_beta, *v_null;
+    double eps;
+} polar_par;
+
+static double softplus(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+/* One query row against n real keys (key j at K + j*kstride, value at V + j*vstride).
+ * Materialised form of Appendix C.2: all n real logits plus the null logit, one softmax,
+ * channels from the weights.  Outputs o[D], *mu, *meff, *neff.  w is scratch of n doubles. */
+static void polar_row_materialised(const double* qi, const double* K, const double* V, size_t kstride,
+                                   size_t vstride, long n, int D, int h, const polar_par* P,
+                                   double* o, double* mu, double* meff, double* neff, double* w) {
+    const double a = softplus(P->temp_raw[h]);
+    const double s = softplus(P->null_slope_raw[h]);
+    const double t = 1.0 + a * log((double)n);                          /* Section 3.2: t_i */
+    const double nu = P->null_bias[h] + s * sqrt(log((double)n + 1.0)); /* Section 3.2: nu_i */
+    const double lnull = t * nu;                                        /* virtual null logit */
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    double m = lnull;
+    for (long j = 0; j < n; ++j) {
+        double d = 0.0;
+        for (int x = 0; x < D; ++x) d += qi[x] * K[j * kstride + x];
+        w[j] = t * d * inv_sqrt_d;
+        if (w[j] > m) m = w[j];
+    }
+    /* single softmax over {real logits} U {null logit} */
+    double Z = exp(lnull - m);
+    for (long j = 0; j < n; ++j) { w[j] = exp(w[j] - m); Z += w[j]; }
+    const double wnull = exp(lnull - m) / Z;
+    double R = 0.0, Q2 = 0.0;
+    for (long j = 0; j < n; ++j) { w[j] /= Z; R += w[j]; Q2 += w[j] * w[j]; }
+    /* magnitude channel: participation ratio of the real weights, scaled by real mass */
+    const double ne = R * R / Q2;
+    const double me = ne * R;
+    const double muv = tanh(P->mag_beta[h] * log1p(me));
+    /* direction channel: s_i = sum_j w_ij v_j + w_null v_null, c_i = s_i / max(||s_i||, eps) */
+    double nrm2 = 0.0;
+    for (int x = 0; x < D; ++x) {
+        double acc = wnull * P->v_null[(size_t)h * D + x];
+        for (long j = 0; j < n; ++j) acc += w[j] * V[j * vstride + x];
+        o[x] = acc;
+        nrm2 += acc * acc;
+    }
+    const double nrm = sqrt(nrm2);
+    const double den = nrm > P->eps ? nrm : P->eps;
+    for (int x = 0; x < D; ++x) o[x] = muv * (o[x] / den);
+    *mu = muv; *meff = me; *neff = ne;
+}
+
+/* Streaming form of Appendix C.3 / Table 6, with the key range cut into `nsplit`
+ * contiguous segments whose (M, L, Q2, S) states are combined afterwards.  Inside a
+ * segment keys arrive in blocks of `block`: M <- max(M, max a); rho = exp(M_old - M_new);
+ * L <- rho L + sum p; Q2 <- rho^2 Q2 + sum p^2; S <- rho S + sum p v.  M covers real keys
+ * only; the null logit enters at finalisation with the common origin M* = max(M, l_null). */
+static void polar_row_streaming(const double* qi, const double* K, const double* V, size_t kstride,
+                                size_t vstride, long n, int D, int h, const polar_par* P, long block,
+                                int nsplit, double* o, double* mu, double* meff, double* neff,
+                                double* scratch /* (D+3)*nsplit + block */) {
+    const double a = softplus(P->temp_raw[h]);
+    const double s = softplus(P->null_slope_raw[h]);
+    const double t = 1.0 + a * log((double)n);
+    const double nu = P->null_bias[h] + s * sqrt(log((double)n + 1.0));
+    const double lnull = t * nu;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    double* st = scratch;                       /* per split: M, L, Q2, S[D] */
+    double* blk = scratch + (size_t)(D + 3) * nsplit;
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const long j0 = n * sp / nsplit, j1 = n * (sp + 1) / nsplit;
+        double M = -INFINITY, L = 0.0, Q2 = 0.0;
+        double* Sv = st + (size_t)sp * (D + 3) + 3;
+        for (int x = 0; x < D; ++x) Sv[x] = 0.0;
+        for (long jb = j0; jb < j1; jb += block) {
+            const long je = (jb + block < j1) ? jb + block : j1;
+            double bmax = -INFINITY;
+            for (long j = jb; j < je; ++j) {
+                double d = 0.0;
+                for (int x = 0; x < D; ++x) d += qi[x] * K[j * kstride + x];
+                blk[j - jb] = t * d * inv_sqrt_d;
+                if (blk[j - jb] > bmax) bmax = blk[j - jb];
+            }
+            const double Mn = bmax > M ? bmax : M;
+            const double rho = exp(M - Mn); /* exp(-inf) = 0 on the first block */
+            L *= rho; Q2 *= rho * rho;
+            for (int x = 0; x < D; ++x) Sv[x] *= rho;
+            for (long j = jb; j < je; ++j) {
+                const double p = exp(blk[j - jb] - Mn);
+                L += p; Q2 += p * p;
+                for (int x = 0; x < D; ++x) Sv[x] += p * V[j * vstride + x];
+            }
+            M = Mn;
+        }
+        st[(size_t)sp * (D + 3) + 0] = M;
+        st[(size_t)sp * (D + 3) + 1] = L;
+        st[(size_t)sp * (D + 3) + 2] = Q2;
+    }
+    /* combine segments: M = max M_x, r_x = exp(M_x - M), L = sum r_x L_x,
+     * Q2 = sum r_x^2 Q2_x, S = sum r_x S_x (empty segments have M = -inf, r = 0) */
+    double M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) if (st[(size_t)sp * (D + 3)] > M) M = st[(size_t)sp * (D + 3)];
+    double L = 0.0, Q2 = 0.0;
+    for (int x = 0; x < D; ++x) o[x] = 0.0;
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const double* e = st + (size_t)sp * (D + 3);
+        if (e[0] == -INFINITY) continue;
+        const double r = exp(e[0] - M);
+        L += r * e[1]; Q2 += r * r * e[2];
+        for (int x = 0; x < D; ++x) o[x] += r * e[3 + x];
+    }
+    /* finalise: merge the null with origin M* = max(M, l_null) */
+    const double Ms = M > lnull ? M : lnull;
+    const double pnull = exp(lnull - Ms);
+    const double Ls = L * exp(M - Ms);
+    const double Z = Ls + pnull;
+    const double ne = L * L / Q2;          /* scale-free: the origin cancels */
+    const double me = ne * Ls / Z;
+    const double muv = tanh(P->mag_beta[h] * log1p(me));
+    double nrm2 = 0.0;
+    for (int x = 0; x < D; ++x) {
+        o[x] = (o[x] * exp(M - Ms) + pnull * P->v_null[(size_t)h * D + x]) / Z;
+        nrm2 += o[x] * o[x];
+    }
+    const double nrm = sqrt(nrm2);
+    const double den = nrm > P->eps ? nrm : P->eps;
+    for (int x = 0; x < D; ++x) o[x] = muv * (o[x] / den);
+    *mu = muv; *meff = me; *neff = ne;
+}
+
+typedef struct {
+    int B, T, Hq, Hkv, D;
+    const double *q, *k, *v;
+    polar_par P;
+    const int64_t* rows; long nrows;
+    int mode; long block; int nsplit;
+    double *o, *mu, *meff, *neff;
+} polar_ctx;
+
+/* task = ((b * nrows) + r) * Hq + h */
+static void polar_task(long task, void* p) {
+    const polar_ctx* c = (const polar_ctx*)p;
+    const int h = (int)(task % c->Hq);
+    const long r = (task / c->Hq) % c->nrows;
+    const int b = (int)(task / ((long)c->Hq * c->nrows));
+    const long i = c->rows ? (long)c->rows[r] : r;
+    const int hk = h / (c->Hq / c->Hkv);
+    const int D = c->D;
+    const double* qi = c->q + (((size_t)b * c->T + i) * c->Hq + h) * D;
+    const double* K = c->k + ((size_t)b * c->T * c->Hkv + hk) * D;
+    const double* V = c->v + ((size_t)b * c->T * c->Hkv + hk) * D;
+    const size_t stride = (size_t)c->Hkv * D;
+    const size_t out = ((size_t)b * c->nrows + r) * c->Hq + h;
+    if (c->mode == 0) {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+        polar_row_materialised(qi, K, V, stride, stride, i + 1, D, h, &c->P, c->o + out * D, c->mu + out,
+                               c->meff + out, c->neff + out, w);
+        free(w);
+    } else {
+        double* sc = (double*)malloc(sizeof(double) * ((size_t)(D + 3) * c->nsplit + c->block));
+        polar_row_streaming(qi, K, V, stride, stride, i + 1, D, h, &c->P, c->block, c->nsplit, c->o + out * D,
+                            c->mu + out, c->meff + out, c->neff + out, sc);
+        free(sc);
+    }
+}
+
+/* Causal Polar attention for the query rows listed in `rows` (NULL = all T rows).
+ *   q [B, T, Hq, D];  k, v [B, T, Hkv, D];  query head h reads kv head h / (Hq / Hkv).
+ * Outputs (row-sampled layout): o [B, nrows, Hq, D]; mu, meff, neff [B, nrows, Hq].
+ * mode 0 = materialised single softmax (Appendix C.2); mode 1 = streaming statistics
+ * (Table 6) with key blocks of `block` and `nsplit` merged key segments. */
+int oracle_polar_fwd(int B, int T, int Hq, int Hkv, int D,
+                     const double* q, const double* k, const double* v,
+                     const double* temp_raw, const double* null_slope_raw, const double* null_bias,
+                     const double* mag_beta, const double* v_null, double eps,
+                     const int64_t* rows, long nrows, int mode, long block, int nsplit,
+                     double* o, double* mu, double* meff, double* neff, int nthreads) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return -1;
+    if (!q || !k || !v || !temp_raw || !null_slope_raw || !null_bias || !mag_beta || !v_null) return -1;
+    if (!o || !mu || !meff || !neff) return -1;
+    if (mode != 0 && (block < 1 || nsplit < 1)) return -1;
+    if (!rows) nrows = T;
+    for (long r = 0; rows && r < nrows; ++r) if (rows[r] < 0 || rows[r] >= T) return -1;
+    polar_ctx c = {B, T, Hq, Hkv, D, q, k, v,
+                   {temp_raw, null_slope_raw, null_bias, mag_beta, v_null, eps},
+                   rows, nrows, mode, block, nsplit, o, mu, meff, neff};
+    run_tasks(polar_task, &c, (long)B * nrows * Hq, nthreads);
+    return 0;
+}
+
+/* Decode: one query per (b, h) against cache slots 0..cache_len-1 (the newest token is
+ * already in slot cache_len-1), i.e. the last row of the causal forward with n = cache_len.
+ *   q [B, Hq, D];  k_cache, v_cache [B, Lmax, Hkv, D];  o [B, Hq, D];  mu, meff, neff [B, Hq]. */
+typedef struct {
+    int B, Hq, Hkv, D; long cache_len, Lmax;
+    const double *q, *kc, *vc; polar_par P;
+    double *o, *mu, *meff, *neff;
+} polar_dec_ctx;
+
+static void polar_dec_task(long task, void* p) {
+    const polar_dec_ctx* c = (const polar_dec_ctx*)p;
+    const int b = (int)(task / c->Hq), h = (int)(task % c->Hq);
+    const int hk = h / (c->Hq / c->Hkv), D = c->D;
+    const size_t stride = (size_t)c->Hkv * D;
+    const double* K = c->kc + ((size_t)b * c->Lmax * c->Hkv + hk) * D;
+    const double* V = c->vc + ((size_t)b * c->Lmax * c->Hkv + hk) * D;
+    double* w = (double*)malloc(sizeof(double) * (size_t)c->cache_len);
+    polar_row_materialised(c->q + ((size_t)b * c->Hq + h) * D, K, V, stride, stride, c->cache_len, D, h, &c->P,
+                           c->o + ((size_t)b * c->Hq + h) * D, c->mu + task, c->meff + task, c->neff + task, w);
+    free(w);
+}
+
+int oracle_polar_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax,
+                        const double* q, const double* k_cache, const double* v_cache,
+                        const double* temp_raw, const double* null_slope_raw, const double* null_bias,
+                        const double* mag_beta, const double* v_null, double eps,
+                        double* o, double* mu, double* meff, double* neff, int nthreads) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv || cache_len < 1 || cache_len > Lmax) return -1;
+    if (!q || !k_cache || !v_cache || !temp_raw || !null_slope_raw || !null_bias || !mag_beta || !v_null) return -1;
+    if (!o || !mu || !meff || !neff) return -1;
+    polar_dec_ctx c = {B, Hq, Hkv, D, cache_len, Lmax, q, k_cache, v_cache,
+                       {temp_raw, null_slope_raw, null_bias, mag_beta, v_null, eps}, o, mu, meff, neff};
+    run_tasks(polar_dec_task, &c, (long)B * Hq, nthreads);
+    return 0;
+}

@@ -1,0 +1,60 @@
+"""The oracle pins are strong enough to catch plausible mistakes in the oracle.
+
+Each case copies ``oracle/oracle.c``, plants one mistake by text substitution, builds
+the copy with gcc in a temporary directory, and runs the oracle pin tests against it
+(``ATMA_ORACLE_LIB`` points the wrapper at the copy).  Every mutant must fail at least
+one pin.  CPU only; the real oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "gdn_erase_sign": ("S[r * Dk + j] - be * u[r] * kt[j]", "S[r * Dk + j] + be * u[r] * kt[j]"),
+    "gdn_decay_first_term_only": ("a * (S[r * Dk + j] - be * u[r] * kt[j])", "(a * S[r * Dk + j] - be * u[r] * kt[j])"),
+    "gdn_write_transposed": ("+ be * vt[r] * kt[j]", "+ be * vt[j % Dv] * kt[r % Dk]"),
+    "gdn_output_from_old_key": ("for (int j = 0; j < Dk; ++j) s += S[r * Dk + j] * qt[j];",
+                                "for (int j = 0; j < Dk; ++j) s += S[r * Dk + j] * kt[j];"),
+    "gdn_chunk_decay_sign": ("val = c->beta[TOK(t0 + r)] * exp(g[r] - g[s]) * d;",
+                             "val = c->beta[TOK(t0 + r)] * exp(g[s] - g[r]) * d;"),
+    "polar_temp_log2": ("const double t = 1.0 + a * log((double)n);                          /* Section 3.2: t_i */",
+                        "const double t = 1.0 + a * log2((double)n);"),
+    "polar_n_off_by_one": ("const double nu = P->null_bias[h] + s * sqrt(log((double)n + 1.0)); /* Section 3.2: nu_i */",
+                           "const double nu = P->null_bias[h] + s * sqrt(log((double)n + 2.0));"),
+    "polar_null_without_temperature": ("const double lnull = t * nu;                                        /* virtual null logit */",
+                                       "const double lnull = nu;"),
+    "polar_no_sqrt_d": ("w[j] = t * d * inv_sqrt_d;", "w[j] = t * d;"),
+    "polar_neff_linear": ("const double ne = R * R / Q2;", "const double ne = R / Q2;"),
+    "polar_meff_no_mass": ("const double me = ne * R;", "const double me = ne;"),
+    "polar_mu_log": ("const double muv = tanh(P->mag_beta[h] * log1p(me));\n    /* direction",
+                     "const double muv = tanh(P->mag_beta[h] * log(me));\n    /* direction"),
+    "polar_drop_null_value": ("double acc = wnull * P->v_null[(size_t)h * D + x];", "double acc = 0.0;"),
+    "polar_no_normalise": ("for (int x = 0; x < D; ++x) o[x] = muv * (o[x] / den);\n    *mu = muv; *meff = me; *neff = ne;\n}\n\n/* Streaming",
+                           "for (int x = 0; x < D; ++x) o[x] = muv * o[x];\n    *mu = muv; *meff = me; *neff = ne;\n}\n\n/* Streaming"),
+    "polar_causal_off_by_one": ("polar_row_materialised(qi, K, V, stride, stride, i + 1,",
+                                "polar_row_materialised(qi, K, V, stride, stride, (i + 2 <= c->T ? i + 2 : i + 1),"),
+    "streaming_q2_rho_linear": ("L *= rho; Q2 *= rho * rho;", "L *= rho; Q2 *= rho;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-D_POSIX_C_SOURCE=200809L", "-shared", "-o", str(lib),
+                    str(mutated), "-lm", "-lpthread"], check=True)
+    env = dict(os.environ, ATMA_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_gdn.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_polar.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
