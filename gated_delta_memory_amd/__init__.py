@@ -1,0 +1,236 @@
+"""Python binding of libatma, the MI355X (gfx950) hot path of the ATMA global layer.
+
+Thin argument marshalling over the C ABI declared in ``include/atma.h``: every function
+here has the name of the C entry point it calls, checks tensor shapes/dtypes/devices,
+allocates outputs when the caller passes none, and hands raw device pointers and the
+current HIP stream to the library.  All arithmetic runs in the library's HIP kernels;
+there is no CPU or PyTorch fallback.  Importing this module fails with a clear error
+if the library has not been built (``python -m gated_delta_memory_amd._build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch  # loads the HIP runtime the library shares (same soname, one instance)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libatma.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "atma.h")
+
+ATMA_OK, ATMA_ERR_NULL, ATMA_ERR_SHAPE, ATMA_ERR_UNSUPPORTED, ATMA_ERR_WORKSPACE, ATMA_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
+ATMA_F32, ATMA_BF16 = 0, 1
+CHUNK = 64
+
+
+class AtmaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class PolarParams(ctypes.Structure):
+    """Mirror of ``atma_polar_params`` (host struct of device pointers)."""
+    _fields_ = [("temp_raw", ctypes.c_void_p), ("null_slope_raw", ctypes.c_void_p),
+                ("null_bias", ctypes.c_void_p), ("mag_beta", ctypes.c_void_p),
+                ("v_null", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libatma.so is not built at {LIB_PATH}; run `python -m gated_delta_memory_amd._build` "
+                          f"(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    P = ctypes.POINTER(PolarParams)
+    sig = {
+        "atma_gdn_fwd": ([vp] * 8 + [i] * 7 + [vp, sz, vp], i),
+        "atma_gdn_fwd_workspace_bytes": ([i] * 7, sz),
+        "atma_gdn_decode_step": ([vp] * 7 + [i] * 5 + [vp], i),
+        "atma_polar_attn_fwd": ([vp, vp, vp, P, vp, vp, vp] + [i] * 6 + [vp, sz, vp], i),
+        "atma_polar_attn_workspace_bytes": ([i] * 4, sz),
+        "atma_polar_attn_decode": ([vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
+        "atma_polar_attn_decode_workspace_bytes": ([i] * 4, sz),
+        "atma_status_string": ([i], ctypes.c_char_p),
+        "atma_version": ([], i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def header_functions() -> list[str]:
+    """Names of every function declared in include/atma.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\**\s+\**(atma_[a-z0-9_]+)\s*\(", text, re.M)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != ATMA_OK:
+        raise AtmaError(fn, status, lib.atma_status_string(status).decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATMA_BF16
+    if t.dtype == torch.float32:
+        return ATMA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+
+
+# ------------------------------------------------------------------------------------
+# gated-delta memory
+# ------------------------------------------------------------------------------------
+def atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk=CHUNK, dtype=torch.bfloat16) -> int:
+    return int(lib.atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk,
+                                                ATMA_BF16 if dtype == torch.bfloat16 else ATMA_F32))
+
+
+def atma_gdn_fwd(q, k, v, alpha, beta, init_state=None, *, o=None, final_state=None, workspace=None,
+                 want_final=True, stream=None):
+    """Chunked gated-delta forward.  q, k [B,T,H,Dk], v [B,T,H,Dv] (bf16 or fp32), alpha, beta
+    [B,T,H] fp32, init_state [B,H,Dv,Dk] fp32 or None.  Returns (o, final_state or None)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or alpha.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    _f32(alpha, "alpha"), _f32(beta, "beta"), _f32(init_state, "init_state")
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=q.dtype, device=q.device)
+    if final_state is None and want_final:
+        final_state = torch.empty(B, H, Dv, Dk, dtype=torch.float32, device=q.device)
+    need = atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, CHUNK, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, alpha, beta, init_state, o, final_state, workspace)
+    st = lib.atma_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(init_state), _ptr(o),
+                          _ptr(final_state), B, T, H, Dk, Dv, CHUNK, _dtype_code(q), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("atma_gdn_fwd", st)
+    return o, final_state
+
+
+def atma_gdn_decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """One recurrent step: q, k [B,H,Dk], v [B,H,Dv], alpha, beta [B,H] fp32, state [B,H,Dv,Dk]
+    fp32 (updated in place).  Returns o [B,H,Dv]."""
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if state.shape != (B, H, Dv, Dk):
+        raise ValueError("state shape mismatch")
+    _f32(alpha, "alpha"), _f32(beta, "beta"), _f32(state, "state")
+    if o is None:
+        o = torch.empty(B, H, Dv, dtype=q.dtype, device=q.device)
+    _dev(q, k, v, alpha, beta, state, o)
+    st = lib.atma_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+                                  B, H, Dk, Dv, _dtype_code(q), _stream(stream))
+    _check("atma_gdn_decode_step", st)
+    return o
+
+
+# ------------------------------------------------------------------------------------
+# Polar attention
+# ------------------------------------------------------------------------------------
+def polar_params_struct(params: dict) -> PolarParams:
+    """Pack a dict of per-head fp32 device tensors (temp_raw, null_slope_raw, null_bias,
+    mag_beta [Hq]; v_null [Hq, D]; eps float) into the C struct."""
+    for name in ("temp_raw", "null_slope_raw", "null_bias", "mag_beta", "v_null"):
+        t = params[name]
+        _dev(t)
+        _f32(t, name)
+    return PolarParams(params["temp_raw"].data_ptr(), params["null_slope_raw"].data_ptr(),
+                       params["null_bias"].data_ptr(), params["mag_beta"].data_ptr(),
+                       params["v_null"].data_ptr(), float(params.get("eps", 1e-12)))
+
+
+def atma_polar_attn_fwd(q, k, v, params, *, o=None, mu_out=None, meff_out=None, want_mu=False, stream=None):
+    """Causal Polar attention.  q [B,T,Hq,D], k, v [B,T,Hkv,D] bf16.  Returns (o, mu, meff)
+    (mu / meff are [B,Hq,T] fp32 when requested or passed in, else None)."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    if o is None:
+        o = torch.empty_like(q)
+    if want_mu and mu_out is None:
+        mu_out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    if want_mu and meff_out is None:
+        meff_out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _dev(q, k, v, o, mu_out, meff_out)
+    p = polar_params_struct(params)
+    st = lib.atma_polar_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(o), _ptr(mu_out),
+                                 _ptr(meff_out), B, T, Hq, Hkv, D, _dtype_code(q), None, 0, _stream(stream))
+    _check("atma_polar_attn_fwd", st)
+    return o, mu_out, meff_out
+
+
+def atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D=64) -> int:
+    return int(lib.atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D))
+
+
+def atma_polar_attn_decode(q, k_cache, v_cache, cache_len, params, *, o=None, mu_out=None, want_mu=False,
+                           workspace=None, stream=None):
+    """Decode one token.  q [B,Hq,D]; caches [B,Lmax,Hkv,D] bf16 holding cache_len valid slots
+    (the new token already written at slot cache_len-1).  Returns (o [B,Hq,D], mu [B,Hq] or None)."""
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Lmax, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("inconsistent cache shapes")
+    if o is None:
+        o = torch.empty_like(q)
+    if want_mu and mu_out is None:
+        mu_out = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    need = atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k_cache, v_cache, o, mu_out, workspace)
+    p = polar_params_struct(params)
+    st = lib.atma_polar_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len), Lmax, ctypes.byref(p),
+                                    _ptr(o), _ptr(mu_out), B, Hq, Hkv, D, _dtype_code(q), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("atma_polar_attn_decode", st)
+    return o, mu_out
+
+
+def atma_polar_attn_workspace_bytes(B, T, Hq, D=64) -> int:
+    return int(lib.atma_polar_attn_workspace_bytes(B, T, Hq, D))
+
+
+def atma_status_string(status: int) -> str:
+    return lib.atma_status_string(int(status)).decode()
+
+
+def atma_version() -> int:
+    return int(lib.atma_version())

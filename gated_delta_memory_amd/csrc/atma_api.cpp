@@ -1,0 +1,134 @@
+// C-ABI layer of libatma: host-side validation, then kernel launches on the caller's
+// stream.  Every check happens before the first HIP call, so a rejected call has no side
+// effect on the device.  No allocation, no synchronisation, no exceptions cross the ABI.
+#include "../../include/atma.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+bool pos(int x) { return x >= 1; }
+bool head_width_ok(int d) { return d == 64 || d == 128; }
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const int64_t ab = a * b;
+    if (ab > kMaxElems) return false;
+    const int64_t abc = ab * c;
+    if (abc > kMaxElems) return false;
+    return abc * d <= kMaxElems;
+}
+int launched(hipError_t e) { return e == hipSuccess ? ATMA_OK : ATMA_ERR_LAUNCH; }
+
+int check_params(const atma_polar_params* p) {
+    if (!p || !p->temp_raw || !p->null_slope_raw || !p->null_bias || !p->mag_beta || !p->v_null)
+        return ATMA_ERR_NULL;
+    if (!(p->eps >= 0.0f) || !std::isfinite(p->eps)) return ATMA_ERR_SHAPE;
+    return ATMA_OK;
+}
+
+atma::PolarParamsDev dev_params(const atma_polar_params* p) {
+    return {p->temp_raw, p->null_slope_raw, p->null_bias, p->mag_beta, p->v_null, p->eps};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* atma_status_string(int status) {
+    switch (status) {
+        case ATMA_OK: return "ok";
+        case ATMA_ERR_NULL: return "a required pointer is NULL";
+        case ATMA_ERR_SHAPE: return "invalid or inconsistent size";
+        case ATMA_ERR_UNSUPPORTED: return "unsupported head width, chunk or dtype";
+        case ATMA_ERR_WORKSPACE: return "workspace missing or too small";
+        case ATMA_ERR_LAUNCH: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int atma_version(void) { return 100; }
+
+size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt) {
+    if (!pos(B) || !pos(T) || !pos(H) || !head_width_ok(Dk) || !head_width_ok(Dv) || chunk != 64) return 0;
+    if (dt != ATMA_BF16 && dt != ATMA_F32) return 0;
+    return atma::gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, dt == ATMA_BF16);
+}
+
+int atma_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                 const float* init_state, void* o, float* final_state, int B, int T, int H, int Dk, int Dv,
+                 int chunk, atma_dtype dt, void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !alpha || !beta || !o) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(T) || !pos(H) || !pos(Dk) || !pos(Dv) || !pos(chunk)) return ATMA_ERR_SHAPE;
+    if (!head_width_ok(Dk) || !head_width_ok(Dv) || chunk != 64) return ATMA_ERR_UNSUPPORTED;
+    if (dt != ATMA_BF16 && dt != ATMA_F32) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, Dk > Dv ? Dk : Dv) || !fits(B, H, Dv, Dk)) return ATMA_ERR_SHAPE;
+    if (H > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    const size_t need = atma::gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, dt == ATMA_BF16);
+    if (!workspace || ws_bytes < need) return ATMA_ERR_WORKSPACE;
+    atma::GdnFwdArgs a{q, k, v, alpha, beta, init_state, o, final_state, B, T, H, Dk, Dv, dt == ATMA_BF16,
+                       workspace};
+    return launched(atma::launch_gdn_fwd(a, (hipStream_t)stream));
+}
+
+int atma_gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                         float* state, void* o, int B, int H, int Dk, int Dv, atma_dtype dt, void* stream) {
+    if (!q || !k || !v || !alpha || !beta || !state || !o) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(H) || !pos(Dk) || !pos(Dv)) return ATMA_ERR_SHAPE;
+    if (!head_width_ok(Dk) || !head_width_ok(Dv)) return ATMA_ERR_UNSUPPORTED;
+    if (dt != ATMA_BF16 && dt != ATMA_F32) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, H, Dv, Dk)) return ATMA_ERR_SHAPE;
+    if (H > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    atma::GdnDecodeArgs a{q, k, v, alpha, beta, state, o, B, H, Dk, Dv, dt == ATMA_BF16};
+    return launched(atma::launch_gdn_decode(a, (hipStream_t)stream));
+}
+
+size_t atma_polar_attn_workspace_bytes(int B, int T, int Hq, int D) {
+    (void)B; (void)T; (void)Hq; (void)D;
+    return 0;
+}
+
+int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_polar_params* p, void* o,
+                        float* mu_out, float* meff_out, int B, int T, int Hq, int Hkv, int D, atma_dtype dt,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    (void)workspace; (void)ws_bytes;
+    if (!q || !k || !v || !o) return ATMA_ERR_NULL;
+    const int pc = check_params(p);
+    if (pc != ATMA_OK) return pc;
+    if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D)) return ATMA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if (D != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, Hq, D) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    atma::PolarFwdArgs a{q, k, v, dev_params(p), o, mu_out, meff_out, B, T, Hq, Hkv, D};
+    return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
+}
+
+size_t atma_polar_attn_decode_workspace_bytes(int B, int Hq, int cache_len, int D) {
+    if (!pos(B) || !pos(Hq) || !pos(cache_len) || D != 64) return 0;
+    return atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);
+}
+
+int atma_polar_attn_decode(const void* q, const void* k_cache, const void* v_cache, int cache_len, int Lmax,
+                           const atma_polar_params* p, void* o, float* mu_out, int B, int Hq, int Hkv, int D,
+                           atma_dtype dt, void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !o) return ATMA_ERR_NULL;
+    const int pc = check_params(p);
+    if (pc != ATMA_OK) return pc;
+    if (!pos(B) || !pos(Hq) || !pos(Hkv) || !pos(D) || !pos(cache_len) || !pos(Lmax)) return ATMA_ERR_SHAPE;
+    if (cache_len > Lmax || Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if (D != 64 || dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv)) return ATMA_ERR_UNSUPPORTED;
+    // the cache may exceed 2^31 elements in total (offsets are 64-bit); one sequence may not
+    if (!fits(Lmax, Hkv, D, 1) || !fits(B, Hq, D, 1) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    const size_t need = atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);
+    if (!workspace || ws_bytes < need) return ATMA_ERR_WORKSPACE;
+    atma::PolarDecodeArgs a{q, k_cache, v_cache, dev_params(p), o, mu_out, cache_len, Lmax, B, Hq, Hkv, D,
+                            workspace};
+    return launched(atma::launch_polar_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

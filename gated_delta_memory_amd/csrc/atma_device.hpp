@@ -1,0 +1,117 @@
+// Device-side building blocks shared by the libatma kernels (gfx950 only).
+//
+// MFMA tiles used here are 16x16 outputs.  For one 16x16 tile the accumulator (C/D
+// operand, 4 fp32 per lane) holds element (row 4*G + v, col l % 16) in register v of
+// lane l, where G = l / 16 is the lane group.  An A or B operand "fragment" covers a
+// 32-wide slice of the reduction index: lane l supplies 8 values for row (A) or column
+// (B) l % 16 at reduction offsets kmap(G, e), e = 0..7:
+//     kmap(G, e) = 4G + e            for e < 4
+//                = 16 + 4G + (e - 4) for e >= 4
+// The hardware pairs lane-group/slot positions of A and B, so any bijection works as
+// long as both operands use it; this one makes two vertically stacked accumulator tiles
+// (rows 0-15 and 16-31 of a 32-row block) directly usable as a B fragment without any
+// data movement.
+//   bf16: one v_mfma_f32_16x16x32_bf16 consumes the 8 values (slot 8G + e <-> kmap(G, e)).
+//   fp32: eight v_mfma_f32_16x16x4_f32, the e-th consuming value e of every lane group.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atma {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ constexpr int kmap(int G, int e) { return e < 4 ? 4 * G + e : 12 + 4 * G + e; }
+
+// ---- conversions ---------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// exp2 / log2 on the hardware transcendental unit (ulp-level accurate for normal inputs).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- fragments -------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (bf16)x; }
+    __device__ __forceinline__ void set_raw(int e, bf16 x) { v[e] = x; }
+};
+template <> struct Frag<float> {
+    float v[8];
+    __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+    __device__ __forceinline__ void set_raw(int e, float x) { v[e] = x; }
+};
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// Fragment of a row-major matrix M (leading dimension ld, in elements) whose row for
+// this lane is `row` and whose 32-wide reduction block starts at column k0: the lane
+// reads M[row][k0 + kmap(G, e)] as two contiguous runs of 4.
+__device__ __forceinline__ void load_frag_rows(Frag<bf16>& f, const bf16* M, int ld, int row, int k0) {
+    const int G = lane_id() >> 4;
+    const bf16* p = M + (size_t)row * ld + k0 + 4 * G;
+    bf16x4 lo = *(const bf16x4*)p;
+    bf16x4 hi = *(const bf16x4*)(p + 16);
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void load_frag_rows(Frag<float>& f, const float* M, int ld, int row, int k0) {
+    const int G = lane_id() >> 4;
+    const float* p = M + (size_t)row * ld + k0 + 4 * G;
+    f32x4 lo = *(const f32x4*)p;
+    f32x4 hi = *(const f32x4*)(p + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[e + 4] = hi[e]; }
+}
+// Fragment read down a column: the lane reads M[k0 + kmap(G, e)][col].
+template <typename T>
+__device__ __forceinline__ void load_frag_cols(Frag<T>& f, const T* M, int ld, int col, int k0) {
+    const int G = lane_id() >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.set_raw(e, M[(size_t)(k0 + kmap(G, e)) * ld + col]);
+}
+
+// Two vertically stacked accumulator tiles (reduction rows 0-15 and 16-31) as a B fragment.
+template <typename T>
+__device__ __forceinline__ void acc_to_frag(Frag<T>& f, const f32x4& top, const f32x4& bottom) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.set(e, top[e]); f.set(e + 4, bottom[e]); }
+}
+
+// ---- wave reductions ---------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+}  // namespace atma

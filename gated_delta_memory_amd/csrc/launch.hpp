@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI layer (atma_api.cpp) and the kernel files.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace atma {
+
+struct GdnFwdArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta, *init_state;
+    void* o;
+    float* final_state;
+    int B, T, H, Dk, Dv;
+    bool bf16_io;
+    void* workspace;
+};
+size_t gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16_io);
+hipError_t launch_gdn_fwd(const GdnFwdArgs& a, hipStream_t stream);
+
+struct GdnDecodeArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    float* state;
+    void* o;
+    int B, H, Dk, Dv;
+    bool bf16_io;
+};
+hipError_t launch_gdn_decode(const GdnDecodeArgs& a, hipStream_t stream);
+
+struct PolarParamsDev {
+    const float *temp_raw, *null_slope_raw, *null_bias, *mag_beta, *v_null;
+    float eps;
+};
+
+struct PolarFwdArgs {
+    const void *q, *k, *v;
+    PolarParamsDev p;
+    void* o;
+    float *mu_out, *meff_out;
+    int B, T, Hq, Hkv, D;
+};
+hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream);
+
+struct PolarDecodeArgs {
+    const void *q, *k_cache, *v_cache;
+    PolarParamsDev p;
+    void* o;
+    float* mu_out;
+    int cache_len, Lmax, B, Hq, Hkv, D;
+    void* workspace;
+};
+size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
+// Head layouts the decode kernels have code for: Hkv in {1,2,4,8,16,32}, Hq/Hkv in {1,2,4,8}.
+bool polar_decode_supported(int Hq, int Hkv);
+hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream);
+
+// Sets the dynamic-LDS limit of a kernel once per process.
+template <typename K>
+inline hipError_t ensure_lds_limit(K kernel, size_t bytes) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace atma

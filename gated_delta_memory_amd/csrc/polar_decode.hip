@@ -1,0 +1,232 @@
+// Polar attention, one decode step, for gfx950 (bf16 KV cache, head width 64).
+//
+// The decode query is the last causal row: n = cache_len real keys, temperature
+// t = 1 + softplus(alpha) ln n and null floor nu = b + softplus(gamma) sqrt(ln(n + 1))
+// (ATMA paper, Section 3.2 equation), one softmax over the real logits t q.k_j / sqrt(D) and
+// the null logit t nu (Appendix C.2), channels of Appendix A.2.
+//
+// Split-KV: the cache is cut into contiguous token ranges.  polar_decode_partial streams one
+// range for all heads of one sequence (each token's K and V rows for all kv heads are one
+// contiguous 2*Hkv*D-byte run, read with 16-byte loads) and keeps, per query head, the
+// streaming statistics of Appendix C.3 / Table 6: running maximum M of the real logits,
+// L = sum p, Q2 = sum p^2 and Sv = sum p v.  Those four statistics of two disjoint key
+// ranges combine exactly:  M = max(M_a, M_b), r_x = e^{M_x - M},
+//     L = r_a L_a + r_b L_b,  Q2 = r_a^2 Q2_a + r_b^2 Q2_b,  Sv = r_a Sv_a + r_b Sv_b,
+// so polar_decode_combine merges the ranges per (sequence, head) and finalises with the
+// null sink exactly as the prefill kernel does.  Exponentials are base 2 on logits scaled
+// by log2(e).
+#include "atma_device.hpp"
+#include "launch.hpp"
+
+namespace atma {
+namespace {
+
+constexpr int D = 64;
+constexpr int NT = 256;
+constexpr int REC = 68;     // floats per partial record: M, L, Q2, pad, Sv[64]
+constexpr int UNROLL = 4;   // tokens in flight per thread
+
+__device__ __forceinline__ float softplus(float x) { return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
+
+int num_splits(int B, int cache_len) {
+    const int by_len = (cache_len + 127) / 128;
+    const int target = 1024 / B > 0 ? 1024 / B : 1;
+    int n = by_len < target ? by_len : target;
+    return n < 1 ? 1 : n;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4& r, float* f) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        f[2 * x] = __uint_as_float(r[x] << 16);
+        f[2 * x + 1] = __uint_as_float(r[x] & 0xffff0000u);
+    }
+}
+
+// grid (nsplit, B); block 256.  Thread = (token slot, kv head, 8-wide dim chunk).
+template <int GQ>
+__global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restrict__ q, const bf16* __restrict__ kc,
+                                                           const bf16* __restrict__ vc, PolarParamsDev prm,
+                                                           float* __restrict__ ws, int cache_len, int Lmax,
+                                                           int Hkv) {
+    const int split = blockIdx.x, nsplit = gridDim.x, b = blockIdx.y;
+    const int Hq = Hkv * GQ;
+    const int tpt = Hkv * 8;                 // threads per token
+    const int slots = NT / tpt;              // tokens per pass
+    const int slot = threadIdx.x / tpt;
+    const int hk = (threadIdx.x % tpt) >> 3, chunk = threadIdx.x & 7;
+    const int t_begin = (int)((long)cache_len * split / nsplit);
+    const int t_end = (int)((long)cache_len * (split + 1) / nsplit);
+
+    const float lnn = logf((float)cache_len);
+    float qv[GQ][8], cq[GQ], m[GQ], L[GQ], Q2[GQ], sv[GQ][8];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+        const int h = hk * GQ + g;
+        const float t = 1.0f + softplus(prm.temp_raw[h]) * lnn;
+        cq[g] = t * kLog2e * 0.125f;
+        const u32x4 r = *(const u32x4*)(q + ((size_t)b * Hq + h) * D + chunk * 8);
+        unpack8(r, qv[g]);
+        m[g] = -INFINITY; L[g] = 0.f; Q2[g] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sv[g][x] = 0.f;
+    }
+    const size_t tstride = (size_t)Hkv * D;
+    const bf16* kb = kc + (size_t)b * Lmax * tstride + (size_t)hk * D + chunk * 8;
+    const bf16* vb = vc + (size_t)b * Lmax * tstride + (size_t)hk * D + chunk * 8;
+
+    for (int t0 = t_begin + slot; t0 < t_end; t0 += slots * UNROLL) {
+        u32x4 kr[UNROLL], vr[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int t = t0 + u * slots;
+            if (t < t_end) {
+                kr[u] = *(const u32x4*)(kb + (size_t)t * tstride);
+                vr[u] = *(const u32x4*)(vb + (size_t)t * tstride);
+            } else {
+                kr[u] = u32x4{0u, 0u, 0u, 0u};
+                vr[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) {
+            float lg[UNROLL];
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                float kf[8];
+                unpack8(kr[u], kf);
+                float d = 0.f;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) d += qv[g][x] * kf[x];
+                d += __shfl_xor(d, 4, 8);
+                d += __shfl_xor(d, 2, 8);
+                d += __shfl_xor(d, 1, 8);
+                lg[u] = (t0 + u * slots < t_end) ? d * cq[g] : -INFINITY;
+                bmax = fmaxf(bmax, lg[u]);
+            }
+            const float mnew = fmaxf(m[g], bmax);
+            const float rho = fast_exp2(m[g] - mnew);
+            m[g] = mnew;
+            L[g] *= rho;
+            Q2[g] *= rho * rho;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) sv[g][x] *= rho;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const float p = fast_exp2(lg[u] - mnew);
+                L[g] += p;
+                Q2[g] += p * p;
+                float vf[8];
+                unpack8(vr[u], vf);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) sv[g][x] += p * vf[x];
+            }
+        }
+    }
+
+    // merge the token slots of this workgroup through LDS, then write one record per head
+    __shared__ float part[NT / 8][3];  // per (slot, kv head): M, L, Q2 (written by chunk 0)
+    __shared__ float psv[NT][8];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+        if (chunk == 0) {
+            part[threadIdx.x >> 3][0] = m[g];
+            part[threadIdx.x >> 3][1] = L[g];
+            part[threadIdx.x >> 3][2] = Q2[g];
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) psv[threadIdx.x][x] = sv[g][x];
+        __syncthreads();
+        if (slot == 0) {
+            float M = -INFINITY;
+            for (int s = 0; s < slots; ++s) M = fmaxf(M, part[(s * tpt + threadIdx.x) >> 3][0]);
+            float LL = 0.f, QQ = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int s = 0; s < slots; ++s) {
+                const float* ps = part[(s * tpt + threadIdx.x) >> 3];
+                const float r = (ps[0] == -INFINITY) ? 0.0f : fast_exp2(ps[0] - M);
+                LL += r * ps[1];
+                QQ += r * r * ps[2];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) acc[x] += r * psv[s * tpt + threadIdx.x][x];
+            }
+            const int h = hk * GQ + g;
+            float* rec = ws + (((size_t)b * nsplit + split) * Hq + h) * REC;
+            if (chunk == 0) *(f32x4*)rec = f32x4{M, LL, QQ, 0.f};
+            *(f32x4*)(rec + 4 + chunk * 8) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            *(f32x4*)(rec + 8 + chunk * 8) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        }
+        __syncthreads();
+    }
+}
+
+// grid (Hq, B); block 64: lane d owns value dimension d.
+__global__ __launch_bounds__(64) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
+                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
+                                                           int nsplit, int cache_len) {
+    const int h = blockIdx.x, Hq = gridDim.x, b = blockIdx.y;
+    const int d = threadIdx.x;
+    const float* base = ws + ((size_t)b * nsplit * Hq + h) * REC;
+    const size_t step = (size_t)Hq * REC;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * step]);
+    float L = 0.f, Q2 = 0.f, Sv = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float* r = base + s * step;
+        const float e = (r[0] == -INFINITY) ? 0.0f : fast_exp2(r[0] - M);
+        L += e * r[1];
+        Q2 += e * e * r[2];
+        Sv += e * r[4 + d];
+    }
+    const float n = (float)cache_len;
+    const float t = 1.0f + softplus(prm.temp_raw[h]) * logf(n);
+    const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf(n + 1.0f));
+    const float lnull = t * nu * kLog2e;
+    const float Ms = fmaxf(M, lnull);
+    const float pn = fast_exp2(lnull - Ms);
+    const float f = fast_exp2(M - Ms);
+    const float Ls = L * f;
+    const float Z = Ls + pn;
+    const float neff = L * L / Q2;
+    const float meff = neff * (Ls / Z);
+    const float xarg = prm.mag_beta[h] * log1pf(meff);
+    const float em = expf(-2.0f * xarg);
+    const float mu = (1.0f - em) / (1.0f + em);
+    const float s = (Sv * f + pn * prm.v_null[h * D + d]) / Z;
+    const float nrm = sqrtf(wave_sum(s * s));
+    o[((size_t)b * Hq + h) * D + d] = (bf16)(s * mu / fmaxf(nrm, prm.eps));
+    if (d == 0 && mu_out) mu_out[(size_t)b * Hq + h] = mu;
+}
+
+}  // namespace
+
+size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int Dh) {
+    (void)Dh;
+    return (size_t)B * num_splits(B, cache_len) * Hq * REC * sizeof(float);
+}
+
+hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
+    const int nsplit = num_splits(a.B, a.cache_len);
+    const int gq = a.Hq / a.Hkv;
+    float* ws = (float*)a.workspace;
+#define ATMA_PD_CASE(G)                                                                                    \
+    if (gq == G) {                                                                                         \
+        hipLaunchKernelGGL(polar_decode_partial<G>, dim3(nsplit, a.B), dim3(NT), 0, stream, (const bf16*)a.q, \
+                           (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.p, ws, a.cache_len, a.Lmax,   \
+                           a.Hkv);                                                                         \
+    } else
+    ATMA_PD_CASE(1) ATMA_PD_CASE(2) ATMA_PD_CASE(4) ATMA_PD_CASE(8) { return hipErrorInvalidValue; }
+#undef ATMA_PD_CASE
+    hipLaunchKernelGGL(polar_decode_combine, dim3(a.Hq, a.B), dim3(64), 0, stream, (const float*)ws, a.p,
+                       (bf16*)a.o, a.mu_out, nsplit, a.cache_len);
+    return hipGetLastError();
+}
+
+bool polar_decode_supported(int Hq, int Hkv) {
+    const int gq = Hq / Hkv;
+    const bool g_ok = gq == 1 || gq == 2 || gq == 4 || gq == 8;
+    const bool h_ok = Hkv == 1 || Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16 || Hkv == 32;
+    return g_ok && h_ok;
+}
+
+}  // namespace atma

@@ -1,0 +1,263 @@
+// Causal Polar attention, prefill, for gfx950 (bf16 in/out, head width 64).
+//
+// Definitions (ATMA paper): temperature t_i = 1 + softplus(alpha) ln n_i and null floor
+// nu_i = b + softplus(gamma) sqrt(ln(n_i + 1)) (Section 3.2 equation), with n_i = i + 1 real
+// keys visible to query i; one softmax over the real logits t_i q_i.k_j / sqrt(D) and the
+// virtual null logit t_i nu_i (Appendix C.2); direction c_i = s_i / max(||s_i||, eps) and
+// magnitude mu_i = tanh(beta ln(1 + m_eff)) (Appendix A.2); o_i = mu_i c_i.
+// Streaming form (Appendix C.3, Table 6): per query row keep an origin M for the real
+// logits, L = sum p, Q2 = sum p^2 and Sv = sum p v with p = exp(logit - M); moving the
+// origin by delta scales the three sums by exp(-delta), exp(-2 delta) and exp(-delta).  The
+// null enters once, at the end, with the common origin M* = max(M, null logit):
+//     p_null = e^{l_null - M*},  L* = L e^{M - M*},  Z = L* + p_null,  n_eff = L^2 / Q2,
+//     m_eff = n_eff L* / Z,  s = (Sv e^{M - M*} + p_null v_null) / Z.
+// Every formula is invariant to the choice of origin, so M is moved only when a block's
+// maximum exceeds it by more than 8 (base-2 units): p <= 2^8 keeps every sum far from
+// overflow and most blocks skip the rescale.  Exponentials are base 2 on logits scaled
+// by log2(e).
+//
+// Kernel layout (one workgroup of 4 waves per 128-query tile, head and batch; each wave
+// owns 32 consecutive queries):
+//   * keys stream in blocks of 64 through one LDS buffer (K and V row-major, 16-byte
+//     chunks XOR-swizzled by key so fragment reads are bank-conflict free); the next block
+//     is fetched into registers while the current one is used;
+//   * scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: a lane holds
+//     16 keys of one query column, so row statistics are per-lane partial sums (the two
+//     lanes that share a query are combined with v_permlane32_swap);
+//   * the same registers, cast to bf16, are the B operand of O^T = V^T P^T; the V^T
+//     fragments come straight from the row-major V tile with ds_read_b64_tr_b16;
+//   * L and Q2 are accumulated from the bf16 weights with v_dot2_f32_bf16, so they use
+//     exactly the weights the value sum uses;
+//   * query tiles are scheduled heaviest (last) first for causal load balance.
+#include "atma_device.hpp"
+#include "launch.hpp"
+
+namespace atma {
+namespace {
+
+constexpr int D = 64;
+constexpr int NT = 256;
+constexpr int BQ = 128;  // queries per workgroup
+constexpr int QW = 32;   // queries per wave
+constexpr int BK = 64;   // keys per block
+constexpr float kLazy = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ float softplus(float x) { return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// byte offset of 16-byte chunk c (0..7) of key row `key` in a swizzled 64x64 bf16 tile
+__device__ __forceinline__ int swz(int key, int c) { return key * 128 + ((c ^ (key & 7)) << 4); }
+
+// partner-lane (l ^ 32) combine via v_permlane32_swap
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x4 tr_read(const char* lds_base, int byte_off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_base + byte_off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                          const bf16* __restrict__ v, PolarParamsDev prm,
+                                                          bf16* __restrict__ o, float* __restrict__ mu_out,
+                                                          float* __restrict__ meff_out, int T, int Hq, int Hkv) {
+    __shared__ __align__(16) char Ks[BK * D * 2];
+    __shared__ __align__(16) char Vs[BK * D * 2];
+    const int nqt = (T + BQ - 1) / BQ;
+    const int qt = nqt - 1 - (int)blockIdx.x;  // heaviest tiles first
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int hk = h / (Hq / Hkv);
+    const int lane = lane_id(), w = wave_id();
+    const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+    const int q0 = qt * BQ;
+    const int qw0 = q0 + w * QW;
+    const int qi = qw0 + l32;  // this lane's query
+
+    const float a_t = softplus(prm.temp_raw[h]);
+    const float cq = (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * 0.125f;  // t_i log2(e) / sqrt(64)
+
+    // Q^T fragments (B operand): lane supplies Q[qi][16 ks + 8 G2 + e]
+    const size_t qstride = (size_t)Hq * D;
+    bf16x8 qf[4];
+    {
+        const int qc = min(qi, T - 1);
+        const bf16* qrow = q + ((size_t)b * T + qc) * qstride + (size_t)h * D + 8 * G2;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
+    }
+
+    f32x16 oacc[2] = {f32x16{}, f32x16{}};  // O^T[d = 32 dt + 8(x/4) + 4 G2 + x%4][qi]
+    float m_used = -INFINITY, lsum = 0.f, q2sum = 0.f;
+
+    const int kend = min(T, q0 + BQ);
+    const int nkb = (kend + BK - 1) / BK;
+    const size_t kvstride = (size_t)Hkv * D;
+    const bf16* kbase = k + (size_t)b * T * kvstride + (size_t)hk * D;
+    const bf16* vbase = v + (size_t)b * T * kvstride + (size_t)hk * D;
+    const int ld_key = threadIdx.x >> 3, ld_c = threadIdx.x & 7;
+    u32x4 kreg[2], vreg[2];
+    auto fetch = [&](int kb) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int key = min(kb * BK + ld_key + 32 * r, T - 1);  // rows past T are masked later
+            kreg[r] = *(const u32x4*)(kbase + (size_t)key * kvstride + ld_c * 8);
+            vreg[r] = *(const u32x4*)(vbase + (size_t)key * kvstride + ld_c * 8);
+        }
+    };
+    fetch(0);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        __syncthreads();  // previous block fully consumed
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int off = swz(ld_key + 32 * r, ld_c);
+            *(u32x4*)(Ks + off) = kreg[r];
+            *(u32x4*)(Vs + off) = vreg[r];
+        }
+        __syncthreads();
+        if (kb + 1 < nkb) fetch(kb + 1);
+
+        const int key0 = kb * BK;
+        if (key0 > qw0 + QW - 1) continue;  // whole block in this wave's future
+        const bool edge = (key0 + BK - 1 > qw0) || (key0 + BK > T);
+
+        // S^T = K Q^T : two 32-key sub-tiles
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key = 32 * kt + l32;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 af = *(const bf16x8*)(Ks + swz(key, 2 * ks + G2));
+                s[kt] = mfma32(af, qf[ks], s[kt]);
+            }
+        }
+        // causal / length mask on edge blocks (raw scores; cq > 0 scales them later)
+        if (edge) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int key = key0 + 32 * kt + 8 * (x >> 2) + 4 * G2 + (x & 3);
+                    if (key > qi || key >= T) s[kt][x] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[kt][x]);
+        mx = pair_max(mx) * cq;
+        // lazy origin move (wave-uniform branch)
+        const bool move = mx > m_used + kLazy;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float mnew = move ? mx : m_used;
+            const float rho = fast_exp2(m_used - mnew);
+            m_used = mnew;
+            lsum *= rho;
+            q2sum *= rho * rho;
+            oacc[0] *= rho;
+            oacc[1] *= rho;
+        }
+        // weights, their sums, and O^T += V^T P^T
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                bf16x8 pf;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float p0 = fast_exp2(fmaf(s[kt][8 * st + e], cq, -m_used));
+                    const float p1 = fast_exp2(fmaf(s[kt][8 * st + e + 1], cq, -m_used));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
+                    q2sum = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, q2sum, false);
+                    pf[e] = pp[0];
+                    pf[e + 1] = pp[1];
+                }
+                const int kk = 32 * kt + 16 * st + 4 * G2;  // key of slot e = 0 for this lane group
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const int dcol = 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3);
+                    const int key_a = kk + (i16 >> 2), key_b = key_a + 8;
+                    const bf16x4 lo = tr_read(Vs, swz(key_a, dcol >> 3) + ((dcol & 7) << 1));
+                    const bf16x4 hi = tr_read(Vs, swz(key_b, dcol >> 3) + ((dcol & 7) << 1));
+                    const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[dt] = mfma32(vf, pf, oacc[dt]);
+                }
+            }
+        }
+    }
+
+    // ---- finalise: null merge, channels, output ------------------------------------------------
+    const float L = pair_sum(lsum);
+    const float Q2 = pair_sum(q2sum);
+    const float n = (float)(qi + 1);
+    const float t = 1.0f + a_t * logf(n);
+    const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf(n + 1.0f));
+    const float lnull = t * nu * kLog2e;
+    const float Ms = fmaxf(m_used, lnull);
+    const float pn = fast_exp2(lnull - Ms);
+    const float f = fast_exp2(m_used - Ms);
+    const float Ls = L * f;
+    const float Z = Ls + pn;
+    const float neff = L * L / Q2;
+    const float meff = neff * (Ls / Z);
+    const float xarg = prm.mag_beta[h] * log1pf(meff);
+    const float em = expf(-2.0f * xarg);
+    const float mu = (1.0f - em) / (1.0f + em);
+    const float invZ = 1.0f / Z;
+    float nrm2 = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int d = 32 * dt + 8 * (x >> 2) + 4 * G2 + (x & 3);
+            const float sv = (oacc[dt][x] * f + pn * prm.v_null[h * D + d]) * invZ;
+            oacc[dt][x] = sv;
+            nrm2 += sv * sv;
+        }
+    nrm2 = pair_sum(nrm2);
+    const float scale = mu / fmaxf(sqrtf(nrm2), prm.eps);
+    if (qi < T) {
+        bf16* orow = o + ((size_t)b * T + qi) * qstride + (size_t)h * D;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 y;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) y[x] = (bf16)(oacc[dt][4 * g + x] * scale);
+                *(bf16x4*)(orow + 32 * dt + 8 * g + 4 * G2) = y;
+            }
+        if (G2 == 0) {
+            const size_t si = ((size_t)b * Hq + h) * T + qi;
+            if (mu_out) mu_out[si] = mu;
+            if (meff_out) meff_out[si] = meff;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
+    const int nqt = (a.T + BQ - 1) / BQ;
+    hipLaunchKernelGGL(polar_fwd_kernel, dim3(nqt, a.Hq, a.B), dim3(NT), 0, stream, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
+                       a.Hkv);
+    return hipGetLastError();
+}
+
+}  // namespace atma

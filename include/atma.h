@@ -1,0 +1,151 @@
+/*
+ * atma.h - C ABI of libatma, the MI355X (gfx950) hot path of the ATMA hybrid global
+ * layer: gated-delta compression memory and causal Polar attention, prefill and decode.
+ *
+ * Source of every definition: "ATMA: Long-Context Language Modeling via Polar Attention
+ * and Gated-Delta Compression Memory" (arXiv 2606.25156).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or retains them.  Arrays are dense and row-major with the last
+ *    index fastest.  `stream` is a hipStream_t (NULL = the default stream).
+ *  - Calls are asynchronous on `stream`: the library performs no host synchronisation,
+ *    no allocation and keeps no state between calls (thread-safe; concurrent calls on
+ *    different streams must use different workspaces).
+ *  - Every argument is validated on the host BEFORE anything is launched; a call that
+ *    returns an error has launched nothing.  After the launches a failed
+ *    hipGetLastError() returns ATMA_ERR_LAUNCH.  No C++ exception crosses the ABI.
+ *  - Supported shapes: memory head widths Dk, Dv in {64, 128} (fp32 or bf16); Polar
+ *    head width D = 64 (bf16); chunk = 64; Hq a multiple of Hkv; every size >= 1;
+ *    B * T * H * D below 2^31 for every prefill tensor; a decode KV cache may exceed
+ *    2^31 elements in total but Lmax * Hkv * D must stay below 2^31.
+ *  - Preconditions that are documented but not checked (they live on the device):
+ *    memory q and k rows have unit L2 norm (Appendix A.2 premise); alpha in (0, 1];
+ *    beta in [0, 1]; mag_beta >= 0.  Violating them gives defined but meaningless
+ *    numbers, never out-of-bounds accesses.
+ *  - Numerics: bf16 operands with fp32 accumulation and fp32 statistics; the memory
+ *    state is fp32 in HBM and in registers.  Outputs are written in the input dtype.
+ */
+#ifndef ATMA_H
+#define ATMA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATMA_OK = 0,
+    ATMA_ERR_NULL = -1,        /* a required pointer is NULL                                  */
+    ATMA_ERR_SHAPE = -2,       /* a size is < 1, inconsistent, or too large                   */
+    ATMA_ERR_UNSUPPORTED = -3, /* a head width, chunk or dtype this build has no kernel for   */
+    ATMA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the matching *_workspace_bytes */
+    ATMA_ERR_LAUNCH = -5       /* the HIP runtime reported an error after launch              */
+} atma_status;
+
+typedef enum { ATMA_F32 = 0, ATMA_BF16 = 1 } atma_dtype;
+
+/* Per-head Polar parameters (host struct holding DEVICE pointers, all fp32).
+ *   temp_raw[Hq]       : alpha of Section 3.2; temperature t_i = 1 + softplus(temp_raw) ln n_i
+ *   null_slope_raw[Hq] : gamma of Section 3.2; null floor nu_i = null_bias + softplus(gamma) sqrt(ln(n_i + 1))
+ *   null_bias[Hq]      : b of Section 3.2 (Appendix A.1 assumes b >= 0; not required)
+ *   mag_beta[Hq]       : beta of Appendix A.2; magnitude mu_i = tanh(mag_beta ln(1 + m_eff,i))
+ *   v_null[Hq * D]     : value of the virtual null sink (Appendix C.3: it joins the direction numerator with the null weight)
+ *   eps                : clamp of the direction normaliser max(||s_i||, eps) (Appendix A.2)
+ * n_i is the number of real keys query i may see (i + 1 in prefill, cache_len in decode). */
+typedef struct {
+    const float* temp_raw;
+    const float* null_slope_raw;
+    const float* null_bias;
+    const float* mag_beta;
+    const float* v_null;
+    float eps;
+} atma_polar_params;
+
+/* ---------------------------------------------------------------------------------
+ * Gated-delta memory, chunked prefill (Section 3.3 equation):
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ * with the paper's gamma_t written alpha_t, M_t written S_t and r_t written o_t.
+ * Evaluated exactly (up to rounding) in chunks of `chunk` tokens.
+ *
+ *   q, k        [B, T, H, Dk]  dtype `dt`  (unit-norm rows; no 1/sqrt(D) is applied)
+ *   v           [B, T, H, Dv]  dtype `dt`
+ *   alpha, beta [B, T, H]      fp32
+ *   init_state  [B, H, Dv, Dk] fp32, or NULL for a zero initial state
+ *   o           [B, T, H, Dv]  dtype `dt`  (output)
+ *   final_state [B, H, Dv, Dk] fp32 (output), or NULL; may alias init_state
+ *   Dk, Dv in {64, 128}; chunk == 64; dt == ATMA_BF16 or ATMA_F32.
+ *   workspace   device buffer of at least atma_gdn_fwd_workspace_bytes(...) bytes,
+ *               contents ignored on entry and undefined on exit.
+ * ------------------------------------------------------------------------------- */
+int atma_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                 const float* init_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                 int Dv, int chunk, atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
+
+size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt);
+
+/* ---------------------------------------------------------------------------------
+ * Gated-delta memory, one decode step (the same equation for a single token):
+ *     S <- alpha (S - beta (S k) k^T) + beta v k^T ;  o = S q
+ *   q, k   [B, H, Dk] dtype `dt`;  v [B, H, Dv] dtype `dt`;  alpha, beta [B, H] fp32
+ *   state  [B, H, Dv, Dk] fp32, updated in place;  o [B, H, Dv] dtype `dt` (output)
+ * No workspace.  The recurrent state has a fixed size, so decode cost does not depend
+ * on the context length (Appendix H.1).
+ * ------------------------------------------------------------------------------- */
+int atma_gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, float* state, void* o, int B, int H, int Dk, int Dv,
+                         atma_dtype dt, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Causal Polar attention, prefill (Section 3.2 equation; Appendix A.2 channels;
+ * Appendix C.2 single softmax over real logits plus one virtual null logit; streamed
+ * with the running statistics of Appendix C.3, Table 6).  For query i (0-based) of
+ * head h, with kv head h / (Hq / Hkv), n = i + 1:
+ *     t = 1 + softplus(temp_raw) ln n,   nu = null_bias + softplus(null_slope_raw) sqrt(ln(n+1))
+ *     real logits  l_j = t (q_i . k_j) / sqrt(D), j = 0..i;   null logit  l_0 = t nu
+ *     w = softmax over {l_j} U {l_0};  R = sum_j w_j;  n_eff = R^2 / sum_j w_j^2
+ *     m_eff = n_eff R;  mu = tanh(mag_beta ln(1 + m_eff))
+ *     s = sum_j w_j v_j + w_0 v_null;  c = s / max(||s||, eps);  o_i = mu c
+ *   q        [B, T, Hq, D]  dtype `dt`;  k, v [B, T, Hkv, D] dtype `dt`
+ *   o        [B, T, Hq, D]  dtype `dt` (output)
+ *   mu_out   [B, Hq, T] fp32 (output) or NULL;  meff_out [B, Hq, T] fp32 or NULL
+ *   D == 64 and dt == ATMA_BF16; workspace may be NULL when
+ *   atma_polar_attn_workspace_bytes returns 0 (it does for this build).
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_polar_params* p,
+                        void* o, float* mu_out, float* meff_out, int B, int T, int Hq, int Hkv, int D,
+                        atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
+
+size_t atma_polar_attn_workspace_bytes(int B, int T, int Hq, int D);
+
+/* ---------------------------------------------------------------------------------
+ * Polar attention, one decode step: the last causal row for a KV cache.
+ *   q        [B, Hq, D] dtype `dt`
+ *   k_cache, v_cache [B, Lmax, Hkv, D] dtype `dt`; slots 0..cache_len-1 are valid and the
+ *            caller has already written the new token's k, v into slot cache_len-1.
+ *   n = cache_len in the formulas above (1 <= cache_len <= Lmax).
+ *   D == 64, dt == ATMA_BF16, Hkv in {1, 2, 4, 8, 16, 32} and Hq / Hkv in {1, 2, 4, 8}.
+ *   o        [B, Hq, D] dtype `dt` (output);  mu_out [B, Hq] fp32 or NULL
+ *   workspace at least atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D) bytes
+ *            (per split of the cache: running max, real mass, squared mass and value sum).
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_decode(const void* q, const void* k_cache, const void* v_cache, int cache_len,
+                           int Lmax, const atma_polar_params* p, void* o, float* mu_out, int B, int Hq,
+                           int Hkv, int D, atma_dtype dt, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+size_t atma_polar_attn_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* atma_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int atma_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATMA_H */

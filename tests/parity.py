@@ -1,0 +1,66 @@
+"""Shared helpers for GPU-vs-oracle parity tests.
+
+Error metric: max |x_gpu - x_oracle| / rms(x_oracle), compared element by element on the
+same seeded inputs.  Budgets: 2e-2 for bf16 inputs, 1e-4 for fp32.
+
+Outputs stored in bf16 carry one more unavoidable error: the cast of each element to bf16
+(relative half-ulp 2^-9, one ulp 2^-8).  Where single elements are several times larger
+than the RMS (Polar rows concentrated on a few keys), that cast alone exceeds 2e-2 of the
+RMS even for the exact result, so bf16-typed outputs are scored with ``rel_err_bf16``:
+the same metric after allowing each element one bf16 ulp of its own magnitude.
+"""
+import sys
+
+import numpy as np
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def to_np(t):
+    t = t.detach().cpu()
+    if str(t.dtype) in ("torch.bfloat16", "torch.float16"):
+        t = t.float()
+    return t.double().numpy()
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if rms == 0:
+        return float(np.max(np.abs(got)))
+    return float(np.max(np.abs(got - ref)) / rms)
+
+
+def rel_err_bf16(got, ref) -> float:
+    """max(|got - ref| - 2^-8 |ref|, 0) / rms(ref): the RMS budget on top of the output cast."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    rms = np.sqrt(np.mean(ref ** 2))
+    excess = np.maximum(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref), 0.0)
+    return float(np.max(excess) / rms) if rms > 0 else float(np.max(excess))
+
+
+def out_err(got, ref, dtype: str) -> float:
+    """Metric for an output tensor written in ``dtype``."""
+    return rel_err_bf16(got, ref) if dtype == "bf16" else rel_err(got, ref)
+
+
+def note(msg: str) -> None:
+    """Print and flush progress so a GPU run names the case it is on."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def sample_rows(T: int, seed: int = 0, n_random: int = 24, tile: int = 256, chunk: int = 64):
+    """Query rows to check at long lengths: first and last rows, rows on both sides of
+    query-tile and key-block boundaries, and seeded random rows."""
+    rows = set(range(min(T, 8))) | set(range(max(0, T - 8), T))
+    for b in (tile, chunk):
+        for x in range(b, T, max(b, T // 6 // b * b or b)):
+            rows.update({x - 1, x})
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, T, size=n_random).tolist())
+    return sorted(r for r in rows if 0 <= r < T)

@@ -1,0 +1,125 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function declared in
+include/atma.h, sizes its workspaces, and rejects bad arguments on the host before
+launching anything (these calls never reach a kernel, so no GPU is needed)."""
+import ctypes
+
+import pytest
+
+g = pytest.importorskip("gated_delta_memory_amd")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+NULL = None
+
+
+def test_every_declared_symbol_is_exported():
+    names = g.header_functions()
+    assert len(names) >= 9
+    missing = [n for n in names if not hasattr(g.lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert g.atma_status_string(s)
+    assert g.atma_status_string(42) == "unknown status"
+    assert g.atma_version() >= 100
+
+
+def test_workspace_queries():
+    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, g.ATMA_F32) > 0
+    # bf16 records are smaller than fp32 ones; a ragged tail still gets a full chunk record
+    a = g.lib.atma_gdn_fwd_workspace_bytes(2, 100, 3, 128, 128, 64, g.ATMA_BF16)
+    b = g.lib.atma_gdn_fwd_workspace_bytes(2, 128, 3, 128, 128, 64, g.ATMA_BF16)
+    assert a == b > 0
+    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, g.ATMA_BF16) == 0  # unsupported width
+    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 64, 64, 32, g.ATMA_BF16) == 0  # unsupported chunk
+    assert g.lib.atma_polar_attn_workspace_bytes(1, 1024, 16, 64) == 0
+    assert g.lib.atma_polar_attn_decode_workspace_bytes(1, 16, 262144, 64) > 0
+    assert g.lib.atma_polar_attn_decode_workspace_bytes(1, 16, 0, 64) == 0
+
+
+def _gdn(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, init=NULL, o=FAKE, fin=NULL, B=1, T=8, H=1, Dk=64, Dv=64,
+             chunk=64, dt=g.ATMA_BF16, ws=FAKE, wsb=1, stream=NULL)
+    a.update(over)
+    return g.lib.atma_gdn_fwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["init"], a["o"], a["fin"], a["B"],
+                              a["T"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_gdn_fwd_validation():
+    assert _gdn(q=NULL) == g.ATMA_ERR_NULL
+    assert _gdn(o=NULL) == g.ATMA_ERR_NULL
+    assert _gdn(T=0) == g.ATMA_ERR_SHAPE
+    assert _gdn(B=-1) == g.ATMA_ERR_SHAPE
+    assert _gdn(Dk=96) == g.ATMA_ERR_UNSUPPORTED
+    assert _gdn(chunk=32) == g.ATMA_ERR_UNSUPPORTED
+    assert _gdn(dt=7) == g.ATMA_ERR_UNSUPPORTED
+    assert _gdn(B=70000, T=70000) == g.ATMA_ERR_SHAPE          # element count overflow
+    assert _gdn(ws=NULL) == g.ATMA_ERR_WORKSPACE
+    assert _gdn(wsb=1) == g.ATMA_ERR_WORKSPACE                  # too small
+    need = g.lib.atma_gdn_fwd_workspace_bytes(1, 8, 1, 64, 64, 64, g.ATMA_BF16)
+    assert _gdn(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
+
+
+def test_gdn_decode_validation():
+    f = g.lib.atma_gdn_decode_step
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 1, 8, 128, 128, g.ATMA_BF16, NULL) == g.ATMA_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 128, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 100, 128, g.ATMA_BF16, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 128, 3, NULL) == g.ATMA_ERR_UNSUPPORTED
+
+
+def _params(**over):
+    p = dict(temp_raw=0x1000, null_slope_raw=0x1000, null_bias=0x1000, mag_beta=0x1000, v_null=0x1000, eps=1e-12)
+    p.update(over)
+    return g.PolarParams(**p)
+
+
+def _pfwd(p=None, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, mu=NULL, meff=NULL, B=1, T=16, Hq=4, Hkv=2, D=64, dt=g.ATMA_BF16)
+    a.update(over)
+    pp = ctypes.byref(p if p is not None else _params()) if p is not False else None
+    return g.lib.atma_polar_attn_fwd(a["q"], a["k"], a["v"], pp, a["o"], a["mu"], a["meff"], a["B"], a["T"], a["Hq"],
+                                     a["Hkv"], a["D"], a["dt"], NULL, 0, NULL)
+
+
+def test_polar_fwd_validation():
+    assert _pfwd(q=NULL) == g.ATMA_ERR_NULL
+    assert _pfwd(p=False) == g.ATMA_ERR_NULL
+    assert _pfwd(p=_params(v_null=None)) == g.ATMA_ERR_NULL
+    assert _pfwd(p=_params(eps=-1.0)) == g.ATMA_ERR_SHAPE
+    assert _pfwd(p=_params(eps=float("nan"))) == g.ATMA_ERR_SHAPE
+    assert _pfwd(T=0) == g.ATMA_ERR_SHAPE
+    assert _pfwd(Hq=3, Hkv=2) == g.ATMA_ERR_SHAPE
+    assert _pfwd(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pfwd(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
+
+
+def _pdec(p=None, **over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, L=10, Lmax=16, o=FAKE, mu=NULL, B=1, Hq=16, Hkv=16, D=64, dt=g.ATMA_BF16,
+             ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    pp = ctypes.byref(p if p is not None else _params())
+    return g.lib.atma_polar_attn_decode(a["q"], a["kc"], a["vc"], a["L"], a["Lmax"], pp, a["o"], a["mu"], a["B"],
+                                        a["Hq"], a["Hkv"], a["D"], a["dt"], a["ws"], a["wsb"], NULL)
+
+
+def test_polar_decode_validation():
+    assert _pdec(kc=NULL) == g.ATMA_ERR_NULL
+    assert _pdec(L=0) == g.ATMA_ERR_SHAPE
+    assert _pdec(L=17) == g.ATMA_ERR_SHAPE            # cache_len > Lmax
+    assert _pdec(Hq=16, Hkv=3) == g.ATMA_ERR_SHAPE
+    assert _pdec(Hq=48, Hkv=3) == g.ATMA_ERR_UNSUPPORTED   # head layout without a kernel
+    assert _pdec(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pdec(ws=NULL) == g.ATMA_ERR_WORKSPACE
+    assert _pdec(wsb=16) == g.ATMA_ERR_WORKSPACE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    a = torch.ones(1, 8, 1)
+    with pytest.raises((ValueError, RuntimeError)):
+        g.atma_gdn_fwd(q, q, q, a, a, workspace=torch.zeros(1, dtype=torch.uint8), o=q.clone(),
+                       final_state=torch.zeros(1, 1, 64, 64))

@@ -1,0 +1,125 @@
+"""GPU parity of the Polar attention entry points against the fp64 oracle.
+
+Prefill: every row at small sizes; at the long workloads a seeded sample of rows
+(first and last rows, rows around every 256-query tile and 64-key block boundary,
+random rows), which the oracle computes one by one (rows are independent).
+Decode: the last causal row for a KV cache, against the oracle and against the
+prefill kernel's last row.  Error = max |gpu - oracle| / rms(oracle) <= 2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import TOL, note, out_err, rel_err, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def atma():
+    import gated_delta_memory_amd as g
+
+    assert torch.cuda.is_available()
+    return g
+
+
+def _cpu_params(p):
+    return {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in p.items()}
+
+
+def _dev_params(p):
+    return {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+
+
+def _check_prefill(atma, inp, rows=None, tag=""):
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    o, mu, meff = atma.atma_polar_attn_fwd(q, k, v, _dev_params(inp["params"]), want_mu=True)
+    torch.cuda.synchronize()
+    ref = oracle.polar_fwd(inp["q"], inp["k"], inp["v"], _cpu_params(inp["params"]), rows=rows)
+    idx = slice(None) if rows is None else rows
+    go = to_np(o)[:, idx]
+    gmu = to_np(mu).transpose(0, 2, 1)[:, idx]      # [B,T,Hq] like the oracle
+    gme = to_np(meff).transpose(0, 2, 1)[:, idx]
+    eo, emu, eme = out_err(go, ref["o"], "bf16"), rel_err(gmu, ref["mu"]), rel_err(gme, ref["meff"])
+    note(f"  polar {tag} err_o={eo:.3e} err_mu={emu:.3e} err_meff={eme:.3e}")
+    assert eo <= TOL["bf16"] and emu <= TOL["bf16"] and eme <= TOL["bf16"], (eo, emu, eme)
+    # bounded channels on the GPU output: 0 <= mu <= 1 and ||o|| = mu (direction has unit norm)
+    assert np.all(gmu >= 0) and np.all(gmu <= 1)
+    np.testing.assert_allclose(np.linalg.norm(go, axis=-1), gmu, rtol=2e-2, atol=2e-3)
+    return o, mu
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 1, 1, 1), (1, 77, 2, 2), (2, 300, 4, 2), (1, 513, 3, 1),
+                                        (1, 256, 2, 2), (2, 64, 8, 8)])
+def test_polar_small_all_rows(atma, B, T, Hq, Hkv):
+    inp = workloads.make_polar_inputs(B, T, Hq, Hkv, 64, seed=T + Hq)
+    _check_prefill(atma, inp, tag=f"B{B} T{T} Hq{Hq} Hkv{Hkv}")
+
+
+def test_polar_layer_b8_t2k(atma):
+    """378M-class layer at 2K: B=8, T=2048, Hq=16, d=64 (sampled rows)."""
+    inp = workloads.make_workload("layer_b8_t2k")["polar"]
+    _check_prefill(atma, inp, rows=sample_rows(2048), tag="layer_b8_t2k")
+
+
+def test_polar_prefill_b2_t16k_needle(atma):
+    w = workloads.WORKLOADS["prefill_b2_t16k_needle"]
+    inp = workloads.make_polar_inputs(w.B, w.T, w.polar_Hq, w.polar_Hkv, w.polar_D, needle_frac=w.needle_frac,
+                                      seed=w.seed)
+    _check_prefill(atma, inp, rows=sample_rows(w.T, n_random=12), tag="b2_t16k_needle")
+
+
+def test_polar_prefill_b1_t64k(atma):
+    w = workloads.WORKLOADS["prefill_b1_t64k"]
+    inp = workloads.make_polar_inputs(w.B, w.T, w.polar_Hq, w.polar_Hkv, w.polar_D, seed=w.seed)
+    _check_prefill(atma, inp, rows=sample_rows(w.T, n_random=8), tag="b1_t64k")
+
+
+def test_polar_deterministic(atma):
+    inp = workloads.make_polar_inputs(2, 700, 4, 4, 64, seed=9)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    p = _dev_params(inp["params"])
+    o1, _, _ = atma.atma_polar_attn_fwd(q, k, v, p)
+    o2, _, _ = atma.atma_polar_attn_fwd(q, k, v, p)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("B,L,Lmax,Hq,Hkv", [(1, 1, 1, 16, 16), (2, 1000, 1200, 16, 16), (3, 5000, 5000, 8, 2),
+                                             (1, 129, 4096, 4, 4), (16, 2048, 2048, 16, 16)])
+def test_polar_decode(atma, B, L, Lmax, Hq, Hkv):
+    inp = workloads.make_decode_inputs(B, L, Hq=Hq, Hkv=Hkv, Lmax=Lmax, seed=L)
+    o, mu = atma.atma_polar_attn_decode(inp["q"].cuda(), inp["k_cache"].cuda(), inp["v_cache"].cuda(), L,
+                                        _dev_params(inp["params"]), want_mu=True)
+    torch.cuda.synchronize()
+    ref = oracle.polar_decode(inp["q"], inp["k_cache"], inp["v_cache"], L, _cpu_params(inp["params"]))
+    eo, emu = out_err(to_np(o), ref["o"], "bf16"), rel_err(to_np(mu), ref["mu"])
+    note(f"  polar decode B{B} L{L} Hq{Hq} Hkv{Hkv} err_o={eo:.3e} err_mu={emu:.3e}")
+    assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
+
+
+def test_polar_decode_equals_prefill_last_row(atma):
+    B, T, H = 2, 1500, 4
+    inp = workloads.make_polar_inputs(B, T, H, H, 64, seed=21)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    p = _dev_params(inp["params"])
+    o, mu, _ = atma.atma_polar_attn_fwd(q, k, v, p, want_mu=True)
+    od, mud = atma.atma_polar_attn_decode(q[:, T - 1].contiguous(), k, v, T, p, want_mu=True)
+    torch.cuda.synchronize()
+    assert out_err(to_np(od), to_np(o[:, T - 1]), "bf16") <= TOL["bf16"]
+    assert rel_err(to_np(mud), to_np(mu[:, :, T - 1])) <= TOL["bf16"]
+
+
+def test_polar_decode_262k_context(atma):
+    """Evaluation-length decode: one query against a 262144-token cache, B=1, Hq=Hkv=16."""
+    L = workloads.DECODE_CONTEXT
+    inp = workloads.make_decode_inputs(1, L, device="cuda", seed=0)
+    o, mu = atma.atma_polar_attn_decode(inp["q"], inp["k_cache"], inp["v_cache"], L, inp["params"], want_mu=True)
+    torch.cuda.synchronize()
+    ref = oracle.polar_decode(inp["q"].cpu(), inp["k_cache"].cpu(), inp["v_cache"].cpu(), L,
+                              _cpu_params(inp["params"]))
+    eo, emu = out_err(to_np(o), ref["o"], "bf16"), rel_err(to_np(mu), ref["mu"])
+    note(f"  polar decode 262k err_o={eo:.3e} err_mu={emu:.3e}")
+    assert eo <= TOL["bf16"] and emu <= TOL["bf16"]

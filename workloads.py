@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs shaped like the ATMA paper's workloads.
+"""Seeded synthetic inputs shaped like the ATMA paper's workloads (shared by tests and benchmark).
 
 This module only draws random tensors and lays them out; it holds none of the
 method's arithmetic.  Both the HIP path (through the tests and the benchmark) and
