@@ -20,6 +20,9 @@
 namespace atma {
 
 typedef __bf16 bf16;
+typedef _Float16 half;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -55,6 +58,11 @@ template <> struct Frag<bf16> {
     __device__ __forceinline__ void set(int e, float x) { v[e] = (bf16)x; }
     __device__ __forceinline__ void set_raw(int e, bf16 x) { v[e] = x; }
 };
+template <> struct Frag<half> {
+    f16x8 v;
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (half)x; }
+    __device__ __forceinline__ void set_raw(int e, half x) { v[e] = x; }
+};
 template <> struct Frag<float> {
     float v[8];
     __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
@@ -63,6 +71,9 @@ template <> struct Frag<float> {
 
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<half>& a, const Frag<half>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
 #pragma unroll
@@ -100,6 +111,34 @@ template <typename T>
 __device__ __forceinline__ void acc_to_frag(Frag<T>& f, const f32x4& top, const f32x4& bottom) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { f.set(e, top[e]); f.set(e + 4, bottom[e]); }
+}
+
+// ---- LDS transpose reads and swizzled 16-bit tiles ------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address of a 4-element
+// (8-byte) row r_j; lane i receives element (i mod 4) of rows r_{4e + i/4}, e = 0..3.  With
+// lane j pointing at M[r0 + j/4][c0 + 4 (j mod 4)], lane i receives M[r0 + e][c0 + i].
+__device__ __forceinline__ s16x4 tr_read_b16(const char* lds_byte_addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_byte_addr);
+}
+
+// Byte offset of 16-bit element (r, c) in a row-major tile with RB-byte rows whose
+// 16-byte chunks are XOR-swizzled by the row index (conflict-free column-slice reads).
+template <int RB>
+__device__ __host__ __forceinline__ constexpr int swz16(int r, int c) {
+    return r * RB + ((((c >> 3) ^ (r & ((RB >> 4) - 1 > 15 ? 15 : (RB >> 4) - 1)))) << 4) + ((c & 7) << 1);
+}
+
+// A or B fragment (kmap order) from a swizzled 16-bit tile: row `row`, reduction columns
+// k0 + kmap(G, e) -- two 8-byte reads.
+template <int RB>
+__device__ __forceinline__ f16x8 frag_swz_f16(const char* tile, int row, int k0) {
+    const int G = lane_id() >> 4;
+    const f16x4 lo = *(const f16x4*)(tile + swz16<RB>(row, k0 + 4 * G));
+    const f16x4 hi = *(const f16x4*)(tile + swz16<RB>(row, k0 + 16 + 4 * G));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // ---- wave reductions ---------------------------------------------------------------
