@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the ATMA global-layer hot path on one MI355X.
+
+One step = the gated-delta memory prefill plus the causal Polar attention prefill over
+one batch of the 378M-class layer at the 2K training length (B=8, T=2048; memory: 8 heads
+of width 128; Polar: 16 heads of width 64; bf16 operands, fp32 state and statistics),
+inputs resident in HBM.  Throughput = B*T tokens per step.
+
+Also reported (secondary, fewer steps): the 64K prefill and one decode step against a
+262144-token KV cache at batch 1 and 16 (Polar decode + memory decode step).
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec gated-delta+Polar fwd at T=2K/64K/256K; % MFMA or HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def polar_flops(B, T, Hq, D=64):
+    # QK^T and PV multiply-adds over the causal pairs (diagonal included), 2 flops each
+    return 4.0 * D * B * Hq * T * (T + 1) / 2
+
+
+def gdn_bytes(B, T, H, D=128, es=2):
+    # q, k, v read + o written (es bytes each) and alpha, beta (fp32) per token and head,
+    # plus the final fp32 state
+    return B * H * T * (4 * D * es + 8) + B * H * D * D * 4
+
+
+def decode_bytes(B, L, Hkv=16, D=64, H=8, Dg=128):
+    # K and V cache read once (bf16) + memory state read and written (fp32)
+    return 2 * B * L * Hkv * D * 2 + 2 * B * H * Dg * Dg * 4
+
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 64K prefill and 256K decode lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is "
+              "described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_memory_amd as atma
+    import workloads
+
+    dev = "cuda"
+    w = workloads.WORKLOADS["layer_b8_t2k"]
+    inp = workloads.make_workload(w, device=dev)
+    g, p = inp["gdn"], inp["polar"]
+    B, T = w.B, w.T
+    o_g = torch.empty_like(g["v"])
+    S_g = torch.empty(B, w.gdn_H, w.gdn_D, w.gdn_D, dtype=torch.float32, device=dev)
+    ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(B, T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
+                       device=dev)
+    o_p = torch.empty_like(p["q"])
+
+    def gdn():
+        atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], o=o_g, final_state=S_g, workspace=ws_g)
+
+    def polar():
+        atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p)
+
+    for _ in range(args.warmup):
+        gdn()
+        polar()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    tg, tp = Timer(torch), Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tg(gdn)
+        tp(polar)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    value = B * T * args.steps / elapsed
+    gdn_ms, polar_ms = tg.mean_ms(), tp.mean_ms()
+
+    pf = polar_flops(B, T, w.polar_Hq)
+    gb = gdn_bytes(B, T, w.gdn_H, w.gdn_D)
+    polar_tflops = pf / (polar_ms * 1e-3) / 1e12
+    gdn_gbs = gb / (gdn_ms * 1e-3) / 1e9
+    if polar_ms >= gdn_ms:
+        roofline = {"kernel": "polar_fwd_kernel", "bound": "mfma", "achieved": round(polar_tflops, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(polar_tflops / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None, "launch_ms": round(polar_ms, 4),
+                    "per_launch": f"{pf:.4e} flop = 4*64*B*Hq*T(T+1)/2, B={B} T={T} Hq={w.polar_Hq}"}
+    else:
+        roofline = {"kernel": "atma_gdn_fwd (prep+carry)", "bound": "hbm", "achieved": round(gdn_gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gdn_gbs / PEAK_HBM_GBS, 4),
+                    "traffic": None, "launch_ms": round(gdn_ms, 4),
+                    "per_launch": f"{gb:.4e} B = B*H*T*(4*D*2+8) + B*H*D*D*4"}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "gdn_heads": w.gdn_H, "gdn_head_dim": w.gdn_D,
+                   "polar_heads": w.polar_Hq, "polar_kv_heads": w.polar_Hkv, "polar_head_dim": w.polar_D,
+                   "chunk": w.chunk, "state": "fp32"},
+        "roofline": roofline,
+        "breakdown_ms": {"gdn_fwd": round(gdn_ms, 4), "polar_fwd": round(polar_ms, 4),
+                         "gdn_hbm_GBps": round(gdn_gbs, 1), "polar_TFLOPs": round(polar_tflops, 2)},
+    }
+    del inp, g, p, o_g, S_g, ws_g, o_p
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(torch, atma, workloads)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+def secondary(torch, atma, workloads):
+    res = {}
+    # 64K prefill
+    w = workloads.WORKLOADS["prefill_b1_t64k"]
+    inp = workloads.make_workload(w, device="cuda")
+    g, p = inp["gdn"], inp["polar"]
+    o_g = torch.empty_like(g["v"])
+    ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
+                       device="cuda")
+    S_g = torch.empty(w.B, w.gdn_H, w.gdn_D, w.gdn_D, device="cuda")
+    o_p = torch.empty_like(p["q"])
+    tg, tp = Timer(torch), Timer(torch)
+    for it in range(4):
+        (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
+                                                                  o=o_g, final_state=S_g, workspace=ws_g))
+        (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+    torch.cuda.synchronize()
+    gm, pm = tg.mean_ms(), tp.mean_ms()
+    pf = polar_flops(w.B, w.T, w.polar_Hq)
+    res[w.name] = {"tokens_per_s": round(w.B * w.T / ((gm + pm) * 1e-3), 1), "gdn_ms": round(gm, 3),
+                   "polar_ms": round(pm, 3), "polar_mfma_frac": round(pf / (pm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "gdn_hbm_frac": round(gdn_bytes(w.B, w.T, w.gdn_H) / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del inp, g, p, o_g, ws_g, S_g, o_p
+    torch.cuda.empty_cache()
+    # 256K decode, batch 1 and 16; two state / query buffers alternate so caches cannot serve them
+    L = workloads.DECODE_CONTEXT
+    for B in (1, 16):
+        d = workloads.make_decode_inputs(B, L, device="cuda")
+        ws = torch.empty(atma.atma_polar_attn_decode_workspace_bytes(B, 16, L), dtype=torch.uint8, device="cuda")
+        gd = d["gdn"]
+        states = [gd["state"].clone(), gd["state"].clone()]
+        qs = [d["q"], d["q"].clone()]
+        od = torch.empty_like(d["q"])
+        og = torch.empty(B, 8, 128, dtype=torch.bfloat16, device="cuda")
+        tpd, tgd = Timer(torch), Timer(torch)
+        for it in range(23):
+            i = it & 1
+            fp = lambda: atma.atma_polar_attn_decode(qs[i], d["k_cache"], d["v_cache"], L, d["params"], o=od,
+                                                     workspace=ws)
+            fg = lambda: atma.atma_gdn_decode_step(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], states[i],
+                                                   o=og)
+            if it < 3:
+                fp(), fg()
+            else:
+                tpd(fp)
+                tgd(fg)
+        torch.cuda.synchronize()
+        pm, gm = tpd.mean_ms(), tgd.mean_ms()
+        byts = decode_bytes(B, L)
+        res[f"decode_262k_b{B}"] = {"tokens_per_s": round(B / ((pm + gm) * 1e-3), 1), "polar_us": round(pm * 1e3, 1),
+                                    "gdn_us": round(gm * 1e3, 1),
+                                    "hbm_frac": round(byts / ((pm + gm) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del d, ws, states, qs, od, og
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w):
+    """The fp64 oracle, as it stands, on this host's cores: full memory recurrence and full causal
+    Polar attention for the workload's sequences (same shapes, same seed recipe)."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    nseq = w.B  # the whole batch: no extrapolation
+    inp = workloads.make_workload(w, device="cpu")
+    g, p = inp["gdn"], inp["polar"]
+    sl = slice(0, nseq)
+    gq, gk, gv, ga, gb = (g[x][sl] for x in ("q", "k", "v", "alpha", "beta"))
+    pq, pk, pv = (p[x][sl] for x in ("q", "k", "v"))
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.gdn_sequential(gq, gk, gv, ga, gb, threads=cores)
+    oracle.polar_fwd(pq, pk, pv, p["params"], threads=cores)
+    dt = time.perf_counter() - t0
+    used = max(oracle.threads_used(cores, nseq * w.gdn_H), oracle.threads_used(cores, nseq * w.T * w.polar_Hq))
+    del np
+    return {"value": round(nseq * w.T / dt, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{nseq} of {w.B} sequences of {w.name} (T={w.T}): full fp64 memory recurrence "
+                      f"({w.gdn_H} heads x d={w.gdn_D}) + full causal Polar attention ({w.polar_Hq} heads x d=64)"}
+
+
+if __name__ == "__main__":
+    main()
