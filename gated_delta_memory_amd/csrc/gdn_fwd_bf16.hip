@@ -1,0 +1,631 @@
+// Gated-delta memory, chunked prefill, bf16 inputs, for gfx950.
+//
+// Chunk algebra (exact rewrite of the ATMA paper's Section 3.3 recurrence, derivation in
+// gdn_fwd.hip): for a chunk of C = 64 tokens entering with state S_in,
+//     Delta = U - W S_in^T,  S_out^T = e^{g_last} S_in^T + KD^T Delta,
+//     O     = QG S_in^T + P Delta,
+// with W = Tinv diag(beta e^g) K, U = Tinv diag(beta) V, Tinv = (I + A)^{-1},
+// QG = diag(e^g) Q, KD = diag(e^{g_last - g}) K and P = lower_incl((Q K^T) o E).
+//
+// Three kernels; only the middle one is sequential along the sequence:
+//   gdn_prep_h  (parallel over chunks) - A, P, Tinv (fp32), W and U from an fp32-accurate
+//               hi/lo bf16 split of Tinv, QG and KD^T; writes them as fp16 tiles already in
+//               their consumers' MFMA-fragment order.
+//   gdn_carry_h (one workgroup per 64 state rows of a (batch, head), walks the chunks)
+//               keeps S^T in fp32 MFMA accumulators; per chunk it only forms Delta and the
+//               state update (32 MFMAs per wave), streaming W, KD^T and its U slice through
+//               three LDS stages with direct global->LDS copies issued two chunks ahead.
+//               It writes the fp16 operands it built anyway -- S_in^T and Delta, in MFMA
+//               fragment order -- for the output kernel.
+//   gdn_out_h   (parallel over chunks) - O = QG S_in^T + P Delta, coalesced bf16 stores.
+// fp16 staging (11-bit mantissa) keeps the result within a few 1e-3 of the fp64
+// recurrence; it needs |v| and the state entries below 2^15.
+#include "gdn_common.hpp"
+#include "launch.hpp"
+
+namespace atma {
+namespace {
+
+using gdn::C;
+using gdn::NT;
+using gdn::TileRegs;
+using gdn::copy_out;
+
+// ---- workspace layout ------------------------------------------------------------------
+// Per chunk, in separate arrays indexed by chunk id = (b H + h) NC + c:
+//   RA : W [C][DK] | KDT [DK][C] | U slices [DV/64] x 8 KB      (read by the carry kernel)
+//   RB : QG [C][DK] | P [C][C]                                   (read by the output kernel)
+// (W, KDT, QG and P fragment-major, U slices in the carry's accumulator order; see below)
+//   SF : S_in^T fragments [DV/64][DK/32][4 waves][64 lanes] x 16 B
+//   DF : Delta fragments  [DV/64][2][4 waves][64 lanes] x 16 B
+//   EGL: e^{g_last} (fp32)
+template <int DK, int DV> struct Lay {
+    static constexpr int RBK = DK * 2;  // bytes per W / QG row
+    static constexpr size_t A_W = 0;
+    static constexpr size_t A_KDT = A_W + (size_t)C * DK * 2;
+    static constexpr size_t A_U = A_KDT + (size_t)DK * C * 2;
+    static constexpr size_t USLICE = (size_t)C * 64 * 2;
+    static constexpr size_t RA = A_U + (size_t)(DV / 64) * USLICE;
+    static constexpr size_t B_QG = 0;
+    static constexpr size_t B_P = (size_t)C * DK * 2;
+    static constexpr size_t RB = B_P + (size_t)C * C * 2;
+    static constexpr size_t SF = (size_t)DV * DK * 2;
+    static constexpr size_t DF = (size_t)C * DV * 2;
+    static constexpr size_t STAGE = A_U + USLICE;  // bytes one carry workgroup streams per chunk
+    static size_t total(size_t nchunks) { return nchunks * (RA + RB + SF + DF + sizeof(float)); }
+};
+
+struct Regions {
+    char *ra, *rb, *sf, *df;
+    float* egl;
+};
+template <int DK, int DV>
+Regions regions(void* ws, size_t nchunks) {
+    using L = Lay<DK, DV>;
+    char* p = (char*)ws;
+    Regions r;
+    r.ra = p;
+    r.rb = r.ra + nchunks * L::RA;
+    r.sf = r.rb + nchunks * L::RB;
+    r.df = r.sf + nchunks * L::SF;
+    r.egl = (float*)(r.df + nchunks * L::DF);
+    return r;
+}
+
+// ---- fragment-major tiles -----------------------------------------------------------------
+// An R x K fp16 MFMA A-operand tile is stored as its fragments, [R/16][K/32][64 lanes][8]:
+// element (r, k) sits in fragment (r/16, k/32), lane (r mod 16) + 16 G, slot e, where
+// k mod 32 = kmap(G, e).  A consumer wave then loads each fragment with one 16-byte LDS read
+// per lane (a contiguous, conflict-free 1 KB), with no swizzle arithmetic or repacking.
+template <int K>
+__device__ __forceinline__ constexpr int fm_off(int r, int k) {  // byte offset of element (r, k)
+    const int kk = k & 31;
+    const int G = (kk & 15) >> 2;
+    const int e = (kk & 3) + ((kk >> 4) << 2);
+    return ((((r >> 4) * (K / 32) + (k >> 5)) * 64 + (r & 15) + 16 * G) * 8 + e) * 2;
+}
+template <int K>
+__device__ __forceinline__ f16x8 fm_frag(const char* tile, int rt, int kb) {
+    return *(const f16x8*)(tile + ((rt * (K / 32) + kb) * 64 + lane_id()) * 16);
+}
+// U slice for the carry kernel: [4 waves][4 row tiles][64 lanes] x 4 fp16, lane (l16 + 16 G)
+// of wave w holding U[16 i + 4 G + x][16 w + l16], x = 0..3 (its accumulator layout).
+__device__ __forceinline__ constexpr int u_off(int w, int i, int lane) { return ((w * 4 + i) * 64 + lane) * 8; }
+
+// =========================================================================================
+// prep
+// =========================================================================================
+template <int DK, int DV>
+struct PrepSmem {
+    static constexpr int LDK = DK + 8, LDX = (DK > DV ? DK : DV) + 8, LDA = C + 4;
+    bf16 Ks[C * LDK];
+    bf16 Xs[C * LDX];   // Q, later V
+    float Am[C * LDA];  // A, later the W staging tile
+    float Tm[C * LDA];  // P staging, then Tinv, then the U staging tile
+    float Gs[C];
+    float Bs[C];
+};
+
+// B fragment (kmap order over the chunk positions) of a row-major bf16 LDS tile, columns
+// 16 ct .. 16 ct + 15, by two transpose reads.
+__device__ __forceinline__ Frag<bf16> bfrag_tr(const bf16* tile, int ld, int ct, int kb) {
+    const int G = lane_id() >> 4, l16 = lane_id() & 15;
+    const char* base = (const char*)tile;
+    const int col = 16 * ct + 4 * (l16 & 3);
+    const s16x4 r0 = tr_read_b16(base + ((32 * kb + 4 * G + (l16 >> 2)) * ld + col) * 2);
+    const s16x4 r1 = tr_read_b16(base + ((32 * kb + 16 + 4 * G + (l16 >> 2)) * ld + col) * 2);
+    Frag<bf16> f;
+    f.v = __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0), __builtin_bit_cast(bf16x4, r1), 0, 1, 2, 3, 4, 5,
+                                  6, 7);
+    return f;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                    const bf16* __restrict__ v, const float* __restrict__ alpha,
+                                                    const float* __restrict__ beta, Regions rg, int Tlen, int H) {
+    using S = PrepSmem<DK, DV>;
+    using L = Lay<DK, DV>;
+    constexpr int LDK = S::LDK, LDX = S::LDX, LDA = S::LDA, RBK = L::RBK;
+    extern __shared__ __align__(16) char smem_raw[];
+    S& sm = *reinterpret_cast<S*>(smem_raw);
+
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int NC = gridDim.x;
+    const int t0 = c * C;
+    const int n = min(C, Tlen - t0);
+    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const size_t tok0 = ((size_t)b * Tlen + t0) * H + h;
+    const size_t cid = ((size_t)b * H + h) * NC + c;
+    char* ra = rg.ra + cid * L::RA;
+    char* rb = rg.rb + cid * L::RB;
+
+    // ---- A: K and Q into LDS, cumulative log decay ---------------------------------------
+    {
+        TileRegs<bf16, C, DK> kr, qr;
+        kr.load(k + tok0 * DK, (size_t)H * DK, n);
+        qr.load(q + tok0 * DK, (size_t)H * DK, n);
+        kr.template store<LDK>(sm.Ks);
+        qr.template store<LDX>(sm.Xs);
+    }
+    if (w == 0) {
+        const bool ok = lane < n;
+        float la = ok ? __logf(alpha[tok0 + (size_t)lane * H]) : 0.0f;
+        const float be = ok ? beta[tok0 + (size_t)lane * H] : 0.0f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(la, o, 64);
+            if (lane >= o) la += y;
+        }
+        sm.Gs[lane] = la;
+        sm.Bs[lane] = be;
+        if (lane == C - 1) rg.egl[cid] = __expf(la);
+    }
+    __syncthreads();
+
+    // ---- B: A (strict lower, fp32) and P (fp16, staged in Tm) ------------------------------
+    char* pstage = (char*)sm.Tm;
+    for (int ti = w; ti < 16; ti += 4) {
+        int i, j;
+        if (ti < 10) {
+            i = (ti >= 6) ? 3 : (ti >= 3) ? 2 : (ti >= 1) ? 1 : 0;
+            j = ti - i * (i + 1) / 2;
+        } else {
+            const int u = ti - 10;  // the six strictly upper tiles
+            i = (u < 3) ? 0 : (u < 5) ? 1 : 2;
+            j = (u < 3) ? u + 1 : (u < 5) ? u - 1 : 3;
+        }
+        f32x4 kk = {0, 0, 0, 0}, qk = {0, 0, 0, 0};
+        if (ti < 10) {
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                Frag<bf16> a, bq, bk;
+                load_frag_rows(bk, sm.Ks, LDK, 16 * j + l16, 32 * kb);
+                load_frag_rows(a, sm.Ks, LDK, 16 * i + l16, 32 * kb);
+                load_frag_rows(bq, sm.Xs, LDX, 16 * i + l16, 32 * kb);
+                mma(kk, a, bk);
+                mma(qk, bq, bk);
+            }
+        }
+        const int s = 16 * j + l16;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * i + 4 * G + x;
+            const float e = (s <= r) ? __expf(sm.Gs[r] - sm.Gs[s]) : 0.0f;
+            sm.Am[r * LDA + s] = (s < r) ? sm.Bs[r] * e * kk[x] : 0.0f;
+            *(half*)(pstage + fm_off<C>(r, s)) = (half)(e * qk[x]);
+        }
+    }
+    __syncthreads();
+    copy_out(rb + L::B_P, pstage, C * C * 2);
+
+    // ---- C: QG = diag(e^g) Q and KD^T, straight to the records ------------------------------
+    for (int id = threadIdx.x; id < C * DK / 8; id += NT) {
+        const int r = id / (DK / 8), cc = id % (DK / 8);
+        const float e = __expf(sm.Gs[r]);
+        const bf16x8 x = *(const bf16x8*)&sm.Xs[r * LDX + 8 * cc];
+        f16x8 y;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) y[t] = (half)((float)x[t] * e);
+        *(f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
+        *(f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+    }
+    {
+        const float glast = sm.Gs[C - 1];
+        for (int combo = w * 4 + G; combo < (DK / 16) * (C / 8); combo += 16) {
+            const int cg = combo % (DK / 16), pc = 8 * (combo / (DK / 16));
+            const char* kbase = (const char*)sm.Ks;
+            const int col = 16 * cg + 4 * (l16 & 3);
+            const s16x4 r0 = tr_read_b16(kbase + ((pc + (l16 >> 2)) * LDK + col) * 2);
+            const s16x4 r1 = tr_read_b16(kbase + ((pc + 4 + (l16 >> 2)) * LDK + col) * 2);
+            const bf16x4 k0 = __builtin_bit_cast(bf16x4, r0), k1 = __builtin_bit_cast(bf16x4, r1);
+            f16x8 y;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                y[t] = (half)((float)k0[t] * __expf(glast - sm.Gs[pc + t]));
+                y[t + 4] = (half)((float)k1[t] * __expf(glast - sm.Gs[pc + 4 + t]));
+            }
+            *(f16x4*)(ra + L::A_KDT + fm_off<C>(16 * cg + l16, pc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
+            *(f16x4*)(ra + L::A_KDT + fm_off<C>(16 * cg + l16, pc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+        }
+    }
+    // V is needed only for U: start its load now, land it in Xs after Tinv
+    TileRegs<bf16, C, DV> vr;
+    vr.load(v + tok0 * DV, (size_t)H * DV, n);
+    __syncthreads();  // P staging copied, Q consumed
+
+    // ---- D: Tinv = (I + A)^{-1} -----------------------------------------------------------
+    if (w == 0) {
+        // 16x16 diagonal blocks: lane (blk, col) solves column `col` of block `blk`
+        const int blk = lane >> 4, col = l16, o = 16 * blk;
+        float a[16][16];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+            for (int s4 = 0; s4 < 16; s4 += 4) {
+                if (s4 < r) {
+                    const f32x4 x = *(const f32x4*)&sm.Am[(o + r) * LDA + o + s4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) a[r][s4 + u] = x[u];
+                }
+            }
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == col) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) acc -= a[r][s2] * x[s2];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.Tm[(o + r) * LDA + o + col] = x[r];
+    } else {
+        for (int i = threadIdx.x - 64; i < 6 * 256; i += NT - 64) {
+            const int u = i >> 8, e = i & 255;
+            const int bi = (u < 3) ? 0 : (u < 5) ? 1 : 2;
+            const int bj = (u < 3) ? u + 1 : (u < 5) ? u - 1 : 3;
+            sm.Tm[(16 * bi + (e >> 4)) * LDA + 16 * bj + (e & 15)] = 0.0f;
+        }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        if (w < 4 - d) {
+            const int j = w, i = w + d;
+            f32x4 acc = {0, 0, 0, 0};
+            for (int m = j; m < i; ++m) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float av = sm.Am[(16 * i + l16) * LDA + 16 * m + 4 * G + e];
+                    const float bv = sm.Tm[(16 * m + 4 * G + e) * LDA + 16 * j + l16];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                }
+            }
+            f32x4 y = {0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float av = sm.Tm[(16 * i + l16) * LDA + 16 * i + 4 * G + e];
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, acc[e], y, 0, 0, 0);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sm.Tm[(16 * i + 4 * G + x) * LDA + 16 * j + l16] = -y[x];
+        }
+        __syncthreads();
+    }
+    vr.template store<LDX>(sm.Xs);
+
+    // ---- E: W = Tinv diag(beta e^g) K and U = Tinv diag(beta) V, hi/lo split of Tinv -------
+    {
+        const int i = w;  // row tile
+        const int nkb = (i < 2) ? 1 : 2;
+        Frag<bf16> wh[2], wl[2], uh[2], ul[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = 32 * kb + kmap(G, e);
+                const float t = sm.Tm[(16 * i + l16) * LDA + s];
+                const float tw = t * sm.Bs[s] * __expf(sm.Gs[s]);
+                const float tu = t * sm.Bs[s];
+                const bf16 hw = (bf16)tw, hu = (bf16)tu;
+                wh[kb].set_raw(e, hw);
+                wl[kb].set(e, tw - (float)hw);
+                uh[kb].set_raw(e, hu);
+                ul[kb].set(e, tu - (float)hu);
+            }
+        }
+        __syncthreads();  // Tinv consumed, V landed: Am and Tm become staging tiles
+        char* wstage = (char*)sm.Am;
+        char* ustage = (char*)sm.Tm;
+#pragma unroll
+        for (int ct = 0; ct < DK / 16; ++ct) {
+            f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb < nkb) {
+                    const Frag<bf16> bk = bfrag_tr(sm.Ks, LDK, ct, kb);
+                    mma(acc, wh[kb], bk);
+                    mma(acc, wl[kb], bk);
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                *(half*)(wstage + fm_off<DK>(16 * i + 4 * G + x, 16 * ct + l16)) = (half)acc[x];
+        }
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) {
+            f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb < nkb) {
+                    const Frag<bf16> bv = bfrag_tr(sm.Xs, LDX, ct, kb);
+                    mma(acc, uh[kb], bv);
+                    mma(acc, ul[kb], bv);
+                }
+            }
+            f16x4 y;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) y[x] = (half)acc[x];
+            *(f16x4*)(ustage + (ct >> 2) * L::USLICE + u_off(ct & 3, i, lane)) = y;
+        }
+        __syncthreads();
+        copy_out(ra + L::A_W, wstage, C * DK * 2);
+        copy_out(ra + L::A_U, ustage, C * DV * 2);
+    }
+}
+
+// =========================================================================================
+// carry (sequential)
+// =========================================================================================
+// One LDS object per stage, so the compiler's wait-count analysis can tell the stage being
+// read from the stages the asynchronous copies are filling.
+constexpr int kStageMax = 40960 + 1024;  // tiles + e^{g_last} (one word per lane)
+__shared__ __align__(16) char g_stage0[kStageMax];
+__shared__ __align__(16) char g_stage1[kStageMax];
+__shared__ __align__(16) char g_stage2[kStageMax];
+
+template <int DK, int DV>
+struct Carry {
+    using L = Lay<DK, DV>;
+    static constexpr int RBK = L::RBK, NKT = DK / 16;
+    static constexpr int NCH = (int)L::STAGE / 16;  // 16-byte copies per chunk
+    static constexpr int TPT = NCH / NT;             // tile copies per thread per chunk
+    static constexpr int DPT = TPT + 1;              // all copies per thread per chunk (+ e^{g_last})
+    static constexpr int SPT = DK / 32 + 2;          // fragment stores per thread per chunk
+    static_assert(L::STAGE + 1024 <= kStageMax, "stage too large");
+    static_assert(NCH % NT == 0, "stage must be a whole number of copy rounds");
+
+    const char* ra0;   // this (batch, head)'s first chunk record
+    char* sf0;
+    char* df0;
+    const float* egl;
+    int sl;
+
+    // Starts the copy of chunk c into `dst`.  The chunk's e^{g_last} is copied into the
+    // stage too (every lane copies the same word, so all threads issue the same operations)
+    // and read back from LDS: a plain global load carried across the loop would make the
+    // compiler wait for every copy in flight.
+    __device__ __forceinline__ void issue(int c, char* dst) const {
+        const int w = wave_id();
+        const char* src = ra0 + (size_t)c * L::RA;
+        gdn::lds_dma4((const void*)(egl + c), (const void*)(dst + L::STAGE + w * 256));
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+            const int ch = m * NT + (int)threadIdx.x;
+            const size_t off = (size_t)ch * 16 < L::A_U ? (size_t)ch * 16
+                                                        : L::A_U + sl * L::USLICE + ((size_t)ch * 16 - L::A_U);
+            gdn::lds_dma16((const void*)(src + off), (const void*)(dst + (m * NT + w * 64) * 16));
+        }
+    }
+
+    __device__ __forceinline__ void step(int c, const char* sW, f32x4* st) const {
+        const int lane = lane_id(), w = wave_id();
+        const char* sK = sW + L::A_KDT;
+        const char* sU = sW + L::A_U;
+        // All LDS operands of the chunk are requested in two batches ahead of their MFMAs
+        // (with one wave per SIMD nothing else hides LDS latency); the scheduling barriers
+        // keep the compiler from sinking the reads next to their uses.
+        f16x8 wf[4][DK / 32];
+        f16x4 u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) wf[i][kb] = fm_frag<DK>(sW, i, kb);
+            u[i] = *(const f16x4*)(sU + u_off(w, i, lane));
+        }
+        const float eg = *(const float*)(sW + L::STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        // S_in^T as fp16 B fragments; also kept for the output kernel
+        Frag<half> sf[DK / 32];
+        char* sfo = sf0 + (size_t)c * L::SF + (size_t)sl * (DK / 32) * 4096;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            acc_to_frag(sf[kb], st[2 * kb], st[2 * kb + 1]);
+            *(f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16) = sf[kb].v;
+        }
+        f16x8 kf[NKT][2];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) kf[t][kb] = fm_frag<C>(sK, t, kb);
+        __builtin_amdgcn_sched_barrier(0);
+        // Delta = U - W S_in^T
+        f32x4 dl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dl[i] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Frag<half> a;
+                a.v = wf[i][kb];
+                mma(dl[i], a, sf[kb]);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dl[i][x] = (float)u[i][x] - dl[i][x];
+        Frag<half> df[2];
+        char* dfo = df0 + (size_t)c * L::DF + (size_t)sl * 2 * 4096;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            acc_to_frag(df[kb], dl[2 * kb], dl[2 * kb + 1]);
+            *(f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16) = df[kb].v;
+        }
+        // S_out^T = e^{g_last} S_in^T + KD^T Delta
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) st[t] *= eg;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                Frag<half> a;
+                a.v = kf[t][kb];
+                mma(st[t], a, df[kb]);
+            }
+    }
+};
+
+// Pipeline: the copy of chunk c + 2 is issued while chunk c is computed, always (a chunk
+// past the end re-copies the last one into a stage that is never read again), so every
+// iteration issues the same operations: DPT copies (tiles and e^{g_last})
+// and SPT fragment stores per thread.  Before chunk c >= 1 is read, the operations issued
+// after its copy are at least the stores of chunk c - 1 and the copy of chunk c + 1; with
+// in-order retirement, waiting until no more than DPT + SPT are outstanding is sufficient.
+// Chunk 0 waits until only the copy of chunk 1 may be outstanding.
+// One workgroup per CU (the three stages fill the LDS): let the scheduler use the whole
+// register file to keep more LDS reads in flight.
+template <int DK, int DV>
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
+    Regions rg, const float* init_state, float* final_state,
+                                                     int Tlen, int H) {
+    using L = Lay<DK, DV>;
+    using K = Carry<DK, DV>;
+    constexpr int NKT = DK / 16;
+    const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const int NC = (Tlen + C - 1) / C;
+    const size_t c0 = ((size_t)b * H + h) * NC;
+    const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, sl};
+    const int row = sl * 64 + 16 * w + l16;  // state row held by this lane's accumulators
+
+    f32x4 st[NKT];  // st[t][x] = S[row][16 t + 4 G + x]
+    const size_t srow = (((size_t)b * H + h) * DV + row) * DK;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+        st[t] = init_state ? *(const f32x4*)(init_state + srow + 16 * t + 4 * G) : f32x4{0, 0, 0, 0};
+
+    gdn::wait_vmcnt<0>();  // initial state in registers before the untracked copies start
+    const int last = NC - 1;
+    k.issue(0, g_stage0);
+    k.issue(min(1, last), g_stage1);
+    gdn::wait_vmcnt<K::DPT>();
+    gdn::lds_barrier();
+    k.issue(min(2, last), g_stage2);
+    k.step(0, g_stage0, st);
+    for (int c = 1; c < NC; c += 3) {
+        gdn::wait_vmcnt<K::DPT + K::SPT>();
+        gdn::lds_barrier();
+        k.issue(min(c + 2, last), g_stage0);
+        k.step(c, g_stage1, st);
+        if (c + 1 >= NC) break;
+        gdn::wait_vmcnt<K::DPT + K::SPT>();
+        gdn::lds_barrier();
+        k.issue(min(c + 3, last), g_stage1);
+        k.step(c + 1, g_stage2, st);
+        if (c + 2 >= NC) break;
+        gdn::wait_vmcnt<K::DPT + K::SPT>();
+        gdn::lds_barrier();
+        k.issue(min(c + 4, last), g_stage2);
+        k.step(c + 2, g_stage0, st);
+    }
+    if (final_state) {
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) *(f32x4*)(final_state + srow + 16 * t + 4 * G) = st[t];
+    }
+}
+
+// =========================================================================================
+// output
+// =========================================================================================
+template <int DK, int DV>
+struct OutSmem {
+    static constexpr int LDO = DV + 8;
+    char rb[Lay<DK, DV>::RB];  // QG | P
+    bf16 Os[C * LDO];
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT, 2) void gdn_out_h(Regions rg, bf16* __restrict__ o, int Tlen, int H) {
+    using L = Lay<DK, DV>;
+    using S = OutSmem<DK, DV>;
+    constexpr int RBK = L::RBK, LDO = S::LDO;
+    extern __shared__ __align__(16) char smem_raw[];
+    S& sm = *reinterpret_cast<S*>(smem_raw);
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int NC = gridDim.x;
+    const int t0 = c * C, n = min(C, Tlen - t0);
+    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const size_t cid = ((size_t)b * H + h) * NC + c;
+    {
+        const char* src = rg.rb + cid * L::RB;
+        for (int i = threadIdx.x * 16; i < (int)L::RB; i += NT * 16) *(u32x4*)(sm.rb + i) = *(const u32x4*)(src + i);
+    }
+    __syncthreads();
+    const char* sQ = sm.rb + L::B_QG;
+    const char* sP = sm.rb + L::B_P;
+    const char* sfc = rg.sf + cid * L::SF;
+    const char* dfc = rg.df + cid * L::DF;
+    // n-tiles of 16 state rows: carry slice sl, wave w' -> n-tile 4 sl + w'
+#pragma unroll
+    for (int nt = w; nt < DV / 16; nt += 4) {
+        const int sl = nt >> 2, wp = nt & 3;
+        Frag<half> sf[DK / 32], df[2];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+            sf[kb].v = *(const f16x8*)(sfc + (size_t)sl * (DK / 32) * 4096 + ((kb * 4 + wp) * 64 + lane) * 16);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) df[kb].v = *(const f16x8*)(dfc + (size_t)sl * 2 * 4096 + ((kb * 4 + wp) * 64 + lane) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                Frag<half> a;
+                a.v = fm_frag<DK>(sQ, i, kb);
+                mma(acc, a, sf[kb]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < (i < 2 ? 1 : 2); ++kb) {
+                Frag<half> a;
+                a.v = fm_frag<C>(sP, i, kb);
+                mma(acc, a, df[kb]);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sm.Os[(16 * i + 4 * G + x) * LDO + 16 * nt + l16] = (bf16)acc[x];
+        }
+    }
+    __syncthreads();
+    for (int id = threadIdx.x; id < C * (DV / 8); id += NT) {
+        const int r = id / (DV / 8), cc = id % (DV / 8);
+        if (r < n) *(u32x4*)(o + (((size_t)b * Tlen + t0 + r) * H + h) * DV + 8 * cc) = *(const u32x4*)&sm.Os[r * LDO + 8 * cc];
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
+    const int NC = (a.T + C - 1) / C;
+    const Regions rg = regions<DK, DV>(a.workspace, (size_t)a.B * a.H * NC);
+    const size_t prep_smem = sizeof(PrepSmem<DK, DV>), out_smem = sizeof(OutSmem<DK, DV>);
+    static const hipError_t attr = [&] {
+        const hipError_t e = ensure_lds_limit(gdn_prep_h<DK, DV>, prep_smem);
+        return e != hipSuccess ? e : ensure_lds_limit(gdn_out_h<DK, DV>, out_smem);
+    }();
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gdn_prep_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), prep_smem, stream, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, rg, a.T, a.H);
+    hipLaunchKernelGGL((gdn_carry_h<DK, DV>), dim3(DV / 64, a.H, a.B), dim3(NT), 0, stream, rg, a.init_state,
+                       a.final_state, a.T, a.H);
+    hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, rg, (bf16*)a.o, a.T, a.H);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gdn_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+    const size_t nchunks = (size_t)B * H * ((T + C - 1) / C);
+    if (Dk == 64 && Dv == 64) return Lay<64, 64>::total(nchunks);
+    if (Dk == 64 && Dv == 128) return Lay<64, 128>::total(nchunks);
+    if (Dk == 128 && Dv == 64) return Lay<128, 64>::total(nchunks);
+    if (Dk == 128 && Dv == 128) return Lay<128, 128>::total(nchunks);
+    return 0;
+}
+
+hipError_t launch_gdn_bf16(const GdnFwdArgs& a, hipStream_t stream) {
+    if (a.Dk == 64 && a.Dv == 64) return launch<64, 64>(a, stream);
+    if (a.Dk == 64 && a.Dv == 128) return launch<64, 128>(a, stream);
+    if (a.Dk == 128 && a.Dv == 64) return launch<128, 64>(a, stream);
+    if (a.Dk == 128 && a.Dv == 128) return launch<128, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace atma

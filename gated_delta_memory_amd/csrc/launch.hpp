@@ -17,6 +17,9 @@ struct GdnFwdArgs {
 };
 size_t gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16_io);
 hipError_t launch_gdn_fwd(const GdnFwdArgs& a, hipStream_t stream);
+// bf16-input fast path (fp16-staged operands), used by launch_gdn_fwd
+size_t gdn_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+hipError_t launch_gdn_bf16(const GdnFwdArgs& a, hipStream_t stream);
 
 struct GdnDecodeArgs {
     const void *q, *k, *v;
