@@ -1,7 +1,7 @@
 // C-ABI layer of libatma: host-side validation, then kernel launches on the caller's
 // stream.  Every check happens before the first HIP call, so a rejected call has no side
 // effect on the device.  No allocation, no synchronisation, no exceptions cross the ABI.
-#include "../../include/atma.h"
+#include "atma.h"
 
 #include <hip/hip_runtime.h>
 

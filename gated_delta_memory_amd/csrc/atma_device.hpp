@@ -141,6 +141,55 @@ __device__ __forceinline__ f16x8 frag_swz_f16(const char* tile, int row, int k0)
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding: vmcnt bits [3:0]
+// and [15:14], expcnt [6:4], lgkmcnt [11:8]).  Vector memory operations, loads, LDS-DMA
+// copies and stores alike, retire in issue order on this architecture.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Asynchronous global->LDS copy of 16 bytes per lane: lane l writes LDS bytes
+// [lds_base + 16 l, lds_base + 16 l + 16).  Issued from inline assembly so the compiler
+// does not track it: callers retire it with an explicit wait_vmcnt before a barrier and
+// only then read the destination.  (Tracked copies make the compiler's conservative
+// wait-count analysis stall on every LDS read while any copy is in flight.)
+__device__ __forceinline__ void lds_dma16(const void* gaddr, const void* lds_wave_base) {
+    typedef __attribute__((address_space(3))) const char* lds_ptr;
+    const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_ptr)lds_wave_base);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gaddr), "s"(base)
+        : "memory", "m0");
+}
+// Same, 4 bytes per lane (lane l writes [lds_base + 4 l, lds_base + 4 l + 4)).
+__device__ __forceinline__ void lds_dma4(const void* gaddr, const void* lds_wave_base) {
+    typedef __attribute__((address_space(3))) const char* lds_ptr;
+    const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_ptr)lds_wave_base);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, off"
+        :
+        : "v"(gaddr), "s"(base)
+        : "memory", "m0");
+}
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, then
+// s_barrier, without the release/acquire fences of __syncthreads() (those would also wait
+// for every global store and asynchronous copy in flight).  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---- wave reductions ---------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -18,9 +18,9 @@
 //
 // Kernel layout (one workgroup of 4 waves per 128-query tile, head and batch; each wave
 // owns 32 consecutive queries):
-//   * keys stream in blocks of 64 through one LDS buffer (K and V row-major, 16-byte
-//     chunks XOR-swizzled by key so fragment reads are bank-conflict free); the next block
-//     is fetched into registers while the current one is used;
+//   * keys stream in blocks of 64 through two LDS stages (K and V row-major, 16-byte chunks
+//     XOR-swizzled by key so fragment reads are bank-conflict free), filled by asynchronous
+//     global->LDS copies one block ahead, one barrier per block;
 //   * scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: a lane holds
 //     16 keys of one query column, so row statistics are per-lane partial sums (the two
 //     lanes that share a query are combined with v_permlane32_swap);
@@ -69,12 +69,14 @@ __device__ __forceinline__ bf16x4 tr_read(const char* lds_base, int byte_off) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// Two K/V stages, one LDS object each (the copy into one stage overlaps the reads of the other).
+__shared__ __align__(16) char g_kv0[2 * BK * D * 2];
+__shared__ __align__(16) char g_kv1[2 * BK * D * 2];
+
 __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
                                                           float* __restrict__ meff_out, int T, int Hq, int Hkv) {
-    __shared__ __align__(16) char Ks[BK * D * 2];
-    __shared__ __align__(16) char Vs[BK * D * 2];
     const int nqt = (T + BQ - 1) / BQ;
     const int qt = nqt - 1 - (int)blockIdx.x;  // heaviest tiles first
     const int h = blockIdx.y, b = blockIdx.z;
@@ -99,38 +101,30 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
     }
 
     f32x16 oacc[2] = {f32x16{}, f32x16{}};  // O^T[d = 32 dt + 8(x/4) + 4 G2 + x%4][qi]
-    float m_used = -INFINITY, lsum = 0.f, q2sum = 0.f;
+    float m_used = -INFINITY;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f}, q2sum[4] = {0.f, 0.f, 0.f, 0.f};  // split to shorten dependency chains
 
     const int kend = min(T, q0 + BQ);
     const int nkb = (kend + BK - 1) / BK;
     const size_t kvstride = (size_t)Hkv * D;
     const bf16* kbase = k + (size_t)b * T * kvstride + (size_t)hk * D;
     const bf16* vbase = v + (size_t)b * T * kvstride + (size_t)hk * D;
-    const int ld_key = threadIdx.x >> 3, ld_c = threadIdx.x & 7;
-    u32x4 kreg[2], vreg[2];
-    auto fetch = [&](int kb) {
+    // Asynchronous copy of key block kb into a stage [K tile | V tile]: 16-byte chunk ch of the
+    // stage lands at LDS slot ch; the source is chosen so the tile comes out XOR-swizzled.
+    auto issue = [&](int kb, char* stage) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int key = min(kb * BK + ld_key + 32 * r, T - 1);  // rows past T are masked later
-            kreg[r] = *(const u32x4*)(kbase + (size_t)key * kvstride + ld_c * 8);
-            vreg[r] = *(const u32x4*)(vbase + (size_t)key * kvstride + ld_c * 8);
+        for (int m = 0; m < 4; ++m) {
+            const int ch = m * NT + (int)threadIdx.x;  // 0..1023: K rows 0..63, then V rows 0..63
+            const int r = (ch >> 3) & 63, pc = ch & 7;
+            const int key = min(kb * BK + r, T - 1);  // rows past T are masked later
+            const bf16* src = (m < 2 ? kbase : vbase) + (size_t)key * kvstride + ((pc ^ (r & 7)) << 3);
+            lds_dma16(src, stage + (m * NT + w * 64) * 16);
         }
     };
-    fetch(0);
-
-    for (int kb = 0; kb < nkb; ++kb) {
-        __syncthreads();  // previous block fully consumed
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int off = swz(ld_key + 32 * r, ld_c);
-            *(u32x4*)(Ks + off) = kreg[r];
-            *(u32x4*)(Vs + off) = vreg[r];
-        }
-        __syncthreads();
-        if (kb + 1 < nkb) fetch(kb + 1);
-
+    auto block = [&](int kb, const char* Ks) {
+        const char* Vs = Ks + BK * D * 2;
         const int key0 = kb * BK;
-        if (key0 > qw0 + QW - 1) continue;  // whole block in this wave's future
+        if (key0 > qw0 + QW - 1) return;  // whole block in this wave's future
         const bool edge = (key0 + BK - 1 > qw0) || (key0 + BK > T);
 
         // S^T = K Q^T : two 32-key sub-tiles
@@ -151,7 +145,7 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
                     const int key = key0 + 32 * kt + 8 * (x >> 2) + 4 * G2 + (x & 3);
-                    if (key > qi || key >= T) s[kt][x] = -INFINITY;
+                    s[kt][x] = (key > qi || key >= T) ? -INFINITY : s[kt][x];
                 }
         }
         float mx = -INFINITY;
@@ -166,8 +160,11 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
             const float mnew = move ? mx : m_used;
             const float rho = fast_exp2(m_used - mnew);
             m_used = mnew;
-            lsum *= rho;
-            q2sum *= rho * rho;
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                lsum[a4] *= rho;
+                q2sum[a4] *= rho * rho;
+            }
             oacc[0] *= rho;
             oacc[1] *= rho;
         }
@@ -177,13 +174,15 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 bf16x8 pf;
+                float& ls = lsum[2 * kt + st];
+                float& qs = q2sum[2 * kt + st];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     const float p0 = fast_exp2(fmaf(s[kt][8 * st + e], cq, -m_used));
                     const float p1 = fast_exp2(fmaf(s[kt][8 * st + e + 1], cq, -m_used));
                     const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
-                    q2sum = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, q2sum, false);
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(bf16)1.0f, (bf16)1.0f}, ls, false);
+                    qs = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, qs, false);
                     pf[e] = pp[0];
                     pf[e + 1] = pp[1];
                 }
@@ -199,11 +198,20 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
                 }
             }
         }
+    };
+
+    // two-stage pipeline: the copy of block kb + 1 overlaps the computation of block kb
+    issue(0, g_kv0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (kb + 1 < nkb) issue(kb + 1, (kb & 1) ? g_kv0 : g_kv1);
+        block(kb, (kb & 1) ? g_kv1 : g_kv0);
     }
 
     // ---- finalise: null merge, channels, output ------------------------------------------------
-    const float L = pair_sum(lsum);
-    const float Q2 = pair_sum(q2sum);
+    const float L = pair_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+    const float Q2 = pair_sum((q2sum[0] + q2sum[1]) + (q2sum[2] + q2sum[3]));
     const float n = (float)(qi + 1);
     const float t = 1.0f + a_t * logf(n);
     const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf(n + 1.0f));

@@ -43,6 +43,20 @@ def rel_err_bf16(got, ref) -> float:
     return float(np.max(excess) / rms) if rms > 0 else float(np.max(excess))
 
 
+def rel_err_elem(got, ref) -> float:
+    """max |got - ref| / |ref| over elements (denominator floored at 1e-6 rms(ref)).
+
+    For positive quantities with a heavy-tailed spread, such as the effective count
+    m_eff (1 up to T): rounding the attention weights to bf16 moves each of them by up
+    to 2^-9 of itself, so the error of such a quantity scales with its own value and an
+    RMS-normalised metric would charge the largest rows many times over."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    floor = 1e-6 * max(np.sqrt(np.mean(ref ** 2)), 1e-30)
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor)))
+
+
 def out_err(got, ref, dtype: str) -> float:
     """Metric for an output tensor written in ``dtype``."""
     return rel_err_bf16(got, ref) if dtype == "bf16" else rel_err(got, ref)

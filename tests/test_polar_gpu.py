@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from parity import TOL, note, out_err, rel_err, sample_rows, to_np
+from parity import TOL, note, out_err, rel_err, rel_err_elem, sample_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def _check_prefill(atma, inp, rows=None, tag=""):
     go = to_np(o)[:, idx]
     gmu = to_np(mu).transpose(0, 2, 1)[:, idx]      # [B,T,Hq] like the oracle
     gme = to_np(meff).transpose(0, 2, 1)[:, idx]
-    eo, emu, eme = out_err(go, ref["o"], "bf16"), rel_err(gmu, ref["mu"]), rel_err(gme, ref["meff"])
+    eo, emu, eme = out_err(go, ref["o"], "bf16"), rel_err(gmu, ref["mu"]), rel_err_elem(gme, ref["meff"])
     note(f"  polar {tag} err_o={eo:.3e} err_mu={emu:.3e} err_meff={eme:.3e}")
     assert eo <= TOL["bf16"] and emu <= TOL["bf16"] and eme <= TOL["bf16"], (eo, emu, eme)
     # bounded channels on the GPU output: 0 <= mu <= 1 and ||o|| = mu (direction has unit norm)
