@@ -14,6 +14,7 @@ Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +44,45 @@ def decode_bytes(B, L, Hkv=16, D=64, H=8, Dg=128):
     return 2 * B * L * Hkv * D * 2 + 2 * B * H * Dg * Dg * 4
 
 
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for a
+# device copy of known size; keyed by the SHA-256 of the kernel's sources at the time the
+# counters were taken, so an edited kernel reports null until it is measured again.
+MEASURED_TRAFFIC = {}
+
+
+def _sources_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_memory_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"polar_fwd_kernel": ["polar_fwd.hip", "atma_device.hpp"],
+                  "atma_gdn_fwd (prep+carry+out)": ["gdn_fwd.hip", "gdn_fwd_bf16.hip", "gdn_common.hpp",
+                                                    "atma_device.hpp"]}
+
+
+def measured_traffic(kernel):
+    m = MEASURED_TRAFFIC.get(kernel)
+    if m is None or m["sha"] != _sources_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return m["bytes"]
+
+
+def calibration_copy(torch, mib):
+    """A plain device-to-device copy of `mib` MiB, three times: the reference dispatch that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 class Timer:
     def __init__(self, torch):
         self.torch = torch
@@ -67,6 +107,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true", help="skip the 64K prefill and 256K decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is "
@@ -79,6 +121,8 @@ def main():
     import workloads
 
     dev = "cuda"
+    if args.calib_copy:
+        calibration_copy(torch, args.calib_copy)
     w = workloads.WORKLOADS["layer_b8_t2k"]
     inp = workloads.make_workload(w, device=dev)
     g, p = inp["gdn"], inp["polar"]
@@ -120,12 +164,12 @@ def main():
     if polar_ms >= gdn_ms:
         roofline = {"kernel": "polar_fwd_kernel", "bound": "mfma", "achieved": round(polar_tflops, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(polar_tflops / PEAK_BF16_TFLOPS, 4),
-                    "traffic": None, "launch_ms": round(polar_ms, 4),
+                    "traffic": measured_traffic("polar_fwd_kernel"), "launch_ms": round(polar_ms, 4),
                     "per_launch": f"{pf:.4e} flop = 4*64*B*Hq*T(T+1)/2, B={B} T={T} Hq={w.polar_Hq}"}
     else:
-        roofline = {"kernel": "atma_gdn_fwd (prep+carry)", "bound": "hbm", "achieved": round(gdn_gbs, 1),
+        roofline = {"kernel": "atma_gdn_fwd (prep+carry+out)", "bound": "hbm", "achieved": round(gdn_gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gdn_gbs / PEAK_HBM_GBS, 4),
-                    "traffic": None, "launch_ms": round(gdn_ms, 4),
+                    "traffic": measured_traffic("atma_gdn_fwd (prep+carry+out)"), "launch_ms": round(gdn_ms, 4),
                     "per_launch": f"{gb:.4e} B = B*H*T*(4*D*2+8) + B*H*D*D*4"}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

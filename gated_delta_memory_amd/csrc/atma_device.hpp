@@ -166,6 +166,23 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, const void* lds_wav
         : "v"(gaddr), "s"(base)
         : "memory", "m0");
 }
+// LDS byte address of a __shared__ object (a constant for a named array).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    typedef __attribute__((address_space(3))) const char* lds_ptr;
+    return (unsigned)(size_t)(lds_ptr)p;
+}
+// Same copy with the global address split into a wave-uniform 64-bit base and a per-lane
+// 32-bit byte offset, and the LDS destination given as a wave-uniform byte address.
+__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsigned lds_wave_addr) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(m0v)
+        : "memory", "m0");
+}
 // Same, 4 bytes per lane (lane l writes [lds_base + 4 l, lds_base + 4 l + 4)).
 __device__ __forceinline__ void lds_dma4(const void* gaddr, const void* lds_wave_base) {
     typedef __attribute__((address_space(3))) const char* lds_ptr;

@@ -51,8 +51,14 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// byte offset of 16-byte chunk c (0..7) of key row `key` in a swizzled 64x64 bf16 tile
-__device__ __forceinline__ int swz(int key, int c) { return key * 128 + ((c ^ (key & 7)) << 4); }
+// Byte offset of 16-byte chunk c (0..7) of key row `key` in a 64x64 bf16 tile.  The LDS has
+// 64 four-byte banks, so rows r and r + 1 (128 bytes apart) use disjoint bank halves and only
+// rows of equal parity can collide.  K tiles are read 16 bytes per lane with rows 0..15 in one
+// bank cycle: XOR-ing the chunk with (r >> 1) & 7 gives those rows eight distinct chunks per
+// parity.  V tiles are read by ds_read_b64_tr_b16, which takes four consecutive rows and two
+// adjacent chunks per 16-lane group: XOR-ing with 2 (r & 3) spreads them over all eight chunks.
+__device__ __forceinline__ int swz_k(int key, int c) { return key * 128 + ((c ^ ((key >> 1) & 7)) << 4); }
+__device__ __forceinline__ int swz_v(int key, int c) { return key * 128 + ((c ^ ((key & 3) << 1)) << 4); }
 
 // partner-lane (l ^ 32) combine via v_permlane32_swap
 __device__ __forceinline__ float pair_max(float x) {
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
     const int qt = nqt - 1 - (int)blockIdx.x;  // heaviest tiles first
     const int h = blockIdx.y, b = blockIdx.z;
     const int hk = h / (Hq / Hkv);
-    const int lane = lane_id(), w = wave_id();
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());  // wave-uniform
     const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
     const int q0 = qt * BQ;
     const int qw0 = q0 + w * QW;
@@ -107,37 +113,78 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
     const int kend = min(T, q0 + BQ);
     const int nkb = (kend + BK - 1) / BK;
     const size_t kvstride = (size_t)Hkv * D;
+    const unsigned rowbytes = (unsigned)(kvstride * 2);
     const bf16* kbase = k + (size_t)b * T * kvstride + (size_t)hk * D;
     const bf16* vbase = v + (size_t)b * T * kvstride + (size_t)hk * D;
+
     // Asynchronous copy of key block kb into a stage [K tile | V tile]: 16-byte chunk ch of the
-    // stage lands at LDS slot ch; the source is chosen so the tile comes out XOR-swizzled.
-    auto issue = [&](int kb, char* stage) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int ch = m * NT + (int)threadIdx.x;  // 0..1023: K rows 0..63, then V rows 0..63
-            const int r = (ch >> 3) & 63, pc = ch & 7;
-            const int key = min(kb * BK + r, T - 1);  // rows past T are masked later
-            const bf16* src = (m < 2 ? kbase : vbase) + (size_t)key * kvstride + ((pc ^ (r & 7)) << 3);
-            lds_dma16(src, stage + (m * NT + w * 64) * 16);
+    // stage lands at LDS slot ch (row ch / 8, position ch % 8); the source chunk is chosen so
+    // the tile comes out swizzled.  Thread t moves chunks t, t + 256 (K) and t + 512,
+    // t + 768 (V): rows r0 = t / 8 and r0 + 32 of each tile.
+    const int r0 = (int)threadIdx.x >> 3, pc = (int)threadIdx.x & 7;
+    const unsigned koff0 = (unsigned)(((pc ^ ((r0 >> 1) & 7)) << 4));        // (r0 + 32) has the same swizzle
+    const unsigned voff0 = (unsigned)(((pc ^ ((r0 & 3) << 1)) << 4));
+    auto issue = [&](int kb, const char* stage) {
+        const size_t blk = (size_t)kb * BK * kvstride;
+        const unsigned lds = lds_addr(stage) + (unsigned)(w * 64 * 16);
+        int ra = r0, rb = r0 + 32;
+        if (kb * BK + BK > T) {  // last block of a ragged sequence: rows past T repeat row T - 1 (masked later)
+            ra = min(ra, T - 1 - kb * BK);
+            rb = min(rb, T - 1 - kb * BK);
         }
+        lds_dma16(kbase + blk, ra * rowbytes + koff0, lds);
+        lds_dma16(kbase + blk, rb * rowbytes + koff0, lds + NT * 16);
+        lds_dma16(vbase + blk, ra * rowbytes + voff0, lds + 2 * NT * 16);
+        lds_dma16(vbase + blk, rb * rowbytes + voff0, lds + 3 * NT * 16);
     };
+
+    // Lane-constant fragment offsets inside a stage.  K (A operand of S^T = K Q^T): lane reads
+    // key 32 kt + l32, d = 16 ks + 8 G2 .. + 7.  V^T (A operand of O^T = V^T P^T) via transposed
+    // reads: for weight slot group (kt, st) the 16-lane group g16 reads keys
+    // 32 kt + 16 st + 4 G2 + (i16 / 4) (+ 8 for the upper half of the fragment), columns
+    // 32 dt + 16 (g16 & 1) + 4 (i16 & 3) .. + 3.
+    int koff[4], voff[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[ks] = swz_k(l32, 2 * ks + G2);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+        const int dcol = 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3);
+        voff[dt] = swz_v(4 * G2 + (i16 >> 2), dcol >> 3) + ((dcol & 7) << 1);
+    }
+
     auto block = [&](int kb, const char* Ks) {
         const char* Vs = Ks + BK * D * 2;
         const int key0 = kb * BK;
         if (key0 > qw0 + QW - 1) return;  // whole block in this wave's future
         const bool edge = (key0 + BK - 1 > qw0) || (key0 + BK > T);
 
-        // S^T = K Q^T : two 32-key sub-tiles
+        // all fragment reads of the block up front: their latency overlaps the MFMAs and the
+        // weight computation
+        bf16x8 kf[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = *(const bf16x8*)(Ks + koff[ks] + kt * 32 * 128);
+        bf16x8 vf[2][2][2];  // [kt][st][dt]
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const int base = voff[dt] + (32 * kt + 16 * st) * 128;
+                    const bf16x4 lo = tr_read(Vs, base);
+                    const bf16x4 hi = tr_read(Vs, base + 8 * 128);
+                    vf[kt][st][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+
+        // S^T = K Q^T : two 32-key sub-tiles, chains interleaved
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int key = 32 * kt + l32;
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 af = *(const bf16x8*)(Ks + swz(key, 2 * ks + G2));
-                s[kt] = mfma32(af, qf[ks], s[kt]);
-            }
-        }
+            for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(kf[kt][ks], qf[ks], s[kt]);
+
         // causal / length mask on edge blocks (raw scores; cq > 0 scales them later)
         if (edge) {
 #pragma unroll
@@ -186,27 +233,26 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
                     pf[e] = pp[0];
                     pf[e + 1] = pp[1];
                 }
-                const int kk = 32 * kt + 16 * st + 4 * G2;  // key of slot e = 0 for this lane group
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt) {
-                    const int dcol = 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3);
-                    const int key_a = kk + (i16 >> 2), key_b = key_a + 8;
-                    const bf16x4 lo = tr_read(Vs, swz(key_a, dcol >> 3) + ((dcol & 7) << 1));
-                    const bf16x4 hi = tr_read(Vs, swz(key_b, dcol >> 3) + ((dcol & 7) << 1));
-                    const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[dt] = mfma32(vf, pf, oacc[dt]);
-                }
+                for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma32(vf[kt][st][dt], pf, oacc[dt]);
             }
         }
     };
 
-    // two-stage pipeline: the copy of block kb + 1 overlaps the computation of block kb
+    // two-stage pipeline: the copy of block kb + 1 overlaps the computation of block kb.  The
+    // loop is unrolled by two so each stage is a fixed LDS address and every fragment read
+    // takes its offset as an immediate.
     issue(0, g_kv0);
-    for (int kb = 0; kb < nkb; ++kb) {
+    for (int kb = 0; kb < nkb; kb += 2) {
         wait_vmcnt<0>();
         lds_barrier();
-        if (kb + 1 < nkb) issue(kb + 1, (kb & 1) ? g_kv0 : g_kv1);
-        block(kb, (kb & 1) ? g_kv1 : g_kv0);
+        if (kb + 1 < nkb) issue(kb + 1, g_kv1);
+        block(kb, g_kv0);
+        if (kb + 1 >= nkb) break;
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (kb + 2 < nkb) issue(kb + 2, g_kv0);
+        block(kb + 1, g_kv1);
     }
 
     // ---- finalise: null merge, channels, output ------------------------------------------------
