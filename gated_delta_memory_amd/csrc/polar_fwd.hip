@@ -28,7 +28,8 @@
 //     fragments come straight from the row-major V tile with ds_read_b64_tr_b16;
 //   * L and Q2 are accumulated from the bf16 weights with v_dot2_f32_bf16, so they use
 //     exactly the weights the value sum uses;
-//   * query tiles are scheduled heaviest (last) first for causal load balance.
+//   * query tiles are scheduled heaviest (last) first for causal load balance, and the tiles of
+//     one (batch, head) go to one XCD so their K/V stream is shared in that XCD's L2.
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -83,9 +84,15 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
                                                           float* __restrict__ meff_out, int T, int Hq, int Hkv) {
+    // Workgroup i is dispatched to XCD i % 8.  The flat grid is renumbered so that every XCD
+    // receives a contiguous range of (batch, head, tile) items, and the tiles of one head
+    // share that XCD's L2 for their K/V stream; within a head, heaviest (last) tiles first.
     const int nqt = (T + BQ - 1) / BQ;
-    const int qt = nqt - 1 - (int)blockIdx.x;  // heaviest tiles first
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
+    const int item = xcd * per + min(xcd, extra) + (wg >> 3);
+    const int bh = item / nqt;
+    const int qt = nqt - 1 - (item - bh * nqt);
+    const int h = bh % Hq, b = bh / Hq;
     const int hk = h / (Hq / Hkv);
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());  // wave-uniform
     const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
@@ -308,7 +315,8 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
 
 hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
     const int nqt = (a.T + BQ - 1) / BQ;
-    hipLaunchKernelGGL(polar_fwd_kernel, dim3(nqt, a.Hq, a.B), dim3(NT), 0, stream, (const bf16*)a.q,
+    if ((long long)nqt * a.Hq * a.B > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(polar_fwd_kernel, dim3(nqt * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
                        a.Hkv);
     return hipGetLastError();
