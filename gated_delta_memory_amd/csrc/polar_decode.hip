@@ -160,23 +160,70 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     }
 }
 
-// grid (Hq, B); block 64: lane d owns value dimension d.
-__global__ __launch_bounds__(64) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
-                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
-                                                           int nsplit, int cache_len) {
+// grid (Hq, B); block 256: lane d of wave j owns value dimension d of the ranges s = j (mod 4).
+// Each wave merges its ranges with a running maximum (records are read eight at a time,
+// independently of the merge), then the four partial merges are combined through LDS.
+constexpr int CNT = 256;
+__global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
+                                                            bf16* __restrict__ o, float* __restrict__ mu_out,
+                                                            int nsplit, int cache_len) {
     const int h = blockIdx.x, Hq = gridDim.x, b = blockIdx.y;
-    const int d = threadIdx.x;
+    const int d = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const float* base = ws + ((size_t)b * nsplit * Hq + h) * REC;
     const size_t step = (size_t)Hq * REC;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * step]);
-    float L = 0.f, Q2 = 0.f, Sv = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float* r = base + s * step;
-        const float e = (r[0] == -INFINITY) ? 0.0f : fast_exp2(r[0] - M);
-        L += e * r[1];
-        Q2 += e * e * r[2];
-        Sv += e * r[4 + d];
+    float M = -INFINITY, L = 0.f, Q2 = 0.f, Sv = 0.f;
+    constexpr int U = 8;
+    for (int s0 = wv; s0 < nsplit; s0 += 4 * U) {
+        float rm[U], rl[U], rq[U], rs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sp = s0 + 4 * u;
+            if (sp < nsplit) {
+                const float* r = base + sp * step;
+                rm[u] = r[0];
+                rl[u] = r[1];
+                rq[u] = r[2];
+                rs[u] = r[4 + d];
+            } else {
+                rm[u] = -INFINITY;
+                rl[u] = rq[u] = rs[u] = 0.f;
+            }
+        }
+        float bm = M;
+#pragma unroll
+        for (int u = 0; u < U; ++u) bm = fmaxf(bm, rm[u]);
+        if (bm == -INFINITY) continue;  // nothing seen yet (empty ranges)
+        const float e0 = fast_exp2(M - bm);  // 0 when M = -inf
+        L *= e0;
+        Q2 *= e0 * e0;
+        Sv *= e0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float e = (rm[u] == -INFINITY) ? 0.0f : fast_exp2(rm[u] - bm);
+            L += e * rl[u];
+            Q2 += e * e * rq[u];
+            Sv += e * rs[u];
+        }
+        M = bm;
+    }
+    __shared__ float part[4][3];
+    __shared__ float psv[4][64];
+    if (d == 0) {
+        part[wv][0] = M;
+        part[wv][1] = L;
+        part[wv][2] = Q2;
+    }
+    psv[wv][d] = Sv;
+    __syncthreads();
+    if (wv != 0) return;
+    M = fmaxf(fmaxf(part[0][0], part[1][0]), fmaxf(part[2][0], part[3][0]));
+    L = Q2 = Sv = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float e = (part[j][0] == -INFINITY) ? 0.0f : fast_exp2(part[j][0] - M);
+        L += e * part[j][1];
+        Q2 += e * e * part[j][2];
+        Sv += e * psv[j][d];
     }
     const float n = (float)cache_len;
     const float t = 1.0f + softplus(prm.temp_raw[h]) * logf(n);
@@ -217,7 +264,7 @@ hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
     } else
     ATMA_PD_CASE(1) ATMA_PD_CASE(2) ATMA_PD_CASE(4) ATMA_PD_CASE(8) { return hipErrorInvalidValue; }
 #undef ATMA_PD_CASE
-    hipLaunchKernelGGL(polar_decode_combine, dim3(a.Hq, a.B), dim3(64), 0, stream, (const float*)ws, a.p,
+    hipLaunchKernelGGL(polar_decode_combine, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
                        (bf16*)a.o, a.mu_out, nsplit, a.cache_len);
     return hipGetLastError();
 }

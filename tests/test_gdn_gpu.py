@@ -73,6 +73,13 @@ def test_gdn_prefill_b1_t64k(atma):
     _run_and_check(atma, inp, "bf16", tag="b1_t64k")
 
 
+def test_gdn_prefill_b1_t256k(atma):
+    """Evaluation-length prefill: B=1, T=262144, H=8, d=128, all heads against the sequential oracle."""
+    w = workloads.WORKLOADS["prefill_b1_t256k"]
+    inp = workloads.make_gdn_inputs(w.B, w.T, w.gdn_H, w.gdn_D, dtype=w.dtype, seed=w.seed)
+    _run_and_check(atma, inp, "bf16", tag="b1_t256k")
+
+
 def test_gdn_resume_equals_one_pass(atma):
     """prefill(T1) then prefill(T2, init=final) equals prefill(T1+T2) (state carry across calls)."""
     inp = workloads.make_gdn_inputs(2, 300, 2, 128, 128, dtype="bf16", seed=7)

@@ -77,6 +77,13 @@ def test_polar_prefill_b1_t64k(atma):
     _check_prefill(atma, inp, rows=sample_rows(w.T, n_random=8), tag="b1_t64k")
 
 
+def test_polar_prefill_b1_t256k(atma):
+    """Evaluation-length prefill: B=1, T=262144, Hq=16 (sampled rows)."""
+    w = workloads.WORKLOADS["prefill_b1_t256k"]
+    inp = workloads.make_polar_inputs(w.B, w.T, w.polar_Hq, w.polar_Hkv, w.polar_D, seed=w.seed)
+    _check_prefill(atma, inp, rows=sample_rows(w.T, n_random=8), tag="b1_t256k")
+
+
 def test_polar_deterministic(atma):
     inp = workloads.make_polar_inputs(2, 700, 4, 4, 64, seed=9)
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
@@ -122,4 +129,19 @@ def test_polar_decode_262k_context(atma):
                               _cpu_params(inp["params"]))
     eo, emu = out_err(to_np(o), ref["o"], "bf16"), rel_err(to_np(mu), ref["mu"])
     note(f"  polar decode 262k err_o={eo:.3e} err_mu={emu:.3e}")
+    assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
+
+
+def test_polar_decode_262k_context_b16(atma):
+    """Evaluation-length decode at batch 16 (262144-token caches); sequences 0 and 11 are checked
+    against the oracle (sequences are independent)."""
+    L = workloads.DECODE_CONTEXT
+    inp = workloads.make_decode_inputs(16, L, device="cuda", seed=3)
+    o, mu = atma.atma_polar_attn_decode(inp["q"], inp["k_cache"], inp["v_cache"], L, inp["params"], want_mu=True)
+    torch.cuda.synchronize()
+    idx = [0, 11]
+    ref = oracle.polar_decode(inp["q"][idx].cpu(), inp["k_cache"][idx].cpu(), inp["v_cache"][idx].cpu(), L,
+                              _cpu_params(inp["params"]))
+    eo, emu = out_err(to_np(o[idx]), ref["o"], "bf16"), rel_err(to_np(mu[idx]), ref["mu"])
+    note(f"  polar decode 262k b16 err_o={eo:.3e} err_mu={emu:.3e}")
     assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
