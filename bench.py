@@ -48,7 +48,13 @@ def decode_bytes(B, L, Hkv=16, D=64, H=8, Dg=128):
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for a
 # device copy of known size; keyed by the SHA-256 of the kernel's sources at the time the
 # counters were taken, so an edited kernel reports null until it is measured again.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # layer_b8_t2k: FETCH_SIZE 49,294 KiB x 2.0 + WRITE_SIZE 32,768 KiB x 1.0 per dispatch
+    "polar_fwd_kernel": {"sha": "4a5c07e5f868ef39", "bytes": 134508544},
+    # layer_b8_t2k, prep + carry + out: FETCH (49,766 + 82,032 + 73,752) KiB x 2.0
+    # + WRITE (147,520 + 102,400 + 32,768) KiB x 1.0
+    "atma_gdn_fwd (prep+carry+out)": {"sha": "b381695d36416938", "bytes": 710438912},
+}
 
 
 def _sources_sha(names):
@@ -161,16 +167,13 @@ def main():
     gb = gdn_bytes(B, T, w.gdn_H, w.gdn_D)
     polar_tflops = pf / (polar_ms * 1e-3) / 1e12
     gdn_gbs = gb / (gdn_ms * 1e-3) / 1e9
-    if polar_ms >= gdn_ms:
-        roofline = {"kernel": "polar_fwd_kernel", "bound": "mfma", "achieved": round(polar_tflops, 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(polar_tflops / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic("polar_fwd_kernel"), "launch_ms": round(polar_ms, 4),
-                    "per_launch": f"{pf:.4e} flop = 4*64*B*Hq*T(T+1)/2, B={B} T={T} Hq={w.polar_Hq}"}
-    else:
-        roofline = {"kernel": "atma_gdn_fwd (prep+carry+out)", "bound": "hbm", "achieved": round(gdn_gbs, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gdn_gbs / PEAK_HBM_GBS, 4),
-                    "traffic": measured_traffic("atma_gdn_fwd (prep+carry+out)"), "launch_ms": round(gdn_ms, 4),
-                    "per_launch": f"{gb:.4e} B = B*H*T*(4*D*2+8) + B*H*D*D*4"}
+    # The step's longest single kernel is the Polar prefill kernel (the memory call is three
+    # shorter kernels: prep, carry, output; see the rocprofv3 summaries), so it carries the
+    # roofline object; the memory call's HBM fraction is reported beside it.
+    roofline = {"kernel": "polar_fwd_kernel", "bound": "mfma", "achieved": round(polar_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(polar_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("polar_fwd_kernel"), "launch_ms": round(polar_ms, 4),
+                "per_launch": f"{pf:.4e} flop = 4*64*B*Hq*T(T+1)/2, B={B} T={T} Hq={w.polar_Hq}"}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -180,7 +183,10 @@ def main():
                    "chunk": w.chunk, "state": "fp32"},
         "roofline": roofline,
         "breakdown_ms": {"gdn_fwd": round(gdn_ms, 4), "polar_fwd": round(polar_ms, 4),
-                         "gdn_hbm_GBps": round(gdn_gbs, 1), "polar_TFLOPs": round(polar_tflops, 2)},
+                         "gdn_hbm_GBps": round(gdn_gbs, 1), "gdn_hbm_frac": round(gdn_gbs / PEAK_HBM_GBS, 4),
+                         "gdn_bytes_per_call": f"{gb:.4e} B = B*H*T*(4*D*2+8) + B*H*D*D*4",
+                         "gdn_traffic": measured_traffic("atma_gdn_fwd (prep+carry+out)"),
+                         "polar_TFLOPs": round(polar_tflops, 2)},
     }
     del inp, g, p, o_g, S_g, ws_g, o_p
     torch.cuda.empty_cache()
@@ -205,6 +211,28 @@ def secondary(torch, atma, workloads):
     o_p = torch.empty_like(p["q"])
     tg, tp = Timer(torch), Timer(torch)
     for it in range(4):
+        (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
+                                                                  o=o_g, final_state=S_g, workspace=ws_g))
+        (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+    torch.cuda.synchronize()
+    gm, pm = tg.mean_ms(), tp.mean_ms()
+    pf = polar_flops(w.B, w.T, w.polar_Hq)
+    res[w.name] = {"tokens_per_s": round(w.B * w.T / ((gm + pm) * 1e-3), 1), "gdn_ms": round(gm, 3),
+                   "polar_ms": round(pm, 3), "polar_mfma_frac": round(pf / (pm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "gdn_hbm_frac": round(gdn_bytes(w.B, w.T, w.gdn_H) / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del inp, g, p, o_g, ws_g, S_g, o_p
+    torch.cuda.empty_cache()
+    # 256K prefill, once (one warm-up, one timed call of each)
+    w = workloads.WORKLOADS["prefill_b1_t256k"]
+    inp = workloads.make_workload(w, device="cuda")
+    g, p = inp["gdn"], inp["polar"]
+    o_g = torch.empty_like(g["v"])
+    ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
+                       device="cuda")
+    S_g = torch.empty(w.B, w.gdn_H, w.gdn_D, w.gdn_D, device="cuda")
+    o_p = torch.empty_like(p["q"])
+    tg, tp = Timer(torch), Timer(torch)
+    for it in range(2):
         (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
                                                                   o=o_g, final_state=S_g, workspace=ws_g))
         (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
