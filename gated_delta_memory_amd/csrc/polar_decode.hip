@@ -30,7 +30,7 @@ __device__ __forceinline__ float softplus(float x) { return x > 0.0f ? x + log1p
 
 int num_splits(int B, int cache_len) {
     const int by_len = (cache_len + 127) / 128;
-    const int target = 1024 / B > 0 ? 1024 / B : 1;
+    const int target = 512 / B > 0 ? 512 / B : 1;  // about two workgroups per CU
     int n = by_len < target ? by_len : target;
     return n < 1 ? 1 : n;
 }
@@ -160,10 +160,11 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     }
 }
 
-// grid (Hq, B); block 256: lane d of wave j owns value dimension d of the ranges s = j (mod 4).
-// Each wave merges its ranges with a running maximum (records are read eight at a time,
-// independently of the merge), then the four partial merges are combined through LDS.
-constexpr int CNT = 256;
+// grid (Hq, B); block 1024: lane d of wave j owns value dimension d of the ranges s = j (mod 16).
+// Each wave merges its ranges with a running maximum, eight records per round (their loads
+// are independent of the merge), then the sixteen partial merges are combined through LDS.
+constexpr int CNW = 16;        // waves per combine workgroup
+constexpr int CNT = 64 * CNW;  // threads per combine workgroup
 __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
                                                             bf16* __restrict__ o, float* __restrict__ mu_out,
                                                             int nsplit, int cache_len) {
@@ -173,25 +174,24 @@ __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restr
     const size_t step = (size_t)Hq * REC;
     float M = -INFINITY, L = 0.f, Q2 = 0.f, Sv = 0.f;
     constexpr int U = 8;
-    for (int s0 = wv; s0 < nsplit; s0 += 4 * U) {
-        float rm[U], rl[U], rq[U], rs[U];
+    for (int s0 = wv; s0 < nsplit; s0 += CNW * U) {
+        f32x4 hd[U];  // M, L, Q2, pad of each record
+        float rs[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int sp = s0 + 4 * u;
+            const int sp = s0 + CNW * u;
             if (sp < nsplit) {
                 const float* r = base + sp * step;
-                rm[u] = r[0];
-                rl[u] = r[1];
-                rq[u] = r[2];
+                hd[u] = *(const f32x4*)r;
                 rs[u] = r[4 + d];
             } else {
-                rm[u] = -INFINITY;
-                rl[u] = rq[u] = rs[u] = 0.f;
+                hd[u] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
+                rs[u] = 0.f;
             }
         }
         float bm = M;
 #pragma unroll
-        for (int u = 0; u < U; ++u) bm = fmaxf(bm, rm[u]);
+        for (int u = 0; u < U; ++u) bm = fmaxf(bm, hd[u][0]);
         if (bm == -INFINITY) continue;  // nothing seen yet (empty ranges)
         const float e0 = fast_exp2(M - bm);  // 0 when M = -inf
         L *= e0;
@@ -199,15 +199,15 @@ __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restr
         Sv *= e0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float e = (rm[u] == -INFINITY) ? 0.0f : fast_exp2(rm[u] - bm);
-            L += e * rl[u];
-            Q2 += e * e * rq[u];
+            const float e = (hd[u][0] == -INFINITY) ? 0.0f : fast_exp2(hd[u][0] - bm);
+            L += e * hd[u][1];
+            Q2 += e * e * hd[u][2];
             Sv += e * rs[u];
         }
         M = bm;
     }
-    __shared__ float part[4][3];
-    __shared__ float psv[4][64];
+    __shared__ float part[CNW][3];
+    __shared__ float psv[CNW][64];
     if (d == 0) {
         part[wv][0] = M;
         part[wv][1] = L;
@@ -216,10 +216,12 @@ __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restr
     psv[wv][d] = Sv;
     __syncthreads();
     if (wv != 0) return;
-    M = fmaxf(fmaxf(part[0][0], part[1][0]), fmaxf(part[2][0], part[3][0]));
+    M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CNW; ++j) M = fmaxf(M, part[j][0]);
     L = Q2 = Sv = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < CNW; ++j) {
         const float e = (part[j][0] == -INFINITY) ? 0.0f : fast_exp2(part[j][0] - M);
         L += e * part[j][1];
         Q2 += e * e * part[j][2];
