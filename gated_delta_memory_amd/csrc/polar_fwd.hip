@@ -80,7 +80,7 @@ __device__ __forceinline__ bf16x4 tr_read(const char* lds_base, int byte_off) {
 __shared__ __align__(16) char g_kv0[2 * BK * D * 2];
 __shared__ __align__(16) char g_kv1[2 * BK * D * 2];
 
-__global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
                                                           float* __restrict__ meff_out, int T, int Hq, int Hkv) {
@@ -165,32 +165,13 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
         if (key0 > qw0 + QW - 1) return;  // whole block in this wave's future
         const bool edge = (key0 + BK - 1 > qw0) || (key0 + BK > T);
 
-        // all fragment reads of the block up front: their latency overlaps the MFMAs and the
-        // weight computation
-        bf16x8 kf[2][4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = *(const bf16x8*)(Ks + koff[ks] + kt * 32 * 128);
-        bf16x8 vf[2][2][2];  // [kt][st][dt]
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt) {
-                    const int base = voff[dt] + (32 * kt + 16 * st) * 128;
-                    const bf16x4 lo = tr_read(Vs, base);
-                    const bf16x4 hi = tr_read(Vs, base + 8 * 128);
-                    vf[kt][st][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
 
         // S^T = K Q^T : two 32-key sub-tiles, chains interleaved
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(kf[kt][ks], qf[ks], s[kt]);
+            for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(*(const bf16x8*)(Ks + koff[ks] + kt * 32 * 128), qf[ks], s[kt]);
 
         // causal / length mask on edge blocks (raw scores; cq > 0 scales them later)
         if (edge) {
@@ -241,7 +222,12 @@ __global__ __launch_bounds__(NT, 2) void polar_fwd_kernel(const bf16* __restrict
                     pf[e + 1] = pp[1];
                 }
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma32(vf[kt][st][dt], pf, oacc[dt]);
+                for (int dt = 0; dt < 2; ++dt) {
+                    const int base = voff[dt] + (32 * kt + 16 * st) * 128;
+                    const bf16x4 lo = tr_read(Vs, base);
+                    const bf16x4 hi = tr_read(Vs, base + 8 * 128);
+                    oacc[dt] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf, oacc[dt]);
+                }
             }
         }
     };
