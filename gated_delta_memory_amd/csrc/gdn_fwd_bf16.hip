@@ -102,8 +102,9 @@ struct PrepSmem {
     bf16 Xs[C * LDX];   // Q, later V
     float Am[C * LDA];  // A, later the W staging tile
     float Tm[C * LDA];  // P staging, then Tinv, then the U staging tile
-    float Gs[C];
-    float Bs[C];
+    float Gs[C];  // g_r = sum_{s <= r} ln alpha_s
+    float Bs[C];  // beta_r
+    float Es[C];  // beta_r e^{g_r}
 };
 
 // B fragment (kmap order over the chunk positions) of a row-major bf16 LDS tile, columns
@@ -134,17 +135,19 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
     const int NC = gridDim.x;
     const int t0 = c * C;
     const int n = min(C, Tlen - t0);
-    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id()), G = lane >> 4, l16 = lane & 15;
     const size_t tok0 = ((size_t)b * Tlen + t0) * H + h;
     const size_t cid = ((size_t)b * H + h) * NC + c;
     char* ra = rg.ra + cid * L::RA;
     char* rb = rg.rb + cid * L::RB;
 
-    // ---- A: K and Q into LDS, cumulative log decay ---------------------------------------
+    // ---- A: K and Q into LDS, cumulative log decay; V's load starts here and lands after D --
+    TileRegs<bf16, C, DV> vr;
     {
         TileRegs<bf16, C, DK> kr, qr;
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
         qr.load(q + tok0 * DK, (size_t)H * DK, n);
+        vr.load(v + tok0 * DV, (size_t)H * DV, n);
         kr.template store<LDK>(sm.Ks);
         qr.template store<LDX>(sm.Xs);
     }
@@ -159,6 +162,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         }
         sm.Gs[lane] = la;
         sm.Bs[lane] = be;
+        sm.Es[lane] = be * __expf(la);
         if (lane == C - 1) rg.egl[cid] = __expf(la);
     }
     __syncthreads();
@@ -175,31 +179,42 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
             i = (u < 3) ? 0 : (u < 5) ? 1 : 2;
             j = (u < 3) ? u + 1 : (u < 5) ? u - 1 : 3;
         }
+        // gate values of this lane's rows r = 16 i + 4 G + x and column s = 16 j + l16
+        const f32x4 gr = *(const f32x4*)&sm.Gs[16 * i + 4 * G];
+        const f32x4 br = *(const f32x4*)&sm.Bs[16 * i + 4 * G];
+        const float gs = sm.Gs[16 * j + l16];
         f32x4 kk = {0, 0, 0, 0}, qk = {0, 0, 0, 0};
         if (ti < 10) {
+            // every fragment of the tile is requested before the first MFMA waits on one
+            Frag<bf16> a[DK / 32], bq[DK / 32], bk[DK / 32];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                Frag<bf16> a, bq, bk;
-                load_frag_rows(bk, sm.Ks, LDK, 16 * j + l16, 32 * kb);
-                load_frag_rows(a, sm.Ks, LDK, 16 * i + l16, 32 * kb);
-                load_frag_rows(bq, sm.Xs, LDX, 16 * i + l16, 32 * kb);
-                mma(kk, a, bk);
-                mma(qk, bq, bk);
+                load_frag_rows(bk[kb], sm.Ks, LDK, 16 * j + l16, 32 * kb);
+                load_frag_rows(a[kb], sm.Ks, LDK, 16 * i + l16, 32 * kb);
+                load_frag_rows(bq[kb], sm.Xs, LDX, 16 * i + l16, 32 * kb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                mma(kk, a[kb], bk[kb]);
+                mma(qk, bq[kb], bk[kb]);
             }
         }
         const int s = 16 * j + l16;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * i + 4 * G + x;
-            const float e = (s <= r) ? __expf(sm.Gs[r] - sm.Gs[s]) : 0.0f;
-            sm.Am[r * LDA + s] = (s < r) ? sm.Bs[r] * e * kk[x] : 0.0f;
-            *(half*)(pstage + fm_off<C>(r, s)) = (half)(e * qk[x]);
+            // g_r - g_s <= 0 wherever the mask keeps the entry (s <= r)
+            const float e = __expf(fminf(gr[x] - gs, 0.0f));
+            sm.Am[r * LDA + s] = (s < r) ? br[x] * e * kk[x] : 0.0f;
+            *(half*)(pstage + fm_off<C>(r, s)) = (half)((s <= r) ? e * qk[x] : 0.0f);
         }
     }
     __syncthreads();
     copy_out(rb + L::B_P, pstage, C * C * 2);
 
     // ---- C: QG = diag(e^g) Q and KD^T, straight to the records ------------------------------
+#pragma unroll
     for (int id = threadIdx.x; id < C * DK / 8; id += NT) {
         const int r = id / (DK / 8), cc = id % (DK / 8);
         const float e = __expf(sm.Gs[r]);
@@ -212,8 +227,10 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
     }
     {
         const float glast = sm.Gs[C - 1];
+#pragma unroll
         for (int combo = w * 4 + G; combo < (DK / 16) * (C / 8); combo += 16) {
             const int cg = combo % (DK / 16), pc = 8 * (combo / (DK / 16));
+            const f32x4 g0 = *(const f32x4*)&sm.Gs[pc], g1 = *(const f32x4*)&sm.Gs[pc + 4];
             const char* kbase = (const char*)sm.Ks;
             const int col = 16 * cg + 4 * (l16 & 3);
             const s16x4 r0 = tr_read_b16(kbase + ((pc + (l16 >> 2)) * LDK + col) * 2);
@@ -222,16 +239,13 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
             f16x8 y;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                y[t] = (half)((float)k0[t] * __expf(glast - sm.Gs[pc + t]));
-                y[t + 4] = (half)((float)k1[t] * __expf(glast - sm.Gs[pc + 4 + t]));
+                y[t] = (half)((float)k0[t] * __expf(glast - g0[t]));
+                y[t + 4] = (half)((float)k1[t] * __expf(glast - g1[t]));
             }
             *(f16x4*)(ra + L::A_KDT + fm_off<C>(16 * cg + l16, pc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
             *(f16x4*)(ra + L::A_KDT + fm_off<C>(16 * cg + l16, pc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
         }
     }
-    // V is needed only for U: start its load now, land it in Xs after Tinv
-    TileRegs<bf16, C, DV> vr;
-    vr.load(v + tok0 * DV, (size_t)H * DV, n);
     __syncthreads();  // P staging copied, Q consumed
 
     // ---- D: Tinv = (I + A)^{-1} -----------------------------------------------------------
@@ -300,12 +314,20 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         Frag<bf16> wh[2], wl[2], uh[2], ul[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            // slots e < 4 hold chunk positions 32 kb + 4 G + e, slots e >= 4 hold 32 kb + 16 + 4 G + e - 4
+            f32x4 tv[2], bv[2], ev[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int s0 = 32 * kb + 16 * hh + 4 * G;
+                tv[hh] = *(const f32x4*)&sm.Tm[(16 * i + l16) * LDA + s0];
+                bv[hh] = *(const f32x4*)&sm.Bs[s0];
+                ev[hh] = *(const f32x4*)&sm.Es[s0];
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int s = 32 * kb + kmap(G, e);
-                const float t = sm.Tm[(16 * i + l16) * LDA + s];
-                const float tw = t * sm.Bs[s] * __expf(sm.Gs[s]);
-                const float tu = t * sm.Bs[s];
+                const float t = tv[e >> 2][e & 3];
+                const float tw = t * ev[e >> 2][e & 3];
+                const float tu = t * bv[e >> 2][e & 3];
                 const bf16 hw = (bf16)tw, hu = (bf16)tu;
                 wh[kb].set_raw(e, hw);
                 wl[kb].set(e, tw - (float)hw);
@@ -316,15 +338,22 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         __syncthreads();  // Tinv consumed, V landed: Am and Tm become staging tiles
         char* wstage = (char*)sm.Am;
         char* ustage = (char*)sm.Tm;
+        // B fragments of a whole product are requested before its MFMAs (one LDS round trip)
+        Frag<bf16> bx[(DK > DV ? DK : DV) / 16][2];
+#pragma unroll
+        for (int ct = 0; ct < DK / 16; ++ct)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDK, ct, kb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ct = 0; ct < DK / 16; ++ct) {
             f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb < nkb) {
-                    const Frag<bf16> bk = bfrag_tr(sm.Ks, LDK, ct, kb);
-                    mma(acc, wh[kb], bk);
-                    mma(acc, wl[kb], bk);
+                    mma(acc, wh[kb], bx[ct][kb]);
+                    mma(acc, wl[kb], bx[ct][kb]);
                 }
             }
 #pragma unroll
@@ -332,14 +361,19 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
                 *(half*)(wstage + fm_off<DK>(16 * i + 4 * G + x, 16 * ct + l16)) = (half)acc[x];
         }
 #pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Xs, LDX, ct, kb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
             f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb < nkb) {
-                    const Frag<bf16> bv = bfrag_tr(sm.Xs, LDX, ct, kb);
-                    mma(acc, uh[kb], bv);
-                    mma(acc, ul[kb], bv);
+                    mma(acc, uh[kb], bx[ct][kb]);
+                    mma(acc, ul[kb], bx[ct][kb]);
                 }
             }
             f16x4 y;
