@@ -16,8 +16,8 @@
 // overflow and most blocks skip the rescale.  Exponentials are base 2 on logits scaled
 // by log2(e).
 //
-// Kernel layout (one workgroup of 4 waves per 128-query tile, head and batch; each wave
-// owns 32 consecutive queries):
+// Kernel layout (one workgroup of 4 waves per pair of 128-query tiles of one head and batch;
+// within a tile each wave owns 32 consecutive queries):
 //   * keys stream in blocks of 64 through two LDS stages (K and V row-major, 16-byte chunks
 //     XOR-swizzled by key so fragment reads are bank-conflict free), filled by asynchronous
 //     global->LDS copies one block ahead, one barrier per block;
@@ -28,8 +28,9 @@
 //     fragments come straight from the row-major V tile with ds_read_b64_tr_b16;
 //   * L and Q2 are accumulated from the bf16 weights with v_dot2_f32_bf16, so they use
 //     exactly the weights the value sum uses;
-//   * query tiles are scheduled heaviest (last) first for causal load balance, and the tiles of
-//     one (batch, head) go to one XCD so their K/V stream is shared in that XCD's L2.
+//   * a workgroup computes two query tiles of one (batch, head), the k-th heaviest and the
+//     k-th lightest, so all workgroups stream the same number of key blocks (causal balance);
+//     the tiles of one (batch, head) go to one XCD so their K/V stream is shared in its L2.
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -83,42 +84,27 @@ __shared__ __align__(16) char g_kv1[2 * BK * D * 2];
 __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
-                                                          float* __restrict__ meff_out, int T, int Hq, int Hkv) {
-    // Workgroup i is dispatched to XCD i % 8.  The flat grid is renumbered so that every XCD
-    // receives a contiguous range of (batch, head, tile) items, and the tiles of one head
-    // share that XCD's L2 for their K/V stream; within a head, heaviest (last) tiles first.
+                                                          float* __restrict__ meff_out, int T, int Hq, int Hkv,
+                                                          int paired) {
+    // Work items.  With `paired` set (few tiles in all), a workgroup computes two query tiles
+    // of one (batch, head), tile nqt - 1 - p and tile p: every pair streams the same number of
+    // key blocks (causal balance) and the per-tile start-up and finalisation are spread over
+    // twice the work.  Otherwise a workgroup computes one tile, heaviest (last) tiles first.
+    // Workgroup i is dispatched to XCD i % 8; the flat grid is renumbered so that every XCD
+    // receives a contiguous range of items and the tiles of one (batch, head) share that
+    // XCD's L2 for their K/V stream.
     const int nqt = (T + BQ - 1) / BQ;
+    const int per_bh = paired ? (nqt + 1) / 2 : nqt;
     const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
     const int item = xcd * per + min(xcd, extra) + (wg >> 3);
-    const int bh = item / nqt;
-    const int qt = nqt - 1 - (item - bh * nqt);
+    const int bh = item / per_bh;
+    const int pr = item - bh * per_bh;
     const int h = bh % Hq, b = bh / Hq;
     const int hk = h / (Hq / Hkv);
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());  // wave-uniform
     const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
-    const int q0 = qt * BQ;
-    const int qw0 = q0 + w * QW;
-    const int qi = qw0 + l32;  // this lane's query
-
     const float a_t = softplus(prm.temp_raw[h]);
-    const float cq = (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * 0.125f;  // t_i log2(e) / sqrt(64)
-
-    // Q^T fragments (B operand): lane supplies Q[qi][16 ks + 8 G2 + e]
     const size_t qstride = (size_t)Hq * D;
-    bf16x8 qf[4];
-    {
-        const int qc = min(qi, T - 1);
-        const bf16* qrow = q + ((size_t)b * T + qc) * qstride + (size_t)h * D + 8 * G2;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
-    }
-
-    f32x16 oacc[2] = {f32x16{}, f32x16{}};  // O^T[d = 32 dt + 8(x/4) + 4 G2 + x%4][qi]
-    float m_used = -INFINITY;
-    float lsum[4] = {0.f, 0.f, 0.f, 0.f}, q2sum[4] = {0.f, 0.f, 0.f, 0.f};  // split to shorten dependency chains
-
-    const int kend = min(T, q0 + BQ);
-    const int nkb = (kend + BK - 1) / BK;
     const size_t kvstride = (size_t)Hkv * D;
     const unsigned rowbytes = (unsigned)(kvstride * 2);
     const bf16* kbase = k + (size_t)b * T * kvstride + (size_t)hk * D;
@@ -158,6 +144,28 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
         const int dcol = 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3);
         voff[dt] = swz_v(4 * G2 + (i16 >> 2), dcol >> 3) + ((dcol & 7) << 1);
     }
+
+  auto tile = [&](int qt) {
+    const int q0 = qt * BQ;
+    const int qw0 = q0 + w * QW;
+    const int qi = qw0 + l32;  // this lane's query
+    const float cq = (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * 0.125f;  // t_i log2(e) / sqrt(64)
+
+    // Q^T fragments (B operand): lane supplies Q[qi][16 ks + 8 G2 + e]
+    bf16x8 qf[4];
+    {
+        const int qc = min(qi, T - 1);
+        const bf16* qrow = q + ((size_t)b * T + qc) * qstride + (size_t)h * D + 8 * G2;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
+    }
+
+    f32x16 oacc[2] = {f32x16{}, f32x16{}};  // O^T[d = 32 dt + 8(x/4) + 4 G2 + x%4][qi]
+    float m_used = -INFINITY;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f}, q2sum[4] = {0.f, 0.f, 0.f, 0.f};  // split to shorten dependency chains
+
+    const int kend = min(T, q0 + BQ);
+    const int nkb = (kend + BK - 1) / BK;
 
     auto block = [&](int kb, const char* Ks) {
         const char* Vs = Ks + BK * D * 2;
@@ -295,16 +303,27 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
             if (meff_out) meff_out[si] = meff;
         }
     }
+  };
+
+    tile(nqt - 1 - pr);
+    if (paired && pr != nqt - 1 - pr) {
+        lds_barrier();  // every wave is done with the stages before they are refilled
+        tile(pr);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
     const int nqt = (a.T + BQ - 1) / BQ;
-    if ((long long)nqt * a.Hq * a.B > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(polar_fwd_kernel, dim3(nqt * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
+    const long long ntiles = (long long)nqt * a.Hq * a.B;
+    if (ntiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // pair tiles when there are at most about two rounds of workgroups (4 per CU on 256 CUs)
+    const int paired = ntiles <= 2048 * 2 ? 1 : 0;
+    const int per_bh = paired ? (nqt + 1) / 2 : nqt;
+    hipLaunchKernelGGL(polar_fwd_kernel, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
-                       a.Hkv);
+                       a.Hkv, paired);
     return hipGetLastError();
 }
 
