@@ -18,6 +18,14 @@
 //               It writes the fp16 operands it built anyway -- S_in^T and Delta, in MFMA
 //               fragment order -- for the output kernel.
 //   gdn_out_h   (parallel over chunks) - O = QG S_in^T + P Delta, coalesced bf16 stores.
+// Long sequences with few (batch, head) pairs leave most of the GPU idle during the carry, so
+// the sequence is cut into segments.  Per chunk the state map is affine in S,
+//     S_out = S_in A_c + B_c,  A_c = e^{g_last} I - W^T KD,  B_c = U^T KD,
+// and so is a whole segment: S_end = S_start A_seg + B_seg.  A summary pass (the carry
+// kernel in summary mode, all segments in parallel) runs the segment from S_start = 0 for the
+// Dv real state rows (giving B_seg) and from S_start = I with U = 0 for Dk extra rows (giving
+// A_seg); gdn_seg_scan then walks the segments in order, S_start(s+1) = S_start(s) A_seg(s) +
+// B_seg(s) in fp32, and the carry proper runs every segment in parallel from its S_start.
 // fp16 staging (11-bit mantissa) keeps the result within a few 1e-3 of the fp64
 // recurrence; it needs |v| and the state entries below 2^15.
 #include "gdn_common.hpp"
@@ -52,15 +60,17 @@ template <int DK, int DV> struct Lay {
     static constexpr size_t SF = (size_t)DV * DK * 2;
     static constexpr size_t DF = (size_t)C * DV * 2;
     static constexpr size_t STAGE = A_U + USLICE;  // bytes one carry workgroup streams per chunk
-    static size_t total(size_t nchunks) { return nchunks * (RA + RB + SF + DF + sizeof(float)); }
+    static size_t total(size_t nchunks) { return nchunks * (RA + RB + SF + DF + sizeof(float)); }  // + seg_bytes
 };
 
 struct Regions {
     char *ra, *rb, *sf, *df;
     float* egl;
+    float* seg;  // segment summaries [B H][nseg][Dv + Dk rows][Dk]: B_seg rows, then A_seg rows
+    float* sst;  // segment start states [B H][nseg][Dv][Dk]
 };
 template <int DK, int DV>
-Regions regions(void* ws, size_t nchunks) {
+Regions regions(void* ws, size_t nchunks, size_t nbh, int nseg) {
     using L = Lay<DK, DV>;
     char* p = (char*)ws;
     Regions r;
@@ -69,7 +79,35 @@ Regions regions(void* ws, size_t nchunks) {
     r.sf = r.rb + nchunks * L::RB;
     r.df = r.sf + nchunks * L::SF;
     r.egl = (float*)(r.df + nchunks * L::DF);
+    char* q = (char*)(r.egl + nchunks);
+    q += (256 - (size_t)q % 256) % 256;
+    r.seg = nseg > 1 ? (float*)q : nullptr;
+    r.sst = nseg > 1 ? r.seg + nbh * nseg * (size_t)(DV + DK) * DK : nullptr;
     return r;
+}
+template <int DK, int DV>
+size_t seg_bytes(size_t nbh, int nseg) {
+    return nseg > 1 ? 256 + nbh * nseg * ((size_t)(DV + DK) * DK + (size_t)DV * DK) * sizeof(float) : 0;
+}
+
+// Number of segments: a cost model over the carry's per-chunk step (about 1.3 us) and the
+// scan's per-segment step (about 1.5 us), with one carry workgroup per CU on 256 CUs.
+int choose_nseg(int B, int T, int H, int Dk, int Dv) {
+    const int NC = (T + C - 1) / C;
+    const double bh = (double)B * H, tc = 1.3, ts = 1.5;
+    auto rounds = [](double wgs) { return wgs <= 256.0 ? 1.0 : (double)(long long)((wgs + 255.0) / 256.0); };
+    int best = 1;
+    double best_cost = rounds(bh * Dv / 64) * NC * tc;
+    for (int g = 2; g <= 64 && 4 * g <= NC; g *= 2) {
+        const int len = (NC + g - 1) / g;
+        const double cost = (rounds(bh * g * (Dv + Dk) / 64) + rounds(bh * g * Dv / 64)) * len * tc + g * ts;
+        if (cost < best_cost) {
+            best = g;
+            best_cost = cost;
+        }
+    }
+    const int len = (NC + best - 1) / best;
+    return (NC + len - 1) / len;  // every segment non-empty
 }
 
 // ---- fragment-major tiles -----------------------------------------------------------------
@@ -397,14 +435,14 @@ __shared__ __align__(16) char g_stage0[kStageMax];
 __shared__ __align__(16) char g_stage1[kStageMax];
 __shared__ __align__(16) char g_stage2[kStageMax];
 
-template <int DK, int DV>
+template <int DK, int DV, bool STORE>
 struct Carry {
     using L = Lay<DK, DV>;
     static constexpr int RBK = L::RBK, NKT = DK / 16;
     static constexpr int NCH = (int)L::STAGE / 16;  // 16-byte copies per chunk
     static constexpr int TPT = NCH / NT;             // tile copies per thread per chunk
     static constexpr int DPT = TPT + 1;              // all copies per thread per chunk (+ e^{g_last})
-    static constexpr int SPT = DK / 32 + 2;          // fragment stores per thread per chunk
+    static constexpr int SPT = STORE ? DK / 32 + 2 : 0;  // fragment stores per thread per chunk
     static_assert(L::STAGE + 1024 <= kStageMax, "stage too large");
     static_assert(NCH % NT == 0, "stage must be a whole number of copy rounds");
 
@@ -412,7 +450,8 @@ struct Carry {
     char* sf0;
     char* df0;
     const float* egl;
-    int sl;
+    int sl;       // U slice copied with each chunk
+    float ukeep;  // 1 for real state rows, 0 for the identity rows of a segment summary
 
     // Starts the copy of chunk c into `dst`.  The chunk's e^{g_last} is copied into the
     // stage too (every lane copies the same word, so all threads issue the same operations)
@@ -454,7 +493,7 @@ struct Carry {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
             acc_to_frag(sf[kb], st[2 * kb], st[2 * kb + 1]);
-            *(f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16) = sf[kb].v;
+            if constexpr (STORE) *(f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16) = sf[kb].v;
         }
         f16x8 kf[NKT][2];
 #pragma unroll
@@ -477,13 +516,13 @@ struct Carry {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) dl[i][x] = (float)u[i][x] - dl[i][x];
+            for (int x = 0; x < 4; ++x) dl[i][x] = ukeep * (float)u[i][x] - dl[i][x];
         Frag<half> df[2];
         char* dfo = df0 + (size_t)c * L::DF + (size_t)sl * 2 * 4096;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             acc_to_frag(df[kb], dl[2 * kb], dl[2 * kb + 1]);
-            *(f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16) = df[kb].v;
+            if constexpr (STORE) *(f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16) = df[kb].v;
         }
         // S_out^T = e^{g_last} S_in^T + KD^T Delta
 #pragma unroll
@@ -508,53 +547,142 @@ struct Carry {
 // Chunk 0 waits until only the copy of chunk 1 may be outstanding.
 // One workgroup per CU (the three stages fill the LDS): let the scheduler use the whole
 // register file to keep more LDS reads in flight.
-template <int DK, int DV>
+//
+// Grid (slices, H nseg, B); the workgroup walks the chunks of segment s of (b, h).
+// STORE (the carry proper): Dv / 64 slices of real state rows, starting from the segment's
+// start state (the initial state when there is one segment); writes the S_in^T and Delta
+// fragments for the output kernel and, in the last segment, the final state.
+// !STORE (segment summary): (Dv + Dk) / 64 slices; real rows start from zero, the Dk extra
+// rows start from the identity with U ignored; the end state goes to the summary region.
+template <int DK, int DV, bool STORE>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
-    Regions rg, const float* init_state, float* final_state,
-                                                     int Tlen, int H) {
+    Regions rg, const float* init_state, float* final_state, int Tlen, int H, int nseg, int seglen) {
     using L = Lay<DK, DV>;
-    using K = Carry<DK, DV>;
+    using K = Carry<DK, DV, STORE>;
     constexpr int NKT = DK / 16;
-    const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int sl = blockIdx.x, h = (int)blockIdx.y / nseg, sg = (int)blockIdx.y % nseg, b = blockIdx.z;
     const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
     const int NC = (Tlen + C - 1) / C;
-    const size_t c0 = ((size_t)b * H + h) * NC;
-    const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, sl};
+    const int cb = sg * seglen, n = min(NC - cb, seglen);  // this segment's chunks
+    const size_t bh = (size_t)b * H + h;
+    const size_t c0 = bh * NC + cb;
+    const bool real = sl < DV / 64;
+    const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, real ? sl : 0,
+              real ? 1.0f : 0.0f};
     const int row = sl * 64 + 16 * w + l16;  // state row held by this lane's accumulators
 
     f32x4 st[NKT];  // st[t][x] = S[row][16 t + 4 G + x]
-    const size_t srow = (((size_t)b * H + h) * DV + row) * DK;
+    if constexpr (STORE) {
+        const float* src = nseg > 1 ? rg.sst + (bh * nseg + sg) * DV * DK : init_state ? init_state + bh * DV * DK
+                                                                                      : nullptr;
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
-        st[t] = init_state ? *(const f32x4*)(init_state + srow + 16 * t + 4 * G) : f32x4{0, 0, 0, 0};
+        for (int t = 0; t < NKT; ++t)
+            st[t] = src ? *(const f32x4*)(src + (size_t)row * DK + 16 * t + 4 * G) : f32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) st[t][x] = (!real && 16 * t + 4 * G + x == row - DV) ? 1.0f : 0.0f;
+    }
 
     gdn::wait_vmcnt<0>();  // initial state in registers before the untracked copies start
-    const int last = NC - 1;
+    const int last = n - 1;
+    const int NC_seg = n;
     k.issue(0, g_stage0);
     k.issue(min(1, last), g_stage1);
     gdn::wait_vmcnt<K::DPT>();
     gdn::lds_barrier();
     k.issue(min(2, last), g_stage2);
     k.step(0, g_stage0, st);
-    for (int c = 1; c < NC; c += 3) {
+    for (int c = 1; c < NC_seg; c += 3) {
         gdn::wait_vmcnt<K::DPT + K::SPT>();
         gdn::lds_barrier();
         k.issue(min(c + 2, last), g_stage0);
         k.step(c, g_stage1, st);
-        if (c + 1 >= NC) break;
+        if (c + 1 >= NC_seg) break;
         gdn::wait_vmcnt<K::DPT + K::SPT>();
         gdn::lds_barrier();
         k.issue(min(c + 3, last), g_stage1);
         k.step(c + 1, g_stage2, st);
-        if (c + 2 >= NC) break;
+        if (c + 2 >= NC_seg) break;
         gdn::wait_vmcnt<K::DPT + K::SPT>();
         gdn::lds_barrier();
         k.issue(min(c + 4, last), g_stage2);
         k.step(c + 2, g_stage0, st);
     }
-    if (final_state) {
+    if constexpr (STORE) {
+        if (final_state && sg == nseg - 1) {
 #pragma unroll
-        for (int t = 0; t < NKT; ++t) *(f32x4*)(final_state + srow + 16 * t + 4 * G) = st[t];
+            for (int t = 0; t < NKT; ++t)
+                *(f32x4*)(final_state + (bh * DV + row) * DK + 16 * t + 4 * G) = st[t];
+        }
+    } else {
+        float* dst = rg.seg + ((bh * nseg + sg) * (DV + DK) + row) * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) *(f32x4*)(dst + 16 * t + 4 * G) = st[t];
+    }
+}
+
+// =========================================================================================
+// segment scan (sequential over segments, parallel over 16-row blocks of the state)
+// =========================================================================================
+// Grid (Dv / 16, H, B), 4 waves.  The workgroup owns state rows 16 rt .. 16 rt + 15 of (b, h)
+// (rows of S evolve independently): S_start(0) = initial state (or 0), S_start(s + 1) =
+// S_start(s) A_seg(s) + B_seg(s), exact fp32 products on v_mfma_f32_16x16x4_f32.  Wave w
+// computes output column tiles w, w + 4, ...
+template <int DK, int DV>
+struct ScanSmem {
+    static constexpr int LDS_S = DK + 4, LDS_A = DK + 16;  // strides with conflict-free operand reads
+    float S[16 * LDS_S];
+    float A[DK * LDS_A];
+};
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_seg_scan(Regions rg, const float* init_state, int H, int nseg) {
+    using S = ScanSmem<DK, DV>;
+    constexpr int LDS_S = S::LDS_S, LDS_A = S::LDS_A;
+    extern __shared__ __align__(16) char smem_raw[];
+    S& sm = *reinterpret_cast<S*>(smem_raw);
+    const int rt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const size_t bh = (size_t)b * H + h;
+    // start state rows into LDS and out as S_start(0)
+    for (int i = threadIdx.x; i < 16 * DK / 4; i += NT) {
+        const int r = i / (DK / 4), c4 = i % (DK / 4);
+        const size_t gi = (bh * DV + 16 * rt + r) * DK + 4 * c4;
+        const f32x4 x = init_state ? *(const f32x4*)(init_state + gi) : f32x4{0, 0, 0, 0};
+        *(f32x4*)&sm.S[r * LDS_S + 4 * c4] = x;
+        *(f32x4*)(rg.sst + bh * nseg * DV * DK + (size_t)(16 * rt + r) * DK + 4 * c4) = x;
+    }
+    for (int sg = 0; sg + 1 < nseg; ++sg) {
+        const float* sum = rg.seg + (bh * nseg + sg) * (DV + DK) * DK;
+        for (int i = threadIdx.x; i < DK * DK / 4; i += NT) {  // A_seg(sg) into LDS
+            const int r = i / (DK / 4), c4 = i % (DK / 4);
+            *(f32x4*)&sm.A[r * LDS_A + 4 * c4] = *(const f32x4*)(sum + (size_t)(DV + r) * DK + 4 * c4);
+        }
+        __syncthreads();
+        f32x4 acc[DK / 64];
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) {
+            const int ct = w + 4 * j;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[j][x] = sum[(size_t)(16 * rt + 4 * G + x) * DK + 16 * ct + l16];  // B_seg
+#pragma unroll 8
+            for (int kk = 0; kk < DK / 4; ++kk)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.S[l16 * LDS_S + 4 * kk + G],
+                                                              sm.A[(4 * kk + G) * LDS_A + 16 * ct + l16], acc[j],
+                                                              0, 0, 0);
+        }
+        __syncthreads();  // every wave is done reading S and A
+        float* nxt = rg.sst + (bh * nseg + sg + 1) * DV * DK;
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) {
+            const int ct = w + 4 * j;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                sm.S[(4 * G + x) * LDS_S + 16 * ct + l16] = acc[j][x];
+                nxt[(size_t)(16 * rt + 4 * G + x) * DK + 16 * ct + l16] = acc[j][x];
+            }
+        }
     }
 }
 
@@ -628,17 +756,29 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(Regions rg, bf16* __restrict_
 template <int DK, int DV>
 hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
     const int NC = (a.T + C - 1) / C;
-    const Regions rg = regions<DK, DV>(a.workspace, (size_t)a.B * a.H * NC);
+    const size_t nbh = (size_t)a.B * a.H;
+    const int nseg = choose_nseg(a.B, a.T, a.H, DK, DV);
+    const int seglen = (NC + nseg - 1) / nseg;
+    const Regions rg = regions<DK, DV>(a.workspace, nbh * NC, nbh, nseg);
     const size_t prep_smem = sizeof(PrepSmem<DK, DV>), out_smem = sizeof(OutSmem<DK, DV>);
+    const size_t scan_smem = sizeof(ScanSmem<DK, DV>);
     static const hipError_t attr = [&] {
-        const hipError_t e = ensure_lds_limit(gdn_prep_h<DK, DV>, prep_smem);
-        return e != hipSuccess ? e : ensure_lds_limit(gdn_out_h<DK, DV>, out_smem);
+        hipError_t e = ensure_lds_limit(gdn_prep_h<DK, DV>, prep_smem);
+        if (e == hipSuccess) e = ensure_lds_limit(gdn_out_h<DK, DV>, out_smem);
+        if (e == hipSuccess) e = ensure_lds_limit(gdn_seg_scan<DK, DV>, scan_smem);
+        return e;
     }();
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gdn_prep_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), prep_smem, stream, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, rg, a.T, a.H);
-    hipLaunchKernelGGL((gdn_carry_h<DK, DV>), dim3(DV / 64, a.H, a.B), dim3(NT), 0, stream, rg, a.init_state,
-                       a.final_state, a.T, a.H);
+    if (nseg > 1) {
+        hipLaunchKernelGGL((gdn_carry_h<DK, DV, false>), dim3((DV + DK) / 64, a.H * nseg, a.B), dim3(NT), 0, stream,
+                           rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen);
+        hipLaunchKernelGGL((gdn_seg_scan<DK, DV>), dim3(DV / 16, a.H, a.B), dim3(NT), scan_smem, stream, rg,
+                           a.init_state, a.H, nseg);
+    }
+    hipLaunchKernelGGL((gdn_carry_h<DK, DV, true>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream, rg,
+                       a.init_state, a.final_state, a.T, a.H, nseg, seglen);
     hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, rg, (bf16*)a.o, a.T, a.H);
     return hipGetLastError();
 }
@@ -646,11 +786,12 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t gdn_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
-    const size_t nchunks = (size_t)B * H * ((T + C - 1) / C);
-    if (Dk == 64 && Dv == 64) return Lay<64, 64>::total(nchunks);
-    if (Dk == 64 && Dv == 128) return Lay<64, 128>::total(nchunks);
-    if (Dk == 128 && Dv == 64) return Lay<128, 64>::total(nchunks);
-    if (Dk == 128 && Dv == 128) return Lay<128, 128>::total(nchunks);
+    const size_t nbh = (size_t)B * H, nchunks = nbh * ((T + C - 1) / C);
+    const int nseg = choose_nseg(B, T, H, Dk, Dv);
+    if (Dk == 64 && Dv == 64) return Lay<64, 64>::total(nchunks) + seg_bytes<64, 64>(nbh, nseg);
+    if (Dk == 64 && Dv == 128) return Lay<64, 128>::total(nchunks) + seg_bytes<64, 128>(nbh, nseg);
+    if (Dk == 128 && Dv == 64) return Lay<128, 64>::total(nchunks) + seg_bytes<128, 64>(nbh, nseg);
+    if (Dk == 128 && Dv == 128) return Lay<128, 128>::total(nchunks) + seg_bytes<128, 128>(nbh, nseg);
     return 0;
 }
 

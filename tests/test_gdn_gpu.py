@@ -52,6 +52,30 @@ def test_gdn_shapes_with_initial_state(atma, B, T, H, Dk, Dv, dtype):
     _run_and_check(atma, inp, dtype, init=init, tag=f"B{B} T{T} H{H} Dk{Dk} Dv{Dv}")
 
 
+@pytest.mark.parametrize("B,T,H,Dk,Dv", [(1, 2000, 2, 128, 128), (1, 1500, 1, 64, 128), (2, 1000, 1, 128, 64),
+                                         (1, 4096, 1, 64, 64)])
+def test_gdn_segmented_carry(atma, B, T, H, Dk, Dv):
+    """Few (batch, head) pairs over many chunks: the library cuts the sequence into segments
+    (summary pass, fp32 scan of the segment maps, parallel carry); every row is checked, with
+    an initial state and a ragged last chunk where T is not a multiple of 64."""
+    inp = workloads.make_gdn_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=T + Dk)
+    init = torch.randn(B, H, Dv, Dk, generator=torch.Generator().manual_seed(T + 1)) * 0.3
+    _run_and_check(atma, inp, "bf16", init=init, tag=f"segmented B{B} T{T} H{H} Dk{Dk} Dv{Dv}")
+
+
+def test_gdn_segmented_carry_long_memory(atma):
+    """Segmented carry with gates close to 1 (alpha in (0.998, 1), small beta), so a segment's
+    start state still weighs in thousands of tokens later and the fp32 scan of the segment
+    maps (S_start A_seg + B_seg) is what the result depends on."""
+    B, T, H, D = 1, 4096, 2, 128
+    inp = workloads.make_gdn_inputs(B, T, H, D, dtype="bf16", seed=11)
+    gen = torch.Generator().manual_seed(12)
+    inp["alpha"] = 1.0 - 0.002 * torch.rand(B, T, H, generator=gen)
+    inp["beta"] = torch.sigmoid(torch.randn(B, T, H, generator=gen) - 2.0)
+    init = torch.randn(B, H, D, D, generator=gen) * 0.3
+    _run_and_check(atma, inp, "bf16", init=init, tag="segmented long memory")
+
+
 def test_gdn_layer_b8_t2k(atma):
     """378M-class layer at 2K: B=8, T=2048, H=8, d=128, bf16 inputs."""
     inp = workloads.make_workload("layer_b8_t2k")["gdn"]
