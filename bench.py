@@ -138,11 +138,12 @@ def main():
                        device=dev)
     o_p = torch.empty_like(p["q"])
 
-    def gdn():
-        atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], o=o_g, final_state=S_g, workspace=ws_g)
+    def gdn(stream=None):
+        atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], o=o_g, final_state=S_g, workspace=ws_g,
+                          stream=stream)
 
-    def polar():
-        atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p)
+    def polar(stream=None):
+        atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p, stream=stream)
 
     for _ in range(args.warmup):
         gdn()
@@ -187,6 +188,29 @@ def main():
                          "gdn_traffic": measured_traffic("atma_gdn_fwd (prep+carry+out)"),
                          "polar_TFLOPs": round(polar_tflops, 2)},
     }
+    # The memory and Polar calls are independent given their inputs: the same step with the memory
+    # call on a second stream (default priority) overlapping the Polar call.
+    if not args.no_secondary:
+        side = torch.cuda.Stream()
+        main_s = torch.cuda.current_stream()
+
+        def step2():
+            side.wait_stream(main_s)
+            gdn(stream=side)
+            polar(stream=main_s)
+            main_s.wait_stream(side)
+
+        for _ in range(args.warmup):
+            step2()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step2()
+        torch.cuda.synchronize()
+        el2 = time.perf_counter() - t0
+        out["two_streams"] = {"tokens_per_s": round(B * T * args.steps / el2, 1),
+                              "ms_per_step": round(el2 * 1e3 / args.steps, 4),
+                              "note": "memory call on a second stream overlapping the Polar call"}
     del inp, g, p, o_g, S_g, ws_g, o_p
     torch.cuda.empty_cache()
 

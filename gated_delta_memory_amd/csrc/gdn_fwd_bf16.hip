@@ -653,19 +653,43 @@ __global__ __launch_bounds__(NT) void gdn_seg_scan(Regions rg, const float* init
         *(f32x4*)&sm.S[r * LDS_S + 4 * c4] = x;
         *(f32x4*)(rg.sst + bh * nseg * DV * DK + (size_t)(16 * rt + r) * DK + 4 * c4) = x;
     }
-    for (int sg = 0; sg + 1 < nseg; ++sg) {
+    // A_seg(sg) travels through registers one step ahead (its loads overlap the MFMAs of the
+    // previous step), B_seg(sg) rows go straight into the accumulators.
+    constexpr int AR = DK * DK / 4 / NT;
+    f32x4 areg[AR];
+    f32x4 breg[DK / 64];
+    auto load_ab = [&](int sg) {
         const float* sum = rg.seg + (bh * nseg + sg) * (DV + DK) * DK;
-        for (int i = threadIdx.x; i < DK * DK / 4; i += NT) {  // A_seg(sg) into LDS
-            const int r = i / (DK / 4), c4 = i % (DK / 4);
-            *(f32x4*)&sm.A[r * LDS_A + 4 * c4] = *(const f32x4*)(sum + (size_t)(DV + r) * DK + 4 * c4);
+#pragma unroll
+        for (int m = 0; m < AR; ++m) {
+            const int i = threadIdx.x + m * NT, r = i / (DK / 4), c4 = i % (DK / 4);
+            areg[m] = *(const f32x4*)(sum + (size_t)(DV + r) * DK + 4 * c4);
         }
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) breg[j][x] = sum[(size_t)(16 * rt + 4 * G + x) * DK + 16 * (w + 4 * j) + l16];
+    };
+    auto store_a = [&]() {
+#pragma unroll
+        for (int m = 0; m < AR; ++m) {
+            const int i = threadIdx.x + m * NT, r = i / (DK / 4), c4 = i % (DK / 4);
+            *(f32x4*)&sm.A[r * LDS_A + 4 * c4] = areg[m];
+        }
+    };
+    if (nseg > 1) {
+        load_ab(0);
+        store_a();
+    }
+    __syncthreads();
+    for (int sg = 0; sg + 1 < nseg; ++sg) {
         f32x4 acc[DK / 64];
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j) acc[j] = breg[j];
+        if (sg + 2 < nseg) load_ab(sg + 1);
 #pragma unroll
         for (int j = 0; j < DK / 64; ++j) {
             const int ct = w + 4 * j;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) acc[j][x] = sum[(size_t)(16 * rt + 4 * G + x) * DK + 16 * ct + l16];  // B_seg
 #pragma unroll 8
             for (int kk = 0; kk < DK / 4; ++kk)
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.S[l16 * LDS_S + 4 * kk + G],
@@ -683,6 +707,8 @@ __global__ __launch_bounds__(NT) void gdn_seg_scan(Regions rg, const float* init
                 nxt[(size_t)(16 * rt + 4 * G + x) * DK + 16 * ct + l16] = acc[j][x];
             }
         }
+        if (sg + 2 < nseg) store_a();
+        __syncthreads();
     }
 }
 
