@@ -560,7 +560,13 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     using L = Lay<DK, DV>;
     using K = Carry<DK, DV, STORE>;
     constexpr int NKT = DK / 16;
-    const int sl = blockIdx.x, h = (int)blockIdx.y / nseg, sg = (int)blockIdx.y % nseg, b = blockIdx.z;
+    // slices of one (b, h, segment) on one XCD (workgroup i runs on XCD i % 8)
+    const int nsl = (int)gridDim.x, nwg = nsl * (int)gridDim.y * (int)gridDim.z;
+    const int wgi = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int per = nwg >> 3, extra = nwg & 7, xcd = wgi & 7;
+    const int item = xcd * per + min(xcd, extra) + (wgi >> 3);
+    const int sl = item % nsl, yy = (item / nsl) % (int)gridDim.y, b = item / (nsl * (int)gridDim.y);
+    const int h = yy / nseg, sg = yy % nseg;
     const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
     const int NC = (Tlen + C - 1) / C;
     const int cb = sg * seglen, n = min(NC - cb, seglen);  // this segment's chunks
