@@ -196,6 +196,19 @@ __device__ __forceinline__ void lds_dma4(const void* gaddr, const void* lds_wave
         : "memory", "m0");
 }
 
+// Same with a wave-uniform 64-bit base, a per-lane 32-bit byte offset and a wave-uniform LDS
+// byte address, 4 bytes per lane.
+__device__ __forceinline__ void lds_dma4(const void* sbase, unsigned voff, unsigned lds_wave_addr) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(m0v)
+        : "memory", "m0");
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, then
 // s_barrier, without the release/acquire fences of __syncthreads() (those would also wait
 // for every global store and asynchronous copy in flight).  The empty asm statements keep

@@ -62,6 +62,7 @@ using atma::wait_vmcnt;
 using atma::lds_dma16;
 using atma::lds_dma4;
 using atma::lds_barrier;
+using atma::lds_addr;
 
 }  // namespace gdn
 }  // namespace atma

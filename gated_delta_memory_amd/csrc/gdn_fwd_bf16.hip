@@ -457,16 +457,20 @@ struct Carry {
     // stage too (every lane copies the same word, so all threads issue the same operations)
     // and read back from LDS: a plain global load carried across the loop would make the
     // compiler wait for every copy in flight.
+    // The copies take a wave-uniform source base and LDS address (scalar registers) and a
+    // per-lane 32-bit offset, so issuing one costs a handful of scalar instructions.
     __device__ __forceinline__ void issue(int c, char* dst) const {
-        const int w = wave_id();
+        const int w = __builtin_amdgcn_readfirstlane(wave_id());
         const char* src = ra0 + (size_t)c * L::RA;
-        gdn::lds_dma4((const void*)(egl + c), (const void*)(dst + L::STAGE + w * 256));
+        const unsigned lds = gdn::lds_addr(dst) + (unsigned)(w * 64 * 16);
+        gdn::lds_dma4((const void*)(egl + c), 0u, gdn::lds_addr(dst) + (unsigned)(L::STAGE + w * 256));
 #pragma unroll
         for (int m = 0; m < TPT; ++m) {
-            const int ch = m * NT + (int)threadIdx.x;
-            const size_t off = (size_t)ch * 16 < L::A_U ? (size_t)ch * 16
-                                                        : L::A_U + sl * L::USLICE + ((size_t)ch * 16 - L::A_U);
-            gdn::lds_dma16((const void*)(src + off), (const void*)(dst + (m * NT + w * 64) * 16));
+            const unsigned ch = (unsigned)(m * NT) + threadIdx.x;
+            const unsigned off = ch * 16 < (unsigned)L::A_U
+                                     ? ch * 16
+                                     : (unsigned)(L::A_U + sl * L::USLICE) + (ch * 16 - (unsigned)L::A_U);
+            gdn::lds_dma16((const void*)src, off, lds + (unsigned)(m * NT * 16));
         }
     }
 
