@@ -53,9 +53,15 @@ struct TileRegs {
     }
 };
 
-// Copies `bytes` (multiple of 16) from LDS to global memory with 16-byte stores.
+// Copies `bytes` (multiple of 16) from LDS to global memory with 16-byte stores; streaming
+// (non-temporal) stores for data no kernel reads back soon, so it does not displace what does.
+template <bool STREAM = false>
 __device__ __forceinline__ void copy_out(char* __restrict__ dst, const char* src, int bytes) {
-    for (int i = threadIdx.x * 16; i < bytes; i += NT * 16) *(u32x4*)(dst + i) = *(const u32x4*)(src + i);
+    for (int i = threadIdx.x * 16; i < bytes; i += NT * 16) {
+        const u32x4 x = *(const u32x4*)(src + i);
+        if constexpr (STREAM) __builtin_nontemporal_store(x, (u32x4*)(dst + i));
+        else *(u32x4*)(dst + i) = x;
+    }
 }
 
 using atma::wait_vmcnt;

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         }
     }
     __syncthreads();
-    copy_out(rb + L::B_P, pstage, C * C * 2);
+    copy_out<true>(rb + L::B_P, pstage, C * C * 2);
 
     // ---- C: QG = diag(e^g) Q and KD^T, straight to the records ------------------------------
 #pragma unroll
@@ -260,8 +260,8 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         f16x8 y;
 #pragma unroll
         for (int t = 0; t < 8; ++t) y[t] = (half)((float)x[t] * e);
-        *(f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
-        *(f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+        __builtin_nontemporal_store(__builtin_shufflevector(y, y, 0, 1, 2, 3), (f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc)));
+        __builtin_nontemporal_store(__builtin_shufflevector(y, y, 4, 5, 6, 7), (f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc + 4)));
     }
     {
         const float glast = sm.Gs[C - 1];
@@ -497,7 +497,7 @@ struct Carry {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
             acc_to_frag(sf[kb], st[2 * kb], st[2 * kb + 1]);
-            if constexpr (STORE) *(f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16) = sf[kb].v;
+            if constexpr (STORE) __builtin_nontemporal_store(sf[kb].v, (f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16));
         }
         f16x8 kf[NKT][2];
 #pragma unroll
@@ -526,7 +526,7 @@ struct Carry {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             acc_to_frag(df[kb], dl[2 * kb], dl[2 * kb + 1]);
-            if constexpr (STORE) *(f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16) = df[kb].v;
+            if constexpr (STORE) __builtin_nontemporal_store(df[kb].v, (f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16));
         }
         // S_out^T = e^{g_last} S_in^T + KD^T Delta
 #pragma unroll
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(Regions rg, bf16* __restrict_
     __syncthreads();
     for (int id = threadIdx.x; id < C * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cc = id % (DV / 8);
-        if (r < n) *(u32x4*)(o + (((size_t)b * Tlen + t0 + r) * H + h) * DV + 8 * cc) = *(const u32x4*)&sm.Os[r * LDO + 8 * cc];
+        if (r < n) __builtin_nontemporal_store(*(const u32x4*)&sm.Os[r * LDO + 8 * cc], (u32x4*)(o + (((size_t)b * Tlen + t0 + r) * H + h) * DV + 8 * cc));
     }
 }
 
