@@ -8,16 +8,19 @@
 // QG = diag(e^g) Q, KD = diag(e^{g_last - g}) K and P = lower_incl((Q K^T) o E).
 //
 // Three kernels; only the middle one is sequential along the sequence:
-//   gdn_prep_h  (parallel over chunks) - A, P, Tinv (fp32), W and U from an fp32-accurate
-//               hi/lo bf16 split of Tinv, QG and KD^T; writes them as fp16 tiles already in
-//               their consumers' MFMA-fragment order.
+//   gdn_prep_h  (parallel over chunks) - A, Tinv (fp32), W and U from an fp32-accurate
+//               hi/lo bf16 split of Tinv, and KD^T; writes them as fp16 tiles already in
+//               the carry's MFMA-fragment order, plus the chunk's g for the output kernel.
+//               It needs neither Q nor P, so its LDS (K, later V; A; Tinv) fits three
+//               workgroups per CU.
 //   gdn_carry_h (one workgroup per 64 state rows of a (batch, head), walks the chunks)
 //               keeps S^T in fp32 MFMA accumulators; per chunk it only forms Delta and the
 //               state update (32 MFMAs per wave), streaming W, KD^T and its U slice through
 //               three LDS stages with direct global->LDS copies issued two chunks ahead.
 //               It writes the fp16 operands it built anyway -- S_in^T and Delta, in MFMA
 //               fragment order -- for the output kernel.
-//   gdn_out_h   (parallel over chunks) - O = QG S_in^T + P Delta, coalesced bf16 stores.
+//   gdn_out_h   (parallel over chunks) - QG and P from the bf16 Q and K tiles, then
+//               O = QG S_in^T + P Delta, coalesced bf16 stores.
 // Long sequences with few (batch, head) pairs leave most of the GPU idle during the carry, so
 // the sequence is cut into segments.  Per chunk the state map is affine in S,
 //     S_out = S_in A_c + B_c,  A_c = e^{g_last} I - W^T KD,  B_c = U^T KD,
@@ -42,8 +45,8 @@ using gdn::copy_out;
 // ---- workspace layout ------------------------------------------------------------------
 // Per chunk, in separate arrays indexed by chunk id = (b H + h) NC + c:
 //   RA : W [C][DK] | KDT [DK][C] | U slices [DV/64] x 8 KB      (read by the carry kernel)
-//   RB : QG [C][DK] | P [C][C]                                   (read by the output kernel)
-// (W, KDT, QG and P fragment-major, U slices in the carry's accumulator order; see below)
+//   RB : g [C] (fp32 cumulative log decay)                       (read by the output kernel)
+// (W and KDT fragment-major, U slices in the carry's accumulator order; see below)
 //   SF : S_in^T fragments [DV/64][DK/32][4 waves][64 lanes] x 16 B
 //   DF : Delta fragments  [DV/64][2][4 waves][64 lanes] x 16 B
 //   EGL: e^{g_last} (fp32)
@@ -54,9 +57,7 @@ template <int DK, int DV> struct Lay {
     static constexpr size_t A_U = A_KDT + (size_t)DK * C * 2;
     static constexpr size_t USLICE = (size_t)C * 64 * 2;
     static constexpr size_t RA = A_U + (size_t)(DV / 64) * USLICE;
-    static constexpr size_t B_QG = 0;
-    static constexpr size_t B_P = (size_t)C * DK * 2;
-    static constexpr size_t RB = B_P + (size_t)C * C * 2;
+    static constexpr size_t RB = (size_t)C * sizeof(float);  // g_r of the chunk (for the output kernel)
     static constexpr size_t SF = (size_t)DV * DK * 2;
     static constexpr size_t DF = (size_t)C * DV * 2;
     static constexpr size_t STAGE = A_U + USLICE;  // bytes one carry workgroup streams per chunk
@@ -135,9 +136,8 @@ __device__ __forceinline__ constexpr int u_off(int w, int i, int lane) { return 
 // =========================================================================================
 template <int DK, int DV>
 struct PrepSmem {
-    static constexpr int LDK = DK + 8, LDX = (DK > DV ? DK : DV) + 8, LDA = C + 4;
-    bf16 Ks[C * LDK];
-    bf16 Xs[C * LDX];   // Q, later V
+    static constexpr int LDK = (DK > DV ? DK : DV) + 8, LDX = LDK, LDA = C + 4;
+    bf16 Ks[C * LDK];   // K, then V once W is formed
     float Am[C * LDA];  // A, later the W staging tile
     float Tm[C * LDA];  // P staging, then Tinv, then the U staging tile
     float Gs[C];  // g_r = sum_{s <= r} ln alpha_s
@@ -160,7 +160,7 @@ __device__ __forceinline__ Frag<bf16> bfrag_tr(const bf16* tile, int ld, int ct,
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                     const bf16* __restrict__ v, const float* __restrict__ alpha,
                                                     const float* __restrict__ beta, Regions rg, int Tlen, int H) {
     using S = PrepSmem<DK, DV>;
@@ -179,15 +179,13 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
     char* ra = rg.ra + cid * L::RA;
     char* rb = rg.rb + cid * L::RB;
 
-    // ---- A: K and Q into LDS, cumulative log decay; V's load starts here and lands after D --
+    // ---- A: K into LDS, cumulative log decay; V's load starts here and lands after W --------
     TileRegs<bf16, C, DV> vr;
     {
-        TileRegs<bf16, C, DK> kr, qr;
+        TileRegs<bf16, C, DK> kr;
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
-        qr.load(q + tok0 * DK, (size_t)H * DK, n);
         vr.load(v + tok0 * DV, (size_t)H * DV, n);
         kr.template store<LDK>(sm.Ks);
-        qr.template store<LDX>(sm.Xs);
     }
     if (w == 0) {
         const bool ok = lane < n;
@@ -201,12 +199,12 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         sm.Gs[lane] = la;
         sm.Bs[lane] = be;
         sm.Es[lane] = be * __expf(la);
+        __builtin_nontemporal_store(la, (float*)rb + lane);
         if (lane == C - 1) rg.egl[cid] = __expf(la);
     }
     __syncthreads();
 
-    // ---- B: A (strict lower, fp32) and P (fp16, staged in Tm) ------------------------------
-    char* pstage = (char*)sm.Tm;
+    // ---- B: A = strict_lower(diag(beta) (K K^T) o E) in fp32 ----------------------------------
     for (int ti = w; ti < 16; ti += 4) {
         int i, j;
         if (ti < 10) {
@@ -221,48 +219,30 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         const f32x4 gr = *(const f32x4*)&sm.Gs[16 * i + 4 * G];
         const f32x4 br = *(const f32x4*)&sm.Bs[16 * i + 4 * G];
         const float gs = sm.Gs[16 * j + l16];
-        f32x4 kk = {0, 0, 0, 0}, qk = {0, 0, 0, 0};
+        f32x4 kk = {0, 0, 0, 0};
         if (ti < 10) {
             // every fragment of the tile is requested before the first MFMA waits on one
-            Frag<bf16> a[DK / 32], bq[DK / 32], bk[DK / 32];
+            Frag<bf16> a[DK / 32], bk[DK / 32];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
                 load_frag_rows(bk[kb], sm.Ks, LDK, 16 * j + l16, 32 * kb);
                 load_frag_rows(a[kb], sm.Ks, LDK, 16 * i + l16, 32 * kb);
-                load_frag_rows(bq[kb], sm.Xs, LDX, 16 * i + l16, 32 * kb);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                mma(kk, a[kb], bk[kb]);
-                mma(qk, bq[kb], bk[kb]);
-            }
+            for (int kb = 0; kb < DK / 32; ++kb) mma(kk, a[kb], bk[kb]);
         }
         const int s = 16 * j + l16;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * i + 4 * G + x;
-            // g_r - g_s <= 0 wherever the mask keeps the entry (s <= r)
+            // g_r - g_s <= 0 wherever the mask keeps the entry (s < r)
             const float e = __expf(fminf(gr[x] - gs, 0.0f));
             sm.Am[r * LDA + s] = (s < r) ? br[x] * e * kk[x] : 0.0f;
-            *(half*)(pstage + fm_off<C>(r, s)) = (half)((s <= r) ? e * qk[x] : 0.0f);
         }
     }
-    __syncthreads();
-    copy_out<true>(rb + L::B_P, pstage, C * C * 2);
 
-    // ---- C: QG = diag(e^g) Q and KD^T, straight to the records ------------------------------
-#pragma unroll
-    for (int id = threadIdx.x; id < C * DK / 8; id += NT) {
-        const int r = id / (DK / 8), cc = id % (DK / 8);
-        const float e = __expf(sm.Gs[r]);
-        const bf16x8 x = *(const bf16x8*)&sm.Xs[r * LDX + 8 * cc];
-        f16x8 y;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) y[t] = (half)((float)x[t] * e);
-        __builtin_nontemporal_store(__builtin_shufflevector(y, y, 0, 1, 2, 3), (f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc)));
-        __builtin_nontemporal_store(__builtin_shufflevector(y, y, 4, 5, 6, 7), (f16x4*)(rb + L::B_QG + fm_off<DK>(r, 8 * cc + 4)));
-    }
+    // ---- C: KD^T, straight to the records ----------------------------------------------------
     {
         const float glast = sm.Gs[C - 1];
 #pragma unroll
@@ -284,7 +264,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
             *(f16x4*)(ra + L::A_KDT + fm_off<C>(16 * cg + l16, pc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
         }
     }
-    __syncthreads();  // P staging copied, Q consumed
+    __syncthreads();  // A complete
 
     // ---- D: Tinv = (I + A)^{-1} -----------------------------------------------------------
     if (w == 0) {
@@ -343,7 +323,6 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
         }
         __syncthreads();
     }
-    vr.template store<LDX>(sm.Xs);
 
     // ---- E: W = Tinv diag(beta e^g) K and U = Tinv diag(beta) V, hi/lo split of Tinv -------
     {
@@ -373,7 +352,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
                 ul[kb].set(e, tu - (float)hu);
             }
         }
-        __syncthreads();  // Tinv consumed, V landed: Am and Tm become staging tiles
+        __syncthreads();  // Tinv consumed: Am and Tm become staging tiles
         char* wstage = (char*)sm.Am;
         char* ustage = (char*)sm.Tm;
         // B fragments of a whole product are requested before its MFMAs (one LDS round trip)
@@ -398,11 +377,14 @@ __global__ __launch_bounds__(NT, 2) void gdn_prep_h(const bf16* __restrict__ q, 
             for (int x = 0; x < 4; ++x)
                 *(half*)(wstage + fm_off<DK>(16 * i + 4 * G + x, 16 * ct + l16)) = (half)acc[x];
         }
+        __syncthreads();  // every wave is done with K: V takes its place
+        vr.template store<LDX>(sm.Ks);
+        __syncthreads();
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Xs, LDX, ct, kb);
+                if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDX, ct, kb);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
@@ -725,32 +707,97 @@ __global__ __launch_bounds__(NT) void gdn_seg_scan(Regions rg, const float* init
 // =========================================================================================
 // output
 // =========================================================================================
+// The output kernel forms QG = diag(e^g) Q and P = lower_incl((Q K^T) o E) itself from the
+// bf16 inputs (its MFMA operands in fp16, fragment-major in LDS), then
+// O = QG S_in^T + P Delta with the S_in^T and Delta fragments the carry wrote.
 template <int DK, int DV>
 struct OutSmem {
-    static constexpr int LDO = DV + 8;
-    char rb[Lay<DK, DV>::RB];  // QG | P
-    bf16 Os[C * LDO];
+    static constexpr int LDQ = DK + 8, LDO = DV + 8;
+    static constexpr int QK_BYTES = 2 * C * LDQ * 2;
+    static constexpr int OS_BYTES = C * LDO * 2;
+    union {
+        struct {
+            bf16 Qs[C * LDQ];
+            bf16 Ks[C * LDQ];
+        } in;
+        bf16 Os[C * LDO];  // output staging, once QG and P are built
+    } u;
+    char qg[C * DK * 2];  // QG, fragment-major fp16
+    char pm[C * C * 2];   // P, fragment-major fp16
+    float Gs[C];
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NT, 2) void gdn_out_h(Regions rg, bf16* __restrict__ o, int Tlen, int H) {
+__global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, const bf16* __restrict__ k, Regions rg,
+                                                   bf16* __restrict__ o, int Tlen, int H) {
     using L = Lay<DK, DV>;
     using S = OutSmem<DK, DV>;
-    constexpr int RBK = L::RBK, LDO = S::LDO;
+    constexpr int LDQ = S::LDQ, LDO = S::LDO;
     extern __shared__ __align__(16) char smem_raw[];
     S& sm = *reinterpret_cast<S*>(smem_raw);
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int NC = gridDim.x;
     const int t0 = c * C, n = min(C, Tlen - t0);
-    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id()), G = lane >> 4, l16 = lane & 15;
     const size_t cid = ((size_t)b * H + h) * NC + c;
+    const size_t tok0 = ((size_t)b * Tlen + t0) * H + h;
     {
-        const char* src = rg.rb + cid * L::RB;
-        for (int i = threadIdx.x * 16; i < (int)L::RB; i += NT * 16) *(u32x4*)(sm.rb + i) = *(const u32x4*)(src + i);
+        TileRegs<bf16, C, DK> qr, kr;
+        qr.load(q + tok0 * DK, (size_t)H * DK, n);
+        kr.load(k + tok0 * DK, (size_t)H * DK, n);
+        if (threadIdx.x < C) sm.Gs[threadIdx.x] = ((const float*)(rg.rb + cid * L::RB))[threadIdx.x];
+        qr.template store<LDQ>(sm.u.in.Qs);
+        kr.template store<LDQ>(sm.u.in.Ks);
     }
     __syncthreads();
-    const char* sQ = sm.rb + L::B_QG;
-    const char* sP = sm.rb + L::B_P;
+    // QG = diag(e^g) Q
+#pragma unroll
+    for (int id = threadIdx.x; id < C * DK / 8; id += NT) {
+        const int r = id / (DK / 8), cc = id % (DK / 8);
+        const float e = __expf(sm.Gs[r]);
+        const bf16x8 x = *(const bf16x8*)&sm.u.in.Qs[r * LDQ + 8 * cc];
+        f16x8 y;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) y[t] = (half)((float)x[t] * e);
+        *(f16x4*)(sm.qg + fm_off<DK>(r, 8 * cc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
+        *(f16x4*)(sm.qg + fm_off<DK>(r, 8 * cc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+    }
+    // P tiles (i, j): the ten on or below the diagonal from Q K^T, the six above it zero
+    for (int ti = w; ti < 16; ti += 4) {
+        int i, j;
+        if (ti < 10) {
+            i = (ti >= 6) ? 3 : (ti >= 3) ? 2 : (ti >= 1) ? 1 : 0;
+            j = ti - i * (i + 1) / 2;
+        } else {
+            const int uu = ti - 10;
+            i = (uu < 3) ? 0 : (uu < 5) ? 1 : 2;
+            j = (uu < 3) ? uu + 1 : (uu < 5) ? uu - 1 : 3;
+        }
+        const f32x4 gr = *(const f32x4*)&sm.Gs[16 * i + 4 * G];
+        const float gs = sm.Gs[16 * j + l16];
+        f32x4 qk = {0, 0, 0, 0};
+        if (ti < 10) {
+            Frag<bf16> a[DK / 32], bk[DK / 32];
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                load_frag_rows(bk[kb], sm.u.in.Ks, LDQ, 16 * j + l16, 32 * kb);
+                load_frag_rows(a[kb], sm.u.in.Qs, LDQ, 16 * i + l16, 32 * kb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) mma(qk, a[kb], bk[kb]);
+        }
+        const int s2 = 16 * j + l16;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * i + 4 * G + x;
+            const float e = __expf(fminf(gr[x] - gs, 0.0f));  // g_r - g_s <= 0 where s <= r
+            *(half*)(sm.pm + fm_off<C>(r, s2)) = (half)((s2 <= r) ? e * qk[x] : 0.0f);
+        }
+    }
+    __syncthreads();  // QG and P ready; the input tiles are dead and the output staging reuses them
+    const char* sQ = sm.qg;
+    const char* sP = sm.pm;
     const char* sfc = rg.sf + cid * L::SF;
     const char* dfc = rg.df + cid * L::DF;
     // n-tiles of 16 state rows: carry slice sl, wave w' -> n-tile 4 sl + w'
@@ -779,13 +826,15 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(Regions rg, bf16* __restrict_
                 mma(acc, a, df[kb]);
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) sm.Os[(16 * i + 4 * G + x) * LDO + 16 * nt + l16] = (bf16)acc[x];
+            for (int x = 0; x < 4; ++x) sm.u.Os[(16 * i + 4 * G + x) * LDO + 16 * nt + l16] = (bf16)acc[x];
         }
     }
     __syncthreads();
     for (int id = threadIdx.x; id < C * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cc = id % (DV / 8);
-        if (r < n) __builtin_nontemporal_store(*(const u32x4*)&sm.Os[r * LDO + 8 * cc], (u32x4*)(o + (((size_t)b * Tlen + t0 + r) * H + h) * DV + 8 * cc));
+        if (r < n)
+            __builtin_nontemporal_store(*(const u32x4*)&sm.u.Os[r * LDO + 8 * cc],
+                                        (u32x4*)(o + (((size_t)b * Tlen + t0 + r) * H + h) * DV + 8 * cc));
     }
 }
 
@@ -815,7 +864,8 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
     }
     hipLaunchKernelGGL((gdn_carry_h<DK, DV, true>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream, rg,
                        a.init_state, a.final_state, a.T, a.H, nseg, seglen);
-    hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, rg, (bf16*)a.o, a.T, a.H);
+    hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, (const bf16*)a.q,
+                       (const bf16*)a.k, rg, (bf16*)a.o, a.T, a.H);
     return hipGetLastError();
 }
 
