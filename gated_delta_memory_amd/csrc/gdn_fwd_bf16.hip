@@ -355,51 +355,58 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
         __syncthreads();  // Tinv consumed: Am and Tm become staging tiles
         char* wstage = (char*)sm.Am;
         char* ustage = (char*)sm.Tm;
-        // B fragments of a whole product are requested before its MFMAs (one LDS round trip)
-        Frag<bf16> bx[(DK > DV ? DK : DV) / 16][2];
+        // B fragments are requested four column tiles at a time before their MFMAs (one LDS
+        // round trip per group, 32 registers of fragments)
+        Frag<bf16> bx[4][2];
 #pragma unroll
-        for (int ct = 0; ct < DK / 16; ++ct)
+        for (int c0 = 0; c0 < DK / 16; c0 += 4) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDK, ct, kb);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < DK / 16; ++ct) {
-            f32x4 acc = {0, 0, 0, 0};
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDK, c0 + ct, kb);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < nkb) {
-                    mma(acc, wh[kb], bx[ct][kb]);
-                    mma(acc, wl[kb], bx[ct][kb]);
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (kb < nkb) {
+                        mma(acc, wh[kb], bx[ct][kb]);
+                        mma(acc, wl[kb], bx[ct][kb]);
+                    }
                 }
-            }
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-                *(half*)(wstage + fm_off<DK>(16 * i + 4 * G + x, 16 * ct + l16)) = (half)acc[x];
+                for (int x = 0; x < 4; ++x)
+                    *(half*)(wstage + fm_off<DK>(16 * i + 4 * G + x, 16 * (c0 + ct) + l16)) = (half)acc[x];
+            }
         }
         __syncthreads();  // every wave is done with K: V takes its place
         vr.template store<LDX>(sm.Ks);
         __syncthreads();
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct)
+        for (int c0 = 0; c0 < DV / 16; c0 += 4) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDX, ct, kb);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) {
-            f32x4 acc = {0, 0, 0, 0};
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDX, c0 + ct, kb);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < nkb) {
-                    mma(acc, uh[kb], bx[ct][kb]);
-                    mma(acc, ul[kb], bx[ct][kb]);
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (kb < nkb) {
+                        mma(acc, uh[kb], bx[ct][kb]);
+                        mma(acc, ul[kb], bx[ct][kb]);
+                    }
                 }
-            }
-            f16x4 y;
+                f16x4 y;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) y[x] = (half)acc[x];
-            *(f16x4*)(ustage + (ct >> 2) * L::USLICE + u_off(ct & 3, i, lane)) = y;
+                for (int x = 0; x < 4; ++x) y[x] = (half)acc[x];
+                *(f16x4*)(ustage + ((c0 + ct) >> 2) * L::USLICE + u_off((c0 + ct) & 3, i, lane)) = y;
+            }
         }
         __syncthreads();
         copy_out(ra + L::A_W, wstage, C * DK * 2);
