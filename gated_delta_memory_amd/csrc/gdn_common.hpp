@@ -16,13 +16,19 @@ struct TileRegs {
     static constexpr int NVEC = ROWS * COLS / VEC;
     static constexpr int PER = (NVEC + NT - 1) / NT;
     u32x4 r[PER];
+    // STREAM: non-temporal loads, for data no later kernel reads
+    template <bool STREAM = false>
     __device__ __forceinline__ void load(const T* g, size_t ld, int nrows) {
 #pragma unroll
         for (int m = 0; m < PER; ++m) {
             const int i = threadIdx.x + m * NT;
             const int row = i / (COLS / VEC), cv = i % (COLS / VEC);
             u32x4 x = {0u, 0u, 0u, 0u};
-            if (i < NVEC && row < nrows) x = *(const u32x4*)(g + (size_t)row * ld + cv * VEC);
+            if (i < NVEC && row < nrows) {
+                const u32x4* src = (const u32x4*)(g + (size_t)row * ld + cv * VEC);
+                if constexpr (STREAM) x = __builtin_nontemporal_load(src);
+                else x = *src;
+            }
             r[m] = x;
         }
     }

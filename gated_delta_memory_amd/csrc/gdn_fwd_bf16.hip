@@ -184,7 +184,7 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
     {
         TileRegs<bf16, C, DK> kr;
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
-        vr.load(v + tok0 * DV, (size_t)H * DV, n);
+        vr.template load<true>(v + tok0 * DV, (size_t)H * DV, n);
         kr.template store<LDK>(sm.Ks);
     }
     if (w == 0) {
@@ -750,7 +750,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
     const size_t tok0 = ((size_t)b * Tlen + t0) * H + h;
     {
         TileRegs<bf16, C, DK> qr, kr;
-        qr.load(q + tok0 * DK, (size_t)H * DK, n);
+        qr.template load<true>(q + tok0 * DK, (size_t)H * DK, n);
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
         if (threadIdx.x < C) sm.Gs[threadIdx.x] = ((const float*)(rg.rb + cid * L::RB))[threadIdx.x];
         qr.template store<LDQ>(sm.u.in.Qs);
@@ -814,9 +814,9 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
         Frag<half> sf[DK / 32], df[2];
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb)
-            sf[kb].v = *(const f16x8*)(sfc + (size_t)sl * (DK / 32) * 4096 + ((kb * 4 + wp) * 64 + lane) * 16);
+            sf[kb].v = __builtin_nontemporal_load((const f16x8*)(sfc + (size_t)sl * (DK / 32) * 4096 + ((kb * 4 + wp) * 64 + lane) * 16));
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) df[kb].v = *(const f16x8*)(dfc + (size_t)sl * 2 * 4096 + ((kb * 4 + wp) * 64 + lane) * 16);
+        for (int kb = 0; kb < 2; ++kb) df[kb].v = __builtin_nontemporal_load((const f16x8*)(dfc + (size_t)sl * 2 * 4096 + ((kb * 4 + wp) * 64 + lane) * 16));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x4 acc = {0, 0, 0, 0};

@@ -7,7 +7,8 @@
 //
 // Split-KV: the cache is cut into contiguous token ranges.  polar_decode_partial streams one
 // range for all heads of one sequence (each token's K and V rows for all kv heads are one
-// contiguous 2*Hkv*D-byte run, read with 16-byte loads) and keeps, per query head, the
+// contiguous 2*Hkv*D-byte run, read with 16-byte non-temporal loads: the cache is read once
+// per step, so it should not displace anything in the caches) and keeps, per query head, the
 // streaming statistics of Appendix C.3 / Table 6: running maximum M of the real logits,
 // L = sum p, Q2 = sum p^2 and Sv = sum p v.  Those four statistics of two disjoint key
 // ranges combine exactly:  M = max(M_a, M_b), r_x = e^{M_x - M},
@@ -81,8 +82,8 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
         for (int u = 0; u < UNROLL; ++u) {
             const int t = t0 + u * slots;
             if (t < t_end) {
-                kr[u] = *(const u32x4*)(kb + (size_t)t * tstride);
-                vr[u] = *(const u32x4*)(vb + (size_t)t * tstride);
+                kr[u] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)t * tstride));
+                vr[u] = __builtin_nontemporal_load((const u32x4*)(vb + (size_t)t * tstride));
             } else {
                 kr[u] = u32x4{0u, 0u, 0u, 0u};
                 vr[u] = u32x4{0u, 0u, 0u, 0u};
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
                 for (int x = 0; x < 8; ++x) acc[x] += r * psv[s * tpt + threadIdx.x][x];
             }
             const int h = hk * GQ + g;
-            float* rec = ws + (((size_t)b * nsplit + split) * Hq + h) * REC;
+            float* rec = ws + (((size_t)b * Hq + h) * nsplit + split) * REC;
             if (chunk == 0) *(f32x4*)rec = f32x4{M, LL, QQ, 0.f};
             *(f32x4*)(rec + 4 + chunk * 8) = f32x4{acc[0], acc[1], acc[2], acc[3]};
             *(f32x4*)(rec + 8 + chunk * 8) = f32x4{acc[4], acc[5], acc[6], acc[7]};
@@ -160,50 +161,42 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     }
 }
 
-// grid (Hq, B); block 1024: lane d of wave j owns value dimension d of the ranges s = j (mod 16).
-// Each wave merges its ranges with a running maximum, eight records per round (their loads
-// are independent of the merge), then the sixteen partial merges are combined through LDS.
+// grid (Hq, B); block 1024.  Wave j merges the ranges s = 64 j .. 64 j + 63 (then + 1024, ...)
+// in one round of loads: lane i reads the header (M, L, Q2) of range 64 j + i and every lane d
+// reads value dimension d of all 64 ranges, so all loads are in flight together.  The wave's
+// merge weights e_i = exp(M_i - max M) are formed per lane and broadcast with v_readlane for the
+// value sum; the sixteen wave merges are combined through LDS.
 constexpr int CNW = 16;        // waves per combine workgroup
 constexpr int CNT = 64 * CNW;  // threads per combine workgroup
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
 __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
                                                             bf16* __restrict__ o, float* __restrict__ mu_out,
                                                             int nsplit, int cache_len) {
     const int h = blockIdx.x, Hq = gridDim.x, b = blockIdx.y;
     const int d = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const float* base = ws + ((size_t)b * nsplit * Hq + h) * REC;
-    const size_t step = (size_t)Hq * REC;
+    const float* base = ws + ((size_t)b * Hq + h) * nsplit * REC;  // records of (b, h), split-major
     float M = -INFINITY, L = 0.f, Q2 = 0.f, Sv = 0.f;
-    constexpr int U = 8;
-    for (int s0 = wv; s0 < nsplit; s0 += CNW * U) {
-        f32x4 hd[U];  // M, L, Q2, pad of each record
-        float rs[U];
+    for (int s0 = 64 * wv; s0 < nsplit; s0 += 64 * CNW) {
+        const int cnt = min(64, nsplit - s0);
+        const float* r0 = base + (size_t)s0 * REC;
+        const f32x4 hd = d < cnt ? *(const f32x4*)(r0 + d * REC) : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+        float rs[64];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int sp = s0 + CNW * u;
-            if (sp < nsplit) {
-                const float* r = base + sp * step;
-                hd[u] = *(const f32x4*)r;
-                rs[u] = r[4 + d];
-            } else {
-                hd[u] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
-                rs[u] = 0.f;
-            }
-        }
-        float bm = M;
-#pragma unroll
-        for (int u = 0; u < U; ++u) bm = fmaxf(bm, hd[u][0]);
+        for (int i = 0; i < 64; ++i) rs[i] = i < cnt ? r0[i * REC + 4 + d] : 0.f;
+        const float bm = fmaxf(M, wave_max(hd[0]));
         if (bm == -INFINITY) continue;  // nothing seen yet (empty ranges)
         const float e0 = fast_exp2(M - bm);  // 0 when M = -inf
-        L *= e0;
-        Q2 *= e0 * e0;
-        Sv *= e0;
+        const float e = (hd[0] == -INFINITY) ? 0.0f : fast_exp2(hd[0] - bm);
+        L = L * e0 + wave_sum(e * hd[1]);
+        Q2 = Q2 * e0 * e0 + wave_sum(e * e * hd[2]);
+        float acc = Sv * e0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float e = (hd[u][0] == -INFINITY) ? 0.0f : fast_exp2(hd[u][0] - bm);
-            L += e * hd[u][1];
-            Q2 += e * e * hd[u][2];
-            Sv += e * rs[u];
-        }
+        for (int i = 0; i < 64; ++i) acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), i)), rs[i], acc);
+        Sv = acc;
         M = bm;
     }
     __shared__ float part[CNW][3];
