@@ -39,7 +39,7 @@ class PolarParams(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libatma.so is not built at {LIB_PATH}; run `python -m gated_delta_memory_amd._build` "
+        raise ImportError(f"libatma.so is not built at {LIB_PATH}; run `python gated_delta_memory_amd/_build.py` "
                           f"(or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
@@ -52,6 +52,7 @@ def _load() -> ctypes.CDLL:
         "atma_polar_attn_workspace_bytes": ([i] * 4, sz),
         "atma_polar_attn_decode": ([vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_polar_attn_decode_workspace_bytes": ([i] * 4, sz),
+        "atma_polar_attn_decode_varlen": ([vp, vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_status_string": ([i], ctypes.c_char_p),
         "atma_version": ([], i),
     }
@@ -221,6 +222,34 @@ def atma_polar_attn_decode(q, k_cache, v_cache, cache_len, params, *, o=None, mu
                                     _ptr(o), _ptr(mu_out), B, Hq, Hkv, D, _dtype_code(q), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     _check("atma_polar_attn_decode", st)
+    return o, mu_out
+
+
+def atma_polar_attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len, params, *, o=None, mu_out=None,
+                                  want_mu=False, workspace=None, stream=None):
+    """Decode one token for sequences of different cache lengths.  q [B,Hq,D]; caches
+    [B,Lmax,Hkv,D] bf16; cache_lens int32 [B] on the device (1 <= cache_lens[b] <= max_cache_len).
+    Returns (o [B,Hq,D], mu [B,Hq] or None)."""
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Lmax, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("inconsistent cache shapes")
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,):
+        raise ValueError("cache_lens must be an int32 tensor of shape [B]")
+    if o is None:
+        o = torch.empty_like(q)
+    if want_mu and mu_out is None:
+        mu_out = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    need = atma_polar_attn_decode_workspace_bytes(B, Hq, max_cache_len, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k_cache, v_cache, cache_lens, o, mu_out, workspace)
+    p = polar_params_struct(params)
+    st = lib.atma_polar_attn_decode_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
+                                           int(max_cache_len), Lmax, ctypes.byref(p), _ptr(o), _ptr(mu_out), B, Hq,
+                                           Hkv, D, _dtype_code(q), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("atma_polar_attn_decode_varlen", st)
     return o, mu_out
 
 

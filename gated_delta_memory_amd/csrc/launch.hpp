@@ -52,6 +52,9 @@ struct PolarDecodeArgs {
     float* mu_out;
     int cache_len, Lmax, B, Hq, Hkv, D;
     void* workspace;
+    // per-sequence cache lengths on the device (NULL: every sequence has cache_len); with them,
+    // cache_len is the upper bound that sizes the split grid
+    const int* lens = nullptr;
 };
 size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
 // Head layouts the decode kernels have code for: Hkv in {1,2,4,8,16,32}, Hq/Hkv in {1,2,4,8}.

@@ -16,6 +16,9 @@
 // so polar_decode_combine merges the ranges per (sequence, head) and finalises with the
 // null sink exactly as the prefill kernel does.  Exponentials are base 2 on logits scaled
 // by log2(e).
+// Heterogeneous batches pass one cache length per sequence (device array): the split grid is
+// sized by the longest, and each sequence cuts its own length into the same number of ranges.
+// A length outside [1, bound] is an error the host cannot see; that sequence's outputs are NaN.
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -48,14 +51,16 @@ __device__ __forceinline__ void unpack8(const u32x4& r, float* f) {
 template <int GQ>
 __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                                                            const bf16* __restrict__ vc, PolarParamsDev prm,
-                                                           float* __restrict__ ws, int cache_len, int Lmax,
-                                                           int Hkv) {
+                                                           float* __restrict__ ws, int max_len, int Lmax,
+                                                           int Hkv, const int* __restrict__ lens) {
     const int split = blockIdx.x, nsplit = gridDim.x, b = blockIdx.y;
     const int Hq = Hkv * GQ;
     const int tpt = Hkv * 8;                 // threads per token
     const int slots = NT / tpt;              // tokens per pass
     const int slot = threadIdx.x / tpt;
     const int hk = (threadIdx.x % tpt) >> 3, chunk = threadIdx.x & 7;
+    int cache_len = lens ? lens[b] : max_len;
+    if (cache_len < 1 || cache_len > max_len) cache_len = 0;  // invalid: no keys (the combine writes NaN)
     const int t_begin = (int)((long)cache_len * split / nsplit);
     const int t_end = (int)((long)cache_len * (split + 1) / nsplit);
 
@@ -175,8 +180,14 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
                                                             bf16* __restrict__ o, float* __restrict__ mu_out,
-                                                            int nsplit, int cache_len) {
+                                                            int nsplit, int max_len, const int* __restrict__ lens) {
     const int h = blockIdx.x, Hq = gridDim.x, b = blockIdx.y;
+    const int cache_len = lens ? lens[b] : max_len;
+    if (cache_len < 1 || cache_len > max_len) {  // invalid length: NaN outputs for this sequence
+        if (threadIdx.x < 64) o[((size_t)b * Hq + h) * D + threadIdx.x] = (bf16)__builtin_nanf("");
+        if (threadIdx.x == 0 && mu_out) mu_out[(size_t)b * Hq + h] = __builtin_nanf("");
+        return;
+    }
     const int d = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const float* base = ws + ((size_t)b * Hq + h) * nsplit * REC;  // records of (b, h), split-major
     float M = -INFINITY, L = 0.f, Q2 = 0.f, Sv = 0.f;
@@ -255,12 +266,12 @@ hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
     if (gq == G) {                                                                                         \
         hipLaunchKernelGGL(polar_decode_partial<G>, dim3(nsplit, a.B), dim3(NT), 0, stream, (const bf16*)a.q, \
                            (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.p, ws, a.cache_len, a.Lmax,   \
-                           a.Hkv);                                                                         \
+                           a.Hkv, a.lens);                                                                 \
     } else
     ATMA_PD_CASE(1) ATMA_PD_CASE(2) ATMA_PD_CASE(4) ATMA_PD_CASE(8) { return hipErrorInvalidValue; }
 #undef ATMA_PD_CASE
     hipLaunchKernelGGL(polar_decode_combine, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
-                       (bf16*)a.o, a.mu_out, nsplit, a.cache_len);
+                       (bf16*)a.o, a.mu_out, nsplit, a.cache_len, a.lens);
     return hipGetLastError();
 }
 

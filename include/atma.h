@@ -138,6 +138,25 @@ int atma_polar_attn_decode(const void* q, const void* k_cache, const void* v_cac
 
 size_t atma_polar_attn_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
 
+/* ---------------------------------------------------------------------------------
+ * Polar attention, one decode step for a batch of sequences with different cache lengths
+ * (heterogeneous serving batches).  Same operation as atma_polar_attn_decode with
+ * n = cache_lens[b] for sequence b.
+ *   cache_lens    [B] int32 in device memory: valid slots 0..cache_lens[b]-1 of sequence b
+ *                 (the new token's k, v already written at slot cache_lens[b]-1)
+ *   max_cache_len host-side bound, 1 <= cache_lens[b] <= max_cache_len <= Lmax; it sizes
+ *                 the split grid and the workspace:
+ *                 atma_polar_attn_decode_workspace_bytes(B, Hq, max_cache_len, D) bytes.
+ *   Other arguments as for atma_polar_attn_decode.  The lengths are read on the device, so
+ *   the host cannot check them: a sequence whose length lies outside [1, max_cache_len] gets
+ *   NaN in o (and mu_out); the other sequences are unaffected.
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                  const int* cache_lens, int max_cache_len, int Lmax,
+                                  const atma_polar_params* p, void* o, float* mu_out, int B, int Hq,
+                                  int Hkv, int D, atma_dtype dt, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* atma_status_string(int status);
 

@@ -115,6 +115,30 @@ def test_polar_decode_validation():
     assert _pdec(wsb=16) == g.ATMA_ERR_WORKSPACE
 
 
+def _pdecv(p=None, **over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, Lb=10, Lmax=16, o=FAKE, mu=NULL, B=2, Hq=16, Hkv=16, D=64,
+             dt=g.ATMA_BF16, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    pp = ctypes.byref(p if p is not None else _params())
+    return g.lib.atma_polar_attn_decode_varlen(a["q"], a["kc"], a["vc"], a["lens"], a["Lb"], a["Lmax"], pp, a["o"],
+                                               a["mu"], a["B"], a["Hq"], a["Hkv"], a["D"], a["dt"], a["ws"], a["wsb"],
+                                               NULL)
+
+
+def test_polar_decode_varlen_validation():
+    assert _pdecv(lens=NULL) == g.ATMA_ERR_NULL
+    assert _pdecv(o=NULL) == g.ATMA_ERR_NULL
+    assert _pdecv(Lb=0) == g.ATMA_ERR_SHAPE
+    assert _pdecv(Lb=17) == g.ATMA_ERR_SHAPE           # bound > Lmax
+    assert _pdecv(B=0) == g.ATMA_ERR_SHAPE
+    assert _pdecv(Hq=16, Hkv=3) == g.ATMA_ERR_SHAPE
+    assert _pdecv(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pdecv(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
+    assert _pdecv(ws=NULL) == g.ATMA_ERR_WORKSPACE
+    need = g.lib.atma_polar_attn_decode_workspace_bytes(2, 16, 10, 64)
+    assert _pdecv(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
+
+
 def test_binding_rejects_host_tensors():
     import torch
 

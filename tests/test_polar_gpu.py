@@ -107,6 +107,43 @@ def test_polar_decode(atma, B, L, Lmax, Hq, Hkv):
     assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("lens,Lmax,Hq,Hkv", [([1, 77, 1000, 4096], 4096, 16, 16), ([300, 5, 2048], 2048, 8, 2),
+                                               ([64, 63, 65, 129, 1, 200], 256, 4, 4)])
+def test_polar_decode_varlen(atma, lens, Lmax, Hq, Hkv):
+    """Heterogeneous batch: sequence b sees its own cache length; each row is checked against
+    the oracle run on that sequence alone."""
+    B = len(lens)
+    inp = workloads.make_decode_inputs(B, Lmax, Hq=Hq, Hkv=Hkv, Lmax=Lmax, seed=B + Lmax)
+    dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, mu = atma.atma_polar_attn_decode_varlen(inp["q"].cuda(), inp["k_cache"].cuda(), inp["v_cache"].cuda(), dl,
+                                               max(lens), _dev_params(inp["params"]), want_mu=True)
+    torch.cuda.synchronize()
+    for bi, L in enumerate(lens):
+        ref = oracle.polar_decode(inp["q"][bi:bi + 1], inp["k_cache"][bi:bi + 1], inp["v_cache"][bi:bi + 1], L,
+                                  _cpu_params(inp["params"]))
+        eo, emu = out_err(to_np(o[bi:bi + 1]), ref["o"], "bf16"), rel_err(to_np(mu[bi:bi + 1]), ref["mu"])
+        note(f"  polar decode varlen b{bi} L{L} err_o={eo:.3e} err_mu={emu:.3e}")
+        assert eo <= TOL["bf16"] and emu <= TOL["bf16"], (bi, L, eo, emu)
+
+
+def test_polar_decode_varlen_matches_uniform_and_flags_bad_lengths(atma):
+    """Equal lengths give exactly the uniform-length result; a length outside [1, bound] turns
+    only that sequence's outputs into NaN."""
+    B, L, Lmax = 4, 3000, 4096
+    inp = workloads.make_decode_inputs(B, Lmax, Lmax=Lmax, device="cuda", seed=5)
+    p = _dev_params(inp["params"])
+    ou, muu = atma.atma_polar_attn_decode(inp["q"], inp["k_cache"], inp["v_cache"], L, p, want_mu=True)
+    dl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    ov, muv = atma.atma_polar_attn_decode_varlen(inp["q"], inp["k_cache"], inp["v_cache"], dl, L, p, want_mu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ou, ov) and torch.equal(muu, muv)
+    bad = torch.tensor([L, 0, L + 1, L], dtype=torch.int32, device="cuda")
+    ob, mub = atma.atma_polar_attn_decode_varlen(inp["q"], inp["k_cache"], inp["v_cache"], bad, L, p, want_mu=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(ob[1:3].float()).all() and torch.isnan(mub[1:3]).all()
+    assert torch.equal(ob[[0, 3]], ou[[0, 3]]) and torch.equal(mub[[0, 3]], muu[[0, 3]])
+
+
 def test_polar_decode_equals_prefill_last_row(atma):
     B, T, H = 2, 1500, 4
     inp = workloads.make_polar_inputs(B, T, H, H, 64, seed=21)
