@@ -50,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "atma_gdn_decode_step": ([vp] * 7 + [i] * 5 + [vp], i),
         "atma_polar_attn_fwd": ([vp, vp, vp, P, vp, vp, vp] + [i] * 6 + [vp, sz, vp], i),
         "atma_polar_attn_workspace_bytes": ([i] * 4, sz),
+        "atma_polar_attn_fwd_varlen": ([vp, vp, vp, vp, i, i, P, vp, vp, vp] + [i] * 5 + [vp], i),
         "atma_polar_attn_decode": ([vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_polar_attn_decode_workspace_bytes": ([i] * 4, sz),
         "atma_polar_attn_decode_varlen": ([vp, vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
@@ -195,6 +196,31 @@ def atma_polar_attn_fwd(q, k, v, params, *, o=None, mu_out=None, meff_out=None, 
                                  _ptr(meff_out), B, T, Hq, Hkv, D, _dtype_code(q), None, 0, _stream(stream))
     _check("atma_polar_attn_fwd", st)
     return o, mu_out, meff_out
+
+
+def atma_polar_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, params, *, o=None, want_mu=False, stream=None):
+    """Packed causal Polar prefill.  q [total,Hq,D], k/v [total,Hkv,D] bf16; cu_seqlens int32
+    [nseq+1] on the device.  Returns (o [total,Hq,D], mu [Hq,total] or None, meff [Hq,total] or None)."""
+    total, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (total, Hkv, D) or v.shape != k.shape:
+        raise ValueError("inconsistent packed shapes")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be an int32 vector of nseq + 1 offsets")
+    nseq = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty_like(q)
+    mu = meff = None
+    if want_mu:
+        mu = torch.empty(Hq, total, dtype=torch.float32, device=q.device)
+        meff = torch.empty(Hq, total, dtype=torch.float32, device=q.device)
+    _dev(q, k, v, cu_seqlens, o, mu, meff)
+    p = polar_params_struct(params)
+    st = lib.atma_polar_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, int(max_seqlen),
+                                        ctypes.byref(p), _ptr(o), _ptr(mu), _ptr(meff), total, Hq, Hkv, D,
+                                        _dtype_code(q), _stream(stream))
+    _check("atma_polar_attn_fwd_varlen", st)
+    return o, mu, meff
 
 
 def atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D=64) -> int:

@@ -108,6 +108,22 @@ int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_
     return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
 }
 
+int atma_polar_attn_fwd_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens, int nseq,
+                               int max_seqlen, const atma_polar_params* p, void* o, float* mu_out, float* meff_out,
+                               int total_T, int Hq, int Hkv, int D, atma_dtype dt, void* stream) {
+    if (!q || !k || !v || !cu_seqlens || !o) return ATMA_ERR_NULL;
+    const int pc = check_params(p);
+    if (pc != ATMA_OK) return pc;
+    if (!pos(nseq) || !pos(max_seqlen) || !pos(total_T) || !pos(Hq) || !pos(Hkv) || !pos(D)) return ATMA_ERR_SHAPE;
+    if (Hq % Hkv != 0 || max_seqlen > total_T) return ATMA_ERR_SHAPE;
+    if (D != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(1, total_T, Hq, D) || !fits(nseq, max_seqlen, 1, 1) || Hq > 65535 || nseq > 65535)
+        return ATMA_ERR_SHAPE;
+    atma::PolarFwdArgs a{q, k, v, dev_params(p), o, mu_out, meff_out, nseq, max_seqlen, Hq, Hkv, D, cu_seqlens,
+                         total_T};
+    return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
+}
+
 size_t atma_polar_attn_decode_workspace_bytes(int B, int Hq, int cache_len, int D) {
     if (!pos(B) || !pos(Hq) || !pos(cache_len) || D != 64) return 0;
     return atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);

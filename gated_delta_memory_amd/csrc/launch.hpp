@@ -42,6 +42,9 @@ struct PolarFwdArgs {
     void* o;
     float *mu_out, *meff_out;
     int B, T, Hq, Hkv, D;
+    // packed batch: B sequences with row offsets cu[0..B] (device), T = the longest, total rows
+    const int* cu = nullptr;
+    int total = 0;
 };
 hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream);
 

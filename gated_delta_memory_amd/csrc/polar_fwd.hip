@@ -31,6 +31,11 @@
 //   * a workgroup computes two query tiles of one (batch, head), the k-th heaviest and the
 //     k-th lightest, so all workgroups stream the same number of key blocks (causal balance);
 //     the tiles of one (batch, head) go to one XCD so their K/V stream is shared in its L2.
+// Packed batches (sequences of different lengths concatenated, offsets cu[0..B] on the device)
+// use the same kernel: the grid is sized for the longest sequence and each workgroup reads its
+// sequence's bounds, skipping tiles past its end.  Offsets that are not a valid partition of
+// the packed rows (or a sequence longer than the declared maximum) skip that sequence, so a
+// malformed offset array can never address memory outside the buffers.
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -84,8 +89,8 @@ __shared__ __align__(16) char g_kv1[2 * BK * D * 2];
 __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
-                                                          float* __restrict__ meff_out, int T, int Hq, int Hkv,
-                                                          int paired) {
+                                                          float* __restrict__ meff_out, int Tmax, int Hq, int Hkv,
+                                                          int paired, const int* __restrict__ cu, int total) {
     // Work items.  With `paired` set (few tiles in all), a workgroup computes two query tiles
     // of one (batch, head), tile nqt - 1 - p and tile p: every pair streams the same number of
     // key blocks (causal balance) and the per-tile start-up and finalisation are spread over
@@ -93,22 +98,37 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     // Workgroup i is dispatched to XCD i % 8; the flat grid is renumbered so that every XCD
     // receives a contiguous range of items and the tiles of one (batch, head) share that
     // XCD's L2 for their K/V stream.
-    const int nqt = (T + BQ - 1) / BQ;
-    const int per_bh = paired ? (nqt + 1) / 2 : nqt;
+    const int nqt_grid = (Tmax + BQ - 1) / BQ;
+    const int per_bh = paired ? (nqt_grid + 1) / 2 : nqt_grid;
     const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
     const int item = xcd * per + min(xcd, extra) + (wg >> 3);
     const int bh = item / per_bh;
     const int pr = item - bh * per_bh;
     const int h = bh % Hq, b = bh / Hq;
     const int hk = h / (Hq / Hkv);
+    // this sequence: first packed row seq0 and length T
+    size_t seq0;
+    int T;
+    if (cu) {
+        const int s0 = cu[b], s1 = cu[b + 1];
+        if (s0 < 0 || s1 < s0 || s1 > total || s1 - s0 > Tmax) return;  // malformed offsets
+        seq0 = (size_t)s0;
+        T = s1 - s0;
+    } else {
+        seq0 = (size_t)b * Tmax;
+        T = Tmax;
+    }
+    const int nqt = (T + BQ - 1) / BQ;
+    if (pr >= (paired ? (nqt + 1) / 2 : nqt)) return;  // past the end of this sequence
+    const size_t mu_base = cu ? (size_t)h * total + seq0 : ((size_t)b * Hq + h) * Tmax;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());  // wave-uniform
     const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
     const float a_t = softplus(prm.temp_raw[h]);
     const size_t qstride = (size_t)Hq * D;
     const size_t kvstride = (size_t)Hkv * D;
     const unsigned rowbytes = (unsigned)(kvstride * 2);
-    const bf16* kbase = k + (size_t)b * T * kvstride + (size_t)hk * D;
-    const bf16* vbase = v + (size_t)b * T * kvstride + (size_t)hk * D;
+    const bf16* kbase = k + seq0 * kvstride + (size_t)hk * D;
+    const bf16* vbase = v + seq0 * kvstride + (size_t)hk * D;
 
     // Asynchronous copy of key block kb into a stage [K tile | V tile]: 16-byte chunk ch of the
     // stage lands at LDS slot ch (row ch / 8, position ch % 8); the source chunk is chosen so
@@ -155,7 +175,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     bf16x8 qf[4];
     {
         const int qc = min(qi, T - 1);
-        const bf16* qrow = q + ((size_t)b * T + qc) * qstride + (size_t)h * D + 8 * G2;
+        const bf16* qrow = q + (seq0 + qc) * qstride + (size_t)h * D + 8 * G2;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
     }
@@ -287,7 +307,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     nrm2 = pair_sum(nrm2);
     const float scale = mu / fmaxf(sqrtf(nrm2), prm.eps);
     if (qi < T) {
-        bf16* orow = o + ((size_t)b * T + qi) * qstride + (size_t)h * D;
+        bf16* orow = o + (seq0 + qi) * qstride + (size_t)h * D;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -298,7 +318,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
                 *(bf16x4*)(orow + 32 * dt + 8 * g + 4 * G2) = y;
             }
         if (G2 == 0) {
-            const size_t si = ((size_t)b * Hq + h) * T + qi;
+            const size_t si = mu_base + qi;
             if (mu_out) mu_out[si] = mu;
             if (meff_out) meff_out[si] = meff;
         }
@@ -323,7 +343,7 @@ hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
     const int per_bh = paired ? (nqt + 1) / 2 : nqt;
     hipLaunchKernelGGL(polar_fwd_kernel, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
-                       a.Hkv, paired);
+                       a.Hkv, paired, a.cu, a.total);
     return hipGetLastError();
 }
 

@@ -121,6 +121,25 @@ int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_
 size_t atma_polar_attn_workspace_bytes(int B, int T, int Hq, int D);
 
 /* ---------------------------------------------------------------------------------
+ * Causal Polar attention, prefill of a packed batch: nseq sequences of different lengths
+ * concatenated along the token axis (no padding).  Same operation as atma_polar_attn_fwd
+ * within each sequence (n = i + 1 for the sequence's own query i; no attention across
+ * sequences).
+ *   q            [total_T, Hq, D] dtype `dt`;  k, v [total_T, Hkv, D];  o [total_T, Hq, D]
+ *   cu_seqlens   [nseq + 1] int32 in device memory: sequence s holds rows
+ *                cu_seqlens[s] .. cu_seqlens[s+1]-1 (0 = cu_seqlens[0] <= ... <= total_T)
+ *   max_seqlen   host-side bound on every sequence length (sizes the grid), <= total_T
+ *   mu_out, meff_out  [Hq, total_T] fp32 or NULL
+ *   D == 64 and dt == ATMA_BF16.  No workspace.  The offsets are read on the device: a
+ *   sequence whose bounds are not inside [0, total_T], decrease, or exceed max_seqlen is
+ *   skipped (its rows of o are left unwritten); no access leaves the buffers.
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_fwd_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens,
+                               int nseq, int max_seqlen, const atma_polar_params* p, void* o,
+                               float* mu_out, float* meff_out, int total_T, int Hq, int Hkv, int D,
+                               atma_dtype dt, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Polar attention, one decode step: the last causal row for a KV cache.
  *   q        [B, Hq, D] dtype `dt`
  *   k_cache, v_cache [B, Lmax, Hkv, D] dtype `dt`; slots 0..cache_len-1 are valid and the

@@ -139,6 +139,27 @@ def test_polar_decode_varlen_validation():
     assert _pdecv(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
 
 
+def _pfwdv(p=None, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, nseq=3, maxT=100, o=FAKE, mu=NULL, meff=NULL, total=200, Hq=4, Hkv=2,
+             D=64, dt=g.ATMA_BF16)
+    a.update(over)
+    pp = ctypes.byref(p if p is not None else _params())
+    return g.lib.atma_polar_attn_fwd_varlen(a["q"], a["k"], a["v"], a["cu"], a["nseq"], a["maxT"], pp, a["o"],
+                                            a["mu"], a["meff"], a["total"], a["Hq"], a["Hkv"], a["D"], a["dt"], NULL)
+
+
+def test_polar_fwd_varlen_validation():
+    assert _pfwdv(cu=NULL) == g.ATMA_ERR_NULL
+    assert _pfwdv(v=NULL) == g.ATMA_ERR_NULL
+    assert _pfwdv(nseq=0) == g.ATMA_ERR_SHAPE
+    assert _pfwdv(maxT=0) == g.ATMA_ERR_SHAPE
+    assert _pfwdv(maxT=201) == g.ATMA_ERR_SHAPE          # longer than all rows together
+    assert _pfwdv(Hq=4, Hkv=3) == g.ATMA_ERR_SHAPE
+    assert _pfwdv(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pfwdv(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
+    assert _pfwdv(p=_params(v_null=0)) == g.ATMA_ERR_NULL
+
+
 def test_binding_rejects_host_tensors():
     import torch
 

@@ -107,6 +107,52 @@ def test_polar_decode(atma, B, L, Lmax, Hq, Hkv):
     assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv", [([1, 77, 300, 513, 128, 1000], 4, 2), ([2048, 5, 129, 256], 2, 2),
+                                          ([64], 3, 1)])
+def test_polar_fwd_varlen(atma, lens, Hq, Hkv):
+    """Packed prefill: each sequence (all rows, its own causal positions) against the oracle
+    run on that sequence alone."""
+    total = sum(lens)
+    inp = workloads.make_polar_inputs(1, total, Hq, Hkv, 64, seed=total)
+    q, k, v = (inp[x][0].contiguous() for x in ("q", "k", "v"))
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
+    o, mu, meff = atma.atma_polar_attn_fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu, max(lens),
+                                                  _dev_params(inp["params"]), want_mu=True)
+    torch.cuda.synchronize()
+    for si, (s0, s1) in enumerate(zip(cu[:-1].tolist(), cu[1:].tolist())):
+        ref = oracle.polar_fwd(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], _cpu_params(inp["params"]))
+        eo = out_err(to_np(o[None, s0:s1]), ref["o"], "bf16")
+        emu = rel_err(to_np(mu[:, s0:s1]).T[None], ref["mu"])
+        eme = rel_err_elem(to_np(meff[:, s0:s1]).T[None], ref["meff"])
+        note(f"  polar varlen seq{si} T{s1 - s0} err_o={eo:.3e} err_mu={emu:.3e} err_meff={eme:.3e}")
+        assert eo <= TOL["bf16"] and emu <= TOL["bf16"] and eme <= TOL["bf16"], (si, eo, emu, eme)
+
+
+def test_polar_fwd_varlen_matches_fixed_and_skips_bad_offsets(atma):
+    """Equal lengths packed give exactly the fixed-length result; a sequence whose offsets are
+    malformed is skipped (its rows keep their previous contents) and the others are unchanged."""
+    B, T, H = 3, 700, 4
+    inp = workloads.make_polar_inputs(B, T, H, H, 64, seed=33)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    p = _dev_params(inp["params"])
+    of, muf, mef = atma.atma_polar_attn_fwd(q, k, v, p, want_mu=True)
+    qp, kp, vp = (x.reshape(B * T, H, 64) for x in (q, k, v))
+    cu = torch.tensor([0, T, 2 * T, 3 * T], dtype=torch.int32, device="cuda")
+    op, mup, mep = atma.atma_polar_attn_fwd_varlen(qp, kp, vp, cu, T, p, want_mu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(op.reshape(B, T, H, 64), of)
+    assert torch.equal(mup.reshape(H, B, T).permute(1, 0, 2), muf)
+    assert torch.equal(mep.reshape(H, B, T).permute(1, 0, 2), mef)
+    # sequence 1 ends past the packed rows, sequence 2 runs backwards: both skipped, their rows
+    # keep the sentinel; sequence 0 is computed as before
+    for bad, bound in (([0, T, 5 * T, 3 * T], T), ([0, T, 3 * T], T)):  # second: length 2T > bound
+        cb = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        ob, _, _ = atma.atma_polar_attn_fwd_varlen(qp, kp, vp, cb, bound, p, o=torch.full_like(qp, 7.0))
+        torch.cuda.synchronize()
+        assert torch.equal(ob[:T], op[:T])
+        assert (ob[T:].float() == 7.0).all()
+
+
 @pytest.mark.parametrize("lens,Lmax,Hq,Hkv", [([1, 77, 1000, 4096], 4096, 16, 16), ([300, 5, 2048], 2048, 8, 2),
                                                ([64, 63, 65, 129, 1, 200], 256, 4, 4)])
 def test_polar_decode_varlen(atma, lens, Lmax, Hq, Hkv):
