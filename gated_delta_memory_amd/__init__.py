@@ -47,6 +47,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "atma_gdn_fwd": ([vp] * 8 + [i] * 7 + [vp, sz, vp], i),
         "atma_gdn_fwd_workspace_bytes": ([i] * 7, sz),
+        "atma_gdn_fwd_varlen": ([vp] * 6 + [i, i] + [vp] * 3 + [i] * 6 + [vp, sz, vp], i),
         "atma_gdn_decode_step": ([vp] * 7 + [i] * 5 + [vp], i),
         "atma_polar_attn_fwd": ([vp, vp, vp, P, vp, vp, vp] + [i] * 6 + [vp, sz, vp], i),
         "atma_polar_attn_workspace_bytes": ([i] * 4, sz),
@@ -142,6 +143,37 @@ def atma_gdn_fwd(q, k, v, alpha, beta, init_state=None, *, o=None, final_state=N
                           _ptr(final_state), B, T, H, Dk, Dv, CHUNK, _dtype_code(q), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(stream))
     _check("atma_gdn_fwd", st)
+    return o, final_state
+
+
+def atma_gdn_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, max_seqlen, init_state=None, *, o=None, final_state=None,
+                        workspace=None, want_final=True, stream=None):
+    """Packed chunked gated-delta forward.  q, k [total,H,Dk], v [total,H,Dv] bf16, alpha, beta
+    [total,H] fp32, cu_seqlens int32 [nseq+1] on the device, init_state [nseq,H,Dv,Dk] fp32 or
+    None.  Returns (o [total,H,Dv], final_state [nseq,H,Dv,Dk] or None)."""
+    total, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != (total, H) or alpha.shape != (total, H) or beta.shape != (total, H):
+        raise ValueError("inconsistent packed shapes")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be an int32 vector of nseq + 1 offsets")
+    nseq = cu_seqlens.numel() - 1
+    _f32(alpha, "alpha"), _f32(beta, "beta"), _f32(init_state, "init_state")
+    if o is None:
+        o = torch.empty(total, H, Dv, dtype=q.dtype, device=q.device)
+    if final_state is None and want_final:
+        final_state = torch.empty(nseq, H, Dv, Dk, dtype=torch.float32, device=q.device)
+    need = atma_gdn_fwd_workspace_bytes(nseq, max_seqlen, H, Dk, Dv, CHUNK, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, alpha, beta, cu_seqlens, init_state, o, final_state, workspace)
+    st = lib.atma_gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), nseq,
+                                 int(max_seqlen), _ptr(init_state), _ptr(o), _ptr(final_state), total, H, Dk, Dv,
+                                 CHUNK, _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _check("atma_gdn_fwd_varlen", st)
     return o, final_state
 
 

@@ -76,6 +76,25 @@ int atma_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha
     return launched(atma::launch_gdn_fwd(a, (hipStream_t)stream));
 }
 
+int atma_gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                        const int* cu_seqlens, int nseq, int max_seqlen, const float* init_state, void* o,
+                        float* final_state, int total_T, int H, int Dk, int Dv, int chunk, atma_dtype dt,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !alpha || !beta || !cu_seqlens || !o) return ATMA_ERR_NULL;
+    if (!pos(nseq) || !pos(max_seqlen) || !pos(total_T) || !pos(H) || !pos(Dk) || !pos(Dv) || !pos(chunk))
+        return ATMA_ERR_SHAPE;
+    if (max_seqlen > total_T) return ATMA_ERR_SHAPE;
+    if (!head_width_ok(Dk) || !head_width_ok(Dv) || chunk != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(1, total_T, H, Dk > Dv ? Dk : Dv) || !fits(nseq, max_seqlen, H, 1) || !fits(nseq, H, Dv, Dk))
+        return ATMA_ERR_SHAPE;
+    if (H > 65535 || nseq > 65535) return ATMA_ERR_SHAPE;
+    const size_t need = atma::gdn_fwd_workspace_bytes(nseq, max_seqlen, H, Dk, Dv, true);
+    if (!workspace || ws_bytes < need) return ATMA_ERR_WORKSPACE;
+    atma::GdnFwdArgs a{q, k, v, alpha, beta, init_state, o, final_state, nseq, max_seqlen, H, Dk, Dv, true,
+                       workspace, cu_seqlens, total_T};
+    return launched(atma::launch_gdn_fwd(a, (hipStream_t)stream));
+}
+
 int atma_gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                          float* state, void* o, int B, int H, int Dk, int Dv, atma_dtype dt, void* stream) {
     if (!q || !k || !v || !alpha || !beta || !state || !o) return ATMA_ERR_NULL;

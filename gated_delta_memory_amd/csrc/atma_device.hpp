@@ -171,10 +171,20 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     typedef __attribute__((address_space(3))) const char* lds_ptr;
     return (unsigned)(size_t)(lds_ptr)p;
 }
+// A wave-uniform 64-bit pointer, in scalar registers even where the compiler cannot prove it
+// uniform (free when it already is).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const unsigned long long x = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+    return (const void*)(((unsigned long long)hi << 32) | lo);
+}
+
 // Same copy with the global address split into a wave-uniform 64-bit base and a per-lane
 // 32-bit byte offset, and the LDS destination given as a wave-uniform byte address.
 __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsigned lds_wave_addr) {
     const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+    sbase = uniform_ptr(sbase);
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
@@ -200,6 +210,7 @@ __device__ __forceinline__ void lds_dma4(const void* gaddr, const void* lds_wave
 // byte address, 4 bytes per lane.
 __device__ __forceinline__ void lds_dma4(const void* sbase, unsigned voff, unsigned lds_wave_addr) {
     const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+    sbase = uniform_ptr(sbase);
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"

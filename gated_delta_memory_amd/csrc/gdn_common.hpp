@@ -70,6 +70,25 @@ __device__ __forceinline__ void copy_out(char* __restrict__ dst, const char* src
     }
 }
 
+// Packed rows [seq0, seq0 + T) of sequence b.  Without offsets every sequence has Tmax rows;
+// with offsets cu[0..B] (device memory) the bounds are read and checked: a sequence whose
+// offsets leave [0, total], decrease, or span more than Tmax rows is reported invalid, and
+// every kernel skips it, so malformed offsets never address memory outside the buffers.
+__device__ __forceinline__ bool seq_bounds(const int* cu, int b, int Tmax, int total, size_t& seq0, int& T) {
+    if (!cu) {
+        seq0 = (size_t)b * Tmax;
+        T = Tmax;
+        return true;
+    }
+    // b is uniform across the workgroup; readfirstlane keeps the bounds (and everything derived
+    // from them, such as chunk counts and copy addresses) in scalar registers
+    const int s0 = __builtin_amdgcn_readfirstlane(cu[b]), s1 = __builtin_amdgcn_readfirstlane(cu[b + 1]);
+    if (s0 < 0 || s1 < s0 || s1 > total || s1 - s0 > Tmax) return false;
+    seq0 = (size_t)s0;
+    T = s1 - s0;
+    return true;
+}
+
 using atma::wait_vmcnt;
 using atma::lds_dma16;
 using atma::lds_dma4;

@@ -162,7 +162,8 @@ __device__ __forceinline__ Frag<bf16> bfrag_tr(const bf16* tile, int ld, int ct,
 template <int DK, int DV>
 __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                     const bf16* __restrict__ v, const float* __restrict__ alpha,
-                                                    const float* __restrict__ beta, Regions rg, int Tlen, int H) {
+                                                    const float* __restrict__ beta, Regions rg, int Tmax, int H,
+                                                    const int* __restrict__ cu, int total) {
     using S = PrepSmem<DK, DV>;
     using L = Lay<DK, DV>;
     constexpr int LDK = S::LDK, LDX = S::LDX, LDA = S::LDA, RBK = L::RBK;
@@ -170,11 +171,14 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
     S& sm = *reinterpret_cast<S*>(smem_raw);
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int NC = gridDim.x;
+    const int NC = gridDim.x;  // chunk-record stride: chunks of the longest sequence
+    size_t seq0;
+    int Tlen;
+    if (!gdn::seq_bounds(cu, b, Tmax, total, seq0, Tlen) || c * C >= Tlen) return;
     const int t0 = c * C;
     const int n = min(C, Tlen - t0);
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id()), G = lane >> 4, l16 = lane & 15;
-    const size_t tok0 = ((size_t)b * Tlen + t0) * H + h;
+    const size_t tok0 = (seq0 + t0) * H + h;
     const size_t cid = ((size_t)b * H + h) * NC + c;
     char* ra = rg.ra + cid * L::RA;
     char* rb = rg.rb + cid * L::RB;
@@ -549,7 +553,8 @@ struct Carry {
 // rows start from the identity with U ignored; the end state goes to the summary region.
 template <int DK, int DV, bool STORE>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
-    Regions rg, const float* init_state, float* final_state, int Tlen, int H, int nseg, int seglen) {
+    Regions rg, const float* init_state, float* final_state, int Tmax, int H, int nseg, int seglen,
+    const int* __restrict__ cu, int total) {
     using L = Lay<DK, DV>;
     using K = Carry<DK, DV, STORE>;
     constexpr int NKT = DK / 16;
@@ -561,10 +566,14 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     const int sl = item % nsl, yy = (item / nsl) % (int)gridDim.y, b = item / (nsl * (int)gridDim.y);
     const int h = yy / nseg, sg = yy % nseg;
     const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
-    const int NC = (Tlen + C - 1) / C;
-    const int cb = sg * seglen, n = min(NC - cb, seglen);  // this segment's chunks
+    size_t seq0;
+    int Tlen;
+    if (!gdn::seq_bounds(cu, b, Tmax, total, seq0, Tlen)) return;
+    const int NC = (Tlen + C - 1) / C;         // this sequence's chunks
+    const int NCs = (Tmax + C - 1) / C;        // chunk-record stride
+    const int cb = sg * seglen, n = min(NC - cb, seglen);  // this segment's chunks (<= 0: none)
     const size_t bh = (size_t)b * H + h;
-    const size_t c0 = bh * NC + cb;
+    const size_t c0 = bh * NCs + cb;
     const bool real = sl < DV / 64;
     const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, real ? sl : 0,
               real ? 1.0f : 0.0f};
@@ -585,6 +594,26 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     }
 
     gdn::wait_vmcnt<0>();  // initial state in registers before the untracked copies start
+    // the end state: final state (last segment) or segment summary
+    auto finish = [&]() {
+        if constexpr (STORE) {
+            if (final_state && sg == nseg - 1) {
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+                    *(f32x4*)(final_state + (bh * DV + row) * DK + 16 * t + 4 * G) = st[t];
+            }
+        } else {
+            float* dst = rg.seg + ((bh * nseg + sg) * (DV + DK) + row) * DK;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) *(f32x4*)(dst + 16 * t + 4 * G) = st[t];
+        }
+    };
+    // A segment past the end of a (packed) sequence has no chunks: its map is the identity, so
+    // it only passes its start state on.
+    if (n <= 0) {
+        finish();
+        return;
+    }
     const int last = n - 1;
     const int NC_seg = n;
     k.issue(0, g_stage0);
@@ -609,17 +638,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         k.issue(min(c + 4, last), g_stage2);
         k.step(c + 2, g_stage0, st);
     }
-    if constexpr (STORE) {
-        if (final_state && sg == nseg - 1) {
-#pragma unroll
-            for (int t = 0; t < NKT; ++t)
-                *(f32x4*)(final_state + (bh * DV + row) * DK + 16 * t + 4 * G) = st[t];
-        }
-    } else {
-        float* dst = rg.seg + ((bh * nseg + sg) * (DV + DK) + row) * DK;
-#pragma unroll
-        for (int t = 0; t < NKT; ++t) *(f32x4*)(dst + 16 * t + 4 * G) = st[t];
-    }
+    finish();
 }
 
 // =========================================================================================
@@ -736,18 +755,22 @@ struct OutSmem {
 
 template <int DK, int DV>
 __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, const bf16* __restrict__ k, Regions rg,
-                                                   bf16* __restrict__ o, int Tlen, int H) {
+                                                   bf16* __restrict__ o, int Tmax, int H, const int* __restrict__ cu,
+                                                   int total) {
     using L = Lay<DK, DV>;
     using S = OutSmem<DK, DV>;
     constexpr int LDQ = S::LDQ, LDO = S::LDO;
     extern __shared__ __align__(16) char smem_raw[];
     S& sm = *reinterpret_cast<S*>(smem_raw);
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int NC = gridDim.x;
+    const int NC = gridDim.x;  // chunk-record stride
+    size_t seq0;
+    int Tlen;
+    if (!gdn::seq_bounds(cu, b, Tmax, total, seq0, Tlen) || c * C >= Tlen) return;
     const int t0 = c * C, n = min(C, Tlen - t0);
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id()), G = lane >> 4, l16 = lane & 15;
     const size_t cid = ((size_t)b * H + h) * NC + c;
-    const size_t tok0 = ((size_t)b * Tlen + t0) * H + h;
+    const size_t tok0 = (seq0 + t0) * H + h;
     {
         TileRegs<bf16, C, DK> qr, kr;
         qr.template load<true>(q + tok0 * DK, (size_t)H * DK, n);
@@ -841,7 +864,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
         const int r = id / (DV / 8), cc = id % (DV / 8);
         if (r < n)
             __builtin_nontemporal_store(*(const u32x4*)&sm.u.Os[r * LDO + 8 * cc],
-                                        (u32x4*)(o + (((size_t)b * Tlen + t0 + r) * H + h) * DV + 8 * cc));
+                                        (u32x4*)(o + ((seq0 + t0 + r) * H + h) * DV + 8 * cc));
     }
 }
 
@@ -862,17 +885,17 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
     }();
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gdn_prep_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), prep_smem, stream, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, rg, a.T, a.H);
+                       (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, rg, a.T, a.H, a.cu, a.total);
     if (nseg > 1) {
         hipLaunchKernelGGL((gdn_carry_h<DK, DV, false>), dim3((DV + DK) / 64, a.H * nseg, a.B), dim3(NT), 0, stream,
-                           rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen);
+                           rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
         hipLaunchKernelGGL((gdn_seg_scan<DK, DV>), dim3(DV / 16, a.H, a.B), dim3(NT), scan_smem, stream, rg,
                            a.init_state, a.H, nseg);
     }
     hipLaunchKernelGGL((gdn_carry_h<DK, DV, true>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream, rg,
-                       a.init_state, a.final_state, a.T, a.H, nseg, seglen);
+                       a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
     hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, (const bf16*)a.q,
-                       (const bf16*)a.k, rg, (bf16*)a.o, a.T, a.H);
+                       (const bf16*)a.k, rg, (bf16*)a.o, a.T, a.H, a.cu, a.total);
     return hipGetLastError();
 }
 

@@ -14,6 +14,9 @@ struct GdnFwdArgs {
     int B, T, H, Dk, Dv;
     bool bf16_io;
     void* workspace;
+    // packed batch (bf16 path): B sequences with row offsets cu[0..B] (device), T = the longest
+    const int* cu = nullptr;
+    int total = 0;
 };
 size_t gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16_io);
 hipError_t launch_gdn_fwd(const GdnFwdArgs& a, hipStream_t stream);

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     const int slots = NT / tpt;              // tokens per pass
     const int slot = threadIdx.x / tpt;
     const int hk = (threadIdx.x % tpt) >> 3, chunk = threadIdx.x & 7;
-    int cache_len = lens ? lens[b] : max_len;
+    int cache_len = lens ? __builtin_amdgcn_readfirstlane(lens[b]) : max_len;
     if (cache_len < 1 || cache_len > max_len) cache_len = 0;  // invalid: no keys (the combine writes NaN)
     const int t_begin = (int)((long)cache_len * split / nsplit);
     const int t_end = (int)((long)cache_len * (split + 1) / nsplit);
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restr
                                                             bf16* __restrict__ o, float* __restrict__ mu_out,
                                                             int nsplit, int max_len, const int* __restrict__ lens) {
     const int h = blockIdx.x, Hq = gridDim.x, b = blockIdx.y;
-    const int cache_len = lens ? lens[b] : max_len;
+    const int cache_len = lens ? __builtin_amdgcn_readfirstlane(lens[b]) : max_len;
     if (cache_len < 1 || cache_len > max_len) {  // invalid length: NaN outputs for this sequence
         if (threadIdx.x < 64) o[((size_t)b * Hq + h) * D + threadIdx.x] = (bf16)__builtin_nanf("");
         if (threadIdx.x == 0 && mu_out) mu_out[(size_t)b * Hq + h] = __builtin_nanf("");

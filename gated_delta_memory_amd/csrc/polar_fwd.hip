@@ -110,7 +110,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     size_t seq0;
     int T;
     if (cu) {
-        const int s0 = cu[b], s1 = cu[b + 1];
+        const int s0 = __builtin_amdgcn_readfirstlane(cu[b]), s1 = __builtin_amdgcn_readfirstlane(cu[b + 1]);
         if (s0 < 0 || s1 < s0 || s1 > total || s1 - s0 > Tmax) return;  // malformed offsets
         seq0 = (size_t)s0;
         T = s1 - s0;

@@ -87,6 +87,28 @@ int atma_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha
 size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt);
 
 /* ---------------------------------------------------------------------------------
+ * Gated-delta memory, chunked prefill of a packed batch: nseq sequences of different
+ * lengths concatenated along the token axis (no padding); each sequence runs the recurrence
+ * of atma_gdn_fwd on its own rows, from its own initial state.
+ *   q, k, v      [total_T, H, Dk|Dk|Dv] bf16;  alpha, beta [total_T, H] fp32;  o [total_T, H, Dv]
+ *   cu_seqlens   [nseq + 1] int32 in device memory: sequence s holds rows
+ *                cu_seqlens[s] .. cu_seqlens[s+1]-1 (0 = cu_seqlens[0] <= ... <= total_T)
+ *   max_seqlen   host-side bound on every sequence length (sizes grids and workspace),
+ *                <= total_T
+ *   init_state   [nseq, H, Dv, Dk] fp32 or NULL (zeros);  final_state [nseq, H, Dv, Dk] or NULL
+ *   chunk == 64, dt == ATMA_BF16, Dk and Dv in {64, 128}.
+ *   workspace at least atma_gdn_fwd_workspace_bytes(nseq, max_seqlen, H, Dk, Dv, chunk,
+ *   ATMA_BF16) bytes.  The offsets are read on the device: a sequence whose bounds are not
+ *   inside [0, total_T], decrease, or exceed max_seqlen is skipped (its rows of o and its final
+ *   state are left unwritten); no access leaves the buffers.
+ * ------------------------------------------------------------------------------- */
+int atma_gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const int* cu_seqlens, int nseq, int max_seqlen,
+                        const float* init_state, void* o, float* final_state, int total_T, int H,
+                        int Dk, int Dv, int chunk, atma_dtype dt, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Gated-delta memory, one decode step (the same equation for a single token):
  *     S <- alpha (S - beta (S k) k^T) + beta v k^T ;  o = S q
  *   q, k   [B, H, Dk] dtype `dt`;  v [B, H, Dv] dtype `dt`;  alpha, beta [B, H] fp32

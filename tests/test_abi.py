@@ -61,6 +61,29 @@ def test_gdn_fwd_validation():
     assert _gdn(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
 
 
+def _gdnv(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, cu=FAKE, nseq=2, maxT=8, init=NULL, o=FAKE, fin=NULL,
+             total=10, H=1, Dk=64, Dv=64, chunk=64, dt=g.ATMA_BF16, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return g.lib.atma_gdn_fwd_varlen(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["cu"], a["nseq"], a["maxT"],
+                                     a["init"], a["o"], a["fin"], a["total"], a["H"], a["Dk"], a["Dv"], a["chunk"],
+                                     a["dt"], a["ws"], a["wsb"], NULL)
+
+
+def test_gdn_fwd_varlen_validation():
+    assert _gdnv(cu=NULL) == g.ATMA_ERR_NULL
+    assert _gdnv(beta=NULL) == g.ATMA_ERR_NULL
+    assert _gdnv(nseq=0) == g.ATMA_ERR_SHAPE
+    assert _gdnv(maxT=11) == g.ATMA_ERR_SHAPE           # longer than all rows together
+    assert _gdnv(total=0) == g.ATMA_ERR_SHAPE
+    assert _gdnv(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED  # packed batches take the bf16 path
+    assert _gdnv(Dk=96) == g.ATMA_ERR_UNSUPPORTED
+    assert _gdnv(chunk=32) == g.ATMA_ERR_UNSUPPORTED
+    assert _gdnv(ws=NULL) == g.ATMA_ERR_WORKSPACE
+    need = g.lib.atma_gdn_fwd_workspace_bytes(2, 8, 1, 64, 64, 64, g.ATMA_BF16)
+    assert _gdnv(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
+
+
 def test_gdn_decode_validation():
     f = g.lib.atma_gdn_decode_step
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 1, 8, 128, 128, g.ATMA_BF16, NULL) == g.ATMA_ERR_NULL

@@ -5,6 +5,7 @@ the oracle runs the sequential recurrence (ATMA paper, Section 3.3 equation) on 
 copies of the same inputs.  Error = max |gpu - oracle| / rms(oracle); budgets 1e-4 (fp32)
 and 2e-2 (bf16 inputs, fp32 state).
 """
+import numpy as np
 import pytest
 import torch
 
@@ -178,3 +179,53 @@ def test_gdn_decode_steps_match_prefill(atma):
     torch.cuda.synchronize()
     assert rel_err(to_np(torch.stack(outs, dim=1)), to_np(o)) <= 1e-4
     assert rel_err(to_np(St), to_np(S)) <= 1e-4
+
+
+def _packed(inp):
+    """[1, total, ...] workload tensors as packed [total, ...] tensors on the GPU."""
+    return [inp[x][0].contiguous().cuda() for x in ("q", "k", "v", "alpha", "beta")]
+
+
+@pytest.mark.parametrize("lens,H,Dk,Dv", [([1, 64, 65, 300, 129], 2, 128, 128), ([4096, 100, 1500], 1, 64, 128),
+                                          ([2000, 3], 2, 128, 64)])
+def test_gdn_fwd_varlen(atma, lens, H, Dk, Dv):
+    """Packed prefill: every sequence, from its own initial state, against the oracle's
+    sequential recurrence on that sequence alone.  The long-and-short mixes make the library
+    cut the carry into segments, most of them empty for the short sequences."""
+    total = sum(lens)
+    inp = workloads.make_gdn_inputs(1, total, H, Dk, Dv, dtype="bf16", seed=total + Dk)
+    init = torch.randn(len(lens), H, Dv, Dk, generator=torch.Generator().manual_seed(total)) * 0.3
+    q, k, v, a, b = _packed(inp)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
+    o, S = atma.atma_gdn_fwd_varlen(q, k, v, a, b, cu, max(lens), init.cuda())
+    torch.cuda.synchronize()
+    for si, (s0, s1) in enumerate(zip(cu[:-1].tolist(), cu[1:].tolist())):
+        ro, rS = oracle.gdn_sequential(*(inp[x][:, s0:s1] for x in ("q", "k", "v", "alpha", "beta")),
+                                       init_state=init[si:si + 1])
+        eo, eS = out_err(to_np(o[None, s0:s1]), ro, "bf16"), rel_err(to_np(S[si:si + 1]), rS)
+        note(f"  gdn varlen seq{si} T{s1 - s0} err_o={eo:.3e} err_S={eS:.3e}")
+        assert eo <= TOL["bf16"] and eS <= TOL["bf16"], (si, eo, eS)
+
+
+def test_gdn_fwd_varlen_matches_fixed_and_skips_bad_offsets(atma):
+    """Equal lengths packed give exactly the fixed-length result; a sequence whose offsets are
+    malformed is skipped (its rows and final state keep their previous contents)."""
+    B, T, H, D = 2, 700, 2, 128
+    inp = workloads.make_gdn_inputs(B, T, H, D, dtype="bf16", seed=44)
+    q, k, v, a, b = (inp[x].cuda() for x in ("q", "k", "v", "alpha", "beta"))
+    of, Sf = atma.atma_gdn_fwd(q, k, v, a, b)
+    pk = [x.reshape(B * T, *x.shape[2:]) for x in (q, k, v, a, b)]
+    cu = torch.tensor([0, T, 2 * T], dtype=torch.int32, device="cuda")
+    op, Sp = atma.atma_gdn_fwd_varlen(*pk, cu, T)
+    torch.cuda.synchronize()
+    assert torch.equal(op.reshape(B, T, H, D), of) and torch.equal(Sp, Sf)
+    for bad, bound in (([0, T, 5 * T], T), ([0, T, T - 1], T), ([0, T, 2 * T], T - 1)):
+        cb = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        fin = torch.full_like(Sp, 7.0)
+        ob, Sb = atma.atma_gdn_fwd_varlen(*pk, cb, max(bound, 1), o=torch.full_like(op, 7.0), final_state=fin)
+        torch.cuda.synchronize()
+        if bound == T:   # sequence 0 valid, sequence 1 malformed
+            assert torch.equal(ob[:T], op[:T]) and torch.equal(Sb[0], Sp[0])
+            assert (ob[T:].float() == 7.0).all() and (Sb[1] == 7.0).all()
+        else:            # both sequences longer than the declared bound: nothing written
+            assert (ob.float() == 7.0).all() and (Sb == 7.0).all()
