@@ -49,10 +49,10 @@ def decode_bytes(B, L, Hkv=16, D=64, H=8, Dg=128):
 # device copy of known size; keyed by the SHA-256 of the kernel's sources at the time the
 # counters were taken, so an edited kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    # layer_b8_t2k: FETCH_SIZE 62,277 KiB x 2.0 + WRITE_SIZE 32,768 KiB x 1.0 per dispatch
-    "polar_fwd_kernel": {"sha": "0a8f538a786edd5b", "bytes": 161092951},
+    # layer_b8_t2k: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch (profiles/polar_fwd_layer_b8_t2k.txt)
+    "polar_fwd_kernel": {"sha": "ea3ad103af73468e", "bytes": 161242156},
     # layer_b8_t2k, prep + carry + out (one segment at this shape)
-    "atma_gdn_fwd (prep+carry+out)": {"sha": "85da617513e72780", "bytes": 577270230},
+    "atma_gdn_fwd (prep+carry+out)": {"sha": "f23d9f53f9281fbe", "bytes": 577292807},
 }
 
 
