@@ -492,3 +492,128 @@ int oracle_polar_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax
     run_tasks(polar_dec_task, &c, (long)B * Hq, nthreads);
     return 0;
 }
+
+/* ========================================================================= */
+/* Baseline attention cores: NoPE and RoPE (the matched controls)            */
+/* ========================================================================= */
+/* The paper's matched models differ only in the attention core (Section 3.1: NoPE, RoPE
+ * or Polar).  The pages name the two controls without restating them; these are their
+ * textbook definitions (readings listed in the design notes):
+ *   - NoPE: causal softmax attention, logit q_i . k_j / sqrt(D), output sum_j w_ij v_j;
+ *   - RoPE: the same after rotating every adjacent pair (x[2p], x[2p+1]) of q_i and k_j by
+ *     the angle pos * theta^(-2p/D), pos being the token's position (rotary position
+ *     embedding of Su et al.; theta = 10000 in the usual setting). */
+
+/* Rotate one D-vector in place to position `pos`. */
+static void rope_vec(double* x, int D, double pos, double theta) {
+    for (int p = 0; 2 * p + 1 < D; ++p) {
+        const double ang = pos * pow(theta, -2.0 * p / D);
+        const double c = cos(ang), s = sin(ang);
+        const double a = x[2 * p], b = x[2 * p + 1];
+        x[2 * p] = a * c - b * s;
+        x[2 * p + 1] = a * s + b * c;
+    }
+}
+
+/* x, y [B, T, H, D]; row t of every sequence is rotated to position pos0 + t. */
+int oracle_rope(int B, int T, int H, int D, long pos0, double theta, const double* x, double* y) {
+    if (B < 1 || T < 1 || H < 1 || D < 2 || D % 2 || theta <= 0.0 || !x || !y) return -1;
+    for (long b = 0; b < B; ++b)
+        for (long t = 0; t < T; ++t)
+            for (long h = 0; h < H; ++h) {
+                const size_t off = (((size_t)b * T + t) * H + h) * D;
+                memcpy(y + off, x + off, sizeof(double) * D);
+                rope_vec(y + off, D, (double)(pos0 + t), theta);
+            }
+    return 0;
+}
+
+/* One softmax row: query qi (already rotated) against n keys (rows of K with stride ks,
+ * already rotated), values V (stride vs); o [D]. */
+static void softmax_row(const double* qi, const double* K, const double* V, size_t ks, size_t vs, long n, int D,
+                        double* o, double* w) {
+    const double scale = 1.0 / sqrt((double)D);
+    double m = -INFINITY;
+    for (long j = 0; j < n; ++j) {
+        double d = 0.0;
+        for (int e = 0; e < D; ++e) d += qi[e] * K[j * ks + e];
+        w[j] = d * scale;
+        if (w[j] > m) m = w[j];
+    }
+    double z = 0.0;
+    for (long j = 0; j < n; ++j) {
+        w[j] = exp(w[j] - m);
+        z += w[j];
+    }
+    for (int e = 0; e < D; ++e) o[e] = 0.0;
+    for (long j = 0; j < n; ++j)
+        for (int e = 0; e < D; ++e) o[e] += w[j] / z * V[j * vs + e];
+}
+
+typedef struct {
+    int B, T, Hq, Hkv, D;
+    const double *q, *k, *v;
+    double theta;
+    double* o;
+} softmax_ctx;
+
+/* task = b * Hq + h: every query row of one (batch, query head) */
+static void softmax_task(long task, void* p) {
+    const softmax_ctx* c = (const softmax_ctx*)p;
+    const int b = (int)(task / c->Hq), h = (int)(task % c->Hq), hk = h / (c->Hq / c->Hkv), D = c->D;
+    const size_t T = (size_t)c->T;
+    double* K = (double*)malloc(sizeof(double) * T * D);
+    double* w = (double*)malloc(sizeof(double) * T);
+    double* qi = (double*)malloc(sizeof(double) * D);
+    for (size_t j = 0; j < T; ++j) {
+        memcpy(K + j * D, c->k + ((b * T + j) * c->Hkv + hk) * D, sizeof(double) * D);
+        if (c->theta > 0.0) rope_vec(K + j * D, D, (double)j, c->theta);
+    }
+    const double* V = c->v + ((size_t)b * T * c->Hkv + hk) * D;
+    for (size_t i = 0; i < T; ++i) {
+        memcpy(qi, c->q + ((b * T + i) * c->Hq + h) * D, sizeof(double) * D);
+        if (c->theta > 0.0) rope_vec(qi, D, (double)i, c->theta);
+        softmax_row(qi, K, V, D, (size_t)c->Hkv * D, (long)i + 1, D, c->o + ((b * T + i) * c->Hq + h) * D, w);
+    }
+    free(K);
+    free(w);
+    free(qi);
+}
+
+/* Causal softmax attention, NoPE (theta <= 0) or RoPE (theta > 0), all rows.
+ *   q [B, T, Hq, D];  k, v [B, T, Hkv, D];  o [B, T, Hq, D]. */
+int oracle_softmax_attn(int B, int T, int Hq, int Hkv, int D, double theta, const double* q, const double* k,
+                        const double* v, double* o, int nthreads) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || Hq % Hkv || !q || !k || !v || !o) return -1;
+    softmax_ctx c = {B, T, Hq, Hkv, D, q, k, v, theta, o};
+    run_tasks(softmax_task, &c, (long)B * Hq, nthreads);
+    return 0;
+}
+
+/* Decode row of the same cores: the query at position cache_len - 1 against cache slots
+ * 0..cache_len-1, whose keys are given unrotated (position = slot).
+ *   q [B, Hq, D];  k_cache, v_cache [B, Lmax, Hkv, D];  o [B, Hq, D]. */
+int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax, double theta, const double* q,
+                          const double* kc, const double* vc, double* o) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || Hq % Hkv || cache_len < 1 || cache_len > Lmax) return -1;
+    if (!q || !kc || !vc || !o) return -1;
+    double* K = (double*)malloc(sizeof(double) * (size_t)cache_len * D);
+    double* w = (double*)malloc(sizeof(double) * (size_t)cache_len);
+    double* qi = (double*)malloc(sizeof(double) * D);
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hq; ++h) {
+            const int hk = h / (Hq / Hkv);
+            for (long j = 0; j < cache_len; ++j) {
+                memcpy(K + j * D, kc + (((size_t)b * Lmax + j) * Hkv + hk) * D, sizeof(double) * D);
+                if (theta > 0.0) rope_vec(K + j * D, D, (double)j, theta);
+            }
+            memcpy(qi, q + ((size_t)b * Hq + h) * D, sizeof(double) * D);
+            if (theta > 0.0) rope_vec(qi, D, (double)(cache_len - 1), theta);
+            softmax_row(qi, K, vc + ((size_t)b * Lmax * Hkv + hk) * D, D, (size_t)Hkv * D, cache_len, D,
+                        o + ((size_t)b * Hq + h) * D, w);
+        }
+    free(K);
+    free(w);
+    free(qi);
+    return 0;
+}

@@ -39,6 +39,13 @@ MUTANTS = {
     "polar_causal_off_by_one": ("polar_row_materialised(qi, K, V, stride, stride, i + 1,",
                                 "polar_row_materialised(qi, K, V, stride, stride, (i + 2 <= c->T ? i + 2 : i + 1),"),
     "streaming_q2_rho_linear": ("L *= rho; Q2 *= rho * rho;", "L *= rho; Q2 *= rho;"),
+    "rope_reflect": ("x[2 * p + 1] = a * s + b * c;", "x[2 * p + 1] = -a * s + b * c;"),
+    "rope_half_frequency": ("pos * pow(theta, -2.0 * p / D);", "pos * pow(theta, -1.0 * p / D);"),
+    "softmax_no_scale": ("w[j] = d * scale;", "w[j] = d;"),
+    "softmax_sees_next_key": ("(long)i + 1, D, c->o + ((b * T + i) * c->Hq + h) * D, w);",
+                              "(long)(i + 1 < T ? i + 2 : i + 1), D, c->o + ((b * T + i) * c->Hq + h) * D, w);"),
+    "softmax_decode_query_position": ("rope_vec(qi, D, (double)(cache_len - 1), theta);",
+                                      "rope_vec(qi, D, (double)cache_len, theta);"),
 }
 
 
@@ -55,6 +62,7 @@ def test_pins_catch_planted_mistake(tmp_path, name):
     env = dict(os.environ, ATMA_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_gdn.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_polar.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_polar.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_baseline.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
