@@ -223,6 +223,25 @@ def main():
 
 def secondary(torch, atma, workloads):
     res = {}
+    # the matched control cores (NoPE / RoPE causal softmax attention) beside Polar, 2K layer shape
+    w = workloads.WORKLOADS["layer_b8_t2k"]
+    p = workloads.make_workload(w, device="cuda")["polar"]
+    o_p = torch.empty_like(p["q"])
+    ws_r = torch.empty(int(atma.lib.atma_softmax_attn_workspace_bytes(w.B, w.T, w.polar_Hq, w.polar_Hkv, 64,
+                                                                       10000.0)), dtype=torch.uint8, device="cuda")
+    tpo, tno, tro = Timer(torch), Timer(torch), Timer(torch)
+    for it in range(21):
+        (tpo if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+        (tno if it else (lambda f: f()))(lambda: atma.atma_softmax_attn_fwd(p["q"], p["k"], p["v"], 0.0, o=o_p))
+        (tro if it else (lambda f: f()))(lambda: atma.atma_softmax_attn_fwd(p["q"], p["k"], p["v"], 10000.0, o=o_p,
+                                                                            workspace=ws_r))
+    torch.cuda.synchronize()
+    pf = polar_flops(w.B, w.T, w.polar_Hq)
+    res["cores_" + w.name] = {"polar_ms": round(tpo.mean_ms(), 4), "nope_ms": round(tno.mean_ms(), 4),
+                              "rope_ms": round(tro.mean_ms(), 4),
+                              "nope_mfma_frac": round(pf / (tno.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del p, o_p, ws_r
+    torch.cuda.empty_cache()
     # 64K prefill
     w = workloads.WORKLOADS["prefill_b1_t64k"]
     inp = workloads.make_workload(w, device="cuda")

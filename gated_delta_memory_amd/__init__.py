@@ -55,6 +55,10 @@ def _load() -> ctypes.CDLL:
         "atma_polar_attn_decode": ([vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_polar_attn_decode_workspace_bytes": ([i] * 4, sz),
         "atma_polar_attn_decode_varlen": ([vp, vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
+        "atma_rope": ([vp, vp] + [i] * 5 + [f, i, vp], i),
+        "atma_softmax_attn_fwd": ([vp] * 4 + [i] * 5 + [f, i, vp, sz, vp], i),
+        "atma_softmax_attn_workspace_bytes": ([i] * 5 + [f], sz),
+        "atma_softmax_attn_decode": ([vp] * 3 + [i, i, f, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_status_string": ([i], ctypes.c_char_p),
         "atma_version": ([], i),
     }
@@ -309,6 +313,55 @@ def atma_polar_attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len
                                            workspace.numel() * workspace.element_size(), _stream(stream))
     _check("atma_polar_attn_decode_varlen", st)
     return o, mu_out
+
+
+def atma_rope(x, theta=10000.0, pos0=0, *, out=None, stream=None):
+    """Rotary embedding of x [B,T,H,D] bf16 (row t at position pos0 + t).  Returns the rotated copy."""
+    B, T, H, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(x, out)
+    st = lib.atma_rope(_ptr(x), _ptr(out), B, T, H, D, int(pos0), float(theta), _dtype_code(x), _stream(stream))
+    _check("atma_rope", st)
+    return out
+
+
+def atma_softmax_attn_fwd(q, k, v, rope_theta=0.0, *, o=None, workspace=None, stream=None):
+    """NoPE (rope_theta=0) or RoPE causal softmax attention.  q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    if o is None:
+        o = torch.empty_like(q)
+    need = int(lib.atma_softmax_attn_workspace_bytes(B, T, Hq, Hkv, D, float(rope_theta)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, o, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.atma_softmax_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, Hq, Hkv, D, float(rope_theta),
+                                   _dtype_code(q), _ptr(workspace), wsb, _stream(stream))
+    _check("atma_softmax_attn_fwd", st)
+    return o
+
+
+def atma_softmax_attn_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0, *, o=None, workspace=None, stream=None):
+    """Decode row of the NoPE / RoPE core; for RoPE the cache holds rotated keys (atma_rope)."""
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Lmax, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("inconsistent cache shapes")
+    if o is None:
+        o = torch.empty_like(q)
+    need = atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k_cache, v_cache, o, workspace)
+    st = lib.atma_softmax_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len), Lmax, float(rope_theta),
+                                      _ptr(o), B, Hq, Hkv, D, _dtype_code(q), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("atma_softmax_attn_decode", st)
+    return o
 
 
 def atma_polar_attn_workspace_bytes(B, T, Hq, D=64) -> int:

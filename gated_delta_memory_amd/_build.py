@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libatma.so")
 
-SOURCES = ["atma_api.cpp", "gdn_fwd.hip", "gdn_fwd_bf16.hip", "gdn_decode.hip", "polar_fwd.hip", "polar_decode.hip"]
+SOURCES = ["atma_api.cpp", "gdn_fwd.hip", "gdn_fwd_bf16.hip", "gdn_decode.hip", "polar_fwd.hip", "polar_decode.hip",
+           "rope.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are switched off for all device code.

@@ -184,4 +184,63 @@ int atma_polar_attn_decode_varlen(const void* q, const void* k_cache, const void
     return launched(atma::launch_polar_decode(a, (hipStream_t)stream));
 }
 
+int atma_rope(const void* x, void* y, int B, int T, int H, int D, int pos0, float theta, atma_dtype dt,
+              void* stream) {
+    if (!x || !y) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(T) || !pos(H) || !pos(D) || pos0 < 0 || !(theta > 0.0f)) return ATMA_ERR_SHAPE;
+    if (D % 2 != 0 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, D) || (int64_t)pos0 + T > 0x7fffffffLL) return ATMA_ERR_SHAPE;
+    atma::RopeArgs a{x, y, B, T, H, D, pos0, (double)theta};
+    return launched(atma::launch_rope(a, (hipStream_t)stream));
+}
+
+size_t atma_softmax_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, float rope_theta) {
+    if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D) || !fits(B, T, Hq + Hkv, D)) return 0;
+    return rope_theta > 0.0f ? (size_t)B * T * (Hq + Hkv) * D * 2 : 0;
+}
+
+int atma_softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T, int Hq, int Hkv, int D,
+                          float rope_theta, atma_dtype dt, void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !o) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D) || !(rope_theta >= 0.0f)) return ATMA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if (D != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, Hq + Hkv, D) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    const size_t need = atma_softmax_attn_workspace_bytes(B, T, Hq, Hkv, D, rope_theta);
+    if (need && (!workspace || ws_bytes < need)) return ATMA_ERR_WORKSPACE;
+    const hipStream_t st = (hipStream_t)stream;
+    if (rope_theta > 0.0f) {  // rotated copies of q and k in the workspace
+        char* qr = (char*)workspace;
+        char* kr = qr + (size_t)B * T * Hq * D * 2;
+        atma::RopeArgs rq{q, qr, B, T, Hq, D, 0, (double)rope_theta}, rk{k, kr, B, T, Hkv, D, 0, (double)rope_theta};
+        const int s1 = launched(atma::launch_rope(rq, st));
+        if (s1 != ATMA_OK) return s1;
+        const int s2 = launched(atma::launch_rope(rk, st));
+        if (s2 != ATMA_OK) return s2;
+        q = qr;
+        k = kr;
+    }
+    atma::PolarFwdArgs a{q, k, v, atma::PolarParamsDev{}, o, nullptr, nullptr, B, T, Hq, Hkv, D};
+    a.softmax = true;
+    return launched(atma::launch_polar_fwd(a, st));
+}
+
+int atma_softmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, int cache_len, int Lmax,
+                             float rope_theta, void* o, int B, int Hq, int Hkv, int D, atma_dtype dt,
+                             void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !o) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(Hq) || !pos(Hkv) || !pos(D) || !pos(cache_len) || !pos(Lmax) || !(rope_theta >= 0.0f))
+        return ATMA_ERR_SHAPE;
+    if (cache_len > Lmax || Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if (D != 64 || dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv)) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(Lmax, Hkv, D, 1) || !fits(B, Hq, D, 1) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    const size_t need = atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);
+    if (!workspace || ws_bytes < need) return ATMA_ERR_WORKSPACE;
+    atma::PolarDecodeArgs a{q, k_cache, v_cache, atma::PolarParamsDev{}, o, nullptr, cache_len, Lmax, B, Hq, Hkv, D,
+                            workspace};
+    a.softmax = true;
+    a.rope_theta = rope_theta;
+    return launched(atma::launch_polar_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -48,8 +48,20 @@ struct PolarFwdArgs {
     // packed batch: B sequences with row offsets cu[0..B] (device), T = the longest, total rows
     const int* cu = nullptr;
     int total = 0;
+    // plain causal softmax attention (the NoPE / RoPE control core): no temperature, no null,
+    // output sum_j w_j v_j; p, mu_out and meff_out unused
+    bool softmax = false;
 };
 hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream);
+
+// Rotary embedding of x [B, T, H, D] (bf16) into y: row t at position pos0 + t.
+struct RopeArgs {
+    const void* x;
+    void* y;
+    int B, T, H, D, pos0;
+    double theta;
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 struct PolarDecodeArgs {
     const void *q, *k_cache, *v_cache;
@@ -61,6 +73,10 @@ struct PolarDecodeArgs {
     // per-sequence cache lengths on the device (NULL: every sequence has cache_len); with them,
     // cache_len is the upper bound that sizes the split grid
     const int* lens = nullptr;
+    // decode row of the NoPE / RoPE control core (p and mu_out unused); rope_theta > 0 rotates
+    // the query to position cache_len - 1 (cached keys already rotated)
+    bool softmax = false;
+    double rope_theta = 0.0;
 };
 size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
 // Head layouts the decode kernels have code for: Hkv in {1,2,4,8,16,32}, Hq/Hkv in {1,2,4,8}.

@@ -19,6 +19,9 @@
 // Heterogeneous batches pass one cache length per sequence (device array): the split grid is
 // sized by the longest, and each sequence cuts its own length into the same number of ranges.
 // A length outside [1, bound] is an error the host cannot see; that sequence's outputs are NaN.
+// With SOFTMAX set the kernels are the decode row of the NoPE / RoPE control cores: logits
+// q.k / sqrt(D), no temperature, no null, output Sv / L; for RoPE the query is rotated to
+// position cache_len - 1 (angle in fp64) and the cached keys are expected already rotated.
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -48,11 +51,11 @@ __device__ __forceinline__ void unpack8(const u32x4& r, float* f) {
 }
 
 // grid (nsplit, B); block 256.  Thread = (token slot, kv head, 8-wide dim chunk).
-template <int GQ>
+template <int GQ, bool SOFTMAX>
 __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                                                            const bf16* __restrict__ vc, PolarParamsDev prm,
                                                            float* __restrict__ ws, int max_len, int Lmax,
-                                                           int Hkv, const int* __restrict__ lens) {
+                                                           int Hkv, const int* __restrict__ lens, double log2_theta) {
     const int split = blockIdx.x, nsplit = gridDim.x, b = blockIdx.y;
     const int Hq = Hkv * GQ;
     const int tpt = Hkv * 8;                 // threads per token
@@ -65,14 +68,33 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     const int t_end = (int)((long)cache_len * (split + 1) / nsplit);
 
     const float lnn = logf((float)cache_len);
+    // RoPE (control core): the rotation of this thread's four pairs at position cache_len - 1
+    float rc[4] = {1.f, 1.f, 1.f, 1.f}, rs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (SOFTMAX && log2_theta > 0.0) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int p = chunk * 4 + x;
+            double ang = (double)(cache_len - 1) * exp2(-2.0 * p / D * log2_theta);
+            ang -= 6.283185307179586 * floor(ang * 0.15915494309189535);
+            sincosf((float)ang, &rs[x], &rc[x]);
+        }
+    }
     float qv[GQ][8], cq[GQ], m[GQ], L[GQ], Q2[GQ], sv[GQ][8];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
         const int h = hk * GQ + g;
-        const float t = 1.0f + softplus(prm.temp_raw[h]) * lnn;
+        const float t = SOFTMAX ? 1.0f : 1.0f + softplus(prm.temp_raw[h]) * lnn;
         cq[g] = t * kLog2e * 0.125f;
         const u32x4 r = *(const u32x4*)(q + ((size_t)b * Hq + h) * D + chunk * 8);
         unpack8(r, qv[g]);
+        if (SOFTMAX) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float a0 = qv[g][2 * x], a1 = qv[g][2 * x + 1];
+                qv[g][2 * x] = a0 * rc[x] - a1 * rs[x];
+                qv[g][2 * x + 1] = a0 * rs[x] + a1 * rc[x];
+            }
+        }
         m[g] = -INFINITY; L[g] = 0.f; Q2[g] = 0.f;
 #pragma unroll
         for (int x = 0; x < 8; ++x) sv[g][x] = 0.f;
@@ -178,6 +200,7 @@ __device__ __forceinline__ float wave_max(float x) {
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
     return x;
 }
+template <bool SOFTMAX>
 __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
                                                             bf16* __restrict__ o, float* __restrict__ mu_out,
                                                             int nsplit, int max_len, const int* __restrict__ lens) {
@@ -231,6 +254,10 @@ __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restr
         Q2 += e * e * part[j][2];
         Sv += e * psv[j][d];
     }
+    if constexpr (SOFTMAX) {  // control core: o = Sv / L
+        o[((size_t)b * Hq + h) * D + d] = (bf16)(Sv / L);
+        return;
+    }
     const float n = (float)cache_len;
     const float t = 1.0f + softplus(prm.temp_raw[h]) * logf(n);
     const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf(n + 1.0f));
@@ -262,16 +289,24 @@ hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
     const int nsplit = num_splits(a.B, a.cache_len);
     const int gq = a.Hq / a.Hkv;
     float* ws = (float*)a.workspace;
-#define ATMA_PD_CASE(G)                                                                                    \
-    if (gq == G) {                                                                                         \
-        hipLaunchKernelGGL(polar_decode_partial<G>, dim3(nsplit, a.B), dim3(NT), 0, stream, (const bf16*)a.q, \
-                           (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.p, ws, a.cache_len, a.Lmax,   \
-                           a.Hkv, a.lens);                                                                 \
+    const double l2t = a.rope_theta > 0.0 ? log2(a.rope_theta) : 0.0;
+#define ATMA_PD_CASE(G, S)                                                                                 \
+    if (gq == G && a.softmax == S) {                                                                       \
+        hipLaunchKernelGGL((polar_decode_partial<G, S>), dim3(nsplit, a.B), dim3(NT), 0, stream,           \
+                           (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.p, ws,      \
+                           a.cache_len, a.Lmax, a.Hkv, a.lens, l2t);                                       \
     } else
-    ATMA_PD_CASE(1) ATMA_PD_CASE(2) ATMA_PD_CASE(4) ATMA_PD_CASE(8) { return hipErrorInvalidValue; }
+    ATMA_PD_CASE(1, false) ATMA_PD_CASE(2, false) ATMA_PD_CASE(4, false) ATMA_PD_CASE(8, false)
+    ATMA_PD_CASE(1, true) ATMA_PD_CASE(2, true) ATMA_PD_CASE(4, true) ATMA_PD_CASE(8, true) {
+        return hipErrorInvalidValue;
+    }
 #undef ATMA_PD_CASE
-    hipLaunchKernelGGL(polar_decode_combine, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
-                       (bf16*)a.o, a.mu_out, nsplit, a.cache_len, a.lens);
+    if (a.softmax)
+        hipLaunchKernelGGL(polar_decode_combine<true>, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
+                           (bf16*)a.o, nullptr, nsplit, a.cache_len, a.lens);
+    else
+        hipLaunchKernelGGL(polar_decode_combine<false>, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
+                           (bf16*)a.o, a.mu_out, nsplit, a.cache_len, a.lens);
     return hipGetLastError();
 }
 

@@ -36,6 +36,9 @@
 // sequence's bounds, skipping tiles past its end.  Offsets that are not a valid partition of
 // the packed rows (or a sequence longer than the declared maximum) skip that sequence, so a
 // malformed offset array can never address memory outside the buffers.
+// With POLAR false the same kernel is the plain causal softmax attention of the NoPE / RoPE
+// control cores (ATMA paper, Section 3.1): logits q.k / sqrt(D) (no temperature), no null,
+// output sum_j w_j v_j = Sv / L (no direction / magnitude channels).
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -86,6 +89,7 @@ __device__ __forceinline__ bf16x4 tr_read(const char* lds_base, int byte_off) {
 __shared__ __align__(16) char g_kv0[2 * BK * D * 2];
 __shared__ __align__(16) char g_kv1[2 * BK * D * 2];
 
+template <bool POLAR>
 __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     const size_t mu_base = cu ? (size_t)h * total + seq0 : ((size_t)b * Hq + h) * Tmax;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());  // wave-uniform
     const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
-    const float a_t = softplus(prm.temp_raw[h]);
+    const float a_t = POLAR ? softplus(prm.temp_raw[h]) : 0.0f;
     const size_t qstride = (size_t)Hq * D;
     const size_t kvstride = (size_t)Hkv * D;
     const unsigned rowbytes = (unsigned)(kvstride * 2);
@@ -169,7 +173,8 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     const int q0 = qt * BQ;
     const int qw0 = q0 + w * QW;
     const int qi = qw0 + l32;  // this lane's query
-    const float cq = (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * 0.125f;  // t_i log2(e) / sqrt(64)
+    const float cq = POLAR ? (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * 0.125f  // t_i log2(e) / sqrt(64)
+                           : kLog2e * 0.125f;
 
     // Q^T fragments (B operand): lane supplies Q[qi][16 ks + 8 G2 + e]
     bf16x8 qf[4];
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
                     const float p1 = fast_exp2(fmaf(s[kt][8 * st + e + 1], cq, -m_used));
                     const bf16x2 pp = {(bf16)p0, (bf16)p1};
                     ls = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(bf16)1.0f, (bf16)1.0f}, ls, false);
-                    qs = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, qs, false);
+                    if constexpr (POLAR) qs = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, qs, false);
                     pf[e] = pp[0];
                     pf[e + 1] = pp[1];
                 }
@@ -278,6 +283,22 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
 
     // ---- finalise: null merge, channels, output ------------------------------------------------
     const float L = pair_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+    if constexpr (!POLAR) {  // plain softmax: o = Sv / L
+        const float invL = 1.0f / L;
+        if (qi < T) {
+            bf16* orow = o + (seq0 + qi) * qstride + (size_t)h * D;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    bf16x4 y;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) y[x] = (bf16)(oacc[dt][4 * g + x] * invL);
+                    *(bf16x4*)(orow + 32 * dt + 8 * g + 4 * G2) = y;
+                }
+        }
+        return;
+    }
     const float Q2 = pair_sum((q2sum[0] + q2sum[1]) + (q2sum[2] + q2sum[3]));
     const float n = (float)(qi + 1);
     const float t = 1.0f + a_t * logf(n);
@@ -341,9 +362,14 @@ hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
     // pair tiles when there are at most about two rounds of workgroups (4 per CU on 256 CUs)
     const int paired = ntiles <= 2048 * 2 ? 1 : 0;
     const int per_bh = paired ? (nqt + 1) / 2 : nqt;
-    hipLaunchKernelGGL(polar_fwd_kernel, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
-                       a.Hkv, paired, a.cu, a.total);
+    if (a.softmax)
+        hipLaunchKernelGGL(polar_fwd_kernel<false>, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
+                           (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, nullptr, nullptr, a.T, a.Hq,
+                           a.Hkv, paired, a.cu, a.total);
+    else
+        hipLaunchKernelGGL(polar_fwd_kernel<true>, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
+                           (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
+                           a.Hkv, paired, a.cu, a.total);
     return hipGetLastError();
 }
 

@@ -198,6 +198,38 @@ int atma_polar_attn_decode_varlen(const void* q, const void* k_cache, const void
                                   int Hkv, int D, atma_dtype dt, void* workspace, size_t ws_bytes,
                                   void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Control cores: the NoPE and RoPE attention the ATMA paper matches Polar against
+ * (Section 3.1: only the attention core changes among NoPE, RoPE and Polar).  Causal
+ * softmax attention with logits q_i . k_j / sqrt(D) and output o_i = sum_j w_ij v_j (no
+ * temperature, no null, no channels); for RoPE every adjacent pair (x[2p], x[2p+1]) of q and
+ * k at position m is first turned by the angle m * theta^(-2p/D) (rotary position embedding,
+ * theta = 10000 in the usual setting).  Same prefill and decode kernels as Polar.
+ * ------------------------------------------------------------------------------- */
+
+/* Rotary embedding: y = x with row t of every sequence turned to position pos0 + t.
+ *   x, y [B, T, H, D] bf16 (y may alias x), D even, theta > 0, pos0 >= 0.
+ *   The angle is formed in fp64.  Use it to fill a RoPE KV cache with rotated keys. */
+int atma_rope(const void* x, void* y, int B, int T, int H, int D, int pos0, float theta, atma_dtype dt,
+              void* stream);
+
+/* Prefill: q [B, T, Hq, D], k, v [B, T, Hkv, D], o [B, T, Hq, D]; D == 64, bf16.
+ *   rope_theta == 0: NoPE;  rope_theta > 0: RoPE with that base (positions 0..T-1).
+ *   workspace: atma_softmax_attn_workspace_bytes(...) bytes (the rotated q and k; 0 for NoPE). */
+int atma_softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T, int Hq,
+                          int Hkv, int D, float rope_theta, atma_dtype dt, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+size_t atma_softmax_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, float rope_theta);
+
+/* Decode: the query (position cache_len - 1) against cache slots 0..cache_len-1.  For RoPE
+ *   (rope_theta > 0) the cache holds keys already rotated to their slot positions (atma_rope);
+ *   the query is rotated inside.  Shapes, head layouts and workspace as for
+ *   atma_polar_attn_decode (atma_polar_attn_decode_workspace_bytes). */
+int atma_softmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, int cache_len,
+                             int Lmax, float rope_theta, void* o, int B, int Hq, int Hkv, int D,
+                             atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* atma_status_string(int status);
 

@@ -72,9 +72,9 @@ def _declare(lib):
     )
     lib.oracle_polar_decode.argtypes = [i, i, i, i, l, l] + [_dp] * 3 + [_dp] * 5 + [d] + [_dp] * 4 + [i]
     lib.oracle_threads_used.argtypes = [i, l]
-    lib.oracle_rope.argtypes = [i, i, i, i, l, d, _dp, _dp]
-    lib.oracle_softmax_attn.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _dp, i]
-    lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, _dp, _dp, _dp, _dp]
+    lib.oracle_rope.argtypes = [i, i, i, i, l, d, i, _dp, _dp]
+    lib.oracle_softmax_attn.argtypes = [i, i, i, i, i, d, i, _dp, _dp, _dp, _dp, i]
+    lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, i, _dp, _dp, _dp, _dp]
     for f in ("oracle_gdn_sequential", "oracle_gdn_chunked", "oracle_polar_fwd", "oracle_polar_decode",
               "oracle_threads_used", "oracle_rope", "oracle_softmax_attn", "oracle_softmax_decode"):
         getattr(lib, f).restype = ctypes.c_int
@@ -198,34 +198,36 @@ def polar_decode(q, k_cache, v_cache, cache_len, params, threads=0):
     return {"o": o, "mu": mu, "meff": meff, "neff": neff}
 
 
-def rope(x, theta=10000.0, pos0=0):
-    """x [B,T,H,D]; row t rotated to position pos0 + t (adjacent pairs).  Returns fp64."""
+def rope(x, theta=10000.0, pos0=0, bf16=False):
+    """x [B,T,H,D]; row t rotated to position pos0 + t (adjacent pairs), rounded to bf16 values
+    when ``bf16``.  Returns fp64."""
     x = _f64(x)
     B, T, H, D = x.shape
     y = np.empty_like(x)
-    assert _load().oracle_rope(B, T, H, D, int(pos0), float(theta), _ptr(x), _ptr(y)) == 0
+    assert _load().oracle_rope(B, T, H, D, int(pos0), float(theta), int(bf16), _ptr(x), _ptr(y)) == 0
     return y
 
 
-def softmax_attn(q, k, v, rope_theta=0.0, threads=0):
-    """Causal softmax attention (NoPE; RoPE when rope_theta > 0).  q [B,T,Hq,D], k/v
-    [B,T,Hkv,D].  Returns o [B,T,Hq,D]."""
+def softmax_attn(q, k, v, rope_theta=0.0, rotated_bf16=False, threads=0):
+    """Causal softmax attention (NoPE; RoPE when rope_theta > 0, the rotated q and k rounded
+    to bf16 values when ``rotated_bf16``).  q [B,T,Hq,D], k/v [B,T,Hkv,D].  Returns o [B,T,Hq,D]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     assert k.shape == (B, T, Hkv, D) and v.shape == (B, T, Hkv, D)
     o = np.zeros((B, T, Hq, D))
-    assert _load().oracle_softmax_attn(B, T, Hq, Hkv, D, float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                       int(threads)) == 0
+    assert _load().oracle_softmax_attn(B, T, Hq, Hkv, D, float(rope_theta), int(rotated_bf16), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(o), int(threads)) == 0
     return o
 
 
-def softmax_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0):
-    """q [B,Hq,D], caches [B,Lmax,Hkv,D] with unrotated keys.  Returns o [B,Hq,D]."""
+def softmax_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0, rotated_keys_bf16=False):
+    """q [B,Hq,D], caches [B,Lmax,Hkv,D] with unrotated keys (their rotation rounded to bf16
+    values when ``rotated_keys_bf16``).  Returns o [B,Hq,D]."""
     q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
     B, Hq, D = q.shape
     Lmax, Hkv = kc.shape[1], kc.shape[2]
     o = np.zeros((B, Hq, D))
-    assert _load().oracle_softmax_decode(B, Hq, Hkv, D, int(cache_len), Lmax, float(rope_theta), _ptr(q), _ptr(kc),
-                                         _ptr(vc), _ptr(o)) == 0
+    assert _load().oracle_softmax_decode(B, Hq, Hkv, D, int(cache_len), Lmax, float(rope_theta),
+                                         int(rotated_keys_bf16), _ptr(q), _ptr(kc), _ptr(vc), _ptr(o)) == 0
     return o

@@ -504,6 +504,19 @@ int oracle_polar_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax
  *     the angle pos * theta^(-2p/D), pos being the token's position (rotary position
  *     embedding of Su et al.; theta = 10000 in the usual setting). */
 
+/* Round to the nearest bf16 value (ties to even), through fp32 as a bf16 pipeline rounds:
+ * RoPE's rotated q and k are bf16 operands in any bf16 attention (and bf16 in a RoPE KV cache),
+ * so the control core is defined on the rounded rotation when `quant` is set. */
+static double round_bf16(double x) {
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    u &= 0xFFFF0000u;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
 /* Rotate one D-vector in place to position `pos`. */
 static void rope_vec(double* x, int D, double pos, double theta) {
     for (int p = 0; 2 * p + 1 < D; ++p) {
@@ -515,8 +528,9 @@ static void rope_vec(double* x, int D, double pos, double theta) {
     }
 }
 
-/* x, y [B, T, H, D]; row t of every sequence is rotated to position pos0 + t. */
-int oracle_rope(int B, int T, int H, int D, long pos0, double theta, const double* x, double* y) {
+/* x, y [B, T, H, D]; row t of every sequence is rotated to position pos0 + t (then rounded
+ * to bf16 when quant is set). */
+int oracle_rope(int B, int T, int H, int D, long pos0, double theta, int quant, const double* x, double* y) {
     if (B < 1 || T < 1 || H < 1 || D < 2 || D % 2 || theta <= 0.0 || !x || !y) return -1;
     for (long b = 0; b < B; ++b)
         for (long t = 0; t < T; ++t)
@@ -524,6 +538,7 @@ int oracle_rope(int B, int T, int H, int D, long pos0, double theta, const doubl
                 const size_t off = (((size_t)b * T + t) * H + h) * D;
                 memcpy(y + off, x + off, sizeof(double) * D);
                 rope_vec(y + off, D, (double)(pos0 + t), theta);
+                for (int e = 0; quant && e < D; ++e) y[off + e] = round_bf16(y[off + e]);
             }
     return 0;
 }
@@ -554,6 +569,7 @@ typedef struct {
     int B, T, Hq, Hkv, D;
     const double *q, *k, *v;
     double theta;
+    int quant;
     double* o;
 } softmax_ctx;
 
@@ -568,11 +584,13 @@ static void softmax_task(long task, void* p) {
     for (size_t j = 0; j < T; ++j) {
         memcpy(K + j * D, c->k + ((b * T + j) * c->Hkv + hk) * D, sizeof(double) * D);
         if (c->theta > 0.0) rope_vec(K + j * D, D, (double)j, c->theta);
+        for (int e = 0; c->theta > 0.0 && c->quant && e < D; ++e) K[j * D + e] = round_bf16(K[j * D + e]);
     }
     const double* V = c->v + ((size_t)b * T * c->Hkv + hk) * D;
     for (size_t i = 0; i < T; ++i) {
         memcpy(qi, c->q + ((b * T + i) * c->Hq + h) * D, sizeof(double) * D);
         if (c->theta > 0.0) rope_vec(qi, D, (double)i, c->theta);
+        for (int e = 0; c->theta > 0.0 && c->quant && e < D; ++e) qi[e] = round_bf16(qi[e]);
         softmax_row(qi, K, V, D, (size_t)c->Hkv * D, (long)i + 1, D, c->o + ((b * T + i) * c->Hq + h) * D, w);
     }
     free(K);
@@ -580,21 +598,23 @@ static void softmax_task(long task, void* p) {
     free(qi);
 }
 
-/* Causal softmax attention, NoPE (theta <= 0) or RoPE (theta > 0), all rows.
+/* Causal softmax attention, NoPE (theta <= 0) or RoPE (theta > 0), all rows; with quant the
+ * rotated q and k are rounded to bf16 before the scores.
  *   q [B, T, Hq, D];  k, v [B, T, Hkv, D];  o [B, T, Hq, D]. */
-int oracle_softmax_attn(int B, int T, int Hq, int Hkv, int D, double theta, const double* q, const double* k,
-                        const double* v, double* o, int nthreads) {
+int oracle_softmax_attn(int B, int T, int Hq, int Hkv, int D, double theta, int quant, const double* q,
+                        const double* k, const double* v, double* o, int nthreads) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || Hq % Hkv || !q || !k || !v || !o) return -1;
-    softmax_ctx c = {B, T, Hq, Hkv, D, q, k, v, theta, o};
+    softmax_ctx c = {B, T, Hq, Hkv, D, q, k, v, theta, quant, o};
     run_tasks(softmax_task, &c, (long)B * Hq, nthreads);
     return 0;
 }
 
 /* Decode row of the same cores: the query at position cache_len - 1 against cache slots
- * 0..cache_len-1, whose keys are given unrotated (position = slot).
+ * 0..cache_len-1, whose keys are given unrotated (position = slot); with quant the rotated
+ * keys are rounded to bf16 (a RoPE KV cache holds them in bf16), the query is not.
  *   q [B, Hq, D];  k_cache, v_cache [B, Lmax, Hkv, D];  o [B, Hq, D]. */
-int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax, double theta, const double* q,
-                          const double* kc, const double* vc, double* o) {
+int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax, double theta, int quant,
+                          const double* q, const double* kc, const double* vc, double* o) {
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || Hq % Hkv || cache_len < 1 || cache_len > Lmax) return -1;
     if (!q || !kc || !vc || !o) return -1;
     double* K = (double*)malloc(sizeof(double) * (size_t)cache_len * D);
@@ -606,6 +626,7 @@ int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lm
             for (long j = 0; j < cache_len; ++j) {
                 memcpy(K + j * D, kc + (((size_t)b * Lmax + j) * Hkv + hk) * D, sizeof(double) * D);
                 if (theta > 0.0) rope_vec(K + j * D, D, (double)j, theta);
+                for (int e = 0; theta > 0.0 && quant && e < D; ++e) K[j * D + e] = round_bf16(K[j * D + e]);
             }
             memcpy(qi, q + ((size_t)b * Hq + h) * D, sizeof(double) * D);
             if (theta > 0.0) rope_vec(qi, D, (double)(cache_len - 1), theta);

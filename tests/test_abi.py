@@ -183,6 +183,25 @@ def test_polar_fwd_varlen_validation():
     assert _pfwdv(p=_params(v_null=0)) == g.ATMA_ERR_NULL
 
 
+def test_control_core_validation():
+    L = g.lib
+    assert L.atma_rope(NULL, FAKE, 1, 8, 1, 64, 0, 10000.0, g.ATMA_BF16, NULL) == g.ATMA_ERR_NULL
+    assert L.atma_rope(FAKE, FAKE, 1, 8, 1, 63, 0, 10000.0, g.ATMA_BF16, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert L.atma_rope(FAKE, FAKE, 1, 8, 1, 64, 0, 0.0, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE
+    assert L.atma_rope(FAKE, FAKE, 1, 8, 1, 64, -1, 10000.0, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE
+    f = L.atma_softmax_attn_fwd
+    assert f(FAKE, FAKE, NULL, FAKE, 1, 8, 4, 2, 64, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 3, 64, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 128, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 64, -1.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 64, 10000.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_WORKSPACE
+    assert L.atma_softmax_attn_workspace_bytes(1, 8, 4, 2, 64, 0.0) == 0
+    assert L.atma_softmax_attn_workspace_bytes(1, 8, 4, 2, 64, 10000.0) == 8 * 6 * 64 * 2
+    d = L.atma_softmax_attn_decode
+    assert d(FAKE, FAKE, FAKE, 9, 8, 0.0, FAKE, 1, 16, 16, 64, g.ATMA_BF16, FAKE, 1 << 30, NULL) == g.ATMA_ERR_SHAPE
+    assert d(FAKE, FAKE, FAKE, 8, 8, 0.0, FAKE, 1, 16, 16, 64, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_WORKSPACE
+
+
 def test_binding_rejects_host_tensors():
     import torch
 

@@ -109,3 +109,16 @@ def test_identical_keys_give_mean_of_values():
     o = oracle.softmax_attn(q, k, v)
     for i in range(T):
         assert np.allclose(o[0, i, 0], v[0, :i + 1, 0].mean(axis=0), atol=1e-13)
+
+
+def test_rotated_bf16_rounding_matches_torch():
+    """The bf16 rounding of the rotation equals torch's fp64 -> bf16 conversion, and the core
+    with rounded rotations is the NoPE core on those rounded values."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((2, 40, 3, 16)) * 3.0
+    ref = torch.from_numpy(oracle.rope(x, 10000.0, pos0=77)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.rope(x, 10000.0, pos0=77, bf16=True), ref)
+    q, k, v = x[:, :, :2], x[:, :, 2:], rng.standard_normal((2, 40, 1, 16))
+    o = oracle.softmax_attn(q, k, v, rope_theta=10000.0, rotated_bf16=True)
+    o2 = oracle.softmax_attn(oracle.rope(q, bf16=True), oracle.rope(k, bf16=True), v)
+    assert np.abs(o - o2).max() < 1e-13
