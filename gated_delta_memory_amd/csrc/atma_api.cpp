@@ -121,7 +121,7 @@ int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_
     if (pc != ATMA_OK) return pc;
     if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D)) return ATMA_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATMA_ERR_SHAPE;
-    if (D != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if ((D != 64 && D != 128) || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
     if (!fits(B, T, Hq, D) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
     atma::PolarFwdArgs a{q, k, v, dev_params(p), o, mu_out, meff_out, B, T, Hq, Hkv, D};
     return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
@@ -135,7 +135,7 @@ int atma_polar_attn_fwd_varlen(const void* q, const void* k, const void* v, cons
     if (pc != ATMA_OK) return pc;
     if (!pos(nseq) || !pos(max_seqlen) || !pos(total_T) || !pos(Hq) || !pos(Hkv) || !pos(D)) return ATMA_ERR_SHAPE;
     if (Hq % Hkv != 0 || max_seqlen > total_T) return ATMA_ERR_SHAPE;
-    if (D != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if ((D != 64 && D != 128) || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
     if (!fits(1, total_T, Hq, D) || !fits(nseq, max_seqlen, 1, 1) || Hq > 65535 || nseq > 65535)
         return ATMA_ERR_SHAPE;
     atma::PolarFwdArgs a{q, k, v, dev_params(p), o, mu_out, meff_out, nseq, max_seqlen, Hq, Hkv, D, cu_seqlens,
@@ -144,7 +144,7 @@ int atma_polar_attn_fwd_varlen(const void* q, const void* k, const void* v, cons
 }
 
 size_t atma_polar_attn_decode_workspace_bytes(int B, int Hq, int cache_len, int D) {
-    if (!pos(B) || !pos(Hq) || !pos(cache_len) || D != 64) return 0;
+    if (!pos(B) || !pos(Hq) || !pos(cache_len) || (D != 64 && D != 128)) return 0;
     return atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);
 }
 
@@ -156,7 +156,7 @@ int atma_polar_attn_decode(const void* q, const void* k_cache, const void* v_cac
     if (pc != ATMA_OK) return pc;
     if (!pos(B) || !pos(Hq) || !pos(Hkv) || !pos(D) || !pos(cache_len) || !pos(Lmax)) return ATMA_ERR_SHAPE;
     if (cache_len > Lmax || Hq % Hkv != 0) return ATMA_ERR_SHAPE;
-    if (D != 64 || dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv)) return ATMA_ERR_UNSUPPORTED;
+    if (dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv, D)) return ATMA_ERR_UNSUPPORTED;
     // the cache may exceed 2^31 elements in total (offsets are 64-bit); one sequence may not
     if (!fits(Lmax, Hkv, D, 1) || !fits(B, Hq, D, 1) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
     const size_t need = atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);
@@ -175,7 +175,7 @@ int atma_polar_attn_decode_varlen(const void* q, const void* k_cache, const void
     if (pc != ATMA_OK) return pc;
     if (!pos(B) || !pos(Hq) || !pos(Hkv) || !pos(D) || !pos(max_cache_len) || !pos(Lmax)) return ATMA_ERR_SHAPE;
     if (max_cache_len > Lmax || Hq % Hkv != 0) return ATMA_ERR_SHAPE;
-    if (D != 64 || dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv)) return ATMA_ERR_UNSUPPORTED;
+    if (dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv, D)) return ATMA_ERR_UNSUPPORTED;
     if (!fits(Lmax, Hkv, D, 1) || !fits(B, Hq, D, 1) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
     const size_t need = atma::polar_decode_workspace_bytes(B, Hq, max_cache_len, D);
     if (!workspace || ws_bytes < need) return ATMA_ERR_WORKSPACE;
@@ -204,7 +204,7 @@ int atma_softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, 
     if (!q || !k || !v || !o) return ATMA_ERR_NULL;
     if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D) || !(rope_theta >= 0.0f)) return ATMA_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATMA_ERR_SHAPE;
-    if (D != 64 || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if ((D != 64 && D != 128) || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
     if (!fits(B, T, Hq + Hkv, D) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
     const size_t need = atma_softmax_attn_workspace_bytes(B, T, Hq, Hkv, D, rope_theta);
     if (need && (!workspace || ws_bytes < need)) return ATMA_ERR_WORKSPACE;
@@ -232,7 +232,7 @@ int atma_softmax_attn_decode(const void* q, const void* k_cache, const void* v_c
     if (!pos(B) || !pos(Hq) || !pos(Hkv) || !pos(D) || !pos(cache_len) || !pos(Lmax) || !(rope_theta >= 0.0f))
         return ATMA_ERR_SHAPE;
     if (cache_len > Lmax || Hq % Hkv != 0) return ATMA_ERR_SHAPE;
-    if (D != 64 || dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv)) return ATMA_ERR_UNSUPPORTED;
+    if (dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv, D)) return ATMA_ERR_UNSUPPORTED;
     if (!fits(Lmax, Hkv, D, 1) || !fits(B, Hq, D, 1) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
     const size_t need = atma::polar_decode_workspace_bytes(B, Hq, cache_len, D);
     if (!workspace || ws_bytes < need) return ATMA_ERR_WORKSPACE;

@@ -79,8 +79,9 @@ struct PolarDecodeArgs {
     double rope_theta = 0.0;
 };
 size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
-// Head layouts the decode kernels have code for: Hkv in {1,2,4,8,16,32}, Hq/Hkv in {1,2,4,8}.
-bool polar_decode_supported(int Hq, int Hkv);
+// Head layouts the decode kernels have code for: D in {64, 128}, Hkv in {1,2,4,8,16,32} with
+// Hkv * D <= 2048, Hq/Hkv in {1,2,4,8}.
+bool polar_decode_supported(int Hq, int Hkv, int D);
 hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream);
 
 // Sets the dynamic-LDS limit of a kernel once per process.

@@ -28,10 +28,10 @@
 namespace atma {
 namespace {
 
-constexpr int D = 64;
 constexpr int NT = 256;
-constexpr int REC = 68;     // floats per partial record: M, L, Q2, pad, Sv[64]
 constexpr int UNROLL = 4;   // tokens in flight per thread
+// floats per partial record: M, L, Q2, pad, Sv[D]
+__host__ __device__ constexpr int rec_floats(int D) { return 4 + D; }
 
 __device__ __forceinline__ float softplus(float x) { return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
 
@@ -51,17 +51,19 @@ __device__ __forceinline__ void unpack8(const u32x4& r, float* f) {
 }
 
 // grid (nsplit, B); block 256.  Thread = (token slot, kv head, 8-wide dim chunk).
-template <int GQ, bool SOFTMAX>
+template <int D, int GQ, bool SOFTMAX>
 __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                                                            const bf16* __restrict__ vc, PolarParamsDev prm,
                                                            float* __restrict__ ws, int max_len, int Lmax,
                                                            int Hkv, const int* __restrict__ lens, double log2_theta) {
     const int split = blockIdx.x, nsplit = gridDim.x, b = blockIdx.y;
+    constexpr int CH = D / 8;                 // 8-wide dimension chunks (threads) per head
+    constexpr int REC = rec_floats(D);
     const int Hq = Hkv * GQ;
-    const int tpt = Hkv * 8;                 // threads per token
+    const int tpt = Hkv * CH;                // threads per token
     const int slots = NT / tpt;              // tokens per pass
     const int slot = threadIdx.x / tpt;
-    const int hk = (threadIdx.x % tpt) >> 3, chunk = threadIdx.x & 7;
+    const int hk = (threadIdx.x % tpt) / CH, chunk = threadIdx.x % CH;
     int cache_len = lens ? __builtin_amdgcn_readfirstlane(lens[b]) : max_len;
     if (cache_len < 1 || cache_len > max_len) cache_len = 0;  // invalid: no keys (the combine writes NaN)
     const int t_begin = (int)((long)cache_len * split / nsplit);
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     for (int g = 0; g < GQ; ++g) {
         const int h = hk * GQ + g;
         const float t = SOFTMAX ? 1.0f : 1.0f + softplus(prm.temp_raw[h]) * lnn;
-        cq[g] = t * kLog2e * 0.125f;
+        cq[g] = t * kLog2e * (D == 64 ? 0.125f : 0.08838834764831845f);  // t log2(e) / sqrt(D)
         const u32x4 r = *(const u32x4*)(q + ((size_t)b * Hq + h) * D + chunk * 8);
         unpack8(r, qv[g]);
         if (SOFTMAX) {
@@ -127,9 +129,8 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
                 float d = 0.f;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) d += qv[g][x] * kf[x];
-                d += __shfl_xor(d, 4, 8);
-                d += __shfl_xor(d, 2, 8);
-                d += __shfl_xor(d, 1, 8);
+#pragma unroll
+                for (int o = CH / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, CH);
                 lg[u] = (t0 + u * slots < t_end) ? d * cq[g] : -INFINITY;
                 bmax = fmaxf(bmax, lg[u]);
             }
@@ -154,24 +155,24 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     }
 
     // merge the token slots of this workgroup through LDS, then write one record per head
-    __shared__ float part[NT / 8][3];  // per (slot, kv head): M, L, Q2 (written by chunk 0)
+    __shared__ float part[NT / CH][3];  // per (slot, kv head): M, L, Q2 (written by chunk 0)
     __shared__ float psv[NT][8];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
         if (chunk == 0) {
-            part[threadIdx.x >> 3][0] = m[g];
-            part[threadIdx.x >> 3][1] = L[g];
-            part[threadIdx.x >> 3][2] = Q2[g];
+            part[threadIdx.x / CH][0] = m[g];
+            part[threadIdx.x / CH][1] = L[g];
+            part[threadIdx.x / CH][2] = Q2[g];
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x) psv[threadIdx.x][x] = sv[g][x];
         __syncthreads();
         if (slot == 0) {
             float M = -INFINITY;
-            for (int s = 0; s < slots; ++s) M = fmaxf(M, part[(s * tpt + threadIdx.x) >> 3][0]);
+            for (int s = 0; s < slots; ++s) M = fmaxf(M, part[(s * tpt + threadIdx.x) / CH][0]);
             float LL = 0.f, QQ = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             for (int s = 0; s < slots; ++s) {
-                const float* ps = part[(s * tpt + threadIdx.x) >> 3];
+                const float* ps = part[(s * tpt + threadIdx.x) / CH];
                 const float r = (ps[0] == -INFINITY) ? 0.0f : fast_exp2(ps[0] - M);
                 LL += r * ps[1];
                 QQ += r * r * ps[2];
@@ -188,11 +189,12 @@ __global__ __launch_bounds__(NT) void polar_decode_partial(const bf16* __restric
     }
 }
 
-// grid (Hq, B); block 1024.  Wave j merges the ranges s = 64 j .. 64 j + 63 (then + 1024, ...)
-// in one round of loads: lane i reads the header (M, L, Q2) of range 64 j + i and every lane d
-// reads value dimension d of all 64 ranges, so all loads are in flight together.  The wave's
-// merge weights e_i = exp(M_i - max M) are formed per lane and broadcast with v_readlane for the
-// value sum; the sixteen wave merges are combined through LDS.
+// grid (Hq, B); block 1024.  Wave j merges R ranges at a time (R = 64 at D = 64, 32 at D = 128):
+// ranges s = R j .. R j + R - 1 (then + 16 R, ...), in one round of loads: lane i reads the header
+// (M, L, Q2) of range R j + i and every lane reads its value dimensions (d, and d + 64 at D = 128)
+// of all R ranges, so all loads are in flight together.  The wave's merge weights
+// e_i = exp(M_i - max M) are formed per lane and broadcast with v_readlane for the value sums;
+// the sixteen wave merges are combined through LDS.
 constexpr int CNW = 16;        // waves per combine workgroup
 constexpr int CNT = 64 * CNW;  // threads per combine workgroup
 __device__ __forceinline__ float wave_max(float x) {
@@ -200,62 +202,79 @@ __device__ __forceinline__ float wave_max(float x) {
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
     return x;
 }
-template <bool SOFTMAX>
+template <int D, bool SOFTMAX>
 __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restrict__ ws, PolarParamsDev prm,
                                                             bf16* __restrict__ o, float* __restrict__ mu_out,
                                                             int nsplit, int max_len, const int* __restrict__ lens) {
+    constexpr int NV = D / 64;            // value dimensions per lane
+    constexpr int R = 64 / NV;            // ranges per wave and round
+    constexpr int REC = rec_floats(D);
     const int h = blockIdx.x, Hq = gridDim.x, b = blockIdx.y;
     const int cache_len = lens ? __builtin_amdgcn_readfirstlane(lens[b]) : max_len;
     if (cache_len < 1 || cache_len > max_len) {  // invalid length: NaN outputs for this sequence
-        if (threadIdx.x < 64) o[((size_t)b * Hq + h) * D + threadIdx.x] = (bf16)__builtin_nanf("");
+        if (threadIdx.x < D) o[((size_t)b * Hq + h) * D + threadIdx.x] = (bf16)__builtin_nanf("");
         if (threadIdx.x == 0 && mu_out) mu_out[(size_t)b * Hq + h] = __builtin_nanf("");
         return;
     }
     const int d = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const float* base = ws + ((size_t)b * Hq + h) * nsplit * REC;  // records of (b, h), split-major
-    float M = -INFINITY, L = 0.f, Q2 = 0.f, Sv = 0.f;
-    for (int s0 = 64 * wv; s0 < nsplit; s0 += 64 * CNW) {
-        const int cnt = min(64, nsplit - s0);
+    float M = -INFINITY, L = 0.f, Q2 = 0.f, Sv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) Sv[j] = 0.f;
+    for (int s0 = R * wv; s0 < nsplit; s0 += R * CNW) {
+        const int cnt = min(R, nsplit - s0);
         const float* r0 = base + (size_t)s0 * REC;
         const f32x4 hd = d < cnt ? *(const f32x4*)(r0 + d * REC) : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-        float rs[64];
+        float rs[NV][R];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) rs[i] = i < cnt ? r0[i * REC + 4 + d] : 0.f;
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) rs[j][i] = i < cnt ? r0[i * REC + 4 + 64 * j + d] : 0.f;
         const float bm = fmaxf(M, wave_max(hd[0]));
         if (bm == -INFINITY) continue;  // nothing seen yet (empty ranges)
         const float e0 = fast_exp2(M - bm);  // 0 when M = -inf
         const float e = (hd[0] == -INFINITY) ? 0.0f : fast_exp2(hd[0] - bm);
         L = L * e0 + wave_sum(e * hd[1]);
         Q2 = Q2 * e0 * e0 + wave_sum(e * e * hd[2]);
-        float acc = Sv * e0;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), i)), rs[i], acc);
-        Sv = acc;
+        for (int j = 0; j < NV; ++j) {
+            float acc = Sv[j] * e0;
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), i)), rs[j][i], acc);
+            Sv[j] = acc;
+        }
         M = bm;
     }
     __shared__ float part[CNW][3];
-    __shared__ float psv[CNW][64];
+    __shared__ float psv[CNW][D];
     if (d == 0) {
         part[wv][0] = M;
         part[wv][1] = L;
         part[wv][2] = Q2;
     }
-    psv[wv][d] = Sv;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) psv[wv][64 * j + d] = Sv[j];
     __syncthreads();
     if (wv != 0) return;
     M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < CNW; ++j) M = fmaxf(M, part[j][0]);
-    L = Q2 = Sv = 0.f;
+    for (int w = 0; w < CNW; ++w) M = fmaxf(M, part[w][0]);
+    L = Q2 = 0.f;
 #pragma unroll
-    for (int j = 0; j < CNW; ++j) {
-        const float e = (part[j][0] == -INFINITY) ? 0.0f : fast_exp2(part[j][0] - M);
-        L += e * part[j][1];
-        Q2 += e * e * part[j][2];
-        Sv += e * psv[j][d];
+    for (int j = 0; j < NV; ++j) Sv[j] = 0.f;
+#pragma unroll
+    for (int w = 0; w < CNW; ++w) {
+        const float e = (part[w][0] == -INFINITY) ? 0.0f : fast_exp2(part[w][0] - M);
+        L += e * part[w][1];
+        Q2 += e * e * part[w][2];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) Sv[j] += e * psv[w][64 * j + d];
     }
+    bf16* orow = o + ((size_t)b * Hq + h) * D;
     if constexpr (SOFTMAX) {  // control core: o = Sv / L
-        o[((size_t)b * Hq + h) * D + d] = (bf16)(Sv / L);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) orow[64 * j + d] = (bf16)(Sv[j] / L);
         return;
     }
     const float n = (float)cache_len;
@@ -272,17 +291,22 @@ __global__ __launch_bounds__(CNT) void polar_decode_combine(const float* __restr
     const float xarg = prm.mag_beta[h] * log1pf(meff);
     const float em = expf(-2.0f * xarg);
     const float mu = (1.0f - em) / (1.0f + em);
-    const float s = (Sv * f + pn * prm.v_null[h * D + d]) / Z;
-    const float nrm = sqrtf(wave_sum(s * s));
-    o[((size_t)b * Hq + h) * D + d] = (bf16)(s * mu / fmaxf(nrm, prm.eps));
+    float sv[NV], ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        sv[j] = (Sv[j] * f + pn * prm.v_null[h * D + 64 * j + d]) / Z;
+        ss += sv[j] * sv[j];
+    }
+    const float sc = mu / fmaxf(sqrtf(wave_sum(ss)), prm.eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) orow[64 * j + d] = (bf16)(sv[j] * sc);
     if (d == 0 && mu_out) mu_out[(size_t)b * Hq + h] = mu;
 }
 
 }  // namespace
 
 size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int Dh) {
-    (void)Dh;
-    return (size_t)B * num_splits(B, cache_len) * Hq * REC * sizeof(float);
+    return (size_t)B * num_splits(B, cache_len) * Hq * rec_floats(Dh) * sizeof(float);
 }
 
 hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
@@ -290,31 +314,30 @@ hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
     const int gq = a.Hq / a.Hkv;
     float* ws = (float*)a.workspace;
     const double l2t = a.rope_theta > 0.0 ? log2(a.rope_theta) : 0.0;
-#define ATMA_PD_CASE(G, S)                                                                                 \
-    if (gq == G && a.softmax == S) {                                                                       \
-        hipLaunchKernelGGL((polar_decode_partial<G, S>), dim3(nsplit, a.B), dim3(NT), 0, stream,           \
+#define ATMA_PD_CASE(DD, G, S)                                                                             \
+    if (a.D == DD && gq == G && a.softmax == S) {                                                          \
+        hipLaunchKernelGGL((polar_decode_partial<DD, G, S>), dim3(nsplit, a.B), dim3(NT), 0, stream,       \
                            (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.p, ws,      \
                            a.cache_len, a.Lmax, a.Hkv, a.lens, l2t);                                       \
+        hipLaunchKernelGGL((polar_decode_combine<DD, S>), dim3(a.Hq, a.B), dim3(CNT), 0, stream,           \
+                           (const float*)ws, a.p, (bf16*)a.o, S ? nullptr : a.mu_out, nsplit, a.cache_len, \
+                           a.lens);                                                                        \
     } else
-    ATMA_PD_CASE(1, false) ATMA_PD_CASE(2, false) ATMA_PD_CASE(4, false) ATMA_PD_CASE(8, false)
-    ATMA_PD_CASE(1, true) ATMA_PD_CASE(2, true) ATMA_PD_CASE(4, true) ATMA_PD_CASE(8, true) {
+#define ATMA_PD_GQ(DD, S) ATMA_PD_CASE(DD, 1, S) ATMA_PD_CASE(DD, 2, S) ATMA_PD_CASE(DD, 4, S) ATMA_PD_CASE(DD, 8, S)
+    ATMA_PD_GQ(64, false) ATMA_PD_GQ(64, true) ATMA_PD_GQ(128, false) ATMA_PD_GQ(128, true) {
         return hipErrorInvalidValue;
     }
+#undef ATMA_PD_GQ
 #undef ATMA_PD_CASE
-    if (a.softmax)
-        hipLaunchKernelGGL(polar_decode_combine<true>, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
-                           (bf16*)a.o, nullptr, nsplit, a.cache_len, a.lens);
-    else
-        hipLaunchKernelGGL(polar_decode_combine<false>, dim3(a.Hq, a.B), dim3(CNT), 0, stream, (const float*)ws, a.p,
-                           (bf16*)a.o, a.mu_out, nsplit, a.cache_len, a.lens);
     return hipGetLastError();
 }
 
-bool polar_decode_supported(int Hq, int Hkv) {
+bool polar_decode_supported(int Hq, int Hkv, int D) {
     const int gq = Hq / Hkv;
     const bool g_ok = gq == 1 || gq == 2 || gq == 4 || gq == 8;
-    const bool h_ok = Hkv == 1 || Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16 || Hkv == 32;
-    return g_ok && h_ok;
+    // a token's K row for all kv heads is read by Hkv * D / 8 threads of one 256-thread workgroup
+    const bool h_ok = (Hkv == 1 || Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16 || Hkv == 32) && Hkv * D / 8 <= NT;
+    return (D == 64 || D == 128) && g_ok && h_ok;
 }
 
 }  // namespace atma

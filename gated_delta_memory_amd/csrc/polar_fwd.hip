@@ -45,12 +45,25 @@
 namespace atma {
 namespace {
 
-constexpr int D = 64;
 constexpr int NT = 256;
 constexpr int BQ = 128;  // queries per workgroup
 constexpr int QW = 32;   // queries per wave
 constexpr int BK = 64;   // keys per block
 constexpr float kLazy = 8.0f;
+
+// Head-width dependent shapes (D = 64 or 128).
+template <int D>
+struct Shape {
+    static constexpr int NKS = D / 16;          // k-steps of the score MFMA
+    static constexpr int NDT = D / 32;          // 32-row tiles of O^T
+    static constexpr int ROWB = D * 2;          // bytes per key row
+    static constexpr int CPR = D / 8;           // 16-byte chunks per row
+    static constexpr int TILE = BK * ROWB;      // bytes of one K (or V) tile
+    static constexpr int CPT = BK * CPR / NT;   // chunks each thread copies per tile
+    static constexpr int RPP = NT / CPR;        // rows per pass of the copy
+    static constexpr int OCC = D == 64 ? 4 : 2; // waves per SIMD (two 2-stage LDS buffers of 64 KB at D=128)
+    static constexpr float kInvSqrtD = D == 64 ? 0.125f : 0.08838834764831845f;
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -61,14 +74,20 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte chunk c (0..7) of key row `key` in a 64x64 bf16 tile.  The LDS has
-// 64 four-byte banks, so rows r and r + 1 (128 bytes apart) use disjoint bank halves and only
-// rows of equal parity can collide.  K tiles are read 16 bytes per lane with rows 0..15 in one
-// bank cycle: XOR-ing the chunk with (r >> 1) & 7 gives those rows eight distinct chunks per
-// parity.  V tiles are read by ds_read_b64_tr_b16, which takes four consecutive rows and two
-// adjacent chunks per 16-lane group: XOR-ing with 2 (r & 3) spreads them over all eight chunks.
-__device__ __forceinline__ int swz_k(int key, int c) { return key * 128 + ((c ^ ((key >> 1) & 7)) << 4); }
-__device__ __forceinline__ int swz_v(int key, int c) { return key * 128 + ((c ^ ((key & 3) << 1)) << 4); }
+// Byte offset of 16-byte chunk c of key row `key` in a 64 x D bf16 tile.  The LDS has 64
+// four-byte banks (256 bytes).  K tiles are read 16 bytes per lane with rows 0..15 in one bank
+// cycle.  D = 64 (128-byte rows): rows r and r + 1 use disjoint bank halves, so XOR-ing the
+// chunk with (r >> 1) & 7 gives the rows of each parity eight distinct chunks.  D = 128
+// (256-byte rows, every row on all banks): XOR with r & 15 gives the sixteen rows sixteen
+// distinct chunks.  V tiles are read by ds_read_b64_tr_b16, which takes four consecutive rows and
+// two adjacent chunks per 16-lane group: XOR-ing with 2 (r & 3) puts the four rows' pieces on
+// four different 32-byte bank groups at either width.
+template <int D>
+__device__ __forceinline__ int swz_k(int key, int c) {
+    return key * (2 * D) + ((c ^ (D == 64 ? ((key >> 1) & 7) : (key & 15))) << 4);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int key, int c) { return key * (2 * D) + ((c ^ ((key & 3) << 1)) << 4); }
 
 // partner-lane (l ^ 32) combine via v_permlane32_swap
 __device__ __forceinline__ float pair_max(float x) {
@@ -85,12 +104,8 @@ __device__ __forceinline__ bf16x4 tr_read(const char* lds_base, int byte_off) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Two K/V stages, one LDS object each (the copy into one stage overlaps the reads of the other).
-__shared__ __align__(16) char g_kv0[2 * BK * D * 2];
-__shared__ __align__(16) char g_kv1[2 * BK * D * 2];
-
-template <bool POLAR>
-__global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+template <int D, bool POLAR>
+__global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
                                                           float* __restrict__ meff_out, int Tmax, int Hq, int Hkv,
@@ -102,6 +117,11 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     // Workgroup i is dispatched to XCD i % 8; the flat grid is renumbered so that every XCD
     // receives a contiguous range of items and the tiles of one (batch, head) share that
     // XCD's L2 for their K/V stream.
+    using SH = Shape<D>;
+    constexpr int NKS = SH::NKS, NDT = SH::NDT, ROWB = SH::ROWB;
+    // Two K/V stages, one LDS object each (the copy into one stage overlaps the reads of the other).
+    __shared__ __align__(16) char g_kv0[2 * SH::TILE];
+    __shared__ __align__(16) char g_kv1[2 * SH::TILE];
     const int nqt_grid = (Tmax + BQ - 1) / BQ;
     const int per_bh = paired ? (nqt_grid + 1) / 2 : nqt_grid;
     const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
@@ -134,25 +154,23 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     const bf16* kbase = k + seq0 * kvstride + (size_t)hk * D;
     const bf16* vbase = v + seq0 * kvstride + (size_t)hk * D;
 
-    // Asynchronous copy of key block kb into a stage [K tile | V tile]: 16-byte chunk ch of the
-    // stage lands at LDS slot ch (row ch / 8, position ch % 8); the source chunk is chosen so
-    // the tile comes out swizzled.  Thread t moves chunks t, t + 256 (K) and t + 512,
-    // t + 768 (V): rows r0 = t / 8 and r0 + 32 of each tile.
-    const int r0 = (int)threadIdx.x >> 3, pc = (int)threadIdx.x & 7;
-    const unsigned koff0 = (unsigned)(((pc ^ ((r0 >> 1) & 7)) << 4));        // (r0 + 32) has the same swizzle
-    const unsigned voff0 = (unsigned)(((pc ^ ((r0 & 3) << 1)) << 4));
+    // Asynchronous copy of key block kb into a stage [K tile | V tile]: 16-byte chunk ch of a
+    // tile lands at LDS slot ch (row ch / CPR, position ch % CPR); the source chunk is chosen so
+    // the tile comes out swizzled.  Thread t moves chunks t + 256 m (m < CPT) of each tile:
+    // rows r0 + RPP m at position pc, all with the same swizzle.
+    const int r0 = (int)threadIdx.x / SH::CPR, pc = (int)threadIdx.x % SH::CPR;
+    const unsigned koff0 = (unsigned)(swz_k<D>(r0, pc) - r0 * ROWB);
+    const unsigned voff0 = (unsigned)(swz_v<D>(r0, pc) - r0 * ROWB);
     auto issue = [&](int kb, const char* stage) {
         const size_t blk = (size_t)kb * BK * kvstride;
         const unsigned lds = lds_addr(stage) + (unsigned)(w * 64 * 16);
-        int ra = r0, rb = r0 + 32;
-        if (kb * BK + BK > T) {  // last block of a ragged sequence: rows past T repeat row T - 1 (masked later)
-            ra = min(ra, T - 1 - kb * BK);
-            rb = min(rb, T - 1 - kb * BK);
+        const bool ragged = kb * BK + BK > T;  // last block of a ragged sequence: rows past T repeat row T - 1
+#pragma unroll
+        for (int m = 0; m < SH::CPT; ++m) {
+            const int r = ragged ? min(r0 + SH::RPP * m, T - 1 - kb * BK) : r0 + SH::RPP * m;
+            lds_dma16(kbase + blk, r * rowbytes + koff0, lds + m * NT * 16);
+            lds_dma16(vbase + blk, r * rowbytes + voff0, lds + SH::TILE + m * NT * 16);
         }
-        lds_dma16(kbase + blk, ra * rowbytes + koff0, lds);
-        lds_dma16(kbase + blk, rb * rowbytes + koff0, lds + NT * 16);
-        lds_dma16(vbase + blk, ra * rowbytes + voff0, lds + 2 * NT * 16);
-        lds_dma16(vbase + blk, rb * rowbytes + voff0, lds + 3 * NT * 16);
     };
 
     // Lane-constant fragment offsets inside a stage.  K (A operand of S^T = K Q^T): lane reads
@@ -160,32 +178,34 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     // reads: for weight slot group (kt, st) the 16-lane group g16 reads keys
     // 32 kt + 16 st + 4 G2 + (i16 / 4) (+ 8 for the upper half of the fragment), columns
     // 32 dt + 16 (g16 & 1) + 4 (i16 & 3) .. + 3.
-    int koff[4], voff[2];
+    int koff[NKS], voff[NDT];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) koff[ks] = swz_k(l32, 2 * ks + G2);
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = swz_k<D>(l32, 2 * ks + G2);
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
         const int dcol = 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3);
-        voff[dt] = swz_v(4 * G2 + (i16 >> 2), dcol >> 3) + ((dcol & 7) << 1);
+        voff[dt] = swz_v<D>(4 * G2 + (i16 >> 2), dcol >> 3) + ((dcol & 7) << 1);
     }
 
   auto tile = [&](int qt) {
     const int q0 = qt * BQ;
     const int qw0 = q0 + w * QW;
     const int qi = qw0 + l32;  // this lane's query
-    const float cq = POLAR ? (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * 0.125f  // t_i log2(e) / sqrt(64)
-                           : kLog2e * 0.125f;
+    const float cq = POLAR ? (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * SH::kInvSqrtD  // t_i log2(e) / sqrt(D)
+                           : kLog2e * SH::kInvSqrtD;
 
     // Q^T fragments (B operand): lane supplies Q[qi][16 ks + 8 G2 + e]
-    bf16x8 qf[4];
+    bf16x8 qf[NKS];
     {
         const int qc = min(qi, T - 1);
         const bf16* qrow = q + (seq0 + qc) * qstride + (size_t)h * D + 8 * G2;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
     }
 
-    f32x16 oacc[2] = {f32x16{}, f32x16{}};  // O^T[d = 32 dt + 8(x/4) + 4 G2 + x%4][qi]
+    f32x16 oacc[NDT];  // O^T[d = 32 dt + 8(x/4) + 4 G2 + x%4][qi]
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
     float m_used = -INFINITY;
     float lsum[4] = {0.f, 0.f, 0.f, 0.f}, q2sum[4] = {0.f, 0.f, 0.f, 0.f};  // split to shorten dependency chains
 
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     const int nkb = (kend + BK - 1) / BK;
 
     auto block = [&](int kb, const char* Ks) {
-        const char* Vs = Ks + BK * D * 2;
+        const char* Vs = Ks + SH::TILE;
         const int key0 = kb * BK;
         if (key0 > qw0 + QW - 1) return;  // whole block in this wave's future
         const bool edge = (key0 + BK - 1 > qw0) || (key0 + BK > T);
@@ -202,9 +222,9 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
         // S^T = K Q^T : two 32-key sub-tiles, chains interleaved
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(*(const bf16x8*)(Ks + koff[ks] + kt * 32 * 128), qf[ks], s[kt]);
+            for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(*(const bf16x8*)(Ks + koff[ks] + kt * 32 * ROWB), qf[ks], s[kt]);
 
         // causal / length mask on edge blocks (raw scores; cq > 0 scales them later)
         if (edge) {
@@ -233,8 +253,8 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
                 lsum[a4] *= rho;
                 q2sum[a4] *= rho * rho;
             }
-            oacc[0] *= rho;
-            oacc[1] *= rho;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= rho;
         }
         // weights, their sums, and O^T += V^T P^T
 #pragma unroll
@@ -255,10 +275,10 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
                     pf[e + 1] = pp[1];
                 }
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt) {
-                    const int base = voff[dt] + (32 * kt + 16 * st) * 128;
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const int base = voff[dt] + (32 * kt + 16 * st) * ROWB;
                     const bf16x4 lo = tr_read(Vs, base);
-                    const bf16x4 hi = tr_read(Vs, base + 8 * 128);
+                    const bf16x4 hi = tr_read(Vs, base + 8 * ROWB);
                     oacc[dt] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf, oacc[dt]);
                 }
             }
@@ -288,7 +308,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
         if (qi < T) {
             bf16* orow = o + (seq0 + qi) * qstride + (size_t)h * D;
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     bf16x4 y;
@@ -317,7 +337,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     const float invZ = 1.0f / Z;
     float nrm2 = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int d = 32 * dt + 8 * (x >> 2) + 4 * G2 + (x & 3);
@@ -330,7 +350,7 @@ __global__ __launch_bounds__(NT, 4) void polar_fwd_kernel(const bf16* __restrict
     if (qi < T) {
         bf16* orow = o + (seq0 + qi) * qstride + (size_t)h * D;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 bf16x4 y;
@@ -362,14 +382,21 @@ hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
     // pair tiles when there are at most about two rounds of workgroups (4 per CU on 256 CUs)
     const int paired = ntiles <= 2048 * 2 ? 1 : 0;
     const int per_bh = paired ? (nqt + 1) / 2 : nqt;
-    if (a.softmax)
-        hipLaunchKernelGGL(polar_fwd_kernel<false>, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
-                           (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, nullptr, nullptr, a.T, a.Hq,
-                           a.Hkv, paired, a.cu, a.total);
-    else
-        hipLaunchKernelGGL(polar_fwd_kernel<true>, dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream, (const bf16*)a.q,
-                           (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o, a.mu_out, a.meff_out, a.T, a.Hq,
-                           a.Hkv, paired, a.cu, a.total);
+#define ATMA_PF_LAUNCH(DD, POL)                                                                            \
+    hipLaunchKernelGGL((polar_fwd_kernel<DD, POL>), dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream,        \
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o,               \
+                       POL ? a.mu_out : nullptr, POL ? a.meff_out : nullptr, a.T, a.Hq, a.Hkv, paired, a.cu, \
+                       a.total)
+    if (a.D == 64) {
+        if (a.softmax) ATMA_PF_LAUNCH(64, false);
+        else ATMA_PF_LAUNCH(64, true);
+    } else if (a.D == 128) {
+        if (a.softmax) ATMA_PF_LAUNCH(128, false);
+        else ATMA_PF_LAUNCH(128, true);
+    } else {
+        return hipErrorInvalidValue;
+    }
+#undef ATMA_PF_LAUNCH
     return hipGetLastError();
 }
 

@@ -133,7 +133,7 @@ int atma_gdn_decode_step(const void* q, const void* k, const void* v, const floa
  *   q        [B, T, Hq, D]  dtype `dt`;  k, v [B, T, Hkv, D] dtype `dt`
  *   o        [B, T, Hq, D]  dtype `dt` (output)
  *   mu_out   [B, Hq, T] fp32 (output) or NULL;  meff_out [B, Hq, T] fp32 or NULL
- *   D == 64 and dt == ATMA_BF16; workspace may be NULL when
+ *   D in {64, 128} and dt == ATMA_BF16; workspace may be NULL when
  *   atma_polar_attn_workspace_bytes returns 0 (it does for this build).
  * ------------------------------------------------------------------------------- */
 int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_polar_params* p,
@@ -152,7 +152,7 @@ size_t atma_polar_attn_workspace_bytes(int B, int T, int Hq, int D);
  *                cu_seqlens[s] .. cu_seqlens[s+1]-1 (0 = cu_seqlens[0] <= ... <= total_T)
  *   max_seqlen   host-side bound on every sequence length (sizes the grid), <= total_T
  *   mu_out, meff_out  [Hq, total_T] fp32 or NULL
- *   D == 64 and dt == ATMA_BF16.  No workspace.  The offsets are read on the device: a
+ *   D in {64, 128} and dt == ATMA_BF16.  No workspace.  The offsets are read on the device: a
  *   sequence whose bounds are not inside [0, total_T], decrease, or exceed max_seqlen is
  *   skipped (its rows of o are left unwritten); no access leaves the buffers.
  * ------------------------------------------------------------------------------- */
@@ -167,7 +167,8 @@ int atma_polar_attn_fwd_varlen(const void* q, const void* k, const void* v, cons
  *   k_cache, v_cache [B, Lmax, Hkv, D] dtype `dt`; slots 0..cache_len-1 are valid and the
  *            caller has already written the new token's k, v into slot cache_len-1.
  *   n = cache_len in the formulas above (1 <= cache_len <= Lmax).
- *   D == 64, dt == ATMA_BF16, Hkv in {1, 2, 4, 8, 16, 32} and Hq / Hkv in {1, 2, 4, 8}.
+ *   D in {64, 128}, dt == ATMA_BF16, Hkv in {1, 2, 4, 8, 16, 32} with Hkv * D <= 2048, and
+ *   Hq / Hkv in {1, 2, 4, 8} (so the real-model layout, 8 query / 2 kv heads at D = 128, works).
  *   o        [B, Hq, D] dtype `dt` (output);  mu_out [B, Hq] fp32 or NULL
  *   workspace at least atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D) bytes
  *            (per split of the cache: running max, real mass, squared mass and value sum).
@@ -213,7 +214,7 @@ int atma_polar_attn_decode_varlen(const void* q, const void* k_cache, const void
 int atma_rope(const void* x, void* y, int B, int T, int H, int D, int pos0, float theta, atma_dtype dt,
               void* stream);
 
-/* Prefill: q [B, T, Hq, D], k, v [B, T, Hkv, D], o [B, T, Hq, D]; D == 64, bf16.
+/* Prefill: q [B, T, Hq, D], k, v [B, T, Hkv, D], o [B, T, Hq, D]; D in {64, 128}, bf16.
  *   rope_theta == 0: NoPE;  rope_theta > 0: RoPE with that base (positions 0..T-1).
  *   workspace: atma_softmax_attn_workspace_bytes(...) bytes (the rotated q and k; 0 for NoPE). */
 int atma_softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T, int Hq,

@@ -114,7 +114,7 @@ def test_polar_fwd_validation():
     assert _pfwd(p=_params(eps=float("nan"))) == g.ATMA_ERR_SHAPE
     assert _pfwd(T=0) == g.ATMA_ERR_SHAPE
     assert _pfwd(Hq=3, Hkv=2) == g.ATMA_ERR_SHAPE
-    assert _pfwd(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pfwd(D=96) == g.ATMA_ERR_UNSUPPORTED
     assert _pfwd(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
 
 
@@ -133,7 +133,8 @@ def test_polar_decode_validation():
     assert _pdec(L=17) == g.ATMA_ERR_SHAPE            # cache_len > Lmax
     assert _pdec(Hq=16, Hkv=3) == g.ATMA_ERR_SHAPE
     assert _pdec(Hq=48, Hkv=3) == g.ATMA_ERR_UNSUPPORTED   # head layout without a kernel
-    assert _pdec(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pdec(D=96) == g.ATMA_ERR_UNSUPPORTED
+    assert _pdec(D=128, Hq=32, Hkv=32) == g.ATMA_ERR_UNSUPPORTED  # 32 kv heads x 128: no kernel
     assert _pdec(ws=NULL) == g.ATMA_ERR_WORKSPACE
     assert _pdec(wsb=16) == g.ATMA_ERR_WORKSPACE
 
@@ -155,7 +156,7 @@ def test_polar_decode_varlen_validation():
     assert _pdecv(Lb=17) == g.ATMA_ERR_SHAPE           # bound > Lmax
     assert _pdecv(B=0) == g.ATMA_ERR_SHAPE
     assert _pdecv(Hq=16, Hkv=3) == g.ATMA_ERR_SHAPE
-    assert _pdecv(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pdecv(D=96) == g.ATMA_ERR_UNSUPPORTED
     assert _pdecv(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
     assert _pdecv(ws=NULL) == g.ATMA_ERR_WORKSPACE
     need = g.lib.atma_polar_attn_decode_workspace_bytes(2, 16, 10, 64)
@@ -178,7 +179,7 @@ def test_polar_fwd_varlen_validation():
     assert _pfwdv(maxT=0) == g.ATMA_ERR_SHAPE
     assert _pfwdv(maxT=201) == g.ATMA_ERR_SHAPE          # longer than all rows together
     assert _pfwdv(Hq=4, Hkv=3) == g.ATMA_ERR_SHAPE
-    assert _pfwdv(D=128) == g.ATMA_ERR_UNSUPPORTED
+    assert _pfwdv(D=96) == g.ATMA_ERR_UNSUPPORTED
     assert _pfwdv(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
     assert _pfwdv(p=_params(v_null=0)) == g.ATMA_ERR_NULL
 
@@ -192,7 +193,7 @@ def test_control_core_validation():
     f = L.atma_softmax_attn_fwd
     assert f(FAKE, FAKE, NULL, FAKE, 1, 8, 4, 2, 64, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_NULL
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 3, 64, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_SHAPE
-    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 128, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 96, 0.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 64, -1.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_SHAPE
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2, 64, 10000.0, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_WORKSPACE
     assert L.atma_softmax_attn_workspace_bytes(1, 8, 4, 2, 64, 0.0) == 0

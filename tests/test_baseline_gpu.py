@@ -33,10 +33,12 @@ def test_rope_matches_oracle(atma, pos0):
     assert e <= 1e-3
 
 
-@pytest.mark.parametrize("B,T,Hq,Hkv,theta", [(1, 1, 1, 1, 0.0), (2, 300, 4, 2, 0.0), (1, 513, 3, 1, 10000.0),
-                                              (2, 2048, 16, 16, 10000.0), (1, 777, 8, 2, 500.0)])
-def test_softmax_attn_fwd(atma, B, T, Hq, Hkv, theta):
-    inp = workloads.make_polar_inputs(B, T, Hq, Hkv, 64, seed=T + Hq)
+@pytest.mark.parametrize("B,T,Hq,Hkv,theta,D", [(1, 1, 1, 1, 0.0, 64), (2, 300, 4, 2, 0.0, 64),
+                                                (1, 513, 3, 1, 10000.0, 64), (2, 2048, 16, 16, 10000.0, 64),
+                                                (1, 777, 8, 2, 500.0, 64), (2, 1024, 8, 2, 10000.0, 128),
+                                                (1, 300, 8, 2, 0.0, 128)])
+def test_softmax_attn_fwd(atma, B, T, Hq, Hkv, theta, D):
+    inp = workloads.make_polar_inputs(B, T, Hq, Hkv, D, seed=T + Hq)
     o = atma.atma_softmax_attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), theta)
     torch.cuda.synchronize()
     # RoPE: the rotated q and k are bf16 operands (defined so; see the oracle)
@@ -46,12 +48,13 @@ def test_softmax_attn_fwd(atma, B, T, Hq, Hkv, theta):
     assert e <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("B,L,Lmax,Hq,Hkv,theta", [(1, 1, 1, 16, 16, 0.0), (2, 1000, 1200, 16, 16, 10000.0),
-                                                   (3, 5000, 5000, 8, 2, 10000.0), (4, 300, 512, 4, 4, 0.0)])
-def test_softmax_attn_decode(atma, B, L, Lmax, Hq, Hkv, theta):
+@pytest.mark.parametrize("B,L,Lmax,Hq,Hkv,theta,D", [(1, 1, 1, 16, 16, 0.0, 64), (2, 1000, 1200, 16, 16, 10000.0, 64),
+                                                     (3, 5000, 5000, 8, 2, 10000.0, 64), (4, 300, 512, 4, 4, 0.0, 64),
+                                                     (2, 3000, 3000, 8, 2, 10000.0, 128)])
+def test_softmax_attn_decode(atma, B, L, Lmax, Hq, Hkv, theta, D):
     """RoPE decode: the library rotates the raw keys into the cache (atma_rope), the oracle
     rotates them itself."""
-    inp = workloads.make_decode_inputs(B, L, Hq=Hq, Hkv=Hkv, Lmax=Lmax, seed=L + Hq)
+    inp = workloads.make_decode_inputs(B, L, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=L + Hq)
     kc = inp["k_cache"].cuda()
     if theta > 0:
         kc = atma.atma_rope(kc, theta)

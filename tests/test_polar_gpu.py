@@ -58,6 +58,20 @@ def test_polar_small_all_rows(atma, B, T, Hq, Hkv):
     _check_prefill(atma, inp, tag=f"B{B} T{T} Hq{Hq} Hkv{Hkv}")
 
 
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 1, 1, 1), (1, 77, 8, 2), (2, 300, 8, 2), (1, 513, 4, 4), (1, 1000, 2, 1)])
+def test_polar_d128_all_rows(atma, B, T, Hq, Hkv):
+    """Head width 128, including the real-model layout of 8 query and 2 kv heads."""
+    inp = workloads.make_polar_inputs(B, T, Hq, Hkv, 128, seed=T + 128 + Hq)
+    _check_prefill(atma, inp, tag=f"D128 B{B} T{T} Hq{Hq} Hkv{Hkv}")
+
+
+def test_polar_d128_gqa_layer_b8_t2k(atma):
+    """The 378M-class model's attention layout at training length: B=8, T=2048, 8 query heads,
+    2 kv heads, D=128 (sampled rows)."""
+    inp = workloads.make_polar_inputs(8, 2048, 8, 2, 128, seed=378)
+    _check_prefill(atma, inp, rows=sample_rows(2048), tag="D128 gqa b8 t2k")
+
+
 def test_polar_layer_b8_t2k(atma):
     """378M-class layer at 2K: B=8, T=2048, Hq=16, d=64 (sampled rows)."""
     inp = workloads.make_workload("layer_b8_t2k")["polar"]
@@ -107,13 +121,13 @@ def test_polar_decode(atma, B, L, Lmax, Hq, Hkv):
     assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("lens,Hq,Hkv", [([1, 77, 300, 513, 128, 1000], 4, 2), ([2048, 5, 129, 256], 2, 2),
-                                          ([64], 3, 1)])
-def test_polar_fwd_varlen(atma, lens, Hq, Hkv):
+@pytest.mark.parametrize("lens,Hq,Hkv,D", [([1, 77, 300, 513, 128, 1000], 4, 2, 64), ([2048, 5, 129, 256], 2, 2, 64),
+                                            ([64], 3, 1, 64), ([700, 3, 1500], 8, 2, 128)])
+def test_polar_fwd_varlen(atma, lens, Hq, Hkv, D):
     """Packed prefill: each sequence (all rows, its own causal positions) against the oracle
     run on that sequence alone."""
     total = sum(lens)
-    inp = workloads.make_polar_inputs(1, total, Hq, Hkv, 64, seed=total)
+    inp = workloads.make_polar_inputs(1, total, Hq, Hkv, D, seed=total)
     q, k, v = (inp[x][0].contiguous() for x in ("q", "k", "v"))
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
     o, mu, meff = atma.atma_polar_attn_fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu, max(lens),
@@ -151,6 +165,31 @@ def test_polar_fwd_varlen_matches_fixed_and_skips_bad_offsets(atma):
         torch.cuda.synchronize()
         assert torch.equal(ob[:T], op[:T])
         assert (ob[T:].float() == 7.0).all()
+
+
+@pytest.mark.parametrize("B,L,Lmax,Hq,Hkv", [(1, 1, 1, 8, 2), (2, 1000, 1200, 8, 2), (3, 5000, 5000, 8, 2),
+                                            (1, 20000, 20000, 16, 16), (4, 129, 4096, 4, 1)])
+def test_polar_decode_d128(atma, B, L, Lmax, Hq, Hkv):
+    inp = workloads.make_decode_inputs(B, L, Hq=Hq, Hkv=Hkv, D=128, Lmax=Lmax, seed=L + 128)
+    o, mu = atma.atma_polar_attn_decode(inp["q"].cuda(), inp["k_cache"].cuda(), inp["v_cache"].cuda(), L,
+                                        _dev_params(inp["params"]), want_mu=True)
+    torch.cuda.synchronize()
+    ref = oracle.polar_decode(inp["q"], inp["k_cache"], inp["v_cache"], L, _cpu_params(inp["params"]))
+    eo, emu = out_err(to_np(o), ref["o"], "bf16"), rel_err(to_np(mu), ref["mu"])
+    note(f"  polar decode D128 B{B} L{L} Hq{Hq} Hkv{Hkv} err_o={eo:.3e} err_mu={emu:.3e}")
+    assert eo <= TOL["bf16"] and emu <= TOL["bf16"]
+
+
+def test_polar_d128_decode_equals_prefill_last_row(atma):
+    B, T, Hq, Hkv = 2, 1500, 8, 2
+    inp = workloads.make_polar_inputs(B, T, Hq, Hkv, 128, seed=22)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    p = _dev_params(inp["params"])
+    o, mu, _ = atma.atma_polar_attn_fwd(q, k, v, p, want_mu=True)
+    od, mud = atma.atma_polar_attn_decode(q[:, T - 1].contiguous(), k, v, T, p, want_mu=True)
+    torch.cuda.synchronize()
+    assert out_err(to_np(od), to_np(o[:, T - 1]), "bf16") <= TOL["bf16"]
+    assert rel_err(to_np(mud), to_np(mu[:, :, T - 1])) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("lens,Lmax,Hq,Hkv", [([1, 77, 1000, 4096], 4096, 16, 16), ([300, 5, 2048], 2048, 8, 2),
