@@ -242,6 +242,19 @@ def secondary(torch, atma, workloads):
                               "nope_mfma_frac": round(pf / (tno.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del p, o_p, ws_r
     torch.cuda.empty_cache()
+    # the real model's attention layout: 8 query / 2 kv heads at head width 128
+    for (B, T, name, reps) in ((8, 2048, "polar_d128_gqa_b8_t2k", 21), (1, 65536, "polar_d128_gqa_b1_t64k", 4)):
+        p = workloads.make_polar_inputs(B, T, 8, 2, 128, device="cuda")
+        o_p = torch.empty_like(p["q"])
+        tq = Timer(torch)
+        for it in range(reps):
+            (tq if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+        torch.cuda.synchronize()
+        fl = 4 * 128 * B * 8 * T * (T + 1) / 2
+        res[name] = {"polar_ms": round(tq.mean_ms(), 4),
+                     "polar_mfma_frac": round(fl / (tq.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del p, o_p
+        torch.cuda.empty_cache()
     # 64K prefill
     w = workloads.WORKLOADS["prefill_b1_t64k"]
     inp = workloads.make_workload(w, device="cuda")
