@@ -22,6 +22,8 @@ arXiv 2606.25156):
                          paper compares Polar against (Section 3.1): causal softmax
                          attention with scale 1/sqrt(D), optionally after rotating
                          adjacent pairs of q and k by position * theta^(-2p/D).
+* ``canon``           - the Canon prologue (Section 3.1): depthwise causal convolution
+                         over tokens, optional residual, optional unit L2 norm per head.
 """
 from __future__ import annotations
 
@@ -75,8 +77,9 @@ def _declare(lib):
     lib.oracle_rope.argtypes = [i, i, i, i, l, d, i, _dp, _dp]
     lib.oracle_softmax_attn.argtypes = [i, i, i, i, i, d, i, _dp, _dp, _dp, _dp, i]
     lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, i, _dp, _dp, _dp, _dp]
+    lib.oracle_canon.argtypes = [i, i, i, i, i, i, d, _dp, _dp, _dp, _dp]
     for f in ("oracle_gdn_sequential", "oracle_gdn_chunked", "oracle_polar_fwd", "oracle_polar_decode",
-              "oracle_threads_used", "oracle_rope", "oracle_softmax_attn", "oracle_softmax_decode"):
+              "oracle_threads_used", "oracle_rope", "oracle_softmax_attn", "oracle_softmax_decode", "oracle_canon"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -231,3 +234,17 @@ def softmax_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0, rotated_keys_
     assert _load().oracle_softmax_decode(B, Hq, Hkv, D, int(cache_len), Lmax, float(rope_theta),
                                          int(rotated_keys_bf16), _ptr(q), _ptr(kc), _ptr(vc), _ptr(o)) == 0
     return o
+
+
+def canon(x, w, state=None, residual=False, heads=0, eps=1e-6):
+    """x [B,T,C]; w [K,C]; state [B,K-1,C] (previous inputs, oldest first) or None.
+    Returns y [B,T,C] (fp64): depthwise causal convolution (+ x when ``residual``), then unit
+    L2 norm of each of ``heads`` channel groups when heads > 0."""
+    x, w = _f64(x), _f64(w)
+    B, T, C = x.shape
+    K = w.shape[0]
+    st = None if state is None else _f64(state)
+    y = np.zeros((B, T, C))
+    assert _load().oracle_canon(B, T, C, K, int(bool(residual)), int(heads), float(eps), _ptr(x), _ptr(w), _ptr(st),
+                                _ptr(y)) == 0
+    return y

@@ -638,3 +638,42 @@ int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lm
     free(qi);
     return 0;
 }
+
+/* ========================================================================= */
+/* Canon prologue: depthwise causal convolution, optional per-head L2 norm    */
+/* ========================================================================= */
+/* Section 3.1 of the paper applies Canon depthwise causal convolutions to q, k and v before
+ * attention; the pages fix neither the width nor a bias or residual.  Reading (listed in the
+ * design notes): per channel c, y_t = sum_{j<K} w[j][c] x_{t-j} (+ x_t with `residual`), the
+ * inputs before the first token taken from `state` (the K-1 previous inputs, oldest first;
+ * zeros when NULL); then, when H > 0, each of the H groups of C/H channels is scaled to unit
+ * L2 norm, y / max(||y||, eps) (the memory path's unit-norm keys and queries).
+ *   x [B, T, C];  w [K, C];  state [B, K-1, C] or NULL;  y [B, T, C]. */
+int oracle_canon(int B, int T, int C, int K, int residual, int H, double eps, const double* x, const double* w,
+                 const double* state, double* y) {
+    if (B < 1 || T < 1 || C < 1 || K < 1 || H < 0 || (H > 0 && C % H) || !x || !w || !y) return -1;
+    for (long b = 0; b < B; ++b) {
+        for (long t = 0; t < T; ++t) {
+            double* yt = y + ((size_t)b * T + t) * C;
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j) {
+                    const long s = t - j;
+                    double xv = 0.0;
+                    if (s >= 0) xv = x[((size_t)b * T + s) * C + c];
+                    else if (state && K - 1 + s >= 0) xv = state[((size_t)b * (K - 1) + (K - 1 + s)) * C + c];
+                    acc += w[(size_t)j * C + c] * xv;
+                }
+                yt[c] = acc + (residual ? x[((size_t)b * T + t) * C + c] : 0.0);
+            }
+            for (int h = 0; h < H; ++h) {
+                const int D = C / H;
+                double n2 = 0.0;
+                for (int e = 0; e < D; ++e) n2 += yt[h * D + e] * yt[h * D + e];
+                const double den = sqrt(n2) > eps ? sqrt(n2) : eps;
+                for (int e = 0; e < D; ++e) yt[h * D + e] /= den;
+            }
+        }
+    }
+    return 0;
+}

@@ -44,6 +44,10 @@ MUTANTS = {
     "softmax_no_scale": ("w[j] = d * scale;", "w[j] = d;"),
     "softmax_sees_next_key": ("(long)i + 1, D, c->o + ((b * T + i) * c->Hq + h) * D, w);",
                               "(long)(i + 1 < T ? i + 2 : i + 1), D, c->o + ((b * T + i) * c->Hq + h) * D, w);"),
+    "canon_anticausal": ("const long s = t - j;", "const long s = t + j < T ? t + j : t - j;"),
+    "canon_state_offset": ("xv = state[((size_t)b * (K - 1) + (K - 1 + s)) * C + c];",
+                           "xv = state[((size_t)b * (K - 1) + (K - 2 + s >= 0 ? K - 2 + s : 0)) * C + c];"),
+    "canon_norm_squared": ("yt[h * D + e] /= den;", "yt[h * D + e] /= den * den;"),
     "softmax_decode_query_position": ("rope_vec(qi, D, (double)(cache_len - 1), theta);",
                                       "rope_vec(qi, D, (double)cache_len, theta);"),
 }
@@ -63,6 +67,7 @@ def test_pins_catch_planted_mistake(tmp_path, name):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_gdn.py"),
                         os.path.join(ROOT, "tests", "test_oracle_polar.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_baseline.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_baseline.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_canon.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
