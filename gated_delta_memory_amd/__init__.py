@@ -59,6 +59,7 @@ def _load() -> ctypes.CDLL:
         "atma_softmax_attn_fwd": ([vp] * 4 + [i] * 5 + [f, i, vp, sz, vp], i),
         "atma_softmax_attn_workspace_bytes": ([i] * 5 + [f], sz),
         "atma_softmax_attn_decode": ([vp] * 3 + [i, i, f, vp] + [i] * 5 + [vp, sz, vp], i),
+        "atma_canon": ([vp] * 5 + [i] * 6 + [f, i, vp], i),
         "atma_status_string": ([i], ctypes.c_char_p),
         "atma_version": ([], i),
     }
@@ -362,6 +363,23 @@ def atma_softmax_attn_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0, *, 
                                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check("atma_softmax_attn_decode", st)
     return o
+
+
+def atma_canon(x, w, state=None, *, residual=False, heads=0, eps=1e-6, update_state=True, y=None, stream=None):
+    """Canon prologue: x [B,T,C] bf16, w [K,C] fp32, state [B,K-1,C] bf16 or None (updated in
+    place with the last K-1 inputs when ``update_state``).  Returns y [B,T,C]."""
+    B, T, C = x.shape
+    K = w.shape[0]
+    if w.shape != (K, C) or (state is not None and state.shape != (B, K - 1, C)):
+        raise ValueError("inconsistent shapes")
+    _f32(w, "w")
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(x, w, state, y)
+    st = lib.atma_canon(_ptr(x), _ptr(w), _ptr(state), _ptr(state) if update_state else None, _ptr(y), B, T, C, K,
+                        int(bool(residual)), int(heads), float(eps), _dtype_code(x), _stream(stream))
+    _check("atma_canon", st)
+    return y
 
 
 def atma_polar_attn_workspace_bytes(B, T, Hq, D=64) -> int:

@@ -243,4 +243,20 @@ int atma_softmax_attn_decode(const void* q, const void* k_cache, const void* v_c
     return launched(atma::launch_polar_decode(a, (hipStream_t)stream));
 }
 
+int atma_canon(const void* x, const float* w, const void* state_in, void* state_out, void* y, int B, int T, int C,
+               int K, int residual, int heads, float eps, atma_dtype dt, void* stream) {
+    if (!x || !w || !y) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(T) || !pos(C) || K < 1 || K > 8 || heads < 0 || !(eps > 0.0f)) return ATMA_ERR_SHAPE;
+    if (x == y) return ATMA_ERR_SHAPE;  // out of place (a token's inputs are read by later tokens)
+    if (dt != ATMA_BF16 || C % 8 != 0) return ATMA_ERR_UNSUPPORTED;
+    if (heads > 0) {
+        if (C % heads != 0) return ATMA_ERR_SHAPE;
+        const int D = C / heads;
+        if (D % 8 != 0 || D > 512 || (D & (D - 1)) != 0) return ATMA_ERR_UNSUPPORTED;  // D / 8 lanes, a power of 2
+    }
+    if (!fits(B, T, C, 1) || !fits(B, K, C, 1)) return ATMA_ERR_SHAPE;
+    atma::CanonArgs a{x, w, state_in, state_out, y, B, T, C, K, residual ? 1 : 0, heads, eps};
+    return launched(atma::launch_canon(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -63,6 +63,19 @@ struct RopeArgs {
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
+// Canon prologue: depthwise causal convolution of x [B, T, C] (bf16) with w [K, C] (fp32),
+// optional residual and unit norm per head (heads > 0), state [B, K-1, C] in and out.
+struct CanonArgs {
+    const void* x;
+    const float* w;
+    const void* state_in;
+    void* state_out;
+    void* y;
+    int B, T, C, K, residual, heads;
+    float eps;
+};
+hipError_t launch_canon(const CanonArgs& a, hipStream_t stream);
+
 struct PolarDecodeArgs {
     const void *q, *k_cache, *v_cache;
     PolarParamsDev p;

@@ -231,6 +231,21 @@ int atma_softmax_attn_decode(const void* q, const void* k_cache, const void* v_c
                              int Lmax, float rope_theta, void* o, int B, int Hq, int Hkv, int D,
                              atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Canon prologue (Section 3.1: Canon depthwise causal convolutions on q, k and v before
+ * attention; the pages fix neither width, bias nor residual): per channel c,
+ *     y_t[c] = sum_{j<K} w[j][c] x_{t-j}[c]  (+ x_t[c] when residual != 0),
+ * inputs before the first token taken from state_in (the K-1 previous inputs, oldest first;
+ * zeros when NULL); then, when heads > 0, each head's D = C / heads channels are scaled to
+ * unit L2 norm, y / max(||y||, eps) (the memory path's unit-norm queries and keys).
+ *   x, y      [B, T, C] bf16 (y must not alias x);  w [K, C] fp32;  1 <= K <= 8;  C % 8 == 0
+ *   heads     0, or a divisor of C with D = C / heads a power of two in [8, 512]
+ *   state_in  [B, K-1, C] bf16 or NULL;  state_out [B, K-1, C] bf16 or NULL: receives the last
+ *             K-1 inputs (from state_in where T < K-1); it may alias state_in (decode: T = 1).
+ * ------------------------------------------------------------------------------- */
+int atma_canon(const void* x, const float* w, const void* state_in, void* state_out, void* y, int B, int T,
+               int C, int K, int residual, int heads, float eps, atma_dtype dt, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* atma_status_string(int status);
 

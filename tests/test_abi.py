@@ -203,6 +203,20 @@ def test_control_core_validation():
     assert d(FAKE, FAKE, FAKE, 8, 8, 0.0, FAKE, 1, 16, 16, 64, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_WORKSPACE
 
 
+def test_canon_validation():
+    c = g.lib.atma_canon
+    Y2 = ctypes.c_void_p(0x2000)  # output, distinct from the input
+    assert c(NULL, FAKE, NULL, NULL, Y2, 1, 8, 64, 4, 0, 0, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_NULL
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 64, 9, 0, 0, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE   # K > 8
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 64, 0, 0, 0, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 60, 4, 0, 0, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 64, 4, 0, 3, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE   # C % heads
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 96, 4, 0, 1, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 64, 4, 0, 0, 1e-6, g.ATMA_F32, NULL) == g.ATMA_ERR_UNSUPPORTED
+    assert c(FAKE, FAKE, NULL, NULL, Y2, 1, 8, 64, 4, 0, 0, 0.0, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE
+    assert c(FAKE, FAKE, NULL, NULL, FAKE, 1, 8, 64, 4, 0, 0, 1e-6, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE  # y == x
+
+
 def test_binding_rejects_host_tensors():
     import torch
 
