@@ -24,6 +24,10 @@ arXiv 2606.25156):
                          adjacent pairs of q and k by position * theta^(-2p/D).
 * ``canon``           - the Canon prologue (Section 3.1): depthwise causal convolution
                          over tokens, optional residual, optional unit L2 norm per head.
+* ``gdn_bwd``, ``polar_bwd`` - gradients of a loss through ``gdn_sequential`` and
+                         ``polar_fwd`` (the chain rule on the same definitions, in reverse;
+                         the paper's materialised path is its gradient reference too,
+                         Appendix C.2).
 """
 from __future__ import annotations
 
@@ -78,8 +82,11 @@ def _declare(lib):
     lib.oracle_softmax_attn.argtypes = [i, i, i, i, i, d, i, _dp, _dp, _dp, _dp, i]
     lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, i, _dp, _dp, _dp, _dp]
     lib.oracle_canon.argtypes = [i, i, i, i, i, i, d, _dp, _dp, _dp, _dp]
+    lib.oracle_gdn_bwd.argtypes = [i, i, i, i, i] + [_dp] * 6 + [_dp, _dp] + [_dp] * 6 + [i]
+    lib.oracle_polar_bwd.argtypes = [i, i, i, i, i] + [_dp] * 3 + [_dp] * 5 + [d, _dp] + [_dp] * 8 + [i]
     for f in ("oracle_gdn_sequential", "oracle_gdn_chunked", "oracle_polar_fwd", "oracle_polar_decode",
-              "oracle_threads_used", "oracle_rope", "oracle_softmax_attn", "oracle_softmax_decode", "oracle_canon"):
+              "oracle_threads_used", "oracle_rope", "oracle_softmax_attn", "oracle_softmax_decode", "oracle_canon",
+              "oracle_gdn_bwd", "oracle_polar_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -248,3 +255,47 @@ def canon(x, w, state=None, residual=False, heads=0, eps=1e-6):
     assert _load().oracle_canon(B, T, C, K, int(bool(residual)), int(heads), float(eps), _ptr(x), _ptr(w), _ptr(st),
                                 _ptr(y)) == 0
     return y
+
+
+# ----------------------------------------------------------------------------
+# gradients
+# ----------------------------------------------------------------------------
+def gdn_bwd(q, k, v, alpha, beta, do, init_state=None, dS_final=None, threads=0):
+    """Gradients through the token-by-token memory recurrence for upstream dO [B,T,H,Dv] (and
+    dS_final [B,H,Dv,Dk] on the final state, or None).  Returns dict dq, dk, dv, dalpha, dbeta,
+    dinit (the gradient on the initial state)."""
+    q, k, v, alpha, beta, init, (B, T, H, Dk, Dv) = _gdn_args(q, k, v, alpha, beta, init_state)
+    g = _f64(do)
+    assert g.shape == (B, T, H, Dv)
+    dsf = None if dS_final is None else _f64(dS_final)
+    out = {"dq": np.zeros((B, T, H, Dk)), "dk": np.zeros((B, T, H, Dk)), "dv": np.zeros((B, T, H, Dv)),
+           "dalpha": np.zeros((B, T, H)), "dbeta": np.zeros((B, T, H)), "dinit": np.zeros((B, H, Dv, Dk))}
+    rc = _load().oracle_gdn_bwd(B, T, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(init),
+                                _ptr(g), _ptr(dsf), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dinit"]), int(threads))
+    assert rc == 0
+    return out
+
+
+def polar_bwd(q, k, v, params, do, threads=0):
+    """Gradients of causal Polar attention (materialised form) for upstream dO [B,T,Hq,D].
+    Returns dict dq, dk, dv and d_temp_raw, d_null_slope_raw, d_null_bias, d_mag_beta [Hq],
+    d_v_null [Hq, D]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, T, Hkv, D) and v.shape == (B, T, Hkv, D)
+    g = _f64(do)
+    assert g.shape == q.shape
+    p = _params(params, Hq, D)
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v)}
+    for n in ("d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta"):
+        out[n] = np.zeros(Hq)
+    out["d_v_null"] = np.zeros((Hq, D))
+    rc = _load().oracle_polar_bwd(
+        B, T, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(p["temp_raw"]), _ptr(p["null_slope_raw"]),
+        _ptr(p["null_bias"]), _ptr(p["mag_beta"]), _ptr(p["v_null"]), p["eps"], _ptr(g), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["d_temp_raw"]), _ptr(out["d_null_slope_raw"]),
+        _ptr(out["d_null_bias"]), _ptr(out["d_mag_beta"]), _ptr(out["d_v_null"]), int(threads))
+    assert rc == 0
+    return out

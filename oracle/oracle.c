@@ -677,3 +677,288 @@ int oracle_canon(int B, int T, int C, int K, int residual, int H, double eps, co
     }
     return 0;
 }
+
+/* ========================================================================= */
+/* Backward: gradients of a scalar loss through the two definitions above     */
+/* ========================================================================= */
+/* The layer is trained end to end, and the paper's materialised path serves as the reference
+ * for its gradients as well as its outputs (Appendix C.2).  The gradients here are the chain
+ * rule applied to the forward definitions exactly as written above, one intermediate at a time,
+ * in reverse order.  Given the upstream
+ * gradient dO of the outputs (and optionally of the final memory state), every function returns
+ * the gradient of every input and parameter. */
+
+/* Gated-delta memory (Section 3.3 equation), reverse pass over the token-by-token recurrence.
+ * With u_t = S_{t-1} k_t and S_t = alpha_t (S_{t-1} - beta_t u_t k_t^T) + beta_t v_t k_t^T,
+ * o_t = S_t q_t, and G the gradient on S_t (dO_t q_t^T plus what flows back from S_{t+1}):
+ *   dq_t     = S_t^T dO_t
+ *   dv_t     = beta_t G k_t
+ *   dbeta_t  = (G k_t) . (v_t - alpha_t u_t)
+ *   dalpha_t = <G, S_{t-1}> - beta_t (G k_t) . u_t
+ *   dk_t     = beta_t G^T v_t - alpha_t beta_t (S_{t-1}^T (G k_t) + G^T u_t)
+ *   G_{t-1}  = alpha_t (G - beta_t (G k_t) k_t^T)
+ * Layouts as the forward; dS_final [B, H, Dv, Dk] or NULL (zero); d_init [B, H, Dv, Dk] or
+ * NULL (the gradient on the initial state, G_{-1}). */
+typedef struct {
+    gdn_ctx g;
+    const double *dO, *dSfin;
+    double *dq, *dk, *dv, *dalpha, *dbeta, *dinit;
+} gdn_bwd_ctx;
+
+static void gdn_bwd_task(long task, void* p) {
+    const gdn_bwd_ctx* bc = (const gdn_bwd_ctx*)p;
+    const gdn_ctx* c = &bc->g;
+    const int b = (int)(task / c->H), h = (int)(task % c->H);
+    const int Dk = c->Dk, Dv = c->Dv, H = c->H, T = c->T;
+    const size_t SS = (size_t)Dv * Dk;
+    /* forward, keeping every state: hist[t + 1] = S_t, hist[0] = initial state */
+    double* hist = (double*)calloc((size_t)(T + 1) * SS, sizeof(double));
+    double* G = (double*)calloc(SS, sizeof(double));
+    double* u = (double*)malloc(sizeof(double) * Dv);
+    double* Gk = (double*)malloc(sizeof(double) * Dv);
+    if (c->init) memcpy(hist, c->init + ((size_t)b * H + h) * SS, sizeof(double) * SS);
+#define TOKB(t) (((size_t)b * T + (t)) * H + h)
+    for (int t = 0; t < T; ++t) {
+        const double* Sp = hist + (size_t)t * SS;
+        double* Sn = hist + (size_t)(t + 1) * SS;
+        const double* kt = c->k + TOKB(t) * Dk;
+        const double* vt = c->v + TOKB(t) * Dv;
+        const double a = c->alpha[TOKB(t)], be = c->beta[TOKB(t)];
+        for (int r = 0; r < Dv; ++r) {
+            double s = 0.0;
+            for (int j = 0; j < Dk; ++j) s += Sp[r * Dk + j] * kt[j];
+            u[r] = s;
+        }
+        for (int r = 0; r < Dv; ++r)
+            for (int j = 0; j < Dk; ++j) Sn[r * Dk + j] = a * (Sp[r * Dk + j] - be * u[r] * kt[j]) + be * vt[r] * kt[j];
+    }
+    if (bc->dSfin) memcpy(G, bc->dSfin + ((size_t)b * H + h) * SS, sizeof(double) * SS);
+    for (int t = T - 1; t >= 0; --t) {
+        const double* Sp = hist + (size_t)t * SS;
+        const double* St = hist + (size_t)(t + 1) * SS;
+        const double* qt = c->q + TOKB(t) * Dk;
+        const double* kt = c->k + TOKB(t) * Dk;
+        const double* vt = c->v + TOKB(t) * Dv;
+        const double* gt = bc->dO + TOKB(t) * Dv;
+        const double a = c->alpha[TOKB(t)], be = c->beta[TOKB(t)];
+        /* o_t = S_t q_t */
+        for (int r = 0; r < Dv; ++r)
+            for (int j = 0; j < Dk; ++j) G[r * Dk + j] += gt[r] * qt[j];
+        double* dqt = bc->dq + TOKB(t) * Dk;
+        for (int j = 0; j < Dk; ++j) {
+            double s = 0.0;
+            for (int r = 0; r < Dv; ++r) s += St[r * Dk + j] * gt[r];
+            dqt[j] = s;
+        }
+        /* the update S_t = alpha (S_{t-1} - beta u k^T) + beta v k^T */
+        for (int r = 0; r < Dv; ++r) {
+            double s = 0.0, s2 = 0.0;
+            for (int j = 0; j < Dk; ++j) { s += Sp[r * Dk + j] * kt[j]; s2 += G[r * Dk + j] * kt[j]; }
+            u[r] = s;
+            Gk[r] = s2;
+        }
+        double db = 0.0, da = 0.0, gku = 0.0;
+        for (int r = 0; r < Dv; ++r) {
+            db += Gk[r] * (vt[r] - a * u[r]);
+            gku += Gk[r] * u[r];
+            for (int j = 0; j < Dk; ++j) da += G[r * Dk + j] * Sp[r * Dk + j];
+        }
+        bc->dbeta[TOKB(t)] = db;
+        bc->dalpha[TOKB(t)] = da - be * gku;
+        double* dvt = bc->dv + TOKB(t) * Dv;
+        for (int r = 0; r < Dv; ++r) dvt[r] = be * Gk[r];
+        double* dkt = bc->dk + TOKB(t) * Dk;
+        for (int j = 0; j < Dk; ++j) {
+            double gv = 0.0, sg = 0.0, gu = 0.0;
+            for (int r = 0; r < Dv; ++r) {
+                gv += G[r * Dk + j] * vt[r];
+                sg += Sp[r * Dk + j] * Gk[r];
+                gu += G[r * Dk + j] * u[r];
+            }
+            dkt[j] = be * gv - a * be * (sg + gu);
+        }
+        /* G_{t-1} = alpha (G - beta (G k) k^T) */
+        for (int r = 0; r < Dv; ++r)
+            for (int j = 0; j < Dk; ++j) G[r * Dk + j] = a * (G[r * Dk + j] - be * Gk[r] * kt[j]);
+    }
+    if (bc->dinit) memcpy(bc->dinit + ((size_t)b * H + h) * SS, G, sizeof(double) * SS);
+#undef TOKB
+    free(hist); free(G); free(u); free(Gk);
+}
+
+int oracle_gdn_bwd(int B, int T, int H, int Dk, int Dv,
+                   const double* q, const double* k, const double* v,
+                   const double* alpha, const double* beta, const double* init_state,
+                   const double* dO, const double* dS_final,
+                   double* dq, double* dk, double* dv, double* dalpha, double* dbeta, double* d_init,
+                   int nthreads) {
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || !q || !k || !v || !alpha || !beta || !dO) return -1;
+    if (!dq || !dk || !dv || !dalpha || !dbeta) return -1;
+    gdn_bwd_ctx bc = {{B, T, H, Dk, Dv, q, k, v, alpha, beta, init_state, NULL, NULL, NULL},
+                      dO, dS_final, dq, dk, dv, dalpha, dbeta, d_init};
+    run_tasks(gdn_bwd_task, &bc, (long)B * H, nthreads);
+    return 0;
+}
+
+/* Polar attention (Section 3.2 equation, Appendix C.2 single softmax, Appendix A.2 channels),
+ * one query row in reverse, with g = dO_i and the forward quantities recomputed as in
+ * polar_row_materialised (weights w_j, null weight w_0, real mass R, squared mass Q2 = sum w_j^2,
+ * m_eff = R^3 / Q2, mu, s, den = max(||s||, eps), c = s / den):
+ *   dmu = g . c,   dc = mu g
+ *   ds  = (dc - c (c . dc)) / den   when ||s|| > eps, else dc / eps
+ *   dm_eff = dmu (1 - mu^2) beta / (1 + m_eff);   dbeta += dmu (1 - mu^2) ln(1 + m_eff)
+ *   dR = dm_eff 3 R^2 / Q2;   dQ2 = -dm_eff R^3 / Q2^2
+ *   dw_j = dR + 2 w_j dQ2 + ds . v_j;   dw_0 = ds . v_null;   dv_j += w_j ds;   dv_null += w_0 ds
+ *   softmax: Sigma = sum_j w_j dw_j + w_0 dw_0;  dl_j = w_j (dw_j - Sigma);  dl_0 = w_0 (dw_0 - Sigma)
+ *   logits l_j = t (q . k_j) / sqrt(D):  dq += sum_j dl_j t k_j / sqrt(D);  dk_j += dl_j t q / sqrt(D)
+ *   dt = sum_j dl_j (q . k_j) / sqrt(D) + dl_0 nu;   dnu = dl_0 t      (null logit l_0 = t nu)
+ *   t = 1 + softplus(temp_raw) ln n:             dtemp_raw += dt ln(n) sigmoid(temp_raw)
+ *   nu = b + softplus(slope_raw) sqrt(ln(n+1)):  dnull_bias += dnu;  dslope_raw += dnu sqrt(ln(n+1)) sigmoid(slope_raw)
+ * dpar[0..3] accumulate dtemp_raw, dslope_raw, dnull_bias, dbeta of head h; dpar[4..4+D) dv_null. */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void polar_row_backward(const double* qi, const double* K, const double* V, size_t kstride, long n, int D,
+                               int h, const polar_par* P, const double* g, double* dqi, double* dK, double* dV,
+                               double* dpar, double* w, double* qk) {
+    const double a = softplus(P->temp_raw[h]);
+    const double sl = softplus(P->null_slope_raw[h]);
+    const double t = 1.0 + a * log((double)n);
+    const double nu = P->null_bias[h] + sl * sqrt(log((double)n + 1.0));
+    const double lnull = t * nu;
+    const double isd = 1.0 / sqrt((double)D);
+    const double* vn = P->v_null + (size_t)h * D;
+    /* forward recomputation */
+    double m = lnull;
+    for (long j = 0; j < n; ++j) {
+        double d = 0.0;
+        for (int x = 0; x < D; ++x) d += qi[x] * K[j * kstride + x];
+        qk[j] = d * isd;
+        w[j] = t * qk[j];
+        if (w[j] > m) m = w[j];
+    }
+    double Z = exp(lnull - m);
+    for (long j = 0; j < n; ++j) { w[j] = exp(w[j] - m); Z += w[j]; }
+    const double w0 = exp(lnull - m) / Z;
+    double R = 0.0, Q2 = 0.0;
+    for (long j = 0; j < n; ++j) { w[j] /= Z; R += w[j]; Q2 += w[j] * w[j]; }
+    const double me = R * R * R / Q2;
+    const double be = P->mag_beta[h];
+    const double mu = tanh(be * log1p(me));
+    double* s = (double*)malloc(sizeof(double) * D * 2);
+    double* ds = s + D;
+    double nrm2 = 0.0;
+    for (int x = 0; x < D; ++x) {
+        double acc = w0 * vn[x];
+        for (long j = 0; j < n; ++j) acc += w[j] * V[j * kstride + x];
+        s[x] = acc;
+        nrm2 += acc * acc;
+    }
+    const double nrm = sqrt(nrm2);
+    const int clamped = !(nrm > P->eps);
+    const double den = clamped ? P->eps : nrm;
+    /* channels */
+    double dmu = 0.0, cdc = 0.0;
+    for (int x = 0; x < D; ++x) dmu += g[x] * s[x] / den;
+    for (int x = 0; x < D; ++x) cdc += (s[x] / den) * (mu * g[x]);
+    for (int x = 0; x < D; ++x) ds[x] = (mu * g[x] - (clamped ? 0.0 : (s[x] / den) * cdc)) / den;
+    const double dme = dmu * (1.0 - mu * mu) * be / (1.0 + me);
+    dpar[3] += dmu * (1.0 - mu * mu) * log1p(me);
+    const double dR = dme * 3.0 * R * R / Q2;
+    const double dQ2 = -dme * R * R * R / (Q2 * Q2);
+    /* weights: dw_j kept in w's place after Sigma is formed */
+    double dw0 = 0.0;
+    for (int x = 0; x < D; ++x) dw0 += ds[x] * vn[x];
+    double Sig = w0 * dw0;
+    for (long j = 0; j < n; ++j) {
+        double dv = 0.0;
+        for (int x = 0; x < D; ++x) dv += ds[x] * V[j * kstride + x];
+        const double dwj = dR + 2.0 * w[j] * dQ2 + dv;
+        Sig += w[j] * dwj;
+        for (int x = 0; x < D; ++x) dV[j * kstride + x] += w[j] * ds[x];
+        qk[j + n] = dwj; /* second half of the scratch holds dw_j */
+    }
+    for (int x = 0; x < D; ++x) dpar[4 + x] += w0 * ds[x];
+    /* softmax and logits */
+    double dt = 0.0;
+    for (long j = 0; j < n; ++j) {
+        const double dl = w[j] * (qk[j + n] - Sig);
+        dt += dl * qk[j];
+        for (int x = 0; x < D; ++x) {
+            dqi[x] += dl * t * isd * K[j * kstride + x];
+            dK[j * kstride + x] += dl * t * isd * qi[x];
+        }
+    }
+    const double dl0 = w0 * (dw0 - Sig);
+    dt += dl0 * nu;
+    const double dnu = dl0 * t;
+    dpar[0] += dt * log((double)n) * sigmoid(P->temp_raw[h]);
+    dpar[1] += dnu * sqrt(log((double)n + 1.0)) * sigmoid(P->null_slope_raw[h]);
+    dpar[2] += dnu;
+    free(s);
+}
+
+typedef struct {
+    int B, T, Hq, Hkv, D;
+    const double *q, *k, *v, *dO;
+    polar_par P;
+    double *dq, *dk, *dv, *dpar; /* dpar [B, Hq, 4 + D] partials, summed over b afterwards */
+} polar_bwd_ctx;
+
+/* task = b * Hkv + hk: every query head of the group and every row, so that the task alone
+ * accumulates the key and value gradients of its (b, hk) */
+static void polar_bwd_task(long task, void* p) {
+    const polar_bwd_ctx* c = (const polar_bwd_ctx*)p;
+    const int b = (int)(task / c->Hkv), hk = (int)(task % c->Hkv);
+    const int D = c->D, G = c->Hq / c->Hkv;
+    const size_t stride = (size_t)c->Hkv * D;
+    const double* K = c->k + ((size_t)b * c->T * c->Hkv + hk) * D;
+    const double* V = c->v + ((size_t)b * c->T * c->Hkv + hk) * D;
+    double* dK = c->dk + ((size_t)b * c->T * c->Hkv + hk) * D;
+    double* dV = c->dv + ((size_t)b * c->T * c->Hkv + hk) * D;
+    double* w = (double*)malloc(sizeof(double) * (size_t)c->T);
+    double* qk = (double*)malloc(sizeof(double) * (size_t)c->T * 2);
+    for (long i = 0; i < c->T; ++i)
+        for (int x = 0; x < D; ++x) dK[i * stride + x] = dV[i * stride + x] = 0.0;
+    for (int h = hk * G; h < (hk + 1) * G; ++h)
+        for (long i = 0; i < c->T; ++i) {
+            const size_t row = ((size_t)b * c->T + i) * c->Hq + h;
+            double* dqi = c->dq + row * D;
+            for (int x = 0; x < D; ++x) dqi[x] = 0.0;
+            polar_row_backward(c->q + row * D, K, V, stride, i + 1, D, h, &c->P, c->dO + row * D, dqi, dK, dV,
+                               c->dpar + ((size_t)b * c->Hq + h) * (4 + D), w, qk);
+        }
+    free(w);
+    free(qk);
+}
+
+/* Gradients of causal Polar attention (materialised form) given dO [B, T, Hq, D].
+ * Outputs dq [B, T, Hq, D]; dk, dv [B, T, Hkv, D]; d_temp_raw, d_null_slope_raw, d_null_bias,
+ * d_mag_beta [Hq]; d_v_null [Hq, D]. */
+int oracle_polar_bwd(int B, int T, int Hq, int Hkv, int D, const double* q, const double* k, const double* v,
+                     const double* temp_raw, const double* null_slope_raw, const double* null_bias,
+                     const double* mag_beta, const double* v_null, double eps, const double* dO,
+                     double* dq, double* dk, double* dv, double* d_temp_raw, double* d_null_slope_raw,
+                     double* d_null_bias, double* d_mag_beta, double* d_v_null, int nthreads) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return -1;
+    if (!q || !k || !v || !temp_raw || !null_slope_raw || !null_bias || !mag_beta || !v_null || !dO) return -1;
+    if (!dq || !dk || !dv || !d_temp_raw || !d_null_slope_raw || !d_null_bias || !d_mag_beta || !d_v_null) return -1;
+    double* dpar = (double*)calloc((size_t)B * Hq * (4 + D), sizeof(double));
+    polar_bwd_ctx c = {B, T, Hq, Hkv, D, q, k, v, dO, {temp_raw, null_slope_raw, null_bias, mag_beta, v_null, eps},
+                       dq, dk, dv, dpar};
+    run_tasks(polar_bwd_task, &c, (long)B * Hkv, nthreads);
+    for (int h = 0; h < Hq; ++h) {
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int x = 0; x < D; ++x) d_v_null[(size_t)h * D + x] = 0.0;
+        for (int b = 0; b < B; ++b) {
+            const double* pp = dpar + ((size_t)b * Hq + h) * (4 + D);
+            for (int e = 0; e < 4; ++e) acc[e] += pp[e];
+            for (int x = 0; x < D; ++x) d_v_null[(size_t)h * D + x] += pp[4 + x];
+        }
+        d_temp_raw[h] = acc[0];
+        d_null_slope_raw[h] = acc[1];
+        d_null_bias[h] = acc[2];
+        d_mag_beta[h] = acc[3];
+    }
+    free(dpar);
+    return 0;
+}

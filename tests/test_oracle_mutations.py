@@ -17,7 +17,8 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 MUTANTS = {
     "gdn_erase_sign": ("S[r * Dk + j] - be * u[r] * kt[j]", "S[r * Dk + j] + be * u[r] * kt[j]"),
     "gdn_decay_first_term_only": ("a * (S[r * Dk + j] - be * u[r] * kt[j])", "(a * S[r * Dk + j] - be * u[r] * kt[j])"),
-    "gdn_write_transposed": ("+ be * vt[r] * kt[j]", "+ be * vt[j % Dv] * kt[r % Dk]"),
+    "gdn_write_transposed": ("S[r * Dk + j] - be * u[r] * kt[j]) + be * vt[r] * kt[j]",
+                             "S[r * Dk + j] - be * u[r] * kt[j]) + be * vt[j % Dv] * kt[r % Dk]"),
     "gdn_output_from_old_key": ("for (int j = 0; j < Dk; ++j) s += S[r * Dk + j] * qt[j];",
                                 "for (int j = 0; j < Dk; ++j) s += S[r * Dk + j] * kt[j];"),
     "gdn_chunk_decay_sign": ("val = c->beta[TOK(t0 + r)] * exp(g[r] - g[s]) * d;",
@@ -50,6 +51,19 @@ MUTANTS = {
     "canon_norm_squared": ("yt[h * D + e] /= den;", "yt[h * D + e] /= den * den;"),
     "softmax_decode_query_position": ("rope_vec(qi, D, (double)(cache_len - 1), theta);",
                                       "rope_vec(qi, D, (double)cache_len, theta);"),
+    "gdn_bwd_beta_sign": ("db += Gk[r] * (vt[r] - a * u[r]);", "db += Gk[r] * (vt[r] + a * u[r]);"),
+    "gdn_bwd_no_decay_of_state_grad": ("G[r * Dk + j] = a * (G[r * Dk + j] - be * Gk[r] * kt[j]);",
+                                       "G[r * Dk + j] = (G[r * Dk + j] - be * Gk[r] * kt[j]);"),
+    "gdn_bwd_dk_drops_term": ("dkt[j] = be * gv - a * be * (sg + gu);", "dkt[j] = be * gv - a * be * sg;"),
+    "gdn_bwd_dq_old_state": ("for (int r = 0; r < Dv; ++r) s += St[r * Dk + j] * gt[r];",
+                             "for (int r = 0; r < Dv; ++r) s += Sp[r * Dk + j] * gt[r];"),
+    "polar_bwd_no_q2_term": ("const double dwj = dR + 2.0 * w[j] * dQ2 + dv;", "const double dwj = dR + dv;"),
+    "polar_bwd_no_projection": ("ds[x] = (mu * g[x] - (clamped ? 0.0 : (s[x] / den) * cdc)) / den;",
+                                "ds[x] = mu * g[x] / den;"),
+    "polar_bwd_null_temperature": ("dt += dl0 * nu;", "dt += 0.0 * nu;"),
+    "polar_bwd_softplus_not_sigmoid": ("dpar[0] += dt * log((double)n) * sigmoid(P->temp_raw[h]);",
+                                       "dpar[0] += dt * log((double)n) * softplus(P->temp_raw[h]);"),
+    "polar_bwd_meff_power": ("const double dR = dme * 3.0 * R * R / Q2;", "const double dR = dme * 2.0 * R * R / Q2;"),
 }
 
 
@@ -68,6 +82,7 @@ def test_pins_catch_planted_mistake(tmp_path, name):
                         os.path.join(ROOT, "tests", "test_oracle_gdn.py"),
                         os.path.join(ROOT, "tests", "test_oracle_polar.py"),
                         os.path.join(ROOT, "tests", "test_oracle_baseline.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_canon.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_canon.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_grad.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
