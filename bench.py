@@ -255,6 +255,42 @@ def secondary(torch, atma, workloads):
                      "polar_mfma_frac": round(fl / (tq.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del p, o_p
         torch.cuda.empty_cache()
+    # training step of the Polar core (training forward + backward) at the 2K layer shapes; the
+    # backward's algorithmic work is the usual five products per visible (query, key) pair
+    # (S recomputed, dP, dV, dK, dQ): 10 D flop per pair per head
+    for (B, T, Hq, Hkv, D, name) in ((8, 2048, 16, 16, 64, "polar_train_layer_b8_t2k"),
+                                     (8, 2048, 8, 2, 128, "polar_train_d128_gqa_b8_t2k")):
+        p = workloads.make_polar_inputs(B, T, Hq, Hkv, D, device="cuda")
+        do = torch.randn(B, T, Hq, D, device="cuda").to(torch.bfloat16)
+        f = dict(dtype=torch.float32, device="cuda")
+        gout = {"dq": torch.empty_like(p["q"]), "dk": torch.empty_like(p["k"]), "dv": torch.empty_like(p["v"]),
+                "d_temp_raw": torch.empty(Hq, **f), "d_null_slope_raw": torch.empty(Hq, **f),
+                "d_null_bias": torch.empty(Hq, **f), "d_mag_beta": torch.empty(Hq, **f),
+                "d_v_null": torch.empty(Hq, D, **f)}
+        ws_b = torch.empty(int(atma.lib.atma_polar_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)), dtype=torch.uint8,
+                           device="cuda")
+        fw = {}
+        tf, tb = Timer(torch), Timer(torch)
+
+        def fwd_train():
+            fw["o"], fw["mu"], fw["st"], fw["dir"] = atma.atma_polar_attn_fwd_train(p["q"], p["k"], p["v"],
+                                                                                    p["params"])
+
+        def bwd():
+            atma.atma_polar_attn_bwd(p["q"], p["k"], p["v"], p["params"], fw["mu"], fw["st"], fw["dir"], do,
+                                     out=gout, workspace=ws_b)
+
+        for it in range(11):
+            (tf if it else (lambda fn: fn()))(fwd_train)
+            (tb if it else (lambda fn: fn()))(bwd)
+        torch.cuda.synchronize()
+        pairs = B * Hq * T * (T + 1) / 2
+        res[name] = {"fwd_train_ms": round(tf.mean_ms(), 4), "bwd_ms": round(tb.mean_ms(), 4),
+                     "bwd_TFLOPs": round(10 * D * pairs / (tb.mean_ms() * 1e-3) / 1e12, 2),
+                     "bwd_mfma_frac": round(10 * D * pairs / (tb.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "tokens_per_s": round(B * T / ((tf.mean_ms() + tb.mean_ms()) * 1e-3), 1)}
+        del p, do, gout, ws_b, fw
+        torch.cuda.empty_cache()
     # 64K prefill
     w = workloads.WORKLOADS["prefill_b1_t64k"]
     inp = workloads.make_workload(w, device="cuda")

@@ -37,6 +37,12 @@ class PolarParams(ctypes.Structure):
                 ("v_null", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
+class PolarParamGrads(ctypes.Structure):
+    """Mirror of ``atma_polar_param_grads`` (host struct of device pointers, fp32 outputs)."""
+    _fields_ = [("temp_raw", ctypes.c_void_p), ("null_slope_raw", ctypes.c_void_p),
+                ("null_bias", ctypes.c_void_p), ("mag_beta", ctypes.c_void_p), ("v_null", ctypes.c_void_p)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libatma.so is not built at {LIB_PATH}; run `python gated_delta_memory_amd/_build.py` "
@@ -60,6 +66,10 @@ def _load() -> ctypes.CDLL:
         "atma_softmax_attn_workspace_bytes": ([i] * 5 + [f], sz),
         "atma_softmax_attn_decode": ([vp] * 3 + [i, i, f, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_canon": ([vp] * 5 + [i] * 6 + [f, i, vp], i),
+        "atma_polar_attn_fwd_train": ([vp, vp, vp, P, vp, vp, vp, vp] + [i] * 6 + [vp], i),
+        "atma_polar_attn_bwd": ([vp, vp, vp, P] + [vp] * 7 + [ctypes.POINTER(PolarParamGrads)] + [i] * 6
+                                + [vp, sz, vp], i),
+        "atma_polar_attn_bwd_workspace_bytes": ([i] * 5, sz),
         "atma_status_string": ([i], ctypes.c_char_p),
         "atma_version": ([], i),
     }
@@ -233,6 +243,57 @@ def atma_polar_attn_fwd(q, k, v, params, *, o=None, mu_out=None, meff_out=None, 
                                  _ptr(meff_out), B, T, Hq, Hkv, D, _dtype_code(q), None, 0, _stream(stream))
     _check("atma_polar_attn_fwd", st)
     return o, mu_out, meff_out
+
+
+def atma_polar_attn_fwd_train(q, k, v, params, *, stream=None):
+    """Training forward of causal Polar attention.  q [B,T,Hq,D], k, v [B,T,Hkv,D] bf16.
+    Returns (o, mu [B,Hq,T], stats [B,Hq,T,4], dir [B,T,Hq,D]) -- the last three are what
+    ``atma_polar_attn_bwd`` reads."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    o = torch.empty_like(q)
+    mu = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    stats = torch.empty(B, Hq, T, 4, dtype=torch.float32, device=q.device)
+    dirn = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    _dev(q, k, v)
+    p = polar_params_struct(params)
+    st = lib.atma_polar_attn_fwd_train(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(o), _ptr(mu), _ptr(stats),
+                                       _ptr(dirn), B, T, Hq, Hkv, D, _dtype_code(q), _stream(stream))
+    _check("atma_polar_attn_fwd_train", st)
+    return o, mu, stats, dirn
+
+
+def atma_polar_attn_bwd(q, k, v, params, mu, stats, dirn, do, *, out=None, workspace=None, stream=None):
+    """Gradients of causal Polar attention for upstream ``do`` [B,T,Hq,D] bf16, from the training
+    forward's (mu, stats, dir).  Returns dict dq, dk, dv (bf16, shaped as q, k, v) and d_temp_raw,
+    d_null_slope_raw, d_null_bias, d_mag_beta [Hq], d_v_null [Hq, D] (fp32).  ``out`` may supply
+    that dict's tensors."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, D) or v.shape != k.shape or do.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if mu.shape != (B, Hq, T) or stats.shape != (B, Hq, T, 4) or dirn.shape != (B, T, Hq, D):
+        raise ValueError("mu / stats / dir do not match the training forward's shapes")
+    if out is None:
+        f = dict(dtype=torch.float32, device=q.device)
+        out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+               "d_temp_raw": torch.empty(Hq, **f), "d_null_slope_raw": torch.empty(Hq, **f),
+               "d_null_bias": torch.empty(Hq, **f), "d_mag_beta": torch.empty(Hq, **f),
+               "d_v_null": torch.empty(Hq, D, **f)}
+    if workspace is None:
+        workspace = torch.empty(lib.atma_polar_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8,
+                                device=q.device)
+    _dev(q, k, v, mu, stats, dirn, do, workspace, *out.values())
+    p = polar_params_struct(params)
+    g = PolarParamGrads(out["d_temp_raw"].data_ptr(), out["d_null_slope_raw"].data_ptr(),
+                        out["d_null_bias"].data_ptr(), out["d_mag_beta"].data_ptr(), out["d_v_null"].data_ptr())
+    st = lib.atma_polar_attn_bwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(mu), _ptr(stats), _ptr(dirn),
+                                 _ptr(do), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), ctypes.byref(g), B, T,
+                                 Hq, Hkv, D, _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("atma_polar_attn_bwd", st)
+    return out
 
 
 def atma_polar_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, params, *, o=None, want_mu=False, stream=None):

@@ -127,6 +127,47 @@ int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_
     return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
 }
 
+int atma_polar_attn_fwd_train(const void* q, const void* k, const void* v, const atma_polar_params* p, void* o,
+                              float* mu_out, float* stats, float* dir, int B, int T, int Hq, int Hkv, int D,
+                              atma_dtype dt, void* stream) {
+    if (!q || !k || !v || !o || !mu_out || !stats || !dir) return ATMA_ERR_NULL;
+    const int pc = check_params(p);
+    if (pc != ATMA_OK) return pc;
+    if (!(p->eps > 0.0f)) return ATMA_ERR_SHAPE;
+    if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D)) return ATMA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if ((D != 64 && D != 128) || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, Hq, D) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    atma::PolarFwdArgs a{q, k, v, dev_params(p), o, mu_out, nullptr, B, T, Hq, Hkv, D};
+    a.stats = stats;
+    a.dir = dir;
+    return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
+}
+
+size_t atma_polar_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D) {
+    if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !head_width_ok(D) || !fits(B, T, Hq, D)) return 0;
+    return atma::polar_bwd_workspace_bytes(B, T, Hq, D);
+}
+
+int atma_polar_attn_bwd(const void* q, const void* k, const void* v, const atma_polar_params* p, const float* mu,
+                        const float* stats, const float* dir, const void* dO, void* dq, void* dk, void* dv,
+                        const atma_polar_param_grads* dp, int B, int T, int Hq, int Hkv, int D, atma_dtype dt,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !mu || !stats || !dir || !dO || !dq || !dk || !dv || !dp) return ATMA_ERR_NULL;
+    if (!dp->temp_raw || !dp->null_slope_raw || !dp->null_bias || !dp->mag_beta || !dp->v_null) return ATMA_ERR_NULL;
+    const int pc = check_params(p);
+    if (pc != ATMA_OK) return pc;
+    if (!(p->eps > 0.0f)) return ATMA_ERR_SHAPE;
+    if (!pos(B) || !pos(T) || !pos(Hq) || !pos(Hkv) || !pos(D)) return ATMA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if ((D != 64 && D != 128) || dt != ATMA_BF16) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, Hq, D) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    if (!workspace || ws_bytes < atma::polar_bwd_workspace_bytes(B, T, Hq, D)) return ATMA_ERR_WORKSPACE;
+    atma::PolarBwdArgs a{q, k, v, dO, dev_params(p), mu, stats, dir, dq, dk, dv, dp->temp_raw, dp->null_slope_raw,
+                         dp->null_bias, dp->mag_beta, dp->v_null, B, T, Hq, Hkv, D, workspace};
+    return launched(atma::launch_polar_bwd(a, (hipStream_t)stream));
+}
+
 int atma_polar_attn_fwd_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens, int nseq,
                                int max_seqlen, const atma_polar_params* p, void* o, float* mu_out, float* meff_out,
                                int total_T, int Hq, int Hkv, int D, atma_dtype dt, void* stream) {

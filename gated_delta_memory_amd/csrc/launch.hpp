@@ -51,8 +51,25 @@ struct PolarFwdArgs {
     // plain causal softmax attention (the NoPE / RoPE control core): no temperature, no null,
     // output sum_j w_j v_j; p, mu_out and meff_out unused
     bool softmax = false;
+    // training outputs (Polar only, NULL when not wanted): per row {lse2, real mass, squared
+    // mass, normaliser} [B, Hq, T, 4] and the direction c [B, T, Hq, D], both fp32
+    float* stats = nullptr;
+    float* dir = nullptr;
 };
 hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream);
+
+// Backward of causal Polar attention (fixed-length batches), from the forward's training outputs.
+struct PolarBwdArgs {
+    const void *q, *k, *v, *dO;
+    PolarParamsDev p;
+    const float *mu, *stats, *dir;
+    void *dq, *dk, *dv;
+    float *d_temp_raw, *d_null_slope_raw, *d_null_bias, *d_mag_beta, *d_v_null;
+    int B, T, Hq, Hkv, D;
+    void* workspace;
+};
+size_t polar_bwd_workspace_bytes(int B, int T, int Hq, int D);
+hipError_t launch_polar_bwd(const PolarBwdArgs& a, hipStream_t stream);
 
 // Rotary embedding of x [B, T, H, D] (bf16) into y: row t at position pos0 + t.
 struct RopeArgs {

@@ -108,7 +108,8 @@ template <int D, bool POLAR>
 __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, PolarParamsDev prm,
                                                           bf16* __restrict__ o, float* __restrict__ mu_out,
-                                                          float* __restrict__ meff_out, int Tmax, int Hq, int Hkv,
+                                                          float* __restrict__ meff_out, float* __restrict__ stats,
+                                                          float* __restrict__ dir, int Tmax, int Hq, int Hkv,
                                                           int paired, const int* __restrict__ cu, int total) {
     // Work items.  With `paired` set (few tiles in all), a workgroup computes two query tiles
     // of one (batch, head), tile nqt - 1 - p and tile p: every pair streams the same number of
@@ -363,6 +364,27 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
             if (mu_out) mu_out[si] = mu;
             if (meff_out) meff_out[si] = meff;
         }
+        if (stats) {  // training: what the backward pass reads instead of recomputing the row
+            const float nrm = sqrtf(nrm2);
+            if (G2 == 0) {
+                // base-2 log partition in the scaled logit units (weight = exp2(cq q.k - lse2)), real
+                // mass, squared mass of the normalised weights, and the normaliser (negative when
+                // the eps clamp was taken)
+                const f32x4 st = {Ms + fast_log2(Z), Ls * invZ, Q2 * f * f * invZ * invZ, nrm > prm.eps ? nrm : -prm.eps};
+                *(f32x4*)(stats + (mu_base + qi) * 4) = st;
+            }
+            const float invden = 1.0f / fmaxf(nrm, prm.eps);
+            float* drow = dir + (seq0 + qi) * qstride + (size_t)h * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 y;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) y[x] = oacc[dt][4 * g + x] * invden;
+                    *(f32x4*)(drow + 32 * dt + 8 * g + 4 * G2) = y;
+                }
+        }
     }
   };
 
@@ -385,8 +407,8 @@ hipError_t launch_polar_fwd(const PolarFwdArgs& a, hipStream_t stream) {
 #define ATMA_PF_LAUNCH(DD, POL)                                                                            \
     hipLaunchKernelGGL((polar_fwd_kernel<DD, POL>), dim3(per_bh * a.Hq * a.B), dim3(NT), 0, stream,        \
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.p, (bf16*)a.o,               \
-                       POL ? a.mu_out : nullptr, POL ? a.meff_out : nullptr, a.T, a.Hq, a.Hkv, paired, a.cu, \
-                       a.total)
+                       POL ? a.mu_out : nullptr, POL ? a.meff_out : nullptr, POL ? a.stats : nullptr,         \
+                       POL ? a.dir : nullptr, a.T, a.Hq, a.Hkv, paired, a.cu, a.total)
     if (a.D == 64) {
         if (a.softmax) ATMA_PF_LAUNCH(64, false);
         else ATMA_PF_LAUNCH(64, true);

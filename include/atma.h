@@ -143,6 +143,57 @@ int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_
 size_t atma_polar_attn_workspace_bytes(int B, int T, int Hq, int D);
 
 /* ---------------------------------------------------------------------------------
+ * Causal Polar attention, training forward: the operation of atma_polar_attn_fwd, also writing
+ * what atma_polar_attn_bwd reads (the layer is trained end to end; the backward recomputes
+ * the weights from these instead of storing the T x T matrix, as the streaming form of
+ * Appendix C.3 does for the forward).
+ *   q, k, v, o as atma_polar_attn_fwd;  mu_out [B, Hq, T] fp32 (required)
+ *   stats    [B, Hq, T, 4] fp32: per row {lse2, R, Q2, den}: lse2 = log2 of the softmax
+ *            partition (real keys and null) in units where weight_j = exp2(t log2(e) q.k_j /
+ *            sqrt(D) - lse2); R = real mass; Q2 = sum_j w_j^2; den = ||s|| when ||s|| > eps,
+ *            else -eps (the clamp was taken)
+ *   dir      [B, T, Hq, D] fp32: the direction c = s / max(||s||, eps)
+ *   D in {64, 128}, dt == ATMA_BF16, eps > 0.  No workspace.
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_fwd_train(const void* q, const void* k, const void* v, const atma_polar_params* p,
+                              void* o, float* mu_out, float* stats, float* dir, int B, int T, int Hq,
+                              int Hkv, int D, atma_dtype dt, void* stream);
+
+/* Gradients of the per-head Polar parameters (DEVICE pointers, fp32, written, not accumulated):
+ * temp_raw, null_slope_raw, null_bias, mag_beta [Hq]; v_null [Hq * D]. */
+typedef struct {
+    float* temp_raw;
+    float* null_slope_raw;
+    float* null_bias;
+    float* mag_beta;
+    float* v_null;
+} atma_polar_param_grads;
+
+/* ---------------------------------------------------------------------------------
+ * Causal Polar attention, backward: gradients of a loss L through o = atma_polar_attn_fwd(...),
+ * given dO = dL/do.  The chain rule on the definitions above (Section 3.2 equation, Appendix
+ * C.2 single softmax, Appendix A.2 channels): with w the weights of row i, R, Q2, m_eff = R^3 / Q2,
+ * mu, s, c and den as in the forward,
+ *   dmu = dO . c;  ds = mu (dO - [||s|| > eps] dmu c) / den;  dm_eff = dmu (1 - mu^2) beta / (1 + m_eff)
+ *   dl_j = w_j (ds . v_j + dR + 2 w_j dQ2 - Sigma) with dR = 3 dm_eff m_eff / R,
+ *   dQ2 = -dm_eff m_eff / Q2, Sigma = dR R + 2 dQ2 Q2 + ds . s;  the null logit likewise;
+ *   dq = t / sqrt(D) sum_j dl_j k_j;  dk_j, dv_j summed over every query (and query head) that
+ *   sees key j;  the parameter gradients summed over every row of the batch.
+ *   q, k, v   the forward's inputs;  mu, stats, dir  the outputs of atma_polar_attn_fwd_train
+ *   dO        [B, T, Hq, D] bf16
+ *   dq        [B, T, Hq, D] bf16;  dk, dv [B, T, Hkv, D] bf16 (written, not accumulated)
+ *   dp        parameter gradients (written)
+ *   workspace at least atma_polar_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) bytes.
+ *   D in {64, 128}, dt == ATMA_BF16, eps > 0.  The result is deterministic (no atomics).
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_bwd(const void* q, const void* k, const void* v, const atma_polar_params* p,
+                        const float* mu, const float* stats, const float* dir, const void* dO, void* dq,
+                        void* dk, void* dv, const atma_polar_param_grads* dp, int B, int T, int Hq,
+                        int Hkv, int D, atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
+
+size_t atma_polar_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D);
+
+/* ---------------------------------------------------------------------------------
  * Causal Polar attention, prefill of a packed batch: nseq sequences of different lengths
  * concatenated along the token axis (no padding).  Same operation as atma_polar_attn_fwd
  * within each sequence (n = i + 1 for the sequence's own query i; no attention across

@@ -94,3 +94,25 @@ def sample_rows(T: int, seed: int = 0, n_random: int = 24, tile: int = 256, chun
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, T, size=n_random).tolist())
     return sorted(r for r in rows if 0 <= r < T)
+
+
+def rel_err_max(got, ref) -> float:
+    """max |got - ref| / max |ref|: the error against the tensor's own scale.
+
+    For gradients, whose elements are heavy-tailed (the largest 10-20 times the RMS) and each a
+    sum whose terms are set by the largest products of its row, bf16 arithmetic leaves an absolute
+    error proportional to that scale; an RMS-normalised maximum would charge it 10-20 times."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    m = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got - ref))) / m if m > 0 else float(np.max(np.abs(got)))
+
+
+def rel_err_fro(got, ref) -> float:
+    """||got - ref||_F / ||ref||_F."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    n = float(np.linalg.norm(ref))
+    return float(np.linalg.norm(got - ref)) / n if n > 0 else float(np.linalg.norm(got))

@@ -1,0 +1,113 @@
+"""GPU parity of the Polar attention backward (atma_polar_attn_fwd_train + atma_polar_attn_bwd)
+against the fp64 oracle's gradients (``oracle.polar_bwd``, pinned by finite differences).
+
+Every element of dq, dk, dv and of the parameter gradients is compared on the same seeded bf16
+inputs and a seeded bf16 upstream gradient, by two measures: max |gpu - oracle| / max |oracle|
+<= 2e-2 (each tensor against its own scale) and ||gpu - oracle||_F / ||oracle||_F <= 1e-2.
+
+Why not the forward's max |error| / rms: the gradients are heavy-tailed (the largest elements are
+10-20 times the RMS) and each element is a sum over keys or queries whose terms are set by the
+largest products of its row, so bf16 arithmetic leaves an absolute error proportional to the
+tensor's top scale.  The backward contracts on bf16 MFMA with three intermediates rounded to bf16
+in series (the direction-sum gradient ds, the weights for dV, the logit gradient for dq and dk,
+each to 2^-9 relative) on top of the forward's own bf16-level direction and magnitude; measured on
+these cases that gives a Frobenius error of about 3e-3 (1.5 x 2^-9) and a max error of 4-6e-3 of
+the top scale -- but 4-12e-2 of the RMS, growing with T as the tails do.  The budgets above leave a
+factor three; a missing or wrong term moves either measure by O(1).
+Cases span several
+128-query / 128-key tiles with ragged tails, one and several query heads per kv head, head
+widths 64 and 128, a single-token sequence, and the clamped direction normaliser.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import note, rel_err_fro, rel_err_max, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_FRO = 2e-2, 1e-2
+
+
+@pytest.fixture(scope="module")
+def atma():
+    import gated_delta_memory_amd as g
+
+    assert torch.cuda.is_available()
+    return g
+
+
+def _run(atma, inp, do, eps=None):
+    p = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp["params"].items()}
+    if eps is not None:
+        p["eps"] = eps
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    o, mu, stats, dirn = atma.atma_polar_attn_fwd_train(q, k, v, p)
+    g = atma.atma_polar_attn_bwd(q, k, v, p, mu, stats, dirn, do.cuda())
+    torch.cuda.synchronize()
+    return o, mu, g
+
+
+def _case(B, T, Hq, Hkv, D, seed):
+    inp = workloads.make_polar_inputs(B, T, Hq, Hkv, D, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn(B, T, Hq, D, generator=gen).to(torch.bfloat16)
+    return inp, do
+
+
+def _check(atma, B, T, Hq, Hkv, D, seed, eps=None):
+    inp, do = _case(B, T, Hq, Hkv, D, seed)
+    o, mu, g = _run(atma, inp, do, eps)
+    cp = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp["params"].items()}
+    if eps is not None:
+        cp["eps"] = eps
+    ref = oracle.polar_bwd(inp["q"], inp["k"], inp["v"], cp, do)
+    names = ("dq", "dk", "dv", "d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta", "d_v_null")
+    emax = {n: rel_err_max(to_np(g[n]), ref[n]) for n in names}
+    efro = {n: rel_err_fro(to_np(g[n]), ref[n]) for n in names}
+    note(f"  polar bwd B{B} T{T} Hq{Hq} Hkv{Hkv} D{D}: " +
+         " ".join(f"{n}={emax[n]:.1e}/{efro[n]:.1e}" for n in names))
+    bad = {n: (emax[n], efro[n]) for n in names if not (emax[n] <= TOL_MAX and efro[n] <= TOL_FRO)}
+    assert not bad, bad
+    return o, mu
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D", [(1, 1, 1, 1, 64), (1, 77, 2, 2, 64), (2, 300, 4, 2, 64),
+                                          (1, 513, 3, 1, 64), (2, 256, 2, 2, 64), (1, 200, 8, 2, 128),
+                                          (1, 640, 2, 2, 128), (2, 129, 4, 4, 128), (1, 2048, 4, 2, 64),
+                                          (1, 1024, 8, 2, 128)])
+def test_polar_bwd_matches_oracle(atma, B, T, Hq, Hkv, D):
+    _check(atma, B, T, Hq, Hkv, D, seed=1000 + T + Hq + D)
+
+
+def test_polar_bwd_clamped_normaliser(atma):
+    """eps above every ||s||: the direction gradient has no projection term."""
+    _check(atma, 1, 150, 2, 1, 64, seed=77, eps=30.0)
+
+
+def test_polar_train_forward_matches_inference_forward(atma):
+    """The training forward writes the same o and mu as the inference forward (bitwise), a unit
+    direction whose scaling by mu is o, and row statistics consistent with m_eff = R^3 / Q2."""
+    inp = workloads.make_polar_inputs(2, 333, 4, 2, 64, seed=5)
+    p = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp["params"].items()}
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    o1, mu1, meff1 = atma.atma_polar_attn_fwd(q, k, v, p, want_mu=True)
+    o2, mu2, stats, dirn = atma.atma_polar_attn_fwd_train(q, k, v, p)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(mu1, mu2)
+    d = to_np(dirn)
+    np.testing.assert_allclose(np.linalg.norm(d, axis=-1), 1.0, rtol=1e-5)
+    np.testing.assert_allclose(d * to_np(mu2).transpose(0, 2, 1)[..., None], to_np(o2), atol=8e-3)
+    st = to_np(stats)
+    np.testing.assert_allclose(st[..., 1] ** 3 / st[..., 2], to_np(meff1), rtol=1e-4)
+    assert np.all(st[..., 1] > 0) and np.all(st[..., 1] <= 1 + 1e-6) and np.all(st[..., 3] > 0)
+
+
+def test_polar_bwd_is_deterministic(atma):
+    inp, do = _case(2, 300, 4, 2, 64, seed=9)
+    _, _, g1 = _run(atma, inp, do)
+    _, _, g2 = _run(atma, inp, do)
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
