@@ -203,6 +203,34 @@ def test_control_core_validation():
     assert d(FAKE, FAKE, FAKE, 8, 8, 0.0, FAKE, 1, 16, 16, 64, g.ATMA_BF16, NULL, 0, NULL) == g.ATMA_ERR_WORKSPACE
 
 
+def test_polar_train_and_backward_validation():
+    pp = ctypes.byref(_params())
+    ft = g.lib.atma_polar_attn_fwd_train
+    assert ft(FAKE, FAKE, FAKE, pp, FAKE, FAKE, FAKE, NULL, 1, 16, 4, 2, 64, g.ATMA_BF16, NULL) == g.ATMA_ERR_NULL
+    assert ft(FAKE, FAKE, FAKE, ctypes.byref(_params(eps=0.0)), FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 2, 64, g.ATMA_BF16,
+              NULL) == g.ATMA_ERR_SHAPE  # the backward needs eps > 0
+    assert ft(FAKE, FAKE, FAKE, pp, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 3, 64, g.ATMA_BF16, NULL) == g.ATMA_ERR_SHAPE
+    assert ft(FAKE, FAKE, FAKE, pp, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 2, 96, g.ATMA_BF16, NULL) == g.ATMA_ERR_UNSUPPORTED
+    grads = g.PolarParamGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    bad = g.PolarParamGrads(0x1000, 0x1000, None, 0x1000, 0x1000)
+    b = g.lib.atma_polar_attn_bwd
+
+    def call(gr=grads, dO=FAKE, B=1, T=16, Hq=4, Hkv=2, D=64, dt=g.ATMA_BF16, ws=FAKE, wsb=1 << 30, p=pp):
+        return b(FAKE, FAKE, FAKE, p, FAKE, FAKE, FAKE, dO, FAKE, FAKE, FAKE, ctypes.byref(gr), B, T, Hq, Hkv, D, dt,
+                 ws, wsb, NULL)
+
+    assert call(dO=NULL) == g.ATMA_ERR_NULL
+    assert call(gr=bad) == g.ATMA_ERR_NULL
+    assert call(T=0) == g.ATMA_ERR_SHAPE
+    assert call(Hq=4, Hkv=3) == g.ATMA_ERR_SHAPE
+    assert call(D=32) == g.ATMA_ERR_UNSUPPORTED
+    assert call(dt=g.ATMA_F32) == g.ATMA_ERR_UNSUPPORTED
+    assert call(ws=NULL) == g.ATMA_ERR_WORKSPACE
+    need = g.lib.atma_polar_attn_bwd_workspace_bytes(1, 16, 4, 2, 64)
+    assert need > 0 and call(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
+    assert g.lib.atma_polar_attn_bwd_workspace_bytes(1, 16, 4, 2, 96) == 0
+
+
 def test_canon_validation():
     c = g.lib.atma_canon
     Y2 = ctypes.c_void_p(0x2000)  # output, distinct from the input
