@@ -291,6 +291,21 @@ def secondary(torch, atma, workloads):
                      "tokens_per_s": round(B * T / ((tf.mean_ms() + tb.mean_ms()) * 1e-3), 1)}
         del p, do, gout, ws_b, fw
         torch.cuda.empty_cache()
+    # memory backward at the 2K layer shape (B=8, H=8, d=128, bf16 inputs, fp32 arithmetic)
+    w = workloads.WORKLOADS["layer_b8_t2k"]
+    g = workloads.make_workload(w, device="cuda")["gdn"]
+    do = torch.randn_like(g["v"])
+    ws_gb = torch.empty(int(atma.lib.atma_gdn_bwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D, 64, 1)),
+                        dtype=torch.uint8, device="cuda")
+    tgb = Timer(torch)
+    for it in range(6):
+        (tgb if it else (lambda fn: fn()))(lambda: atma.atma_gdn_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], do,
+                                                                     workspace=ws_gb))
+    torch.cuda.synchronize()
+    res["gdn_train_" + w.name] = {"bwd_ms": round(tgb.mean_ms(), 4),
+                                  "workspace_MB": round(ws_gb.numel() / 2 ** 20, 1)}
+    del g, do, ws_gb
+    torch.cuda.empty_cache()
     # 64K prefill
     w = workloads.WORKLOADS["prefill_b1_t64k"]
     inp = workloads.make_workload(w, device="cuda")

@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "atma_polar_attn_bwd": ([vp, vp, vp, P] + [vp] * 7 + [ctypes.POINTER(PolarParamGrads)] + [i] * 6
                                 + [vp, sz, vp], i),
         "atma_polar_attn_bwd_workspace_bytes": ([i] * 5, sz),
+        "atma_gdn_bwd": ([vp] * 14 + [i] * 7 + [vp, sz, vp], i),
+        "atma_gdn_bwd_workspace_bytes": ([i] * 7, sz),
         "atma_status_string": ([i], ctypes.c_char_p),
         "atma_version": ([], i),
     }
@@ -209,7 +211,38 @@ def atma_gdn_decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
     return o
 
 
+def atma_gdn_bwd(q, k, v, alpha, beta, do, *, init_state=None, dS_final=None, want_dinit=False, workspace=None,
+                 stream=None):
+    """Gradients of the chunked memory prefill for upstream ``do`` [B,T,H,Dv] (and ``dS_final``
+    [B,H,Dv,Dk] fp32 on the final state).  Returns dict dq, dk, dv (input dtype), dalpha, dbeta
+    [B,T,H] fp32 and dinit [B,H,Dv,Dk] fp32 (None unless ``want_dinit``)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, Dv) or do.shape != v.shape:
+        raise ValueError("inconsistent shapes")
+    if alpha.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("alpha / beta must be [B, T, H]")
+    for t, n in ((alpha, "alpha"), (beta, "beta"), (init_state, "init_state"), (dS_final, "dS_final")):
+        _f32(t, n)
+    dt = _dtype_code(q)
+    f = dict(dtype=torch.float32, device=q.device)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dalpha": torch.empty(B, T, H, **f), "dbeta": torch.empty(B, T, H, **f),
+           "dinit": torch.empty(B, H, Dv, Dk, **f) if want_dinit else None}
+    if workspace is None:
+        workspace = torch.empty(lib.atma_gdn_bwd_workspace_bytes(B, T, H, Dk, Dv, 64, dt), dtype=torch.uint8,
+                                device=q.device)
+    _dev(q, k, v, alpha, beta, do, init_state, dS_final, workspace, *[x for x in out.values() if x is not None])
+    st = lib.atma_gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(init_state), _ptr(do),
+                          _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                          _ptr(out["dbeta"]), _ptr(out["dinit"]), B, T, H, Dk, Dv, 64, dt, _ptr(workspace),
+                          workspace.numel(), _stream(stream))
+    _check("atma_gdn_bwd", st)
+    return out
+
+
 # ------------------------------------------------------------------------------------
+# Polar attention# ------------------------------------------------------------------------------------
 # Polar attention
 # ------------------------------------------------------------------------------------
 def polar_params_struct(params: dict) -> PolarParams:

@@ -18,7 +18,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libatma.so")
 
 SOURCES = ["atma_api.cpp", "gdn_fwd.hip", "gdn_fwd_bf16.hip", "gdn_decode.hip", "polar_fwd.hip", "polar_decode.hip",
-           "rope.hip", "canon.hip", "polar_bwd.hip"]
+           "rope.hip", "canon.hip", "polar_bwd.hip", "gdn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are switched off for all device code.

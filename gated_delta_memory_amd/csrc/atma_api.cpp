@@ -127,6 +127,27 @@ int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_
     return launched(atma::launch_polar_fwd(a, (hipStream_t)stream));
 }
 
+size_t atma_gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt) {
+    if (!pos(B) || !pos(T) || !pos(H) || !head_width_ok(Dk) || !head_width_ok(Dv) || chunk != 64) return 0;
+    if (dt != ATMA_BF16 && dt != ATMA_F32) return 0;
+    return atma::gdn_bwd_workspace_bytes(B, T, H, Dk, Dv);
+}
+
+int atma_gdn_bwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                 const float* init_state, const void* dO, const float* dS_final, void* dq, void* dk, void* dv,
+                 float* dalpha, float* dbeta, float* d_init, int B, int T, int H, int Dk, int Dv, int chunk,
+                 atma_dtype dt, void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta) return ATMA_ERR_NULL;
+    if (!pos(B) || !pos(T) || !pos(H) || !pos(Dk) || !pos(Dv)) return ATMA_ERR_SHAPE;
+    if (!head_width_ok(Dk) || !head_width_ok(Dv) || chunk != 64) return ATMA_ERR_UNSUPPORTED;
+    if (dt != ATMA_BF16 && dt != ATMA_F32) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, Dk > Dv ? Dk : Dv) || H > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    if (!workspace || ws_bytes < atma::gdn_bwd_workspace_bytes(B, T, H, Dk, Dv)) return ATMA_ERR_WORKSPACE;
+    atma::GdnBwdArgs a{q, k, v, dO, alpha, beta, init_state, dS_final, dq, dk, dv, dalpha, dbeta, d_init,
+                       B, T, H, Dk, Dv, dt == ATMA_BF16, workspace};
+    return launched(atma::launch_gdn_bwd(a, (hipStream_t)stream));
+}
+
 int atma_polar_attn_fwd_train(const void* q, const void* k, const void* v, const atma_polar_params* p, void* o,
                               float* mu_out, float* stats, float* dir, int B, int T, int Hq, int Hkv, int D,
                               atma_dtype dt, void* stream) {

@@ -1,0 +1,523 @@
+// Gated-delta memory, chunked backward, for gfx950.
+//
+// Gradients of o_t = S_t q_t through S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+// (ATMA paper, Section 3.3 equation), taken on the exact chunk form of the forward (derivation in
+// gdn_fwd.hip): for a chunk of C = 64 tokens with state S_in,
+//     Delta = U - W S_in^T,   O = QG S_in^T + P Delta,   S_out = e^{g_last} S_in + Delta^T KD,
+//     W = Tinv diag(beta e^g) K,  U = Tinv diag(beta) V,  Tinv = (I + A)^{-1},
+//     A = strict_lower(diag(beta) (K K^T) o E),  P = lower_incl((Q K^T) o E),  E_rs = e^{g_r - g_s},
+//     QG = diag(e^g) Q,  KD = diag(e^{g_last - g}) K.
+// Reverse mode, per chunk, given dO and the gradient dS_out on its output state:
+//     dDelta = P^T dO + KD dS_out^T
+//     dS_in  = e^{g_last} dS_out + dO^T QG - dDelta^T W          (the carry: affine in dS_out)
+//     dU = dDelta, dW = -dDelta S_in, dQG = dO S_in, dP = lower_incl(dO Delta^T), dKD = Delta dS_out
+//     dTinv = dU (diag(beta) V)^T + dW (diag(beta e^g) K)^T,  dA = -strict_lower(Tinv^T dTinv Tinv^T)
+//     dv = beta o (Tinv^T dU),  dq = e^g o dQG + (dP o E) K,
+//     dk = beta e^g o (Tinv^T dW) + e^{g_last - g} o dKD + (dP o E)^T Q + M K + M^T K,  M = dA o beta E
+//     dbeta_r = sum_s dA_rs E_rs k_r.k_s + (Tinv^T dU)_r . v_r + e^{g_r} (Tinv^T dW)_r . k_r
+//     dg_r = rowsum_r(dA o A) - colsum_r(dA o A) + rowsum_r(dP o P) - colsum_r(dP o P)
+//            + beta_r e^{g_r} (Tinv^T dW)_r . k_r + e^{g_r} dQG_r . q_r - dKD_r . KD_r
+//            (+ sum_r dKD_r . KD_r + e^{g_last} <dS_out, S_in> on the last row of the chunk)
+//     d ln(alpha_s) = sum_{r >= s} dg_r within the chunk;  dalpha = d ln(alpha) / alpha.
+// Five kernels, all fp32 arithmetic (inputs bf16 or fp32, converted on load):
+//   prep   (parallel over chunks)  g, A, Tinv (forward substitution), W, U, KD
+//   fcarry (sequential over chunks, one workgroup per 16 state rows)  S_in and Delta per chunk
+//   pre    (parallel over chunks)  P^T dO and dO^T QG
+//   bcarry (sequential, reverse)   dS_out and dDelta per chunk, the gradient on the initial state
+//   post   (parallel over chunks)  every gradient above
+// Matrix products use one LDS-tiled fp32 routine (256 threads, 16 x 16 thread grid, K in slices
+// of 32 staged through LDS).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
+// beta = 0, alpha = 1), which keeps every formula exact for the real rows.
+#include "atma_device.hpp"
+#include "launch.hpp"
+
+namespace atma {
+namespace {
+
+constexpr int NT = 256;
+constexpr int C = 64;
+constexpr int KS = 32;   // k-slice of the tiled product
+constexpr int RB = 16;   // state rows per carry workgroup
+constexpr int LD64 = C + 1;
+
+// C[M][N] = sum_k A(i, k) B(k, j), delivered element by element to epi(i, j, value).  A and B
+// come from functors (global memory or LDS); K slices of 32 are staged in sA [32][M + 1] and
+// sB [32][N + 1].  AK: A's contiguous index in memory is k (else i); BJ: B's is j (else k) --
+// chooses the staging order so that consecutive threads read consecutive addresses.
+template <int M, int N, int K, bool AK, bool BJ, class LA, class LB, class EPI>
+__device__ __forceinline__ void tgemm(float* sA, float* sB, LA la, LB lb, EPI epi) {
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % KS == 0, "tile shape");
+    constexpr int TM = M / 16, TN = N / 16, LDA = M + 1, LDB = N + 1;
+    const int tid = (int)threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    __syncthreads();  // what earlier epilogues wrote (LDS or global) is visible to the staging below
+    float acc[TM][TN];
+#pragma unroll
+    for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) acc[x][y] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KS) {
+        for (int idx = tid; idx < M * KS; idx += NT) {
+            const int i = AK ? idx / KS : idx % M, kk = AK ? idx % KS : idx / M;
+            sA[kk * LDA + i] = la(i, k0 + kk);
+        }
+        for (int idx = tid; idx < N * KS; idx += NT) {
+            const int j = BJ ? idx % N : idx / KS, kk = BJ ? idx / N : idx % KS;
+            sB[kk * LDB + j] = lb(k0 + kk, j);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < KS; ++kk) {
+            float a[TM], b[TN];
+#pragma unroll
+            for (int x = 0; x < TM; ++x) a[x] = sA[kk * LDA + ti + 16 * x];
+#pragma unroll
+            for (int y = 0; y < TN; ++y) b[y] = sB[kk * LDB + tj + 16 * y];
+#pragma unroll
+            for (int x = 0; x < TM; ++x)
+#pragma unroll
+                for (int y = 0; y < TN; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) epi(ti + 16 * x, tj + 16 * y, acc[x][y]);
+}
+
+constexpr size_t STAGE_FLOATS = (size_t)KS * (128 + 1) * 2;  // sA + sB for the largest shapes
+
+// Per-chunk fp32 workspace arrays, chunk id cid = (b H + h) NC + c.
+template <int DK, int DV>
+struct WsLay {
+    static constexpr size_t W = 0, U = W + (size_t)C * DK, KD = U + (size_t)C * DV, TI = KD + (size_t)C * DK,
+                            G = TI + (size_t)C * C, EGL = G + C, SIN = EGL + 4, DL = SIN + (size_t)DV * DK,
+                            E = DL + (size_t)C * DV, F = E + (size_t)C * DV, DDL = F + (size_t)DV * DK,
+                            DSO = DDL + (size_t)C * DV, X0 = DSO + (size_t)DV * DK, X1 = X0 + (size_t)C * DK,
+                            X2 = X1 + (size_t)C * DK, X3 = X2 + (size_t)C * DK, X4 = X3 + (size_t)C * DV,
+                            PER = X4 + (size_t)C * DK;  // floats per chunk
+};
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, size_t i) { return to_f32(p[i]); }
+
+// Token layout helpers: row r of chunk c of (b, h) is token t0 + r; rows >= n read as zero.
+struct ChunkPos {
+    int b, h, c, n, t0;
+    size_t cid;
+};
+__device__ __forceinline__ ChunkPos chunk_pos(int Tlen, int H, int NC) {
+    ChunkPos p;
+    p.c = (int)blockIdx.x; p.h = (int)blockIdx.y; p.b = (int)blockIdx.z;
+    p.t0 = p.c * C;
+    p.n = min(C, Tlen - p.t0);
+    p.cid = ((size_t)p.b * H + p.h) * NC + p.c;
+    return p;
+}
+
+// ---------------------------------------------------------------------------------------------
+// prep: g, A, Tinv, W, U, KD per chunk
+// ---------------------------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, const T* __restrict__ v,
+                                                   const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                   float* __restrict__ ws, int Tlen, int H, int NC) {
+    using L = WsLay<DK, DV>;
+    __shared__ float stage[STAGE_FLOATS];
+    __shared__ float Am[C * LD64], Tm[C * LD64];
+    __shared__ float gs[C], bs[C];
+    const ChunkPos P = chunk_pos(Tlen, H, NC);
+    float* rec = ws + P.cid * L::PER;
+    const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h;
+    const int tid = (int)threadIdx.x;
+    if (tid < 64) {
+        const bool ok = tid < P.n;
+        float la = ok ? logf(alpha[tok0 + (size_t)tid * H]) : 0.0f;
+        bs[tid] = ok ? beta[tok0 + (size_t)tid * H] : 0.0f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(la, o, 64);
+            if (tid >= o) la += y;
+        }
+        gs[tid] = la;
+        rec[L::G + tid] = la;
+    }
+    __syncthreads();
+    const int n = P.n;
+    const size_t ks = (size_t)H * DK, vs = (size_t)H * DV;
+    const T* kc = k + tok0 * DK;
+    const T* vc = v + tok0 * DV;
+    auto krow = [&](int r, int d) { return r < n ? ld(kc, (size_t)r * ks + d) : 0.0f; };
+    // A = strict_lower(diag(beta) (K K^T) o E)
+    tgemm<C, C, DK, true, false>(stage, stage + KS * (C + 1), krow, [&](int d, int s) { return krow(s, d); },
+                                 [&](int r, int s, float x) {
+                                     Am[r * LD64 + s] = s < r ? bs[r] * expf(gs[r] - gs[s]) * x : 0.0f;
+                                 });
+    __syncthreads();
+    // Tinv = (I + A)^{-1}, column j by forward substitution: T[r][j] = [r == j] - sum_{j<=s<r} A[r][s] T[s][j]
+    if (tid < C) {
+        const int j = tid;
+        for (int r = 0; r < C; ++r) {
+            float x = r == j ? 1.0f : 0.0f;
+            for (int s = j; s < r; ++s) x = fmaf(-Am[r * LD64 + s], Tm[s * LD64 + j], x);
+            Tm[r * LD64 + j] = r < j ? 0.0f : x;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < C * C; i += NT) rec[L::TI + i] = Tm[(i / C) * LD64 + (i % C)];
+    // W = Tinv diag(beta e^g) K,  U = Tinv diag(beta) V
+    tgemm<C, DK, C, true, true>(stage, stage + KS * (C + 1), [&](int r, int s) { return Tm[r * LD64 + s]; },
+                                [&](int s, int d) { return bs[s] * expf(gs[s]) * krow(s, d); },
+                                [&](int r, int d, float x) { rec[L::W + (size_t)r * DK + d] = x; });
+    tgemm<C, DV, C, true, true>(stage, stage + KS * (C + 1), [&](int r, int s) { return Tm[r * LD64 + s]; },
+                                [&](int s, int d) { return s < n ? bs[s] * ld(vc, (size_t)s * vs + d) : 0.0f; },
+                                [&](int r, int d, float x) { rec[L::U + (size_t)r * DV + d] = x; });
+    const float glast = gs[n - 1];
+    for (int i = tid; i < C * DK; i += NT) {
+        const int r = i / DK, d = i % DK;
+        rec[L::KD + i] = expf(glast - gs[r]) * krow(r, d);
+    }
+    if (tid == 0) rec[L::EGL] = expf(glast);
+}
+
+// ---------------------------------------------------------------------------------------------
+// fcarry: forward state walk, 16 state rows per workgroup; S_in and Delta per chunk
+// ---------------------------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_fcarry(const float* __restrict__ init, float* __restrict__ ws, int H,
+                                                     int NC) {
+    using L = WsLay<DK, DV>;
+    __shared__ float stage[STAGE_FLOATS];
+    __shared__ float Sb[RB * (DK + 1)], Db[C * (RB + 1)];
+    const int row0 = (int)blockIdx.x * RB, h = (int)blockIdx.y, b = (int)blockIdx.z, tid = (int)threadIdx.x;
+    const size_t bh = (size_t)b * H + h;
+    for (int i = tid; i < RB * DK; i += NT) {
+        const int r = i / DK, d = i % DK;
+        Sb[r * (DK + 1) + d] = init ? init[(bh * DV + row0 + r) * DK + d] : 0.0f;
+    }
+    __syncthreads();
+    for (int c = 0; c < NC; ++c) {
+        float* rec = ws + (bh * NC + c) * L::PER;
+        for (int i = tid; i < RB * DK; i += NT) {
+            const int r = i / DK, d = i % DK;
+            rec[L::SIN + (size_t)(row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
+        }
+        // Delta[:, rows] = U[:, rows] - W S_in[rows, :]^T
+        tgemm<C, RB, DK, true, false>(stage, stage + KS * (C + 1),
+                                      [&](int r, int d) { return rec[L::W + (size_t)r * DK + d]; },
+                                      [&](int d, int i) { return Sb[i * (DK + 1) + d]; },
+                                      [&](int r, int i, float x) {
+                                          const float y = rec[L::U + (size_t)r * DV + row0 + i] - x;
+                                          Db[r * (RB + 1) + i] = y;
+                                          rec[L::DL + (size_t)r * DV + row0 + i] = y;
+                                      });
+        __syncthreads();
+        // S[rows, :] = e^{g_last} S[rows, :] + Delta[:, rows]^T KD
+        const float egl = rec[L::EGL];
+        tgemm<RB, DK, C, false, true>(stage, stage + KS * (RB + 1), [&](int i, int r) { return Db[r * (RB + 1) + i]; },
+                                      [&](int r, int d) { return rec[L::KD + (size_t)r * DK + d]; },
+                                      [&](int i, int d, float x) {
+                                          Sb[i * (DK + 1) + d] = fmaf(egl, Sb[i * (DK + 1) + d], x);
+                                      });
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// pre: E = P^T dO and F = dO^T QG per chunk
+// ---------------------------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const T* __restrict__ k,
+                                                  const T* __restrict__ dO, float* __restrict__ ws, int Tlen, int H,
+                                                  int NC) {
+    using L = WsLay<DK, DV>;
+    __shared__ float stage[STAGE_FLOATS];
+    __shared__ float Pm[C * LD64];
+    __shared__ float gs[C];
+    const ChunkPos P = chunk_pos(Tlen, H, NC);
+    float* rec = ws + P.cid * L::PER;
+    const int tid = (int)threadIdx.x, n = P.n;
+    if (tid < C) gs[tid] = rec[L::G + tid];
+    __syncthreads();
+    const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
+    const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *oc = dO + tok0 * DV;
+    auto qrow = [&](int r, int d) { return r < n ? ld(qc, (size_t)r * ks + d) : 0.0f; };
+    auto orow = [&](int r, int j) { return r < n ? ld(oc, (size_t)r * vs + j) : 0.0f; };
+    tgemm<C, C, DK, true, false>(stage, stage + KS * (C + 1), qrow,
+                                 [&](int d, int s) { return s < n ? ld(kc, (size_t)s * ks + d) : 0.0f; },
+                                 [&](int r, int s, float x) {
+                                     Pm[r * LD64 + s] = s <= r ? x * expf(gs[r] - gs[s]) : 0.0f;
+                                 });
+    __syncthreads();
+    tgemm<C, DV, C, false, true>(stage, stage + KS * (C + 1), [&](int s, int r) { return Pm[r * LD64 + s]; }, orow,
+                                 [&](int s, int j, float x) { rec[L::E + (size_t)s * DV + j] = x; });
+    tgemm<DV, DK, C, false, true>(stage, stage + KS * (DV + 1), [&](int i, int r) { return orow(r, i); },
+                                  [&](int r, int d) { return expf(gs[r]) * qrow(r, d); },
+                                  [&](int i, int d, float x) { rec[L::F + (size_t)i * DK + d] = x; });
+}
+
+// ---------------------------------------------------------------------------------------------
+// bcarry: reverse state-gradient walk, 16 rows of dS per workgroup
+// ---------------------------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_bcarry(const float* __restrict__ dSf, float* __restrict__ dinit,
+                                                     float* __restrict__ ws, int H, int NC) {
+    using L = WsLay<DK, DV>;
+    __shared__ float stage[STAGE_FLOATS];
+    __shared__ float Sb[RB * (DK + 1)], Db[C * (RB + 1)];
+    const int row0 = (int)blockIdx.x * RB, h = (int)blockIdx.y, b = (int)blockIdx.z, tid = (int)threadIdx.x;
+    const size_t bh = (size_t)b * H + h;
+    for (int i = tid; i < RB * DK; i += NT) {
+        const int r = i / DK, d = i % DK;
+        Sb[r * (DK + 1) + d] = dSf ? dSf[(bh * DV + row0 + r) * DK + d] : 0.0f;
+    }
+    __syncthreads();
+    for (int c = NC - 1; c >= 0; --c) {
+        float* rec = ws + (bh * NC + c) * L::PER;
+        for (int i = tid; i < RB * DK; i += NT) {
+            const int r = i / DK, d = i % DK;
+            rec[L::DSO + (size_t)(row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
+        }
+        // dDelta[:, rows] = E[:, rows] + KD dS_out[rows, :]^T
+        tgemm<C, RB, DK, true, false>(stage, stage + KS * (C + 1),
+                                      [&](int r, int d) { return rec[L::KD + (size_t)r * DK + d]; },
+                                      [&](int d, int i) { return Sb[i * (DK + 1) + d]; },
+                                      [&](int r, int i, float x) {
+                                          const float y = rec[L::E + (size_t)r * DV + row0 + i] + x;
+                                          Db[r * (RB + 1) + i] = y;
+                                          rec[L::DDL + (size_t)r * DV + row0 + i] = y;
+                                      });
+        __syncthreads();
+        // dS_in[rows, :] = e^{g_last} dS_out[rows, :] + F[rows, :] - dDelta[:, rows]^T W
+        const float egl = rec[L::EGL];
+        tgemm<RB, DK, C, false, true>(stage, stage + KS * (RB + 1), [&](int i, int r) { return Db[r * (RB + 1) + i]; },
+                                      [&](int r, int d) { return rec[L::W + (size_t)r * DK + d]; },
+                                      [&](int i, int d, float x) {
+                                          Sb[i * (DK + 1) + d] = fmaf(egl, Sb[i * (DK + 1) + d],
+                                                                      rec[L::F + (size_t)(row0 + i) * DK + d] - x);
+                                      });
+        __syncthreads();
+    }
+    if (dinit)
+        for (int i = tid; i < RB * DK; i += NT) {
+            const int r = i / DK, d = i % DK;
+            dinit[(bh * DV + row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
+        }
+}
+
+// ---------------------------------------------------------------------------------------------
+// post: every input gradient of a chunk
+// ---------------------------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, const float* __restrict__ alpha,
+                                                   const float* __restrict__ beta, const T* __restrict__ dO,
+                                                   T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+                                                   float* __restrict__ dalpha, float* __restrict__ dbeta,
+                                                   float* __restrict__ ws, int Tlen, int H, int NC) {
+    using L = WsLay<DK, DV>;
+    __shared__ float stage[STAGE_FLOATS];
+    __shared__ float Tm[C * LD64], QK[C * LD64], KK[C * LD64], dP[C * LD64], dT[C * LD64], Zm[C * LD64];
+    __shared__ float gs[C], bs[C], rowv[6][C], red[NT];
+    const ChunkPos P = chunk_pos(Tlen, H, NC);
+    float* rec = ws + P.cid * L::PER;
+    const int tid = (int)threadIdx.x, n = P.n;
+    if (tid < C) {
+        gs[tid] = rec[L::G + tid];
+        bs[tid] = tid < n ? beta[((size_t)P.b * Tlen + P.t0 + tid) * H + P.h] : 0.0f;
+    }
+    for (int i = tid; i < C * C; i += NT) Tm[(i / C) * LD64 + (i % C)] = rec[L::TI + i];
+    __syncthreads();
+    const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
+    const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *vc = v + tok0 * DV, *oc = dO + tok0 * DV;
+    auto qrow = [&](int r, int d) { return r < n ? ld(qc, (size_t)r * ks + d) : 0.0f; };
+    auto krow = [&](int r, int d) { return r < n ? ld(kc, (size_t)r * ks + d) : 0.0f; };
+    auto vrow = [&](int r, int j) { return r < n ? ld(vc, (size_t)r * vs + j) : 0.0f; };
+    auto orow = [&](int r, int j) { return r < n ? ld(oc, (size_t)r * vs + j) : 0.0f; };
+    float* sB64 = stage + KS * (C + 1);
+    const float* Sin = rec + L::SIN;
+    const float* dSo = rec + L::DSO;
+    // X0 = dQG = dO S_in;  X1 = dW = -dDelta S_in;  X2 = dKD = Delta dS_out
+    tgemm<C, DK, DV, true, true>(stage, sB64, orow, [&](int i, int d) { return Sin[(size_t)i * DK + d]; },
+                                 [&](int r, int d, float x) { rec[L::X0 + (size_t)r * DK + d] = x; });
+    tgemm<C, DK, DV, true, true>(stage, sB64, [&](int r, int i) { return rec[L::DDL + (size_t)r * DV + i]; },
+                                 [&](int i, int d) { return Sin[(size_t)i * DK + d]; },
+                                 [&](int r, int d, float x) { rec[L::X1 + (size_t)r * DK + d] = -x; });
+    tgemm<C, DK, DV, true, true>(stage, sB64, [&](int r, int i) { return rec[L::DL + (size_t)r * DV + i]; },
+                                 [&](int i, int d) { return dSo[(size_t)i * DK + d]; },
+                                 [&](int r, int d, float x) { rec[L::X2 + (size_t)r * DK + d] = x; });
+    // Q K^T and K K^T (raw), dP = lower_incl(dO Delta^T)
+    tgemm<C, C, DK, true, false>(stage, sB64, qrow, [&](int d, int s) { return krow(s, d); },
+                                 [&](int r, int s, float x) { QK[r * LD64 + s] = x; });
+    tgemm<C, C, DK, true, false>(stage, sB64, krow, [&](int d, int s) { return krow(s, d); },
+                                 [&](int r, int s, float x) { KK[r * LD64 + s] = x; });
+    tgemm<C, C, DV, true, false>(stage, sB64, orow, [&](int j, int s) { return rec[L::DL + (size_t)s * DV + j]; },
+                                 [&](int r, int s, float x) { dP[r * LD64 + s] = s <= r ? x : 0.0f; });
+    // dTinv = dDelta (diag(beta) V)^T + dW (diag(beta e^g) K)^T
+    tgemm<C, C, DV, true, false>(stage, sB64, [&](int r, int j) { return rec[L::DDL + (size_t)r * DV + j]; },
+                                 [&](int j, int s) { return bs[s] * vrow(s, j); },
+                                 [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
+    tgemm<C, C, DK, true, false>(stage, sB64, [&](int r, int d) { return rec[L::X1 + (size_t)r * DK + d]; },
+                                 [&](int d, int s) { return bs[s] * expf(gs[s]) * krow(s, d); },
+                                 [&](int r, int s, float x) { dT[r * LD64 + s] += x; });
+    // X3 = Tinv^T dDelta (and dv = beta o X3);  X4 = Tinv^T dW
+    tgemm<C, DV, C, false, true>(stage, sB64, [&](int r, int s) { return Tm[s * LD64 + r]; },
+                                 [&](int s, int j) { return rec[L::DDL + (size_t)s * DV + j]; },
+                                 [&](int r, int j, float x) {
+                                     rec[L::X3 + (size_t)r * DV + j] = x;
+                                     if (r < n) dv[(size_t)r * vs + j + tok0 * DV] = from_f32<T>(bs[r] * x);
+                                 });
+    tgemm<C, DK, C, false, true>(stage, sB64, [&](int r, int s) { return Tm[s * LD64 + r]; },
+                                 [&](int s, int d) { return rec[L::X1 + (size_t)s * DK + d]; },
+                                 [&](int r, int d, float x) { rec[L::X4 + (size_t)r * DK + d] = x; });
+    // Z = dTinv Tinv^T, then dA = -strict_lower(Tinv^T Z) (into dT)
+    tgemm<C, C, C, true, false>(stage, sB64, [&](int r, int s) { return dT[r * LD64 + s]; },
+                                [&](int s, int c2) { return Tm[c2 * LD64 + s]; },
+                                [&](int r, int c2, float x) { Zm[r * LD64 + c2] = x; });
+    tgemm<C, C, C, false, true>(stage, sB64, [&](int r, int s) { return Tm[s * LD64 + r]; },
+                                [&](int s, int c2) { return Zm[s * LD64 + c2]; },
+                                [&](int r, int c2, float x) { dT[r * LD64 + c2] = c2 < r ? -x : 0.0f; });
+    __syncthreads();
+    // row and column sums over the n x n terms (threads 0..63 rows, 64..127 columns):
+    //   rowv[0] = rowsum(dA o A) + rowsum(dP o P),  rowv[1] = colsum(...) of the same,
+    //   rowv[2] = sum_s dA_rs E_rs k_r.k_s (beta's share through A)
+    if (tid < 2 * C) {
+        const int x = tid & (C - 1);
+        float s1 = 0.f, s2 = 0.f;
+        for (int y = 0; y < C; ++y) {
+            const int r = tid < C ? x : y, s = tid < C ? y : x;
+            const float e = s <= r ? expf(gs[r] - gs[s]) : 0.0f;  // never exp of the upper triangle
+            const float dA = dT[r * LD64 + s];
+            const float aA = bs[r] * e * KK[r * LD64 + s];
+            const float pP = s <= r ? QK[r * LD64 + s] * e : 0.0f;
+            s1 = fmaf(dA, aA, fmaf(dP[r * LD64 + s], pP, s1));
+            s2 = fmaf(dA, e * KK[r * LD64 + s], s2);
+        }
+        rowv[tid < C ? 0 : 1][x] = s1;
+        if (tid < C) rowv[2][x] = s2;
+    }
+    __syncthreads();
+    // dP o E into dP, M = dA o beta E into Zm
+    for (int i = tid; i < C * C; i += NT) {
+        const int r = i / C, s = i % C;
+        const float e = s <= r ? expf(gs[r] - gs[s]) : 0.0f;
+        dP[r * LD64 + s] *= e;
+        Zm[r * LD64 + s] = dT[r * LD64 + s] * bs[r] * e;
+    }
+    __syncthreads();
+    // dq = e^g o dQG + (dP o E) K
+    tgemm<C, DK, C, true, true>(stage, sB64, [&](int r, int s) { return dP[r * LD64 + s]; }, krow,
+                                [&](int r, int d, float x) {
+                                    if (r < n)
+                                        dq[tok0 * DK + (size_t)r * ks + d] =
+                                            from_f32<T>(fmaf(expf(gs[r]), rec[L::X0 + (size_t)r * DK + d], x));
+                                });
+    // dk = beta e^g o X4 + e^{g_last - g} o dKD + [(dP o E)^T | M | M^T] [Q; K; K]
+    const float glast = gs[n - 1];
+    tgemm<C, DK, 3 * C, false, true>(
+        stage, sB64,
+        [&](int r, int kk) {
+            return kk < C ? dP[kk * LD64 + r] : kk < 2 * C ? Zm[r * LD64 + kk - C] : Zm[(kk - 2 * C) * LD64 + r];
+        },
+        [&](int kk, int d) { return kk < C ? qrow(kk, d) : krow(kk % C, d); },
+        [&](int r, int d, float x) {
+            if (r < n) {
+                const float y = bs[r] * expf(gs[r]) * rec[L::X4 + (size_t)r * DK + d] +
+                                expf(glast - gs[r]) * rec[L::X2 + (size_t)r * DK + d] + x;
+                dk[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(y);
+            }
+        });
+    // per-row dot products: 4 lanes per row
+    {
+        const int r = tid >> 2, part = tid & 3;
+        float tv = 0.f, tw = 0.f, qg = 0.f, kd = 0.f;
+        for (int d = part; d < DK; d += 4) {
+            const float kr = krow(r, d);
+            tw = fmaf(rec[L::X4 + (size_t)r * DK + d], kr, tw);
+            qg = fmaf(rec[L::X0 + (size_t)r * DK + d], qrow(r, d), qg);
+            kd = fmaf(rec[L::X2 + (size_t)r * DK + d], rec[L::KD + (size_t)r * DK + d], kd);
+        }
+        for (int j = part; j < DV; j += 4) tv = fmaf(rec[L::X3 + (size_t)r * DV + j], vrow(r, j), tv);
+#pragma unroll
+        for (int o = 1; o < 4; o <<= 1) {
+            tv += __shfl_xor(tv, o, 4);
+            tw += __shfl_xor(tw, o, 4);
+            qg += __shfl_xor(qg, o, 4);
+            kd += __shfl_xor(kd, o, 4);
+        }
+        if (part == 0) {
+            const float eg = expf(gs[r]);
+            rowv[3][r] = rowv[2][r] + tv + eg * tw;                                         // dbeta
+            rowv[4][r] = rowv[0][r] - rowv[1][r] + bs[r] * eg * tw + eg * qg - kd;          // dg (less the last-row terms)
+            rowv[5][r] = kd;
+        }
+    }
+    // e^{g_last} <dS_out, S_in>
+    {
+        float acc = 0.f;
+        for (int i = tid; i < DV * DK; i += NT) acc = fmaf(dSo[i], Sin[i], acc);
+        red[tid] = acc;
+    }
+    __syncthreads();
+    for (int o = NT / 2; o >= 1; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        float kdsum = 0.f;
+        for (int r = 0; r < C; ++r) kdsum += rowv[5][r];
+        rowv[4][n - 1] += kdsum + expf(glast) * red[0];
+        // d ln(alpha_s) = sum_{r >= s} dg_r, over the real rows
+        float run = 0.f;
+        for (int s = n - 1; s >= 0; --s) {
+            run += rowv[4][s];
+            const size_t t = ((size_t)P.b * Tlen + P.t0 + s) * H + P.h;
+            dalpha[t] = run / alpha[t];
+            dbeta[t] = rowv[3][s];
+        }
+    }
+}
+
+}  // namespace
+
+size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+    const size_t NC = (size_t)(T + C - 1) / C;
+    size_t per;
+    if (Dk == 64 && Dv == 64) per = WsLay<64, 64>::PER;
+    else if (Dk == 64 && Dv == 128) per = WsLay<64, 128>::PER;
+    else if (Dk == 128 && Dv == 64) per = WsLay<128, 64>::PER;
+    else per = WsLay<128, 128>::PER;
+    return (size_t)B * H * NC * per * sizeof(float);
+}
+
+template <typename T, int DK, int DV>
+static void launch_bwd_typed(const GdnBwdArgs& a, hipStream_t s) {
+    const int NC = (a.T + C - 1) / C;
+    float* ws = (float*)a.workspace;
+    const dim3 gc(NC, a.H, a.B), gr(DV / RB, a.H, a.B);
+    hipLaunchKernelGGL((gdn_bwd_prep<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.k, (const T*)a.v, a.alpha, a.beta,
+                       ws, a.T, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_fcarry<DK, DV>), gr, dim3(NT), 0, s, a.init_state, ws, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_pre<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.q, (const T*)a.k, (const T*)a.dO, ws,
+                       a.T, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_bcarry<DK, DV>), gr, dim3(NT), 0, s, a.dS_final, a.d_init, ws, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_post<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                       a.alpha, a.beta, (const T*)a.dO, (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dalpha, a.dbeta, ws, a.T,
+                       a.H, NC);
+}
+
+template <typename T>
+static hipError_t launch_bwd_dims(const GdnBwdArgs& a, hipStream_t s) {
+    if (a.Dk == 64 && a.Dv == 64) launch_bwd_typed<T, 64, 64>(a, s);
+    else if (a.Dk == 64 && a.Dv == 128) launch_bwd_typed<T, 64, 128>(a, s);
+    else if (a.Dk == 128 && a.Dv == 64) launch_bwd_typed<T, 128, 64>(a, s);
+    else if (a.Dk == 128 && a.Dv == 128) launch_bwd_typed<T, 128, 128>(a, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_bwd(const GdnBwdArgs& a, hipStream_t stream) {
+    return a.bf16_io ? launch_bwd_dims<bf16>(a, stream) : launch_bwd_dims<float>(a, stream);
+}
+
+}  // namespace atma

@@ -24,6 +24,19 @@ hipError_t launch_gdn_fwd(const GdnFwdArgs& a, hipStream_t stream);
 size_t gdn_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 hipError_t launch_gdn_bf16(const GdnFwdArgs& a, hipStream_t stream);
 
+// Backward of the chunked memory prefill (fixed-length batches), fp32 arithmetic.
+struct GdnBwdArgs {
+    const void *q, *k, *v, *dO;
+    const float *alpha, *beta, *init_state, *dS_final;
+    void *dq, *dk, *dv;
+    float *dalpha, *dbeta, *d_init;
+    int B, T, H, Dk, Dv;
+    bool bf16_io;
+    void* workspace;
+};
+size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+hipError_t launch_gdn_bwd(const GdnBwdArgs& a, hipStream_t stream);
+
 struct GdnDecodeArgs {
     const void *q, *k, *v;
     const float *alpha, *beta;

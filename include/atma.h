@@ -109,6 +109,31 @@ int atma_gdn_fwd_varlen(const void* q, const void* k, const void* v, const float
                         void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Gated-delta memory, backward of the chunked prefill: gradients of a loss L through
+ * o = atma_gdn_fwd(...) (and its final state), given dO = dL/do and optionally dS_final =
+ * dL/dS_T.  The chain rule on the Section 3.3 recurrence, taken on its exact chunk form: the
+ * forward is recomputed chunk by chunk (states kept per chunk), the state gradient is carried
+ * backwards (per chunk an affine map, the transpose of the forward's), then every chunk's
+ * input gradients are formed in parallel.  fp32 arithmetic throughout.
+ *   q, k, v, alpha, beta, init_state   the forward's inputs (init_state may be NULL = zero)
+ *   dO        [B, T, H, Dv] dtype `dt`;  dS_final [B, H, Dv, Dk] fp32 or NULL (zero)
+ *   dq, dk    [B, T, H, Dk] dtype `dt`;  dv [B, T, H, Dv] dtype `dt`
+ *   dalpha, dbeta [B, T, H] fp32;  d_init [B, H, Dv, Dk] fp32 or NULL (the gradient on the
+ *             initial state)
+ *   Dk, Dv in {64, 128}; chunk == 64; dt == ATMA_BF16 or ATMA_F32.  All outputs are written,
+ *   not accumulated.  alpha must be > 0 (the gradient divides by it).
+ *   workspace at least atma_gdn_bwd_workspace_bytes(...) bytes (per chunk: the recomputed
+ *   chunk operands, the chunk's input state and its gradient; about 400 KB per chunk at
+ *   Dk = Dv = 128).
+ * ------------------------------------------------------------------------------- */
+int atma_gdn_bwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                 const float* init_state, const void* dO, const float* dS_final, void* dq, void* dk,
+                 void* dv, float* dalpha, float* dbeta, float* d_init, int B, int T, int H, int Dk,
+                 int Dv, int chunk, atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
+
+size_t atma_gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt);
+
+/* ---------------------------------------------------------------------------------
  * Gated-delta memory, one decode step (the same equation for a single token):
  *     S <- alpha (S - beta (S k) k^T) + beta v k^T ;  o = S q
  *   q, k   [B, H, Dk] dtype `dt`;  v [B, H, Dv] dtype `dt`;  alpha, beta [B, H] fp32
