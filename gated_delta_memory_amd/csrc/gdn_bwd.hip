@@ -25,8 +25,7 @@
 //   pre    (parallel over chunks)  P^T dO and dO^T QG
 //   bcarry (sequential, reverse)   dS_out and dDelta per chunk, the gradient on the initial state
 //   post   (parallel over chunks)  every gradient above
-// Matrix products use one LDS-tiled fp32 routine (256 threads, 16 x 16 thread grid, K in slices
-// of 32 staged through LDS).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
+// Matrix products use one LDS-staged fp32 routine on v_mfma_f32_16x16x4_f32 (K in slices of 32).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
 // beta = 0, alpha = 1), which keeps every formula exact for the real rows.
 #include "atma_device.hpp"
 #include "launch.hpp"
@@ -41,51 +40,88 @@ constexpr int RB = 16;   // state rows per carry workgroup
 constexpr int LD64 = C + 1;
 
 // C[M][N] = sum_k A(i, k) B(k, j), delivered element by element to epi(i, j, value).  A and B
-// come from functors (global memory or LDS); K slices of 32 are staged in sA [32][M + 1] and
-// sB [32][N + 1].  AK: A's contiguous index in memory is k (else i); BJ: B's is j (else k) --
-// chooses the staging order so that consecutive threads read consecutive addresses.
+// come from functors (global memory or LDS); K slices of 32 are staged in LDS as sA [32][M + 16]
+// and sB [32][N + 16] (the padding of 16 puts the four k rows one fp32 MFMA reads on four
+// different 16-bank groups).  The product runs on v_mfma_f32_16x16x4_f32: lane l supplies
+// A[i0 + l % 16][k + l / 16] and B[k + l / 16][j0 + l % 16] and holds C[i0 + 4 (l / 16) + v][j0 + l % 16]
+// in accumulator v.  Each wave owns a band of 16-row tiles (all column tiles), or for M = 16 a
+// quarter of the column tiles.  AK: A's contiguous index in memory is k (else i); BJ: B's is j
+// (else k) -- chooses the staging order so that consecutive threads read consecutive addresses.
 template <int M, int N, int K, bool AK, bool BJ, class LA, class LB, class EPI>
-__device__ __forceinline__ void tgemm(float* sA, float* sB, LA la, LB lb, EPI epi) {
+__device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % KS == 0, "tile shape");
-    constexpr int TM = M / 16, TN = N / 16, LDA = M + 1, LDB = N + 1;
-    const int tid = (int)threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    constexpr int MT = M / 16, NTL = N / 16;
+    static_assert(MT % 4 == 0 || (MT == 1 && NTL % 4 == 0), "wave split");
+    constexpr int RT = MT >= 4 ? MT / 4 : 1, CT = MT >= 4 ? NTL : NTL / 4;
+    constexpr int LDA = M + 16, LDB = N + 16;
+    float* sA = stage;
+    float* sB = stage + KS * LDA;
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, G = lane >> 4, c16 = lane & 15;
+    const int rt0 = MT >= 4 ? w * RT : 0, ct0 = MT >= 4 ? 0 : w * CT;
     __syncthreads();  // what earlier epilogues wrote (LDS or global) is visible to the staging below
-    float acc[TM][TN];
+    f32x4 acc[RT][CT];
 #pragma unroll
-    for (int x = 0; x < TM; ++x)
+    for (int x = 0; x < RT; ++x)
 #pragma unroll
-        for (int y = 0; y < TN; ++y) acc[x][y] = 0.f;
-    for (int k0 = 0; k0 < K; k0 += KS) {
-        for (int idx = tid; idx < M * KS; idx += NT) {
+        for (int y = 0; y < CT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // software pipeline: the next K slice is fetched into registers while the current one is
+    // multiplied, so the latency of the operand loads overlaps the MFMAs
+    constexpr int PA = M * KS / NT, PB = N * KS / NT;
+    static_assert(M * KS % NT == 0 && N * KS % NT == 0, "staging split");
+    float ra[PA], rb[PB];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int m = 0; m < PA; ++m) {
+            const int idx = tid + m * NT;
             const int i = AK ? idx / KS : idx % M, kk = AK ? idx % KS : idx / M;
-            sA[kk * LDA + i] = la(i, k0 + kk);
+            ra[m] = la(i, k0 + kk);
         }
-        for (int idx = tid; idx < N * KS; idx += NT) {
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int idx = tid + m * NT;
             const int j = BJ ? idx % N : idx / KS, kk = BJ ? idx / N : idx % KS;
-            sB[kk * LDB + j] = lb(k0 + kk, j);
+            rb[m] = lb(k0 + kk, j);
+        }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += KS) {
+#pragma unroll
+        for (int m = 0; m < PA; ++m) {
+            const int idx = tid + m * NT;
+            const int i = AK ? idx / KS : idx % M, kk = AK ? idx % KS : idx / M;
+            sA[kk * LDA + i] = ra[m];
+        }
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int idx = tid + m * NT;
+            const int j = BJ ? idx % N : idx / KS, kk = BJ ? idx / N : idx % KS;
+            sB[kk * LDB + j] = rb[m];
         }
         __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < KS; ++kk) {
-            float a[TM], b[TN];
+        if (k0 + KS < K) fetch(k0 + KS);
 #pragma unroll
-            for (int x = 0; x < TM; ++x) a[x] = sA[kk * LDA + ti + 16 * x];
+        for (int kk = 0; kk < KS; kk += 4) {
+            float a[RT], b[CT];
 #pragma unroll
-            for (int y = 0; y < TN; ++y) b[y] = sB[kk * LDB + tj + 16 * y];
+            for (int x = 0; x < RT; ++x) a[x] = sA[(kk + G) * LDA + (rt0 + x) * 16 + c16];
 #pragma unroll
-            for (int x = 0; x < TM; ++x)
+            for (int y = 0; y < CT; ++y) b[y] = sB[(kk + G) * LDB + (ct0 + y) * 16 + c16];
 #pragma unroll
-                for (int y = 0; y < TN; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+            for (int x = 0; x < RT; ++x)
+#pragma unroll
+                for (int y = 0; y < CT; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int x = 0; x < TM; ++x)
+    for (int x = 0; x < RT; ++x)
 #pragma unroll
-        for (int y = 0; y < TN; ++y) epi(ti + 16 * x, tj + 16 * y, acc[x][y]);
+        for (int y = 0; y < CT; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) epi((rt0 + x) * 16 + 4 * G + v, (ct0 + y) * 16 + c16, acc[x][y][v]);
 }
 
-constexpr size_t STAGE_FLOATS = (size_t)KS * (128 + 1) * 2;  // sA + sB for the largest shapes
+constexpr size_t STAGE_FLOATS = (size_t)KS * (128 + 16) * 2;  // sA + sB for the largest shapes (M, N <= 128)
 
 // Per-chunk fp32 workspace arrays, chunk id cid = (b H + h) NC + c.
 template <int DK, int DV>
@@ -95,7 +131,8 @@ struct WsLay {
                             E = DL + (size_t)C * DV, F = E + (size_t)C * DV, DDL = F + (size_t)DV * DK,
                             DSO = DDL + (size_t)C * DV, X0 = DSO + (size_t)DV * DK, X1 = X0 + (size_t)C * DK,
                             X2 = X1 + (size_t)C * DK, X3 = X2 + (size_t)C * DK, X4 = X3 + (size_t)C * DV,
-                            PER = X4 + (size_t)C * DK;  // floats per chunk
+                            NQK = X4 + (size_t)C * DK, NKK = NQK + C * C, NDP = NKK + C * C, NDT = NDP + C * C,
+                            NZ = NDT + C * C, PER = NZ + C * C;  // floats per chunk
 };
 
 template <typename T>
@@ -149,27 +186,31 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     const T* vc = v + tok0 * DV;
     auto krow = [&](int r, int d) { return r < n ? ld(kc, (size_t)r * ks + d) : 0.0f; };
     // A = strict_lower(diag(beta) (K K^T) o E)
-    tgemm<C, C, DK, true, false>(stage, stage + KS * (C + 1), krow, [&](int d, int s) { return krow(s, d); },
+    tgemm<C, C, DK, true, false>(stage, krow, [&](int d, int s) { return krow(s, d); },
                                  [&](int r, int s, float x) {
                                      Am[r * LD64 + s] = s < r ? bs[r] * expf(gs[r] - gs[s]) * x : 0.0f;
                                  });
     __syncthreads();
-    // Tinv = (I + A)^{-1}, column j by forward substitution: T[r][j] = [r == j] - sum_{j<=s<r} A[r][s] T[s][j]
-    if (tid < C) {
-        const int j = tid;
+    // Tinv = (I + A)^{-1}, column j by forward substitution: T[r][j] = [r == j] - sum_{j<=s<r} A[r][s] T[s][j];
+    // four lanes per column (adjacent lanes of one wave) split the sum over s and combine it
+    {
+        const int j = tid >> 2, part = tid & 3;
         for (int r = 0; r < C; ++r) {
-            float x = r == j ? 1.0f : 0.0f;
-            for (int s = j; s < r; ++s) x = fmaf(-Am[r * LD64 + s], Tm[s * LD64 + j], x);
-            Tm[r * LD64 + j] = r < j ? 0.0f : x;
+            float x = 0.f;
+            for (int s = j + part; s < r; s += 4) x = fmaf(Am[r * LD64 + s], Tm[s * LD64 + j], x);
+            x += __shfl_xor(x, 1, 4);
+            x += __shfl_xor(x, 2, 4);
+            if (part == 0) Tm[r * LD64 + j] = r < j ? 0.0f : (r == j ? 1.0f : -x);
+            __syncthreads();  // row r is read by the other lanes of its column from row r + 1 on
         }
     }
     __syncthreads();
     for (int i = tid; i < C * C; i += NT) rec[L::TI + i] = Tm[(i / C) * LD64 + (i % C)];
     // W = Tinv diag(beta e^g) K,  U = Tinv diag(beta) V
-    tgemm<C, DK, C, true, true>(stage, stage + KS * (C + 1), [&](int r, int s) { return Tm[r * LD64 + s]; },
+    tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return Tm[r * LD64 + s]; },
                                 [&](int s, int d) { return bs[s] * expf(gs[s]) * krow(s, d); },
                                 [&](int r, int d, float x) { rec[L::W + (size_t)r * DK + d] = x; });
-    tgemm<C, DV, C, true, true>(stage, stage + KS * (C + 1), [&](int r, int s) { return Tm[r * LD64 + s]; },
+    tgemm<C, DV, C, true, true>(stage, [&](int r, int s) { return Tm[r * LD64 + s]; },
                                 [&](int s, int d) { return s < n ? bs[s] * ld(vc, (size_t)s * vs + d) : 0.0f; },
                                 [&](int r, int d, float x) { rec[L::U + (size_t)r * DV + d] = x; });
     const float glast = gs[n - 1];
@@ -203,7 +244,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_fcarry(const float* __restrict__ i
             rec[L::SIN + (size_t)(row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
         }
         // Delta[:, rows] = U[:, rows] - W S_in[rows, :]^T
-        tgemm<C, RB, DK, true, false>(stage, stage + KS * (C + 1),
+        tgemm<C, RB, DK, true, false>(stage,
                                       [&](int r, int d) { return rec[L::W + (size_t)r * DK + d]; },
                                       [&](int d, int i) { return Sb[i * (DK + 1) + d]; },
                                       [&](int r, int i, float x) {
@@ -214,7 +255,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_fcarry(const float* __restrict__ i
         __syncthreads();
         // S[rows, :] = e^{g_last} S[rows, :] + Delta[:, rows]^T KD
         const float egl = rec[L::EGL];
-        tgemm<RB, DK, C, false, true>(stage, stage + KS * (RB + 1), [&](int i, int r) { return Db[r * (RB + 1) + i]; },
+        tgemm<RB, DK, C, false, true>(stage, [&](int i, int r) { return Db[r * (RB + 1) + i]; },
                                       [&](int r, int d) { return rec[L::KD + (size_t)r * DK + d]; },
                                       [&](int i, int d, float x) {
                                           Sb[i * (DK + 1) + d] = fmaf(egl, Sb[i * (DK + 1) + d], x);
@@ -243,15 +284,15 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *oc = dO + tok0 * DV;
     auto qrow = [&](int r, int d) { return r < n ? ld(qc, (size_t)r * ks + d) : 0.0f; };
     auto orow = [&](int r, int j) { return r < n ? ld(oc, (size_t)r * vs + j) : 0.0f; };
-    tgemm<C, C, DK, true, false>(stage, stage + KS * (C + 1), qrow,
+    tgemm<C, C, DK, true, false>(stage, qrow,
                                  [&](int d, int s) { return s < n ? ld(kc, (size_t)s * ks + d) : 0.0f; },
                                  [&](int r, int s, float x) {
                                      Pm[r * LD64 + s] = s <= r ? x * expf(gs[r] - gs[s]) : 0.0f;
                                  });
     __syncthreads();
-    tgemm<C, DV, C, false, true>(stage, stage + KS * (C + 1), [&](int s, int r) { return Pm[r * LD64 + s]; }, orow,
+    tgemm<C, DV, C, false, true>(stage, [&](int s, int r) { return Pm[r * LD64 + s]; }, orow,
                                  [&](int s, int j, float x) { rec[L::E + (size_t)s * DV + j] = x; });
-    tgemm<DV, DK, C, false, true>(stage, stage + KS * (DV + 1), [&](int i, int r) { return orow(r, i); },
+    tgemm<DV, DK, C, false, true>(stage, [&](int i, int r) { return orow(r, i); },
                                   [&](int r, int d) { return expf(gs[r]) * qrow(r, d); },
                                   [&](int i, int d, float x) { rec[L::F + (size_t)i * DK + d] = x; });
 }
@@ -279,7 +320,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_bcarry(const float* __restrict__ d
             rec[L::DSO + (size_t)(row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
         }
         // dDelta[:, rows] = E[:, rows] + KD dS_out[rows, :]^T
-        tgemm<C, RB, DK, true, false>(stage, stage + KS * (C + 1),
+        tgemm<C, RB, DK, true, false>(stage,
                                       [&](int r, int d) { return rec[L::KD + (size_t)r * DK + d]; },
                                       [&](int d, int i) { return Sb[i * (DK + 1) + d]; },
                                       [&](int r, int i, float x) {
@@ -290,7 +331,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_bcarry(const float* __restrict__ d
         __syncthreads();
         // dS_in[rows, :] = e^{g_last} dS_out[rows, :] + F[rows, :] - dDelta[:, rows]^T W
         const float egl = rec[L::EGL];
-        tgemm<RB, DK, C, false, true>(stage, stage + KS * (RB + 1), [&](int i, int r) { return Db[r * (RB + 1) + i]; },
+        tgemm<RB, DK, C, false, true>(stage, [&](int i, int r) { return Db[r * (RB + 1) + i]; },
                                       [&](int r, int d) { return rec[L::W + (size_t)r * DK + d]; },
                                       [&](int i, int d, float x) {
                                           Sb[i * (DK + 1) + d] = fmaf(egl, Sb[i * (DK + 1) + d],
@@ -309,24 +350,27 @@ __global__ __launch_bounds__(NT) void gdn_bwd_bcarry(const float* __restrict__ d
 // post: every input gradient of a chunk
 // ---------------------------------------------------------------------------------------------
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, const T* __restrict__ dO,
                                                    T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
                                                    float* __restrict__ dalpha, float* __restrict__ dbeta,
                                                    float* __restrict__ ws, int Tlen, int H, int NC) {
     using L = WsLay<DK, DV>;
+    // The 64 x 64 intermediates live in this chunk's workspace (cached; the workgroup's working set is
+    // small) rather than LDS, so that two workgroups fit on a CU.
     __shared__ float stage[STAGE_FLOATS];
-    __shared__ float Tm[C * LD64], QK[C * LD64], KK[C * LD64], dP[C * LD64], dT[C * LD64], Zm[C * LD64];
     __shared__ float gs[C], bs[C], rowv[6][C], red[NT];
     const ChunkPos P = chunk_pos(Tlen, H, NC);
     float* rec = ws + P.cid * L::PER;
+    constexpr int LD64 = C;  // row stride of the workspace 64 x 64 arrays
+    const float* Tm = rec + L::TI;
+    float *QK = rec + L::NQK, *KK = rec + L::NKK, *dP = rec + L::NDP, *dT = rec + L::NDT, *Zm = rec + L::NZ;
     const int tid = (int)threadIdx.x, n = P.n;
     if (tid < C) {
         gs[tid] = rec[L::G + tid];
         bs[tid] = tid < n ? beta[((size_t)P.b * Tlen + P.t0 + tid) * H + P.h] : 0.0f;
     }
-    for (int i = tid; i < C * C; i += NT) Tm[(i / C) * LD64 + (i % C)] = rec[L::TI + i];
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *vc = v + tok0 * DV, *oc = dO + tok0 * DV;
@@ -334,47 +378,51 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
     auto krow = [&](int r, int d) { return r < n ? ld(kc, (size_t)r * ks + d) : 0.0f; };
     auto vrow = [&](int r, int j) { return r < n ? ld(vc, (size_t)r * vs + j) : 0.0f; };
     auto orow = [&](int r, int j) { return r < n ? ld(oc, (size_t)r * vs + j) : 0.0f; };
-    float* sB64 = stage + KS * (C + 1);
     const float* Sin = rec + L::SIN;
     const float* dSo = rec + L::DSO;
-    // X0 = dQG = dO S_in;  X1 = dW = -dDelta S_in;  X2 = dKD = Delta dS_out
-    tgemm<C, DK, DV, true, true>(stage, sB64, orow, [&](int i, int d) { return Sin[(size_t)i * DK + d]; },
-                                 [&](int r, int d, float x) { rec[L::X0 + (size_t)r * DK + d] = x; });
-    tgemm<C, DK, DV, true, true>(stage, sB64, [&](int r, int i) { return rec[L::DDL + (size_t)r * DV + i]; },
-                                 [&](int i, int d) { return Sin[(size_t)i * DK + d]; },
-                                 [&](int r, int d, float x) { rec[L::X1 + (size_t)r * DK + d] = -x; });
-    tgemm<C, DK, DV, true, true>(stage, sB64, [&](int r, int i) { return rec[L::DL + (size_t)r * DV + i]; },
+    // X0 = dQG = dO S_in and X1 = dW = -dDelta S_in as one product [dO; dDelta] S_in;  X2 = dKD = Delta dS_out
+    tgemm<2 * C, DK, DV, true, true>(
+        stage, [&](int r, int i) { return r < C ? orow(r, i) : rec[L::DDL + (size_t)(r - C) * DV + i]; },
+        [&](int i, int d) { return Sin[(size_t)i * DK + d]; },
+        [&](int r, int d, float x) {
+            if (r < C) rec[L::X0 + (size_t)r * DK + d] = x;
+            else rec[L::X1 + (size_t)(r - C) * DK + d] = -x;
+        });
+    tgemm<C, DK, DV, true, true>(stage, [&](int r, int i) { return rec[L::DL + (size_t)r * DV + i]; },
                                  [&](int i, int d) { return dSo[(size_t)i * DK + d]; },
                                  [&](int r, int d, float x) { rec[L::X2 + (size_t)r * DK + d] = x; });
     // Q K^T and K K^T (raw), dP = lower_incl(dO Delta^T)
-    tgemm<C, C, DK, true, false>(stage, sB64, qrow, [&](int d, int s) { return krow(s, d); },
-                                 [&](int r, int s, float x) { QK[r * LD64 + s] = x; });
-    tgemm<C, C, DK, true, false>(stage, sB64, krow, [&](int d, int s) { return krow(s, d); },
-                                 [&](int r, int s, float x) { KK[r * LD64 + s] = x; });
-    tgemm<C, C, DV, true, false>(stage, sB64, orow, [&](int j, int s) { return rec[L::DL + (size_t)s * DV + j]; },
+    tgemm<2 * C, C, DK, true, false>(stage, [&](int r, int d) { return r < C ? qrow(r, d) : krow(r - C, d); },
+                                     [&](int d, int s) { return krow(s, d); },
+                                     [&](int r, int s, float x) {
+                                         if (r < C) QK[r * LD64 + s] = x;
+                                         else KK[(r - C) * LD64 + s] = x;
+                                     });
+    tgemm<C, C, DV, true, false>(stage, orow, [&](int j, int s) { return rec[L::DL + (size_t)s * DV + j]; },
                                  [&](int r, int s, float x) { dP[r * LD64 + s] = s <= r ? x : 0.0f; });
     // dTinv = dDelta (diag(beta) V)^T + dW (diag(beta e^g) K)^T
-    tgemm<C, C, DV, true, false>(stage, sB64, [&](int r, int j) { return rec[L::DDL + (size_t)r * DV + j]; },
-                                 [&](int j, int s) { return bs[s] * vrow(s, j); },
-                                 [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
-    tgemm<C, C, DK, true, false>(stage, sB64, [&](int r, int d) { return rec[L::X1 + (size_t)r * DK + d]; },
-                                 [&](int d, int s) { return bs[s] * expf(gs[s]) * krow(s, d); },
-                                 [&](int r, int s, float x) { dT[r * LD64 + s] += x; });
+    tgemm<C, C, DV + DK, true, false>(
+        stage,
+        [&](int r, int j) {
+            return j < DV ? rec[L::DDL + (size_t)r * DV + j] : rec[L::X1 + (size_t)r * DK + j - DV];
+        },
+        [&](int j, int s) { return j < DV ? bs[s] * vrow(s, j) : bs[s] * expf(gs[s]) * krow(s, j - DV); },
+        [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
     // X3 = Tinv^T dDelta (and dv = beta o X3);  X4 = Tinv^T dW
-    tgemm<C, DV, C, false, true>(stage, sB64, [&](int r, int s) { return Tm[s * LD64 + r]; },
+    tgemm<C, DV, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
                                  [&](int s, int j) { return rec[L::DDL + (size_t)s * DV + j]; },
                                  [&](int r, int j, float x) {
                                      rec[L::X3 + (size_t)r * DV + j] = x;
                                      if (r < n) dv[(size_t)r * vs + j + tok0 * DV] = from_f32<T>(bs[r] * x);
                                  });
-    tgemm<C, DK, C, false, true>(stage, sB64, [&](int r, int s) { return Tm[s * LD64 + r]; },
+    tgemm<C, DK, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
                                  [&](int s, int d) { return rec[L::X1 + (size_t)s * DK + d]; },
                                  [&](int r, int d, float x) { rec[L::X4 + (size_t)r * DK + d] = x; });
     // Z = dTinv Tinv^T, then dA = -strict_lower(Tinv^T Z) (into dT)
-    tgemm<C, C, C, true, false>(stage, sB64, [&](int r, int s) { return dT[r * LD64 + s]; },
+    tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return dT[r * LD64 + s]; },
                                 [&](int s, int c2) { return Tm[c2 * LD64 + s]; },
                                 [&](int r, int c2, float x) { Zm[r * LD64 + c2] = x; });
-    tgemm<C, C, C, false, true>(stage, sB64, [&](int r, int s) { return Tm[s * LD64 + r]; },
+    tgemm<C, C, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
                                 [&](int s, int c2) { return Zm[s * LD64 + c2]; },
                                 [&](int r, int c2, float x) { dT[r * LD64 + c2] = c2 < r ? -x : 0.0f; });
     __syncthreads();
@@ -384,6 +432,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
     if (tid < 2 * C) {
         const int x = tid & (C - 1);
         float s1 = 0.f, s2 = 0.f;
+#pragma unroll 16
         for (int y = 0; y < C; ++y) {
             const int r = tid < C ? x : y, s = tid < C ? y : x;
             const float e = s <= r ? expf(gs[r] - gs[s]) : 0.0f;  // never exp of the upper triangle
@@ -398,6 +447,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
     }
     __syncthreads();
     // dP o E into dP, M = dA o beta E into Zm
+#pragma unroll
     for (int i = tid; i < C * C; i += NT) {
         const int r = i / C, s = i % C;
         const float e = s <= r ? expf(gs[r] - gs[s]) : 0.0f;
@@ -406,7 +456,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
     }
     __syncthreads();
     // dq = e^g o dQG + (dP o E) K
-    tgemm<C, DK, C, true, true>(stage, sB64, [&](int r, int s) { return dP[r * LD64 + s]; }, krow,
+    tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return dP[r * LD64 + s]; }, krow,
                                 [&](int r, int d, float x) {
                                     if (r < n)
                                         dq[tok0 * DK + (size_t)r * ks + d] =
@@ -414,8 +464,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
                                 });
     // dk = beta e^g o X4 + e^{g_last - g} o dKD + [(dP o E)^T | M | M^T] [Q; K; K]
     const float glast = gs[n - 1];
-    tgemm<C, DK, 3 * C, false, true>(
-        stage, sB64,
+    tgemm<C, DK, 3 * C, false, true>(stage,
         [&](int r, int kk) {
             return kk < C ? dP[kk * LD64 + r] : kk < 2 * C ? Zm[r * LD64 + kk - C] : Zm[(kk - 2 * C) * LD64 + r];
         },
@@ -431,12 +480,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
     {
         const int r = tid >> 2, part = tid & 3;
         float tv = 0.f, tw = 0.f, qg = 0.f, kd = 0.f;
+#pragma unroll 8
         for (int d = part; d < DK; d += 4) {
             const float kr = krow(r, d);
             tw = fmaf(rec[L::X4 + (size_t)r * DK + d], kr, tw);
             qg = fmaf(rec[L::X0 + (size_t)r * DK + d], qrow(r, d), qg);
             kd = fmaf(rec[L::X2 + (size_t)r * DK + d], rec[L::KD + (size_t)r * DK + d], kd);
         }
+#pragma unroll 8
         for (int j = part; j < DV; j += 4) tv = fmaf(rec[L::X3 + (size_t)r * DV + j], vrow(r, j), tv);
 #pragma unroll
         for (int o = 1; o < 4; o <<= 1) {
@@ -455,7 +506,11 @@ __global__ __launch_bounds__(NT) void gdn_bwd_post(const T* __restrict__ q, cons
     // e^{g_last} <dS_out, S_in>
     {
         float acc = 0.f;
-        for (int i = tid; i < DV * DK; i += NT) acc = fmaf(dSo[i], Sin[i], acc);
+#pragma unroll 4
+        for (int i = tid * 4; i < DV * DK; i += NT * 4) {
+            const f32x4 a = *(const f32x4*)(dSo + i), b = *(const f32x4*)(Sin + i);
+            acc = fmaf(a[0], b[0], fmaf(a[1], b[1], fmaf(a[2], b[2], fmaf(a[3], b[3], acc))));
+        }
         red[tid] = acc;
     }
     __syncthreads();
