@@ -35,7 +35,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int C = 64;
-constexpr int KS = 32;   // k-slice of the tiled product
+constexpr int KS = 16;   // k-slice of the tiled product
 constexpr int RB = 16;   // state rows per carry workgroup
 constexpr int LD64 = C + 1;
 

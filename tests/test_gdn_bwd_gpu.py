@@ -79,3 +79,19 @@ def test_gdn_bwd_is_deterministic(atma):
     torch.cuda.synchronize()
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_gdn_bwd_layer_b8_t2k(atma):
+    """The 2K layer as the benchmark times it (B=8, T=2048, H=8, d=128, bf16, one launch over the
+    whole batch); the oracle's gradients of batch 0 (the kernels treat every batch the same)."""
+    inp = workloads.make_workload("layer_b8_t2k")["gdn"]
+    B, T, H, D = inp["q"].shape
+    do = torch.randn(B, T, H, D, generator=torch.Generator().manual_seed(2049)).to(torch.bfloat16)
+    g = atma.atma_gdn_bwd(*[inp[x].cuda() for x in ("q", "k", "v", "alpha", "beta")], do.cuda(), want_dinit=True)
+    torch.cuda.synchronize()
+    ref = oracle.gdn_bwd(inp["q"][:1], inp["k"][:1], inp["v"][:1], inp["alpha"][:1], inp["beta"][:1], do[:1])
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dinit"):
+        em, ef = rel_err_max(to_np(g[n])[:1], ref[n]), rel_err_fro(to_np(g[n])[:1], ref[n])
+        note(f"  gdn bwd layer_b8_t2k batch 0 {n}: {em:.1e}/{ef:.1e}")
+        tol = 4e-3 if n in ("dq", "dk", "dv") else 1e-4
+        assert em <= tol and ef <= tol, (n, em, ef)

@@ -111,3 +111,18 @@ def test_polar_bwd_is_deterministic(atma):
     _, _, g2 = _run(atma, inp, do)
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_polar_bwd_layer_b8_t2k(atma):
+    """The 2K layer as the benchmark times it (B=8, T=2048, Hq=Hkv=16, D=64, one launch over the
+    whole batch); the oracle's gradients of batch 0 (the kernels treat every batch the same)."""
+    inp = workloads.make_workload("layer_b8_t2k")["polar"]
+    B, T, Hq, D = inp["q"].shape
+    do = torch.randn(B, T, Hq, D, generator=torch.Generator().manual_seed(2048)).to(torch.bfloat16)
+    _, _, g = _run(atma, inp, do)
+    cp = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp["params"].items()}
+    ref = oracle.polar_bwd(inp["q"][:1], inp["k"][:1], inp["v"][:1], cp, do[:1])
+    for n in ("dq", "dk", "dv"):
+        em, ef = rel_err_max(to_np(g[n])[:1], ref[n]), rel_err_fro(to_np(g[n])[:1], ref[n])
+        note(f"  polar bwd layer_b8_t2k batch 0 {n}: {em:.1e}/{ef:.1e}")
+        assert em <= TOL_MAX and ef <= TOL_FRO, (n, em, ef)
