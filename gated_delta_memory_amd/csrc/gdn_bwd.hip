@@ -21,9 +21,9 @@
 //     d ln(alpha_s) = sum_{r >= s} dg_r within the chunk;  dalpha = d ln(alpha) / alpha.
 // Five kernels, all fp32 arithmetic (inputs bf16 or fp32, converted on load):
 //   prep   (parallel over chunks)  g, A, Tinv (forward substitution), W, U, KD
-//   fcarry (sequential over chunks, one workgroup per 16 state rows)  S_in and Delta per chunk
+//   walk   (sequential over chunks, one workgroup per 32 state rows)  S_in and Delta per chunk
 //   pre    (parallel over chunks)  P^T dO and dO^T QG
-//   bcarry (sequential, reverse)   dS_out and dDelta per chunk, the gradient on the initial state
+//   walk   (sequential, reverse)   dS_out and dDelta per chunk, the gradient on the initial state
 //   post   (parallel over chunks)  every gradient above
 // Matrix products use one LDS-staged fp32 routine on v_mfma_f32_16x16x4_f32 (K in slices of 32).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
 // beta = 0, alpha = 1), which keeps every formula exact for the real rows.
@@ -36,7 +36,6 @@ namespace {
 constexpr int NT = 256;
 constexpr int C = 64;
 constexpr int KS = 16;   // k-slice of the tiled product
-constexpr int RB = 16;   // state rows per carry workgroup
 constexpr int LD64 = C + 1;
 
 // C[M][N] = sum_k A(i, k) B(k, j), delivered element by element to epi(i, j, value).  A and B
@@ -222,46 +221,159 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
 }
 
 // ---------------------------------------------------------------------------------------------
-// fcarry: forward state walk, 16 state rows per workgroup; S_in and Delta per chunk
+// walk: the two sequential state walks, one kernel.  A workgroup owns RW = 32 state rows of a
+// (batch, head) and visits the chunks in order (forward) or in reverse (backward):
+//   forward:   S_in stored;  Delta = U[:, rows] - W S^T;           S = e^{g_last} S + Delta^T KD
+//   backward:  dS_out stored; dDelta = E[:, rows] + KD dS^T;       dS = e^{g_last} dS + F[rows, :] - dDelta^T W
+// (S^T and Delta written for the per-chunk kernels).  The chunk's two 64 x Dk operands (W and KD,
+// in the order the walk uses them) sit whole in LDS; the next chunk's operands are loaded into
+// registers while the current chunk multiplies, so the walk waits on memory only once.  Products
+// on v_mfma_f32_16x16x4_f32 straight from LDS: rows padded by 4 floats where a lane reads along
+// the row (A operand), by 16 where the lanes of a group read along a column (B operand), so the
+// 64 lanes of a read hit 64 different banks.
 // ---------------------------------------------------------------------------------------------
-template <int DK, int DV>
-__global__ __launch_bounds__(NT) void gdn_bwd_fcarry(const float* __restrict__ init, float* __restrict__ ws, int H,
-                                                     int NC) {
+constexpr int RW = 32;
+
+template <int DK, int DV, bool BACK>
+__global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0, float* __restrict__ sfinal,
+                                                   float* __restrict__ ws, int H, int NC) {
     using L = WsLay<DK, DV>;
-    __shared__ float stage[STAGE_FLOATS];
-    __shared__ float Sb[RB * (DK + 1)], Db[C * (RB + 1)];
-    const int row0 = (int)blockIdx.x * RB, h = (int)blockIdx.y, b = (int)blockIdx.z, tid = (int)threadIdx.x;
+    constexpr int LA = DK + 4, LB = DK + 16, LS = DK + 4, LX = RW + 16;
+    constexpr size_t OFF_A = BACK ? L::KD : L::W;   // A operand of the first product
+    constexpr size_t OFF_B = BACK ? L::W : L::KD;   // B operand of the second product
+    constexpr size_t OFF_X = BACK ? L::E : L::U;    // added to the first product
+    constexpr size_t OFF_XO = BACK ? L::DDL : L::DL;
+    constexpr size_t OFF_SO = BACK ? L::DSO : L::SIN;
+    constexpr float SG1 = BACK ? 1.0f : -1.0f, SG2 = BACK ? -1.0f : 1.0f;
+    constexpr int NA = C * DK / 4 / NT, NX = C * RW / 4 / NT, NF = RW * DK / 4 / NT;
+    static_assert(NA >= 1 && NX >= 1 && NF >= 1, "split");
+    __shared__ __align__(16) float As[C * LA];
+    __shared__ __align__(16) float Bs[C * LB];
+    __shared__ __align__(16) float St[RW * LS];
+    __shared__ __align__(16) float Xs[C * LX];
+    const int row0 = (int)blockIdx.x * RW, h = (int)blockIdx.y, b = (int)blockIdx.z, tid = (int)threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, G = lane >> 4, c16 = lane & 15;
     const size_t bh = (size_t)b * H + h;
-    for (int i = tid; i < RB * DK; i += NT) {
-        const int r = i / DK, d = i % DK;
-        Sb[r * (DK + 1) + d] = init ? init[(bh * DV + row0 + r) * DK + d] : 0.0f;
+    // state rows in, zero when absent
+    for (int q = tid; q < RW * DK / 4; q += NT) {
+        const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (s0) x = *(const f32x4*)(s0 + (bh * DV + row0 + i) * DK + d4);
+        *(f32x4*)(St + i * LS + d4) = x;
+    }
+    f32x4 ra[NA], rb[NA], rx[NX], rf[NF];
+    float regl;
+    auto fetch = [&](int c) {
+        const float* rec = ws + (bh * NC + c) * L::PER;
+#pragma unroll
+        for (int m = 0; m < NA; ++m) {
+            const int q = tid + m * NT, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            ra[m] = *(const f32x4*)(rec + OFF_A + (size_t)r * DK + d4);
+            rb[m] = *(const f32x4*)(rec + OFF_B + (size_t)r * DK + d4);
+        }
+#pragma unroll
+        for (int m = 0; m < NX; ++m) {
+            const int q = tid + m * NT, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
+            rx[m] = *(const f32x4*)(rec + OFF_X + (size_t)r * DV + row0 + c4);
+        }
+        if constexpr (BACK) {
+#pragma unroll
+            for (int m = 0; m < NF; ++m) {
+                const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                rf[m] = *(const f32x4*)(rec + L::F + (size_t)(row0 + i) * DK + d4);
+            }
+        }
+        regl = rec[L::EGL];
+    };
+    fetch(BACK ? NC - 1 : 0);
+    for (int it = 0; it < NC; ++it) {
+        const int c = BACK ? NC - 1 - it : it;
+        float* rec = ws + (bh * NC + c) * L::PER;
+        const float egl = regl;
+        f32x4 fcur[NF];
+#pragma unroll
+        for (int m = 0; m < NF; ++m) fcur[m] = rf[m];
+        __syncthreads();  // the previous chunk is done with As, Bs, Xs and St
+        // operands of this chunk into LDS; the state (S_in or dS_out) out to the workspace
+#pragma unroll
+        for (int m = 0; m < NA; ++m) {
+            const int q = tid + m * NT, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            *(f32x4*)(As + r * LA + d4) = ra[m];
+            *(f32x4*)(Bs + r * LB + d4) = rb[m];
+        }
+#pragma unroll
+        for (int m = 0; m < NX; ++m) {
+            const int q = tid + m * NT, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
+            *(f32x4*)(Xs + r * LX + c4) = rx[m];
+        }
+        for (int q = tid; q < RW * DK / 4; q += NT) {
+            const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
+        }
+        __syncthreads();
+        if (it + 1 < NC) fetch(BACK ? c - 1 : c + 1);  // in flight during this chunk's products
+        // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns rows 16 w .. 16 w + 15, both column tiles
+        {
+            f32x4 acc[RW / 16];
+#pragma unroll
+            for (int y = 0; y < RW / 16; ++y) acc[y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int k = 0; k < DK; k += 4) {
+                const float a = As[(16 * w + c16) * LA + k + G];
+#pragma unroll
+                for (int y = 0; y < RW / 16; ++y)
+                    acc[y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, St[(16 * y + c16) * LS + k + G], acc[y], 0, 0, 0);
+            }
+#pragma unroll
+            for (int y = 0; y < RW / 16; ++y)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * w + 4 * G + v, i = 16 * y + c16;
+                    const float x = Xs[r * LX + i] + SG1 * acc[y][v];
+                    Xs[r * LX + i] = x;
+                    rec[OFF_XO + (size_t)r * DV + row0 + i] = x;
+                }
+        }
+        __syncthreads();
+        // St = e^{g_last} St (+ F rows)
+#pragma unroll
+        for (int m = 0; m < NF; ++m) {
+            const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            f32x4 x = *(const f32x4*)(St + i * LS + d4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = BACK ? fmaf(egl, x[u], fcur[m][u]) : egl * x[u];
+            *(f32x4*)(St + i * LS + d4) = x;
+        }
+        __syncthreads();
+        // St[i][d] += SG2 * sum_r X[r][i] B[r][d]: wave w owns column tiles of one row tile
+        {
+            constexpr int DT = DK / 16 / (4 / (RW / 16));  // column tiles per wave
+            const int yt = w % (RW / 16), d0 = (w / (RW / 16)) * DT;
+            f32x4 acc[DT];
+#pragma unroll
+            for (int x = 0; x < DT; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k = 0; k < C; k += 4) {
+                const float a = Xs[(k + G) * LX + 16 * yt + c16];
+#pragma unroll
+                for (int x = 0; x < DT; ++x)
+                    acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[(k + G) * LB + 16 * (d0 + x) + c16], acc[x], 0, 0, 0);
+            }
+#pragma unroll
+            for (int x = 0; x < DT; ++x)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 16 * yt + 4 * G + v, d = 16 * (d0 + x) + c16;
+                    St[i * LS + d] += SG2 * acc[x][v];
+                }
+        }
     }
     __syncthreads();
-    for (int c = 0; c < NC; ++c) {
-        float* rec = ws + (bh * NC + c) * L::PER;
-        for (int i = tid; i < RB * DK; i += NT) {
-            const int r = i / DK, d = i % DK;
-            rec[L::SIN + (size_t)(row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
+    if (sfinal)
+        for (int q = tid; q < RW * DK / 4; q += NT) {
+            const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            *(f32x4*)(sfinal + (bh * DV + row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
         }
-        // Delta[:, rows] = U[:, rows] - W S_in[rows, :]^T
-        tgemm<C, RB, DK, true, false>(stage,
-                                      [&](int r, int d) { return rec[L::W + (size_t)r * DK + d]; },
-                                      [&](int d, int i) { return Sb[i * (DK + 1) + d]; },
-                                      [&](int r, int i, float x) {
-                                          const float y = rec[L::U + (size_t)r * DV + row0 + i] - x;
-                                          Db[r * (RB + 1) + i] = y;
-                                          rec[L::DL + (size_t)r * DV + row0 + i] = y;
-                                      });
-        __syncthreads();
-        // S[rows, :] = e^{g_last} S[rows, :] + Delta[:, rows]^T KD
-        const float egl = rec[L::EGL];
-        tgemm<RB, DK, C, false, true>(stage, [&](int i, int r) { return Db[r * (RB + 1) + i]; },
-                                      [&](int r, int d) { return rec[L::KD + (size_t)r * DK + d]; },
-                                      [&](int i, int d, float x) {
-                                          Sb[i * (DK + 1) + d] = fmaf(egl, Sb[i * (DK + 1) + d], x);
-                                      });
-        __syncthreads();
-    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -295,55 +407,6 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
     tgemm<DV, DK, C, false, true>(stage, [&](int i, int r) { return orow(r, i); },
                                   [&](int r, int d) { return expf(gs[r]) * qrow(r, d); },
                                   [&](int i, int d, float x) { rec[L::F + (size_t)i * DK + d] = x; });
-}
-
-// ---------------------------------------------------------------------------------------------
-// bcarry: reverse state-gradient walk, 16 rows of dS per workgroup
-// ---------------------------------------------------------------------------------------------
-template <int DK, int DV>
-__global__ __launch_bounds__(NT) void gdn_bwd_bcarry(const float* __restrict__ dSf, float* __restrict__ dinit,
-                                                     float* __restrict__ ws, int H, int NC) {
-    using L = WsLay<DK, DV>;
-    __shared__ float stage[STAGE_FLOATS];
-    __shared__ float Sb[RB * (DK + 1)], Db[C * (RB + 1)];
-    const int row0 = (int)blockIdx.x * RB, h = (int)blockIdx.y, b = (int)blockIdx.z, tid = (int)threadIdx.x;
-    const size_t bh = (size_t)b * H + h;
-    for (int i = tid; i < RB * DK; i += NT) {
-        const int r = i / DK, d = i % DK;
-        Sb[r * (DK + 1) + d] = dSf ? dSf[(bh * DV + row0 + r) * DK + d] : 0.0f;
-    }
-    __syncthreads();
-    for (int c = NC - 1; c >= 0; --c) {
-        float* rec = ws + (bh * NC + c) * L::PER;
-        for (int i = tid; i < RB * DK; i += NT) {
-            const int r = i / DK, d = i % DK;
-            rec[L::DSO + (size_t)(row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
-        }
-        // dDelta[:, rows] = E[:, rows] + KD dS_out[rows, :]^T
-        tgemm<C, RB, DK, true, false>(stage,
-                                      [&](int r, int d) { return rec[L::KD + (size_t)r * DK + d]; },
-                                      [&](int d, int i) { return Sb[i * (DK + 1) + d]; },
-                                      [&](int r, int i, float x) {
-                                          const float y = rec[L::E + (size_t)r * DV + row0 + i] + x;
-                                          Db[r * (RB + 1) + i] = y;
-                                          rec[L::DDL + (size_t)r * DV + row0 + i] = y;
-                                      });
-        __syncthreads();
-        // dS_in[rows, :] = e^{g_last} dS_out[rows, :] + F[rows, :] - dDelta[:, rows]^T W
-        const float egl = rec[L::EGL];
-        tgemm<RB, DK, C, false, true>(stage, [&](int i, int r) { return Db[r * (RB + 1) + i]; },
-                                      [&](int r, int d) { return rec[L::W + (size_t)r * DK + d]; },
-                                      [&](int i, int d, float x) {
-                                          Sb[i * (DK + 1) + d] = fmaf(egl, Sb[i * (DK + 1) + d],
-                                                                      rec[L::F + (size_t)(row0 + i) * DK + d] - x);
-                                      });
-        __syncthreads();
-    }
-    if (dinit)
-        for (int i = tid; i < RB * DK; i += NT) {
-            const int r = i / DK, d = i % DK;
-            dinit[(bh * DV + row0 + r) * DK + d] = Sb[r * (DK + 1) + d];
-        }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -549,13 +612,13 @@ template <typename T, int DK, int DV>
 static void launch_bwd_typed(const GdnBwdArgs& a, hipStream_t s) {
     const int NC = (a.T + C - 1) / C;
     float* ws = (float*)a.workspace;
-    const dim3 gc(NC, a.H, a.B), gr(DV / RB, a.H, a.B);
+    const dim3 gc(NC, a.H, a.B), gr(DV / RW, a.H, a.B);
     hipLaunchKernelGGL((gdn_bwd_prep<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.k, (const T*)a.v, a.alpha, a.beta,
                        ws, a.T, a.H, NC);
-    hipLaunchKernelGGL((gdn_bwd_fcarry<DK, DV>), gr, dim3(NT), 0, s, a.init_state, ws, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, false>), gr, dim3(NT), 0, s, a.init_state, nullptr, ws, a.H, NC);
     hipLaunchKernelGGL((gdn_bwd_pre<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.q, (const T*)a.k, (const T*)a.dO, ws,
                        a.T, a.H, NC);
-    hipLaunchKernelGGL((gdn_bwd_bcarry<DK, DV>), gr, dim3(NT), 0, s, a.dS_final, a.d_init, ws, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, true>), gr, dim3(NT), 0, s, a.dS_final, a.d_init, ws, a.H, NC);
     hipLaunchKernelGGL((gdn_bwd_post<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                        a.alpha, a.beta, (const T*)a.dO, (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dalpha, a.dbeta, ws, a.T,
                        a.H, NC);
