@@ -64,37 +64,59 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
 #pragma unroll
         for (int y = 0; y < CT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
     // software pipeline: the next K slice is fetched into registers while the current one is
-    // multiplied, so the latency of the operand loads overlaps the MFMAs
-    constexpr int PA = M * KS / NT, PB = N * KS / NT;
-    static_assert(M * KS % NT == 0 && N * KS % NT == 0, "staging split");
-    float ra[PA], rb[PB];
+    // multiplied, so the latency of the operand loads overlaps the MFMAs.  Each thread moves runs
+    // of four elements along the operand's contiguous direction (one 16-byte load where the
+    // source is a row-major fp32 array, and consecutive LDS slots where the slice row is contiguous)
+    constexpr int PA = M * KS / NT / 4, PB = N * KS / NT / 4;
+    static_assert(M * KS % (NT * 4) == 0 && N * KS % (NT * 4) == 0, "staging split");
+    float ra[PA][4], rb[PB][4];
+    auto a_pos = [&](int m, int& i, int& kk) {  // first element of run m of this thread
+        const int q = tid + m * NT;
+        if (AK) { i = q / (KS / 4); kk = (q % (KS / 4)) * 4; }
+        else { kk = q / (M / 4); i = (q % (M / 4)) * 4; }
+    };
+    auto b_pos = [&](int m, int& j, int& kk) {
+        const int q = tid + m * NT;
+        if (BJ) { kk = q / (N / 4); j = (q % (N / 4)) * 4; }
+        else { j = q / (KS / 4); kk = (q % (KS / 4)) * 4; }
+    };
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int m = 0; m < PA; ++m) {
-            const int idx = tid + m * NT;
-            const int i = AK ? idx / KS : idx % M, kk = AK ? idx % KS : idx / M;
-            ra[m] = la(i, k0 + kk);
+            int i, kk;
+            a_pos(m, i, kk);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ra[m][u] = AK ? la(i, k0 + kk + u) : la(i + u, k0 + kk);
         }
 #pragma unroll
         for (int m = 0; m < PB; ++m) {
-            const int idx = tid + m * NT;
-            const int j = BJ ? idx % N : idx / KS, kk = BJ ? idx / N : idx % KS;
-            rb[m] = lb(k0 + kk, j);
+            int j, kk;
+            b_pos(m, j, kk);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rb[m][u] = BJ ? lb(k0 + kk, j + u) : lb(k0 + kk + u, j);
         }
     };
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += KS) {
 #pragma unroll
         for (int m = 0; m < PA; ++m) {
-            const int idx = tid + m * NT;
-            const int i = AK ? idx / KS : idx % M, kk = AK ? idx % KS : idx / M;
-            sA[kk * LDA + i] = ra[m];
+            int i, kk;
+            a_pos(m, i, kk);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (AK) sA[(kk + u) * LDA + i] = ra[m][u];
+                else sA[kk * LDA + i + u] = ra[m][u];
+            }
         }
 #pragma unroll
         for (int m = 0; m < PB; ++m) {
-            const int idx = tid + m * NT;
-            const int j = BJ ? idx % N : idx / KS, kk = BJ ? idx / N : idx % KS;
-            sB[kk * LDB + j] = rb[m];
+            int j, kk;
+            b_pos(m, j, kk);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (BJ) sB[kk * LDB + j + u] = rb[m][u];
+                else sB[(kk + u) * LDB + j] = rb[m][u];
+            }
         }
         __syncthreads();
         if (k0 + KS < K) fetch(k0 + KS);
