@@ -67,9 +67,11 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
     // multiplied, so the latency of the operand loads overlaps the MFMAs.  Each thread moves runs
     // of four elements along the operand's contiguous direction (one 16-byte load where the
     // source is a row-major fp32 array, and consecutive LDS slots where the slice row is contiguous)
-    constexpr int PA = M * KS / NT / 4, PB = N * KS / NT / 4;
+    constexpr int PA = M * KS / NT / 4, PB = N * KS / NT / 4, NS = K / KS;
     static_assert(M * KS % (NT * 4) == 0 && N * KS % (NT * 4) == 0, "staging split");
-    float ra[PA][4], rb[PB][4];
+    // two slices in flight: slice s + 2 is requested while slice s is multiplied (the slice loop
+    // is unrolled so the register buffers are indexed statically)
+    float ra[2][PA][4], rb[2][PB][4];
     auto a_pos = [&](int m, int& i, int& kk) {  // first element of run m of this thread
         const int q = tid + m * NT;
         if (AK) { i = q / (KS / 4); kk = (q % (KS / 4)) * 4; }
@@ -80,32 +82,35 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
         if (BJ) { kk = q / (N / 4); j = (q % (N / 4)) * 4; }
         else { j = q / (KS / 4); kk = (q % (KS / 4)) * 4; }
     };
-    auto fetch = [&](int k0) {
+    auto fetch = [&](int buf, int k0) {
 #pragma unroll
         for (int m = 0; m < PA; ++m) {
             int i, kk;
             a_pos(m, i, kk);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) ra[m][u] = AK ? la(i, k0 + kk + u) : la(i + u, k0 + kk);
+            for (int u = 0; u < 4; ++u) ra[buf][m][u] = AK ? la(i, k0 + kk + u) : la(i + u, k0 + kk);
         }
 #pragma unroll
         for (int m = 0; m < PB; ++m) {
             int j, kk;
             b_pos(m, j, kk);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) rb[m][u] = BJ ? lb(k0 + kk, j + u) : lb(k0 + kk + u, j);
+            for (int u = 0; u < 4; ++u) rb[buf][m][u] = BJ ? lb(k0 + kk, j + u) : lb(k0 + kk + u, j);
         }
     };
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += KS) {
+    fetch(0, 0);
+    if (NS > 1) fetch(1, KS);
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        const int buf = sl & 1;
 #pragma unroll
         for (int m = 0; m < PA; ++m) {
             int i, kk;
             a_pos(m, i, kk);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (AK) sA[(kk + u) * LDA + i] = ra[m][u];
-                else sA[kk * LDA + i + u] = ra[m][u];
+                if (AK) sA[(kk + u) * LDA + i] = ra[buf][m][u];
+                else sA[kk * LDA + i + u] = ra[buf][m][u];
             }
         }
 #pragma unroll
@@ -114,12 +119,12 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
             b_pos(m, j, kk);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (BJ) sB[kk * LDB + j + u] = rb[m][u];
-                else sB[(kk + u) * LDB + j] = rb[m][u];
+                if (BJ) sB[kk * LDB + j + u] = rb[buf][m][u];
+                else sB[(kk + u) * LDB + j] = rb[buf][m][u];
             }
         }
         __syncthreads();
-        if (k0 + KS < K) fetch(k0 + KS);
+        if (sl + 2 < NS) fetch(buf, (sl + 2) * KS);
 #pragma unroll
         for (int kk = 0; kk < KS; kk += 4) {
             float a[RT], b[CT];
