@@ -231,6 +231,25 @@ def test_polar_train_and_backward_validation():
     assert g.lib.atma_polar_attn_bwd_workspace_bytes(1, 16, 4, 2, 96) == 0
 
 
+def test_gdn_backward_validation():
+    f = g.lib.atma_gdn_bwd
+
+    def call(dO=FAKE, B=1, T=16, H=1, Dk=64, Dv=64, chunk=64, dt=g.ATMA_BF16, ws=FAKE, wsb=1 << 30, dq=FAKE):
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, dO, NULL, dq, FAKE, FAKE, FAKE, FAKE, NULL, B, T, H, Dk, Dv,
+                 chunk, dt, ws, wsb, NULL)
+
+    assert call(dO=NULL) == g.ATMA_ERR_NULL
+    assert call(dq=NULL) == g.ATMA_ERR_NULL
+    assert call(T=0) == g.ATMA_ERR_SHAPE
+    assert call(Dk=96) == g.ATMA_ERR_UNSUPPORTED
+    assert call(chunk=32) == g.ATMA_ERR_UNSUPPORTED
+    assert call(dt=3) == g.ATMA_ERR_UNSUPPORTED
+    assert call(ws=NULL) == g.ATMA_ERR_WORKSPACE
+    need = g.lib.atma_gdn_bwd_workspace_bytes(1, 16, 1, 64, 64, 64, g.ATMA_BF16)
+    assert need > 0 and call(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
+    assert g.lib.atma_gdn_bwd_workspace_bytes(1, 16, 1, 64, 64, 32, g.ATMA_BF16) == 0
+
+
 def test_canon_validation():
     c = g.lib.atma_canon
     Y2 = ctypes.c_void_p(0x2000)  # output, distinct from the input
