@@ -16,16 +16,18 @@
  *  - Every argument is validated on the host BEFORE anything is launched; a call that
  *    returns an error has launched nothing.  After the launches a failed
  *    hipGetLastError() returns ATMA_ERR_LAUNCH.  No C++ exception crosses the ABI.
- *  - Supported shapes: memory head widths Dk, Dv in {64, 128} (fp32 or bf16); Polar
- *    head width D = 64 (bf16); chunk = 64; Hq a multiple of Hkv; every size >= 1;
- *    B * T * H * D below 2^31 for every prefill tensor; a decode KV cache may exceed
- *    2^31 elements in total but Lmax * Hkv * D must stay below 2^31.
+ *  - Supported shapes: memory head widths Dk, Dv in {64, 128} (fp32 or bf16); Polar and
+ *    control-core head width D in {64, 128} (bf16); chunk = 64; Hq a multiple of Hkv; every
+ *    size >= 1; B * T * H * D below 2^31 for every prefill tensor; a decode KV cache may
+ *    exceed 2^31 elements in total but Lmax * Hkv * D must stay below 2^31.
  *  - Preconditions that are documented but not checked (they live on the device):
  *    memory q and k rows have unit L2 norm (Appendix A.2 premise); alpha in (0, 1];
  *    beta in [0, 1]; mag_beta >= 0.  Violating them gives defined but meaningless
  *    numbers, never out-of-bounds accesses.
  *  - Numerics: bf16 operands with fp32 accumulation and fp32 statistics; the memory
  *    state is fp32 in HBM and in registers.  Outputs are written in the input dtype.
+ *    The memory backward computes in fp32 throughout; the Polar backward contracts on
+ *    bf16 MFMA like the forward.  Parameter and gate gradients are fp32.
  */
 #ifndef ATMA_H
 #define ATMA_H
