@@ -83,7 +83,7 @@ def _declare(lib):
     lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, i, _dp, _dp, _dp, _dp]
     lib.oracle_canon.argtypes = [i, i, i, i, i, i, d, _dp, _dp, _dp, _dp]
     lib.oracle_gdn_bwd.argtypes = [i, i, i, i, i] + [_dp] * 6 + [_dp, _dp] + [_dp] * 6 + [i]
-    lib.oracle_polar_bwd.argtypes = [i, i, i, i, i] + [_dp] * 3 + [_dp] * 5 + [d, _dp] + [_dp] * 8 + [i]
+    lib.oracle_polar_bwd.argtypes = [i, i, i, i, i] + [_dp] * 3 + [_dp] * 5 + [d, _dp] + [_dp] * 9 + [i]
     for f in ("oracle_gdn_sequential", "oracle_gdn_chunked", "oracle_polar_fwd", "oracle_polar_decode",
               "oracle_threads_used", "oracle_rope", "oracle_softmax_attn", "oracle_softmax_decode", "oracle_canon",
               "oracle_gdn_bwd", "oracle_polar_bwd"):
@@ -280,7 +280,8 @@ def gdn_bwd(q, k, v, alpha, beta, do, init_state=None, dS_final=None, threads=0)
 def polar_bwd(q, k, v, params, do, threads=0):
     """Gradients of causal Polar attention (materialised form) for upstream dO [B,T,Hq,D].
     Returns dict dq, dk, dv and d_temp_raw, d_null_slope_raw, d_null_bias, d_mag_beta [Hq],
-    d_v_null [Hq, D]."""
+    d_v_null [Hq, D]; also abs_<name> [Hq] for the four scalar parameters: the sum over rows of
+    the magnitudes of their per-row contributions (the natural error scale of those sums)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -292,10 +293,14 @@ def polar_bwd(q, k, v, params, do, threads=0):
     for n in ("d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta"):
         out[n] = np.zeros(Hq)
     out["d_v_null"] = np.zeros((Hq, D))
+    absum = np.zeros((4, Hq))
     rc = _load().oracle_polar_bwd(
         B, T, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(p["temp_raw"]), _ptr(p["null_slope_raw"]),
         _ptr(p["null_bias"]), _ptr(p["mag_beta"]), _ptr(p["v_null"]), p["eps"], _ptr(g), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["d_temp_raw"]), _ptr(out["d_null_slope_raw"]),
-        _ptr(out["d_null_bias"]), _ptr(out["d_mag_beta"]), _ptr(out["d_v_null"]), int(threads))
+        _ptr(out["d_null_bias"]), _ptr(out["d_mag_beta"]), _ptr(out["d_v_null"]), _ptr(absum), int(threads))
     assert rc == 0
+    # scale of each scalar parameter gradient as a sum over rows: sum of the rows' magnitudes
+    for e, n in enumerate(("d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta")):
+        out["abs_" + n] = absum[e]
     return out

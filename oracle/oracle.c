@@ -814,12 +814,16 @@ int oracle_gdn_bwd(int B, int T, int H, int Dk, int Dv,
  *   dt = sum_j dl_j (q . k_j) / sqrt(D) + dl_0 nu;   dnu = dl_0 t      (null logit l_0 = t nu)
  *   t = 1 + softplus(temp_raw) ln n:             dtemp_raw += dt ln(n) sigmoid(temp_raw)
  *   nu = b + softplus(slope_raw) sqrt(ln(n+1)):  dnull_bias += dnu;  dslope_raw += dnu sqrt(ln(n+1)) sigmoid(slope_raw)
- * dpar[0..3] accumulate dtemp_raw, dslope_raw, dnull_bias, dbeta of head h; dpar[4..4+D) dv_null. */
+ * dpar[0..3] accumulate dtemp_raw, dslope_raw, dnull_bias, dbeta of head h; dpar[4..4+D) dv_null.
+ * dabs[0..3] accumulate the magnitudes of the same four per-row contributions: the scale of those
+ * sums, against which their rounding error is judged (the terms of a row sum can cancel).  The
+ * temperature's row term is itself a sum over keys (dl_j q.k_j / sqrt(D), plus the null's), so its
+ * magnitude is taken term by term. */
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 static void polar_row_backward(const double* qi, const double* K, const double* V, size_t kstride, long n, int D,
                                int h, const polar_par* P, const double* g, double* dqi, double* dK, double* dV,
-                               double* dpar, double* w, double* qk) {
+                               double* dpar, double* dabs, double* w, double* qk) {
     const double a = softplus(P->temp_raw[h]);
     const double sl = softplus(P->null_slope_raw[h]);
     const double t = 1.0 + a * log((double)n);
@@ -863,6 +867,7 @@ static void polar_row_backward(const double* qi, const double* K, const double* 
     for (int x = 0; x < D; ++x) ds[x] = (mu * g[x] - (clamped ? 0.0 : (s[x] / den) * cdc)) / den;
     const double dme = dmu * (1.0 - mu * mu) * be / (1.0 + me);
     dpar[3] += dmu * (1.0 - mu * mu) * log1p(me);
+    dabs[3] += fabs(dmu * (1.0 - mu * mu) * log1p(me));
     const double dR = dme * 3.0 * R * R / Q2;
     const double dQ2 = -dme * R * R * R / (Q2 * Q2);
     /* weights: dw_j kept in w's place after Sigma is formed */
@@ -879,10 +884,11 @@ static void polar_row_backward(const double* qi, const double* K, const double* 
     }
     for (int x = 0; x < D; ++x) dpar[4 + x] += w0 * ds[x];
     /* softmax and logits */
-    double dt = 0.0;
+    double dt = 0.0, dt_mag = 0.0;
     for (long j = 0; j < n; ++j) {
         const double dl = w[j] * (qk[j + n] - Sig);
         dt += dl * qk[j];
+        dt_mag += fabs(dl * qk[j]);
         for (int x = 0; x < D; ++x) {
             dqi[x] += dl * t * isd * K[j * kstride + x];
             dK[j * kstride + x] += dl * t * isd * qi[x];
@@ -894,6 +900,9 @@ static void polar_row_backward(const double* qi, const double* K, const double* 
     dpar[0] += dt * log((double)n) * sigmoid(P->temp_raw[h]);
     dpar[1] += dnu * sqrt(log((double)n + 1.0)) * sigmoid(P->null_slope_raw[h]);
     dpar[2] += dnu;
+    dabs[0] += (dt_mag + fabs(dl0 * nu)) * log((double)n) * sigmoid(P->temp_raw[h]);
+    dabs[1] += fabs(dnu * sqrt(log((double)n + 1.0)) * sigmoid(P->null_slope_raw[h]));
+    dabs[2] += fabs(dnu);
     free(s);
 }
 
@@ -902,6 +911,7 @@ typedef struct {
     const double *q, *k, *v, *dO;
     polar_par P;
     double *dq, *dk, *dv, *dpar; /* dpar [B, Hq, 4 + D] partials, summed over b afterwards */
+    double* dabs;                /* [B, Hq, 4] magnitudes of the scalar parameter contributions */
 } polar_bwd_ctx;
 
 /* task = b * Hkv + hk: every query head of the group and every row, so that the task alone
@@ -925,7 +935,8 @@ static void polar_bwd_task(long task, void* p) {
             double* dqi = c->dq + row * D;
             for (int x = 0; x < D; ++x) dqi[x] = 0.0;
             polar_row_backward(c->q + row * D, K, V, stride, i + 1, D, h, &c->P, c->dO + row * D, dqi, dK, dV,
-                               c->dpar + ((size_t)b * c->Hq + h) * (4 + D), w, qk);
+                               c->dpar + ((size_t)b * c->Hq + h) * (4 + D), c->dabs + ((size_t)b * c->Hq + h) * 4,
+                               w, qk);
         }
     free(w);
     free(qk);
@@ -933,18 +944,20 @@ static void polar_bwd_task(long task, void* p) {
 
 /* Gradients of causal Polar attention (materialised form) given dO [B, T, Hq, D].
  * Outputs dq [B, T, Hq, D]; dk, dv [B, T, Hkv, D]; d_temp_raw, d_null_slope_raw, d_null_bias,
- * d_mag_beta [Hq]; d_v_null [Hq, D]. */
+ * d_mag_beta [Hq]; d_v_null [Hq, D]; d_abs [4, Hq] or NULL: the sums of the magnitudes of the
+ * per-row contributions to the four scalar parameter gradients (tolerance scale for tests). */
 int oracle_polar_bwd(int B, int T, int Hq, int Hkv, int D, const double* q, const double* k, const double* v,
                      const double* temp_raw, const double* null_slope_raw, const double* null_bias,
                      const double* mag_beta, const double* v_null, double eps, const double* dO,
                      double* dq, double* dk, double* dv, double* d_temp_raw, double* d_null_slope_raw,
-                     double* d_null_bias, double* d_mag_beta, double* d_v_null, int nthreads) {
+                     double* d_null_bias, double* d_mag_beta, double* d_v_null, double* d_abs, int nthreads) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return -1;
     if (!q || !k || !v || !temp_raw || !null_slope_raw || !null_bias || !mag_beta || !v_null || !dO) return -1;
     if (!dq || !dk || !dv || !d_temp_raw || !d_null_slope_raw || !d_null_bias || !d_mag_beta || !d_v_null) return -1;
     double* dpar = (double*)calloc((size_t)B * Hq * (4 + D), sizeof(double));
+    double* dabs = (double*)calloc((size_t)B * Hq * 4, sizeof(double));
     polar_bwd_ctx c = {B, T, Hq, Hkv, D, q, k, v, dO, {temp_raw, null_slope_raw, null_bias, mag_beta, v_null, eps},
-                       dq, dk, dv, dpar};
+                       dq, dk, dv, dpar, dabs};
     run_tasks(polar_bwd_task, &c, (long)B * Hkv, nthreads);
     for (int h = 0; h < Hq; ++h) {
         double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -958,7 +971,13 @@ int oracle_polar_bwd(int B, int T, int Hq, int Hkv, int D, const double* q, cons
         d_null_slope_raw[h] = acc[1];
         d_null_bias[h] = acc[2];
         d_mag_beta[h] = acc[3];
+        for (int e = 0; d_abs && e < 4; ++e) {
+            double m = 0.0;
+            for (int b = 0; b < B; ++b) m += dabs[((size_t)b * Hq + h) * 4 + e];
+            d_abs[(size_t)e * Hq + h] = m;
+        }
     }
     free(dpar);
+    free(dabs);
     return 0;
 }

@@ -70,6 +70,12 @@ def test_gdn_bwd_matches_oracle(atma, B, T, H, Dk, Dv, dtype, init, final):
     _check(atma, B, T, H, Dk, Dv, dtype, init, final, seed=100 + T + Dk + Dv)
 
 
+@pytest.mark.parametrize("T", [63, 64, 65, 128, 129])
+def test_gdn_bwd_chunk_edges(atma, T):
+    """Lengths at and around the 64-token chunk (a ragged last chunk of 1 and of 63 tokens)."""
+    _check(atma, 1, T, 2, 64, 128, "bf16", True, True, seed=300 + T)
+
+
 def test_gdn_bwd_is_deterministic(atma):
     inp = workloads.make_gdn_inputs(1, 150, 2, 128, 128, seed=3)
     do = torch.randn(1, 150, 2, 128, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)

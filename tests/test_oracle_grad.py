@@ -164,3 +164,17 @@ def test_polar_grad_single_key_row():
     g = oracle.polar_bwd(q, k, v, params, dO)
     dq, k0 = g["dq"][0, 0, 0], k[0, 0, 0]
     assert np.allclose(dq - (dq @ k0) / (k0 @ k0) * k0, 0.0, atol=1e-12)
+
+
+def test_polar_grad_magnitude_sums():
+    """The magnitude sums returned beside the scalar parameter gradients bound them (triangle
+    inequality) and equal their absolute value when only one row contributes (T = 1)."""
+    q, k, v, params, dO = _polar_case(8, Hq=2, Hkv=1)
+    g = oracle.polar_bwd(q, k, v, params, dO)
+    for n in ("d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta"):
+        assert np.all(g["abs_" + n] >= np.abs(g[n]) - 1e-15)
+    g1 = oracle.polar_bwd(q[:, :1], k[:, :1], v[:, :1], params, dO[:, :1])
+    for n in ("d_null_slope_raw", "d_null_bias", "d_mag_beta"):
+        assert np.allclose(g1["abs_" + n], np.abs(g1[n]), rtol=1e-12, atol=1e-300)
+    # row 0 sees one key and n = 1 (ln n = 0): it adds nothing to the temperature's gradient
+    assert g1["abs_d_temp_raw"][0] == 0.0 and g1["d_temp_raw"][0] == 0.0
