@@ -188,7 +188,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     using L = WsLay<DK, DV>;
     __shared__ float stage[STAGE_FLOATS];
     __shared__ float Am[C * LD64], Tm[C * LD64];
-    __shared__ float gs[C], bs[C];
+    __shared__ float gs[C], bs[C], g2[C], bsg[C], ekd[C];
     const ChunkPos P = chunk_pos(Tlen, H, NC);
     float* rec = ws + P.cid * L::PER;
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h;
@@ -204,6 +204,11 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
         }
         gs[tid] = la;
         rec[L::G + tid] = la;
+        // exponentials of the gates once per row (base 2 on the hardware unit)
+        const float l2 = la * kLog2e, gl2 = __shfl(la, P.n - 1, 64) * kLog2e;
+        g2[tid] = l2;
+        bsg[tid] = bs[tid] * fast_exp2(l2);
+        ekd[tid] = fast_exp2(gl2 - l2);
     }
     __syncthreads();
     const int n = P.n;
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     // A = strict_lower(diag(beta) (K K^T) o E)
     tgemm<C, C, DK, true, false>(stage, krow, [&](int d, int s) { return krow(s, d); },
                                  [&](int r, int s, float x) {
-                                     Am[r * LD64 + s] = s < r ? bs[r] * expf(gs[r] - gs[s]) * x : 0.0f;
+                                     Am[r * LD64 + s] = s < r ? bs[r] * fast_exp2(g2[r] - g2[s]) * x : 0.0f;
                                  });
     __syncthreads();
     // Tinv = (I + A)^{-1}, column j by forward substitution: T[r][j] = [r == j] - sum_{j<=s<r} A[r][s] T[s][j];
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     for (int i = tid; i < C * C; i += NT) rec[L::TI + i] = Tm[(i / C) * LD64 + (i % C)];
     // W = Tinv diag(beta e^g) K,  U = Tinv diag(beta) V
     tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return Tm[r * LD64 + s]; },
-                                [&](int s, int d) { return bs[s] * expf(gs[s]) * krow(s, d); },
+                                [&](int s, int d) { return bsg[s] * krow(s, d); },
                                 [&](int r, int d, float x) { rec[L::W + (size_t)r * DK + d] = x; });
     tgemm<C, DV, C, true, true>(stage, [&](int r, int s) { return Tm[r * LD64 + s]; },
                                 [&](int s, int d) { return s < n ? bs[s] * ld(vc, (size_t)s * vs + d) : 0.0f; },
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     const float glast = gs[n - 1];
     for (int i = tid; i < C * DK; i += NT) {
         const int r = i / DK, d = i % DK;
-        rec[L::KD + i] = expf(glast - gs[r]) * krow(r, d);
+        rec[L::KD + i] = ekd[r] * krow(r, d);
     }
     if (tid == 0) rec[L::EGL] = expf(glast);
 }
@@ -413,11 +418,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
     using L = WsLay<DK, DV>;
     __shared__ float stage[STAGE_FLOATS];
     __shared__ float Pm[C * LD64];
-    __shared__ float gs[C];
+    __shared__ float g2[C], eg[C];
     const ChunkPos P = chunk_pos(Tlen, H, NC);
     float* rec = ws + P.cid * L::PER;
     const int tid = (int)threadIdx.x, n = P.n;
-    if (tid < C) gs[tid] = rec[L::G + tid];
+    if (tid < C) {
+        g2[tid] = rec[L::G + tid] * kLog2e;
+        eg[tid] = fast_exp2(g2[tid]);
+    }
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *oc = dO + tok0 * DV;
@@ -426,13 +434,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
     tgemm<C, C, DK, true, false>(stage, qrow,
                                  [&](int d, int s) { return s < n ? ld(kc, (size_t)s * ks + d) : 0.0f; },
                                  [&](int r, int s, float x) {
-                                     Pm[r * LD64 + s] = s <= r ? x * expf(gs[r] - gs[s]) : 0.0f;
+                                     Pm[r * LD64 + s] = s <= r ? x * fast_exp2(g2[r] - g2[s]) : 0.0f;
                                  });
     __syncthreads();
     tgemm<C, DV, C, false, true>(stage, [&](int s, int r) { return Pm[r * LD64 + s]; }, orow,
                                  [&](int s, int j, float x) { rec[L::E + (size_t)s * DV + j] = x; });
     tgemm<DV, DK, C, false, true>(stage, [&](int i, int r) { return orow(r, i); },
-                                  [&](int r, int d) { return expf(gs[r]) * qrow(r, d); },
+                                  [&](int r, int d) { return eg[r] * qrow(r, d); },
                                   [&](int i, int d, float x) { rec[L::F + (size_t)i * DK + d] = x; });
 }
 
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     // The 64 x 64 intermediates live in this chunk's workspace (cached; the workgroup's working set is
     // small) rather than LDS, so that two workgroups fit on a CU.
     __shared__ float stage[STAGE_FLOATS];
-    __shared__ float gs[C], bs[C], rowv[6][C], red[NT];
+    __shared__ float gs[C], bs[C], rowv[6][C], red[NT], g2[C], eg[C], bsg[C], ekd[C];
     const ChunkPos P = chunk_pos(Tlen, H, NC);
     float* rec = ws + P.cid * L::PER;
     constexpr int LD64 = C;  // row stride of the workspace 64 x 64 arrays
@@ -460,6 +468,11 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     if (tid < C) {
         gs[tid] = rec[L::G + tid];
         bs[tid] = tid < n ? beta[((size_t)P.b * Tlen + P.t0 + tid) * H + P.h] : 0.0f;
+        // exponentials of the gates once per row (base 2 on the hardware unit)
+        g2[tid] = gs[tid] * kLog2e;
+        eg[tid] = fast_exp2(g2[tid]);
+        bsg[tid] = bs[tid] * eg[tid];
+        ekd[tid] = fast_exp2(rec[L::G + n - 1] * kLog2e - g2[tid]);
     }
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         [&](int r, int j) {
             return j < DV ? rec[L::DDL + (size_t)r * DV + j] : rec[L::X1 + (size_t)r * DK + j - DV];
         },
-        [&](int j, int s) { return j < DV ? bs[s] * vrow(s, j) : bs[s] * expf(gs[s]) * krow(s, j - DV); },
+        [&](int j, int s) { return j < DV ? bs[s] * vrow(s, j) : bsg[s] * krow(s, j - DV); },
         [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
     // X3 = Tinv^T dDelta (and dv = beta o X3);  X4 = Tinv^T dW
     tgemm<C, DV, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
@@ -525,7 +538,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
 #pragma unroll 16
         for (int y = 0; y < C; ++y) {
             const int r = tid < C ? x : y, s = tid < C ? y : x;
-            const float e = s <= r ? expf(gs[r] - gs[s]) : 0.0f;  // never exp of the upper triangle
+            const float e = s <= r ? fast_exp2(g2[r] - g2[s]) : 0.0f;  // never exp of the upper triangle
             const float dA = dT[r * LD64 + s];
             const float aA = bs[r] * e * KK[r * LD64 + s];
             const float pP = s <= r ? QK[r * LD64 + s] * e : 0.0f;
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
 #pragma unroll
     for (int i = tid; i < C * C; i += NT) {
         const int r = i / C, s = i % C;
-        const float e = s <= r ? expf(gs[r] - gs[s]) : 0.0f;
+        const float e = s <= r ? fast_exp2(g2[r] - g2[s]) : 0.0f;
         dP[r * LD64 + s] *= e;
         Zm[r * LD64 + s] = dT[r * LD64 + s] * bs[r] * e;
     }
@@ -550,7 +563,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                 [&](int r, int d, float x) {
                                     if (r < n)
                                         dq[tok0 * DK + (size_t)r * ks + d] =
-                                            from_f32<T>(fmaf(expf(gs[r]), rec[L::X0 + (size_t)r * DK + d], x));
+                                            from_f32<T>(fmaf(eg[r], rec[L::X0 + (size_t)r * DK + d], x));
                                 });
     // dk = beta e^g o X4 + e^{g_last - g} o dKD + [(dP o E)^T | M | M^T] [Q; K; K]
     const float glast = gs[n - 1];
@@ -561,8 +574,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         [&](int kk, int d) { return kk < C ? qrow(kk, d) : krow(kk % C, d); },
         [&](int r, int d, float x) {
             if (r < n) {
-                const float y = bs[r] * expf(gs[r]) * rec[L::X4 + (size_t)r * DK + d] +
-                                expf(glast - gs[r]) * rec[L::X2 + (size_t)r * DK + d] + x;
+                const float y = bsg[r] * rec[L::X4 + (size_t)r * DK + d] + ekd[r] * rec[L::X2 + (size_t)r * DK + d] + x;
                 dk[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(y);
             }
         });
@@ -587,9 +599,9 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
             kd += __shfl_xor(kd, o, 4);
         }
         if (part == 0) {
-            const float eg = expf(gs[r]);
-            rowv[3][r] = rowv[2][r] + tv + eg * tw;                                         // dbeta
-            rowv[4][r] = rowv[0][r] - rowv[1][r] + bs[r] * eg * tw + eg * qg - kd;          // dg (less the last-row terms)
+            const float er = eg[r];
+            rowv[3][r] = rowv[2][r] + tv + er * tw;                                         // dbeta
+            rowv[4][r] = rowv[0][r] - rowv[1][r] + bs[r] * er * tw + er * qg - kd;          // dg (less the last-row terms)
             rowv[5][r] = kd;
         }
     }
