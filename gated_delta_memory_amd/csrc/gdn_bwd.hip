@@ -529,24 +529,32 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                 [&](int s, int c2) { return Zm[s * LD64 + c2]; },
                                 [&](int r, int c2, float x) { dT[r * LD64 + c2] = c2 < r ? -x : 0.0f; });
     __syncthreads();
-    // row and column sums over the n x n terms (threads 0..63 rows, 64..127 columns):
+    // row and column sums over the n x n terms:
     //   rowv[0] = rowsum(dA o A) + rowsum(dP o P),  rowv[1] = colsum(...) of the same,
-    //   rowv[2] = sum_s dA_rs E_rs k_r.k_s (beta's share through A)
-    if (tid < 2 * C) {
-        const int x = tid & (C - 1);
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll 16
-        for (int y = 0; y < C; ++y) {
-            const int r = tid < C ? x : y, s = tid < C ? y : x;
-            const float e = s <= r ? fast_exp2(g2[r] - g2[s]) : 0.0f;  // never exp of the upper triangle
-            const float dA = dT[r * LD64 + s];
-            const float aA = bs[r] * e * KK[r * LD64 + s];
-            const float pP = s <= r ? QK[r * LD64 + s] * e : 0.0f;
-            s1 = fmaf(dA, aA, fmaf(dP[r * LD64 + s], pP, s1));
-            s2 = fmaf(dA, e * KK[r * LD64 + s], s2);
+    //   rowv[2] = sum_s dA_rs E_rs k_r.k_s (beta's share through A).
+    // Thread t visits (r = t / 64 + 4 m, s = t % 64), m = 0..15: every visit reads whole rows of the
+    // workspace arrays (coalesced); a wave covers one row per visit, so row sums are wave
+    // reductions, and column sums stay in the thread (fixed s) until four partials meet in LDS.
+    {
+        const int sc = tid & (C - 1), w0 = tid >> 6;
+        float col = 0.f;
+#pragma unroll 4
+        for (int m = 0; m < C / 4; ++m) {
+            const int r = w0 + 4 * m;
+            const float e = sc <= r ? fast_exp2(g2[r] - g2[sc]) : 0.0f;  // never exp of the upper triangle
+            const float dA = dT[r * LD64 + sc], kk = KK[r * LD64 + sc];
+            const float pP = sc <= r ? QK[r * LD64 + sc] * e : 0.0f;
+            const float t1 = fmaf(dA, bs[r] * e * kk, dP[r * LD64 + sc] * pP);
+            const float r1 = wave_sum(t1), r2 = wave_sum(dA * e * kk);
+            col += t1;
+            if (sc == 0) {
+                rowv[0][r] = r1;
+                rowv[2][r] = r2;
+            }
         }
-        rowv[tid < C ? 0 : 1][x] = s1;
-        if (tid < C) rowv[2][x] = s2;
+        red[tid] = col;
+        __syncthreads();
+        if (tid < C) rowv[1][tid] = (red[tid] + red[tid + C]) + (red[tid + 2 * C] + red[tid + 3 * C]);
     }
     __syncthreads();
     // dP o E into dP, M = dA o beta E into Zm
@@ -578,19 +586,39 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                 dk[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(y);
             }
         });
-    // per-row dot products: 4 lanes per row
+    // per-row dot products: 4 lanes per row, each a contiguous quarter of it (16-byte loads of the
+    // fp32 workspace rows); padded rows contribute nothing (their q, k, v are zero)
     {
         const int r = tid >> 2, part = tid & 3;
+        constexpr int QK4 = DK / 4, QV4 = DV / 4;
         float tv = 0.f, tw = 0.f, qg = 0.f, kd = 0.f;
-#pragma unroll 8
-        for (int d = part; d < DK; d += 4) {
-            const float kr = krow(r, d);
-            tw = fmaf(rec[L::X4 + (size_t)r * DK + d], kr, tw);
-            qg = fmaf(rec[L::X0 + (size_t)r * DK + d], qrow(r, d), qg);
-            kd = fmaf(rec[L::X2 + (size_t)r * DK + d], rec[L::KD + (size_t)r * DK + d], kd);
+        if (r < n) {
+            const float* x4 = rec + L::X4 + (size_t)r * DK + part * QK4;
+            const float* x0 = rec + L::X0 + (size_t)r * DK + part * QK4;
+            const float* x2 = rec + L::X2 + (size_t)r * DK + part * QK4;
+            const float* kdp = rec + L::KD + (size_t)r * DK + part * QK4;
+            const float* x3 = rec + L::X3 + (size_t)r * DV + part * QV4;
+            const T* kp = kc + (size_t)r * ks + part * QK4;
+            const T* qp = qc + (size_t)r * ks + part * QK4;
+            const T* vp = vc + (size_t)r * vs + part * QV4;
+#pragma unroll
+            for (int d = 0; d < QK4; d += 4) {
+                const f32x4 a4 = *(const f32x4*)(x4 + d), a0 = *(const f32x4*)(x0 + d);
+                const f32x4 a2 = *(const f32x4*)(x2 + d), b2 = *(const f32x4*)(kdp + d);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    tw = fmaf(a4[u], ld(kp, d + u), tw);
+                    qg = fmaf(a0[u], ld(qp, d + u), qg);
+                    kd = fmaf(a2[u], b2[u], kd);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < QV4; j += 4) {
+                const f32x4 a3 = *(const f32x4*)(x3 + j);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) tv = fmaf(a3[u], ld(vp, j + u), tv);
+            }
         }
-#pragma unroll 8
-        for (int j = part; j < DV; j += 4) tv = fmaf(rec[L::X3 + (size_t)r * DV + j], vrow(r, j), tv);
 #pragma unroll
         for (int o = 1; o < 4; o <<= 1) {
             tv += __shfl_xor(tv, o, 4);
