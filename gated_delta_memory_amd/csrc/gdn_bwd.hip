@@ -25,7 +25,7 @@
 //   pre    (parallel over chunks)  P^T dO and dO^T QG
 //   walk   (sequential, reverse)   dS_out and dDelta per chunk, the gradient on the initial state
 //   post   (parallel over chunks)  every gradient above
-// Matrix products use one LDS-staged fp32 routine on v_mfma_f32_16x16x4_f32 (K in slices of 32).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
+// Matrix products use one LDS-staged fp32 routine on v_mfma_f32_16x16x4_f32 (K in slices of 16).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
 // beta = 0, alpha = 1), which keeps every formula exact for the real rows.
 #include "atma_device.hpp"
 #include "launch.hpp"
@@ -39,9 +39,12 @@ constexpr int KS = 16;   // k-slice of the tiled product
 constexpr int LD64 = C + 1;
 
 // C[M][N] = sum_k A(i, k) B(k, j), delivered element by element to epi(i, j, value).  A and B
-// come from functors (global memory or LDS); K slices of 32 are staged in LDS as sA [32][M + 16]
-// and sB [32][N + 16] (the padding of 16 puts the four k rows one fp32 MFMA reads on four
-// different 16-bank groups).  The product runs on v_mfma_f32_16x16x4_f32: lane l supplies
+// come from run functors (global memory or LDS) that return four consecutive elements along the
+// operand's contiguous direction: la(i, k) = A(i, k..k+3) if AK, else A(i..i+3, k); lb(k, j) =
+// B(k, j..j+3) if BJ, else B(k..k+3, j) -- one 16-byte (fp32) or 8-byte (bf16) load where the
+// source is a row-major array.  K slices of KS are staged in LDS as sA [KS][M + 16] and sB
+// [KS][N + 16] (the padding of 16 puts the four k rows one fp32 MFMA reads on four different
+// 16-bank groups).  The product runs on v_mfma_f32_16x16x4_f32: lane l supplies
 // A[i0 + l % 16][k + l / 16] and B[k + l / 16][j0 + l % 16] and holds C[i0 + 4 (l / 16) + v][j0 + l % 16]
 // in accumulator v.  Each wave owns a band of 16-row tiles (all column tiles), or for M = 16 a
 // quarter of the column tiles.  AK: A's contiguous index in memory is k (else i); BJ: B's is j
@@ -65,13 +68,13 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
         for (int y = 0; y < CT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
     // software pipeline: the next K slice is fetched into registers while the current one is
     // multiplied, so the latency of the operand loads overlaps the MFMAs.  Each thread moves runs
-    // of four elements along the operand's contiguous direction (one 16-byte load where the
-    // source is a row-major fp32 array, and consecutive LDS slots where the slice row is contiguous)
+    // of four elements along the operand's contiguous direction (consecutive LDS slots where the
+    // slice row is contiguous)
     constexpr int PA = M * KS / NT / 4, PB = N * KS / NT / 4, NS = K / KS;
     static_assert(M * KS % (NT * 4) == 0 && N * KS % (NT * 4) == 0, "staging split");
     // two slices in flight: slice s + 2 is requested while slice s is multiplied (the slice loop
     // is unrolled so the register buffers are indexed statically)
-    float ra[2][PA][4], rb[2][PB][4];
+    f32x4 ra[2][PA], rb[2][PB];
     auto a_pos = [&](int m, int& i, int& kk) {  // first element of run m of this thread
         const int q = tid + m * NT;
         if (AK) { i = q / (KS / 4); kk = (q % (KS / 4)) * 4; }
@@ -87,15 +90,13 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
         for (int m = 0; m < PA; ++m) {
             int i, kk;
             a_pos(m, i, kk);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) ra[buf][m][u] = AK ? la(i, k0 + kk + u) : la(i + u, k0 + kk);
+            ra[buf][m] = la(i, k0 + kk);
         }
 #pragma unroll
         for (int m = 0; m < PB; ++m) {
             int j, kk;
             b_pos(m, j, kk);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) rb[buf][m][u] = BJ ? lb(k0 + kk, j + u) : lb(k0 + kk + u, j);
+            rb[buf][m] = lb(k0 + kk, j);
         }
     };
     fetch(0, 0);
@@ -161,8 +162,18 @@ struct WsLay {
                             NZ = NDT + C * C, PER = NZ + C * C;  // floats per chunk
 };
 
-template <typename T>
-__device__ __forceinline__ float ld(const T* p, size_t i) { return to_f32(p[i]); }
+// Four consecutive elements p[0..3] as fp32: one 16-byte (fp32) or 8-byte (bf16) load.  Every run
+// the products request starts at a multiple of four elements of a row whose length is a multiple
+// of 64, so with 16-byte-aligned base pointers the loads are naturally aligned.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const bf16* p) {
+    const bf16x4 x = *(const bf16x4*)p;
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+// Four elements read one by one (a run that is strided in its source).
+template <class F>
+__device__ __forceinline__ f32x4 gather4(F f) { return f32x4{f(0), f(1), f(2), f(3)}; }
+constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
 
 // Token layout helpers: row r of chunk c of (b, h) is token t0 + r; rows >= n read as zero.
 struct ChunkPos {
@@ -215,9 +226,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     const size_t ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T* kc = k + tok0 * DK;
     const T* vc = v + tok0 * DV;
-    auto krow = [&](int r, int d) { return r < n ? ld(kc, (size_t)r * ks + d) : 0.0f; };
+    auto krow4 = [&](int r, int d) { return r < n ? ld4(kc + (size_t)r * ks + d) : kZero4; };
     // A = strict_lower(diag(beta) (K K^T) o E)
-    tgemm<C, C, DK, true, false>(stage, krow, [&](int d, int s) { return krow(s, d); },
+    tgemm<C, C, DK, true, false>(stage, krow4, [&](int d, int s) { return krow4(s, d); },
                                  [&](int r, int s, float x) {
                                      Am[r * LD64 + s] = s < r ? bs[r] * fast_exp2(g2[r] - g2[s]) * x : 0.0f;
                                  });
@@ -238,16 +249,16 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
     __syncthreads();
     for (int i = tid; i < C * C; i += NT) rec[L::TI + i] = Tm[(i / C) * LD64 + (i % C)];
     // W = Tinv diag(beta e^g) K,  U = Tinv diag(beta) V
-    tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return Tm[r * LD64 + s]; },
-                                [&](int s, int d) { return bsg[s] * krow(s, d); },
+    auto trow4 = [&](int r, int s) { return gather4([&](int u) { return Tm[r * LD64 + s + u]; }); };
+    tgemm<C, DK, C, true, true>(stage, trow4, [&](int s, int d) { return bsg[s] * krow4(s, d); },
                                 [&](int r, int d, float x) { rec[L::W + (size_t)r * DK + d] = x; });
-    tgemm<C, DV, C, true, true>(stage, [&](int r, int s) { return Tm[r * LD64 + s]; },
-                                [&](int s, int d) { return s < n ? bs[s] * ld(vc, (size_t)s * vs + d) : 0.0f; },
+    tgemm<C, DV, C, true, true>(stage, trow4,
+                                [&](int s, int d) { return s < n ? bs[s] * ld4(vc + (size_t)s * vs + d) : kZero4; },
                                 [&](int r, int d, float x) { rec[L::U + (size_t)r * DV + d] = x; });
     const float glast = gs[n - 1];
-    for (int i = tid; i < C * DK; i += NT) {
+    for (int i = 4 * tid; i < C * DK; i += 4 * NT) {
         const int r = i / DK, d = i % DK;
-        rec[L::KD + i] = ekd[r] * krow(r, d);
+        *(f32x4*)(rec + L::KD + i) = ekd[r] * krow4(r, d);
     }
     if (tid == 0) rec[L::EGL] = expf(glast);
 }
@@ -429,18 +440,19 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *oc = dO + tok0 * DV;
-    auto qrow = [&](int r, int d) { return r < n ? ld(qc, (size_t)r * ks + d) : 0.0f; };
-    auto orow = [&](int r, int j) { return r < n ? ld(oc, (size_t)r * vs + j) : 0.0f; };
-    tgemm<C, C, DK, true, false>(stage, qrow,
-                                 [&](int d, int s) { return s < n ? ld(kc, (size_t)s * ks + d) : 0.0f; },
+    auto qrow4 = [&](int r, int d) { return r < n ? ld4(qc + (size_t)r * ks + d) : kZero4; };
+    auto orow4 = [&](int r, int j) { return r < n ? ld4(oc + (size_t)r * vs + j) : kZero4; };
+    tgemm<C, C, DK, true, false>(stage, qrow4,
+                                 [&](int d, int s) { return s < n ? ld4(kc + (size_t)s * ks + d) : kZero4; },
                                  [&](int r, int s, float x) {
                                      Pm[r * LD64 + s] = s <= r ? x * fast_exp2(g2[r] - g2[s]) : 0.0f;
                                  });
     __syncthreads();
-    tgemm<C, DV, C, false, true>(stage, [&](int s, int r) { return Pm[r * LD64 + s]; }, orow,
-                                 [&](int s, int j, float x) { rec[L::E + (size_t)s * DV + j] = x; });
-    tgemm<DV, DK, C, false, true>(stage, [&](int i, int r) { return orow(r, i); },
-                                  [&](int r, int d) { return eg[r] * qrow(r, d); },
+    tgemm<C, DV, C, false, true>(stage,
+                                 [&](int s, int r) { return gather4([&](int u) { return Pm[r * LD64 + s + u]; }); },
+                                 orow4, [&](int s, int j, float x) { rec[L::E + (size_t)s * DV + j] = x; });
+    tgemm<DV, DK, C, false, true>(stage, [&](int i, int r) { return orow4(r, i); },
+                                  [&](int r, int d) { return eg[r] * qrow4(r, d); },
                                   [&](int i, int d, float x) { rec[L::F + (size_t)i * DK + d] = x; });
 }
 
@@ -477,56 +489,56 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *vc = v + tok0 * DV, *oc = dO + tok0 * DV;
-    auto qrow = [&](int r, int d) { return r < n ? ld(qc, (size_t)r * ks + d) : 0.0f; };
-    auto krow = [&](int r, int d) { return r < n ? ld(kc, (size_t)r * ks + d) : 0.0f; };
-    auto vrow = [&](int r, int j) { return r < n ? ld(vc, (size_t)r * vs + j) : 0.0f; };
-    auto orow = [&](int r, int j) { return r < n ? ld(oc, (size_t)r * vs + j) : 0.0f; };
+    auto qrow4 = [&](int r, int d) { return r < n ? ld4(qc + (size_t)r * ks + d) : kZero4; };
+    auto krow4 = [&](int r, int d) { return r < n ? ld4(kc + (size_t)r * ks + d) : kZero4; };
+    auto vrow4 = [&](int r, int j) { return r < n ? ld4(vc + (size_t)r * vs + j) : kZero4; };
+    auto orow4 = [&](int r, int j) { return r < n ? ld4(oc + (size_t)r * vs + j) : kZero4; };
     const float* Sin = rec + L::SIN;
     const float* dSo = rec + L::DSO;
     // X0 = dQG = dO S_in and X1 = dW = -dDelta S_in as one product [dO; dDelta] S_in;  X2 = dKD = Delta dS_out
     tgemm<2 * C, DK, DV, true, true>(
-        stage, [&](int r, int i) { return r < C ? orow(r, i) : rec[L::DDL + (size_t)(r - C) * DV + i]; },
-        [&](int i, int d) { return Sin[(size_t)i * DK + d]; },
+        stage, [&](int r, int i) { return r < C ? orow4(r, i) : ld4(rec + L::DDL + (size_t)(r - C) * DV + i); },
+        [&](int i, int d) { return ld4(Sin + (size_t)i * DK + d); },
         [&](int r, int d, float x) {
             if (r < C) rec[L::X0 + (size_t)r * DK + d] = x;
             else rec[L::X1 + (size_t)(r - C) * DK + d] = -x;
         });
-    tgemm<C, DK, DV, true, true>(stage, [&](int r, int i) { return rec[L::DL + (size_t)r * DV + i]; },
-                                 [&](int i, int d) { return dSo[(size_t)i * DK + d]; },
+    tgemm<C, DK, DV, true, true>(stage, [&](int r, int i) { return ld4(rec + L::DL + (size_t)r * DV + i); },
+                                 [&](int i, int d) { return ld4(dSo + (size_t)i * DK + d); },
                                  [&](int r, int d, float x) { rec[L::X2 + (size_t)r * DK + d] = x; });
     // Q K^T and K K^T (raw), dP = lower_incl(dO Delta^T)
-    tgemm<2 * C, C, DK, true, false>(stage, [&](int r, int d) { return r < C ? qrow(r, d) : krow(r - C, d); },
-                                     [&](int d, int s) { return krow(s, d); },
+    tgemm<2 * C, C, DK, true, false>(stage, [&](int r, int d) { return r < C ? qrow4(r, d) : krow4(r - C, d); },
+                                     [&](int d, int s) { return krow4(s, d); },
                                      [&](int r, int s, float x) {
                                          if (r < C) QK[r * LD64 + s] = x;
                                          else KK[(r - C) * LD64 + s] = x;
                                      });
-    tgemm<C, C, DV, true, false>(stage, orow, [&](int j, int s) { return rec[L::DL + (size_t)s * DV + j]; },
+    tgemm<C, C, DV, true, false>(stage, orow4, [&](int j, int s) { return ld4(rec + L::DL + (size_t)s * DV + j); },
                                  [&](int r, int s, float x) { dP[r * LD64 + s] = s <= r ? x : 0.0f; });
     // dTinv = dDelta (diag(beta) V)^T + dW (diag(beta e^g) K)^T
     tgemm<C, C, DV + DK, true, false>(
         stage,
         [&](int r, int j) {
-            return j < DV ? rec[L::DDL + (size_t)r * DV + j] : rec[L::X1 + (size_t)r * DK + j - DV];
+            return j < DV ? ld4(rec + L::DDL + (size_t)r * DV + j) : ld4(rec + L::X1 + (size_t)r * DK + j - DV);
         },
-        [&](int j, int s) { return j < DV ? bs[s] * vrow(s, j) : bsg[s] * krow(s, j - DV); },
+        [&](int j, int s) { return j < DV ? bs[s] * vrow4(s, j) : bsg[s] * krow4(s, j - DV); },
         [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
     // X3 = Tinv^T dDelta (and dv = beta o X3);  X4 = Tinv^T dW
-    tgemm<C, DV, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
-                                 [&](int s, int j) { return rec[L::DDL + (size_t)s * DV + j]; },
+    tgemm<C, DV, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
+                                 [&](int s, int j) { return ld4(rec + L::DDL + (size_t)s * DV + j); },
                                  [&](int r, int j, float x) {
                                      rec[L::X3 + (size_t)r * DV + j] = x;
                                      if (r < n) dv[(size_t)r * vs + j + tok0 * DV] = from_f32<T>(bs[r] * x);
                                  });
-    tgemm<C, DK, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
-                                 [&](int s, int d) { return rec[L::X1 + (size_t)s * DK + d]; },
+    tgemm<C, DK, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
+                                 [&](int s, int d) { return ld4(rec + L::X1 + (size_t)s * DK + d); },
                                  [&](int r, int d, float x) { rec[L::X4 + (size_t)r * DK + d] = x; });
     // Z = dTinv Tinv^T, then dA = -strict_lower(Tinv^T Z) (into dT)
-    tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return dT[r * LD64 + s]; },
-                                [&](int s, int c2) { return Tm[c2 * LD64 + s]; },
+    tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return ld4(dT + r * LD64 + s); },
+                                [&](int s, int c2) { return ld4(Tm + c2 * LD64 + s); },
                                 [&](int r, int c2, float x) { Zm[r * LD64 + c2] = x; });
-    tgemm<C, C, C, false, true>(stage, [&](int r, int s) { return Tm[s * LD64 + r]; },
-                                [&](int s, int c2) { return Zm[s * LD64 + c2]; },
+    tgemm<C, C, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
+                                [&](int s, int c2) { return ld4(Zm + s * LD64 + c2); },
                                 [&](int r, int c2, float x) { dT[r * LD64 + c2] = c2 < r ? -x : 0.0f; });
     __syncthreads();
     // row and column sums over the n x n terms:
@@ -567,7 +579,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     }
     __syncthreads();
     // dq = e^g o dQG + (dP o E) K
-    tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return dP[r * LD64 + s]; }, krow,
+    tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return ld4(dP + r * LD64 + s); }, krow4,
                                 [&](int r, int d, float x) {
                                     if (r < n)
                                         dq[tok0 * DK + (size_t)r * ks + d] =
@@ -577,9 +589,11 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     const float glast = gs[n - 1];
     tgemm<C, DK, 3 * C, false, true>(stage,
         [&](int r, int kk) {
-            return kk < C ? dP[kk * LD64 + r] : kk < 2 * C ? Zm[r * LD64 + kk - C] : Zm[(kk - 2 * C) * LD64 + r];
+            return kk < C       ? ld4(dP + kk * LD64 + r)
+                   : kk < 2 * C ? gather4([&](int u) { return Zm[(r + u) * LD64 + kk - C]; })
+                                : ld4(Zm + (kk - 2 * C) * LD64 + r);
         },
-        [&](int kk, int d) { return kk < C ? qrow(kk, d) : krow(kk % C, d); },
+        [&](int kk, int d) { return kk < C ? qrow4(kk, d) : krow4(kk % C, d); },
         [&](int r, int d, float x) {
             if (r < n) {
                 const float y = bsg[r] * rec[L::X4 + (size_t)r * DK + d] + ekd[r] * rec[L::X2 + (size_t)r * DK + d] + x;
@@ -605,18 +619,19 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
             for (int d = 0; d < QK4; d += 4) {
                 const f32x4 a4 = *(const f32x4*)(x4 + d), a0 = *(const f32x4*)(x0 + d);
                 const f32x4 a2 = *(const f32x4*)(x2 + d), b2 = *(const f32x4*)(kdp + d);
+                const f32x4 kv = ld4(kp + d), qv = ld4(qp + d);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    tw = fmaf(a4[u], ld(kp, d + u), tw);
-                    qg = fmaf(a0[u], ld(qp, d + u), qg);
+                    tw = fmaf(a4[u], kv[u], tw);
+                    qg = fmaf(a0[u], qv[u], qg);
                     kd = fmaf(a2[u], b2[u], kd);
                 }
             }
 #pragma unroll
             for (int j = 0; j < QV4; j += 4) {
-                const f32x4 a3 = *(const f32x4*)(x3 + j);
+                const f32x4 a3 = *(const f32x4*)(x3 + j), vv = ld4(vp + j);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) tv = fmaf(a3[u], ld(vp, j + u), tv);
+                for (int u = 0; u < 4; ++u) tv = fmaf(a3[u], vv[u], tv);
             }
         }
 #pragma unroll
