@@ -294,9 +294,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
     __shared__ __align__(16) float Bs[C * LB];
     __shared__ __align__(16) float St[RW * LS];
     __shared__ __align__(16) float Xs[C * LX];
-    const int row0 = (int)blockIdx.x * RW, h = (int)blockIdx.y, b = (int)blockIdx.z, tid = (int)threadIdx.x;
+    // Flat grid of (b H + h) * (DV / RW) + slice items.  Workgroup i is dispatched to XCD i % 8;
+    // the items are renumbered so that every XCD takes a contiguous range of them, which puts the
+    // row slices of one (batch, head) on one XCD and lets them share each chunk's W and KD in its L2.
+    const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
+    const int item = xcd * per + min(xcd, extra) + (wg >> 3);
+    const int row0 = (item % (DV / RW)) * RW, tid = (int)threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, G = lane >> 4, c16 = lane & 15;
-    const size_t bh = (size_t)b * H + h;
+    const size_t bh = (size_t)(item / (DV / RW));
     // state rows in, zero when absent
     for (int q = tid; q < RW * DK / 4; q += NT) {
         const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
@@ -306,14 +311,19 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
     }
     f32x4 ra[NA], rb[NA], rx[NX], rf[NF];
     float regl;
-    auto fetch = [&](int c) {
+    // part p of 4 of a chunk's operands (part 0 also takes the small ones): the parts are issued
+    // between the quarters of the first product, so the loads drain while the MFMAs run instead
+    // of stalling the waves at issue
+    static_assert(NA % 4 == 0, "fetch split");
+    auto fetch_part = [&](int c, int p) {
         const float* rec = ws + (bh * NC + c) * L::PER;
 #pragma unroll
-        for (int m = 0; m < NA; ++m) {
+        for (int m = p * (NA / 4); m < (p + 1) * (NA / 4); ++m) {
             const int q = tid + m * NT, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
             ra[m] = *(const f32x4*)(rec + OFF_A + (size_t)r * DK + d4);
             rb[m] = *(const f32x4*)(rec + OFF_B + (size_t)r * DK + d4);
         }
+        if (p != 0) return;
 #pragma unroll
         for (int m = 0; m < NX; ++m) {
             const int q = tid + m * NT, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
@@ -328,7 +338,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
         }
         regl = rec[L::EGL];
     };
-    fetch(BACK ? NC - 1 : 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) fetch_part(BACK ? NC - 1 : 0, p);
     for (int it = 0; it < NC; ++it) {
         const int c = BACK ? NC - 1 - it : it;
         float* rec = ws + (bh * NC + c) * L::PER;
@@ -354,18 +365,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
             *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
         }
         __syncthreads();
-        if (it + 1 < NC) fetch(BACK ? c - 1 : c + 1);  // in flight during this chunk's products
-        // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns rows 16 w .. 16 w + 15, both column tiles
+        // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns rows 16 w .. 16 w + 15, both column tiles;
+        // the next chunk's operands are requested a quarter at a time between the k quarters
         {
             f32x4 acc[RW / 16];
 #pragma unroll
             for (int y = 0; y < RW / 16; ++y) acc[y] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int k = 0; k < DK; k += 4) {
-                const float a = As[(16 * w + c16) * LA + k + G];
 #pragma unroll
-                for (int y = 0; y < RW / 16; ++y)
-                    acc[y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, St[(16 * y + c16) * LS + k + G], acc[y], 0, 0, 0);
+            for (int p = 0; p < 4; ++p) {
+                if (it + 1 < NC) fetch_part(BACK ? c - 1 : c + 1, p);
+#pragma unroll
+                for (int k = p * (DK / 4); k < (p + 1) * (DK / 4); k += 4) {
+                    const float a = As[(16 * w + c16) * LA + k + G];
+#pragma unroll
+                    for (int y = 0; y < RW / 16; ++y)
+                        acc[y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, St[(16 * y + c16) * LS + k + G], acc[y], 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int y = 0; y < RW / 16; ++y)
@@ -694,7 +709,7 @@ template <typename T, int DK, int DV>
 static void launch_bwd_typed(const GdnBwdArgs& a, hipStream_t s) {
     const int NC = (a.T + C - 1) / C;
     float* ws = (float*)a.workspace;
-    const dim3 gc(NC, a.H, a.B), gr(DV / RW, a.H, a.B);
+    const dim3 gc(NC, a.H, a.B), gr((unsigned)(DV / RW) * a.H * a.B);
     hipLaunchKernelGGL((gdn_bwd_prep<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.k, (const T*)a.v, a.alpha, a.beta,
                        ws, a.T, a.H, NC);
     hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, false>), gr, dim3(NT), 0, s, a.init_state, nullptr, ws, a.H, NC);
