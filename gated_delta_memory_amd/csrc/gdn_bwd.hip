@@ -49,8 +49,10 @@ constexpr int LD64 = C + 1;
 // in accumulator v.  Each wave owns a band of 16-row tiles (all column tiles), or for M = 16 a
 // quarter of the column tiles.  AK: A's contiguous index in memory is k (else i); BJ: B's is j
 // (else k) -- chooses the staging order so that consecutive threads read consecutive addresses.
-template <int M, int N, int K, bool AK, bool BJ, class LA, class LB, class EPI>
-__device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
+// tgemm_blk hands the finished accumulators to blk(acc, rt0, ct0): acc[x][y][v] is element
+// (16 (rt0 + x) + 4 (lane / 16) + v, 16 (ct0 + y) + lane % 16); tgemm applies epi to each.
+template <int M, int N, int K, bool AK, bool BJ, class LA, class LB, class BLK>
+__device__ __forceinline__ void tgemm_blk(float* stage, LA la, LB lb, BLK blk) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % KS == 0, "tile shape");
     constexpr int MT = M / 16, NTL = N / 16;
     static_assert(MT % 4 == 0 || (MT == 1 && NTL % 4 == 0), "wave split");
@@ -140,12 +142,42 @@ __device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
         }
         __syncthreads();
     }
+    blk(acc, rt0, ct0);
+}
+
+template <class ACC, class EPI>
+__device__ __forceinline__ void each_elem(const ACC& acc, int rt0, int ct0, EPI epi) {
+    constexpr int RT = sizeof(ACC) / sizeof(acc[0]), CT = sizeof(acc[0]) / sizeof(f32x4);
+    const int lane = (int)threadIdx.x & 63, G = lane >> 4, c16 = lane & 15;
 #pragma unroll
     for (int x = 0; x < RT; ++x)
 #pragma unroll
         for (int y = 0; y < CT; ++y)
 #pragma unroll
             for (int v = 0; v < 4; ++v) epi((rt0 + x) * 16 + 4 * G + v, (ct0 + y) * 16 + c16, acc[x][y][v]);
+}
+
+template <int M, int N, int K, bool AK, bool BJ, class LA, class LB, class EPI>
+__device__ __forceinline__ void tgemm(float* stage, LA la, LB lb, EPI epi) {
+    tgemm_blk<M, N, K, AK, BJ>(stage, la, lb, [&](const auto& acc, int rt0, int ct0) { each_elem(acc, rt0, ct0, epi); });
+}
+
+// For a product with one 16-row tile per wave (M = 64): rowdot(acc, rt0, f) returns, in every lane,
+// the four sums over the product's columns j of C[i][j] f(i, j) for the lane's rows
+// i = 16 rt0 + 4 (lane / 16) + v (the 16 lanes of a row group hold its columns).
+template <int CT, class F>
+__device__ __forceinline__ f32x4 rowdot(const f32x4 (&acc)[1][CT], int rt0, F f) {
+    const int lane = (int)threadIdx.x & 63, G = lane >> 4, c16 = lane & 15;
+    f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int y = 0; y < CT; ++y)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[v] = fmaf(acc[0][y][v], f(16 * rt0 + 4 * G + v, 16 * y + c16), part[v]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[v] += __shfl_xor(part[v], o, 16);
+    return part;
 }
 
 constexpr size_t STAGE_FLOATS = (size_t)KS * (128 + 16) * 2;  // sA + sB for the largest shapes (M, N <= 128)
@@ -156,10 +188,11 @@ struct WsLay {
     static constexpr size_t W = 0, U = W + (size_t)C * DK, KD = U + (size_t)C * DV, TI = KD + (size_t)C * DK,
                             G = TI + (size_t)C * C, EGL = G + C, SIN = EGL + 4, DL = SIN + (size_t)DV * DK,
                             E = DL + (size_t)C * DV, F = E + (size_t)C * DV, DDL = F + (size_t)DV * DK,
-                            DSO = DDL + (size_t)C * DV, X0 = DSO + (size_t)DV * DK, X1 = X0 + (size_t)C * DK,
-                            X2 = X1 + (size_t)C * DK, X3 = X2 + (size_t)C * DK, X4 = X3 + (size_t)C * DV,
+                            DSO = DDL + (size_t)C * DV, X1 = DSO + (size_t)DV * DK,
+                            X2 = X1 + (size_t)C * DK, X4 = X2 + (size_t)C * DK,
                             NQK = X4 + (size_t)C * DK, NKK = NQK + C * C, NDP = NKK + C * C, NDT = NDP + C * C,
-                            NZ = NDT + C * C, PER = NZ + C * C;  // floats per chunk
+                            NZ = NDT + C * C, DSS = NZ + C * C,  // DSS: <dS_out, S_in> per row slice of the walk
+                            PER = DSS + 4;                       // floats per chunk
 };
 
 // Four consecutive elements p[0..3] as fp32: one 16-byte (fp32) or 8-byte (bf16) load.  Every run
@@ -268,7 +301,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
 // (batch, head) and visits the chunks in order (forward) or in reverse (backward):
 //   forward:   S_in stored;  Delta = U[:, rows] - W S^T;           S = e^{g_last} S + Delta^T KD
 //   backward:  dS_out stored; dDelta = E[:, rows] + KD dS^T;       dS = e^{g_last} dS + F[rows, :] - dDelta^T W
-// (S^T and Delta written for the per-chunk kernels).  The chunk's two 64 x Dk operands (W and KD,
+// (S^T and Delta written for the per-chunk kernels; the backward walk also leaves each slice's share
+// of <dS_out, S_in> for the chunk's decay gradient).  The chunk's two 64 x Dk operands (W and KD,
 // in the order the walk uses them) sit whole in LDS; the next chunk's operands are loaded into
 // registers while the current chunk multiplies, so the walk waits on memory only once.  Products
 // on v_mfma_f32_16x16x4_f32 straight from LDS: rows padded by 4 floats where a lane reads along
@@ -309,8 +343,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
         if (s0) x = *(const f32x4*)(s0 + (bh * DV + row0 + i) * DK + d4);
         *(f32x4*)(St + i * LS + d4) = x;
     }
-    f32x4 ra[NA], rb[NA], rx[NX], rf[NF];
+    f32x4 ra[NA], rb[NA], rx[NX], rf[NF], rs[NF];
     float regl;
+    __shared__ float wred[4];
     // part p of 4 of a chunk's operands (part 0 also takes the small ones): the parts are issued
     // between the quarters of the first product, so the loads drain while the MFMAs run instead
     // of stalling the waves at issue
@@ -322,6 +357,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
             const int q = tid + m * NT, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
             ra[m] = *(const f32x4*)(rec + OFF_A + (size_t)r * DK + d4);
             rb[m] = *(const f32x4*)(rec + OFF_B + (size_t)r * DK + d4);
+        }
+        if constexpr (BACK) {
+            if (p == 1)
+#pragma unroll
+                for (int m = 0; m < NF; ++m) {
+                    const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                    rs[m] = *(const f32x4*)(rec + L::SIN + (size_t)(row0 + i) * DK + d4);
+                }
         }
         if (p != 0) return;
 #pragma unroll
@@ -360,11 +403,25 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
             const int q = tid + m * NT, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
             *(f32x4*)(Xs + r * LX + c4) = rx[m];
         }
-        for (int q = tid; q < RW * DK / 4; q += NT) {
-            const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
-            *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
+        if constexpr (BACK) {  // dS_out out, and this slice's share of <dS_out, S_in>
+            float dot = 0.f;
+#pragma unroll
+            for (int m = 0; m < NF; ++m) {
+                const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                const f32x4 x = *(const f32x4*)(St + i * LS + d4);
+                *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = x;
+                dot = fmaf(x[0], rs[m][0], fmaf(x[1], rs[m][1], fmaf(x[2], rs[m][2], fmaf(x[3], rs[m][3], dot))));
+            }
+            dot = wave_sum(dot);
+            if (lane == 0) wred[w] = dot;
+        } else {
+            for (int q = tid; q < RW * DK / 4; q += NT) {
+                const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
+            }
         }
         __syncthreads();
+        if (BACK && tid == 0) rec[L::DSS + row0 / RW] = (wred[0] + wred[1]) + (wred[2] + wred[3]);
         // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns rows 16 w .. 16 w + 15, both column tiles;
         // the next chunk's operands are requested a quarter at a time between the k quarters
         {
@@ -510,17 +567,32 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     auto orow4 = [&](int r, int j) { return r < n ? ld4(oc + (size_t)r * vs + j) : kZero4; };
     const float* Sin = rec + L::SIN;
     const float* dSo = rec + L::DSO;
-    // X0 = dQG = dO S_in and X1 = dW = -dDelta S_in as one product [dO; dDelta] S_in;  X2 = dKD = Delta dS_out
-    tgemm<2 * C, DK, DV, true, true>(
-        stage, [&](int r, int i) { return r < C ? orow4(r, i) : ld4(rec + L::DDL + (size_t)(r - C) * DV + i); },
-        [&](int i, int d) { return ld4(Sin + (size_t)i * DK + d); },
-        [&](int r, int d, float x) {
-            if (r < C) rec[L::X0 + (size_t)r * DK + d] = x;
-            else rec[L::X1 + (size_t)(r - C) * DK + d] = -x;
-        });
-    tgemm<C, DK, DV, true, true>(stage, [&](int r, int i) { return ld4(rec + L::DL + (size_t)r * DV + i); },
-                                 [&](int i, int d) { return ld4(dSo + (size_t)i * DK + d); },
-                                 [&](int r, int d, float x) { rec[L::X2 + (size_t)r * DK + d] = x; });
+    // element loaders for the per-row dot products (rows past n read as zero)
+    auto qel = [&](int r, int d) { return r < n ? to_f32(qc[(size_t)r * ks + d]) : 0.0f; };
+    auto kel = [&](int r, int d) { return r < n ? to_f32(kc[(size_t)r * ks + d]) : 0.0f; };
+    auto vel = [&](int r, int j) { return r < n ? to_f32(vc[(size_t)r * vs + j]) : 0.0f; };
+    // Per-row sums, each formed in the epilogue of the product that makes its left factor (so no
+    // product is read back for them): rowv[0] = dq_r . q_r, [1] = colsum over the n x n terms,
+    // [2] = sum_s dA_rs E_rs k_r . k_s, [3] = X3_r . v_r, [4] = X4_r . k_r, [5] = X2_r . k_r.
+    const int c16 = tid & 15, G4 = ((tid & 63) >> 4) * 4;
+    auto put_rows = [&](int slot, int rt0, f32x4 part) {
+        if (c16 == 0)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) rowv[slot][16 * rt0 + G4 + v] = part[v];
+    };
+    // X1 = dW = -dDelta S_in
+    tgemm<C, DK, DV, true, true>(stage, [&](int r, int i) { return ld4(rec + L::DDL + (size_t)r * DV + i); },
+                                 [&](int i, int d) { return ld4(Sin + (size_t)i * DK + d); },
+                                 [&](int r, int d, float x) { rec[L::X1 + (size_t)r * DK + d] = -x; });
+    // X2 = dKD = Delta dS_out (kept for dk), and X2_r . k_r
+    tgemm_blk<C, DK, DV, true, true>(stage, [&](int r, int i) { return ld4(rec + L::DL + (size_t)r * DV + i); },
+                                     [&](int i, int d) { return ld4(dSo + (size_t)i * DK + d); },
+                                     [&](const auto& acc, int rt0, int ct0) {
+                                         each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
+                                             rec[L::X2 + (size_t)r * DK + d] = x;
+                                         });
+                                         put_rows(5, rt0, rowdot(acc, rt0, kel));
+                                     });
     // Q K^T and K K^T (raw), dP = lower_incl(dO Delta^T)
     tgemm<2 * C, C, DK, true, false>(stage, [&](int r, int d) { return r < C ? qrow4(r, d) : krow4(r - C, d); },
                                      [&](int d, int s) { return krow4(s, d); },
@@ -538,16 +610,24 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         },
         [&](int j, int s) { return j < DV ? bs[s] * vrow4(s, j) : bsg[s] * krow4(s, j - DV); },
         [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
-    // X3 = Tinv^T dDelta (and dv = beta o X3);  X4 = Tinv^T dW
-    tgemm<C, DV, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
-                                 [&](int s, int j) { return ld4(rec + L::DDL + (size_t)s * DV + j); },
-                                 [&](int r, int j, float x) {
-                                     rec[L::X3 + (size_t)r * DV + j] = x;
-                                     if (r < n) dv[(size_t)r * vs + j + tok0 * DV] = from_f32<T>(bs[r] * x);
-                                 });
-    tgemm<C, DK, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
-                                 [&](int s, int d) { return ld4(rec + L::X1 + (size_t)s * DK + d); },
-                                 [&](int r, int d, float x) { rec[L::X4 + (size_t)r * DK + d] = x; });
+    // X3 = Tinv^T dDelta: dv = beta o X3, and X3_r . v_r
+    tgemm_blk<C, DV, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
+                                     [&](int s, int j) { return ld4(rec + L::DDL + (size_t)s * DV + j); },
+                                     [&](const auto& acc, int rt0, int ct0) {
+                                         each_elem(acc, rt0, ct0, [&](int r, int j, float x) {
+                                             if (r < n) dv[(size_t)r * vs + j + tok0 * DV] = from_f32<T>(bs[r] * x);
+                                         });
+                                         put_rows(3, rt0, rowdot(acc, rt0, vel));
+                                     });
+    // X4 = Tinv^T dW (kept for dk), and X4_r . k_r
+    tgemm_blk<C, DK, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
+                                     [&](int s, int d) { return ld4(rec + L::X1 + (size_t)s * DK + d); },
+                                     [&](const auto& acc, int rt0, int ct0) {
+                                         each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
+                                             rec[L::X4 + (size_t)r * DK + d] = x;
+                                         });
+                                         put_rows(4, rt0, rowdot(acc, rt0, kel));
+                                     });
     // Z = dTinv Tinv^T, then dA = -strict_lower(Tinv^T Z) (into dT)
     tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return ld4(dT + r * LD64 + s); },
                                 [&](int s, int c2) { return ld4(Tm + c2 * LD64 + s); },
@@ -556,12 +636,11 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                 [&](int s, int c2) { return ld4(Zm + s * LD64 + c2); },
                                 [&](int r, int c2, float x) { dT[r * LD64 + c2] = c2 < r ? -x : 0.0f; });
     __syncthreads();
-    // row and column sums over the n x n terms:
-    //   rowv[0] = rowsum(dA o A) + rowsum(dP o P),  rowv[1] = colsum(...) of the same,
-    //   rowv[2] = sum_s dA_rs E_rs k_r.k_s (beta's share through A).
-    // Thread t visits (r = t / 64 + 4 m, s = t % 64), m = 0..15: every visit reads whole rows of the
-    // workspace arrays (coalesced); a wave covers one row per visit, so row sums are wave
-    // reductions, and column sums stay in the thread (fixed s) until four partials meet in LDS.
+    // column sums over the n x n terms, rowv[1] = colsum(dA o A + dP o P), and
+    // rowv[2] = sum_s dA_rs E_rs k_r.k_s (so rowsum(dA o A) = beta_r rowv[2]; rowsum(dP o P) is part
+    // of dq_r . q_r).  Thread t visits (r = t / 64 + 4 m, s = t % 64), m = 0..15: every visit reads
+    // whole rows of the workspace arrays (coalesced); a wave covers one row per visit, so row sums are
+    // wave reductions, and column sums stay in the thread (fixed s) until four partials meet in LDS.
     {
         const int sc = tid & (C - 1), w0 = tid >> 6;
         float col = 0.f;
@@ -571,13 +650,10 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
             const float e = sc <= r ? fast_exp2(g2[r] - g2[sc]) : 0.0f;  // never exp of the upper triangle
             const float dA = dT[r * LD64 + sc], kk = KK[r * LD64 + sc];
             const float pP = sc <= r ? QK[r * LD64 + sc] * e : 0.0f;
-            const float t1 = fmaf(dA, bs[r] * e * kk, dP[r * LD64 + sc] * pP);
-            const float r1 = wave_sum(t1), r2 = wave_sum(dA * e * kk);
-            col += t1;
-            if (sc == 0) {
-                rowv[0][r] = r1;
-                rowv[2][r] = r2;
-            }
+            const float dae = dA * e * kk;
+            col += fmaf(dae, bs[r], dP[r * LD64 + sc] * pP);
+            const float r2 = wave_sum(dae);
+            if (sc == 0) rowv[2][r] = r2;
         }
         red[tid] = col;
         __syncthreads();
@@ -593,13 +669,16 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         Zm[r * LD64 + s] = dT[r * LD64 + s] * bs[r] * e;
     }
     __syncthreads();
-    // dq = e^g o dQG + (dP o E) K
-    tgemm<C, DK, C, true, true>(stage, [&](int r, int s) { return ld4(dP + r * LD64 + s); }, krow4,
-                                [&](int r, int d, float x) {
-                                    if (r < n)
-                                        dq[tok0 * DK + (size_t)r * ks + d] =
-                                            from_f32<T>(fmaf(eg[r], rec[L::X0 + (size_t)r * DK + d], x));
-                                });
+    // dq = e^g o dQG + (dP o E) K = [diag(e^g) dO | dP o E] [S_in; K]  (dQG = dO S_in), and dq_r . q_r
+    tgemm_blk<C, DK, DV + C, true, true>(
+        stage, [&](int r, int kk) { return kk < DV ? eg[r] * orow4(r, kk) : ld4(dP + r * LD64 + kk - DV); },
+        [&](int kk, int d) { return kk < DV ? ld4(Sin + (size_t)kk * DK + d) : krow4(kk - DV, d); },
+        [&](const auto& acc, int rt0, int ct0) {
+            each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
+                if (r < n) dq[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(x);
+            });
+            put_rows(0, rt0, rowdot(acc, rt0, qel));
+        });
     // dk = beta e^g o X4 + e^{g_last - g} o dKD + [(dP o E)^T | M | M^T] [Q; K; K]
     const float glast = gs[n - 1];
     tgemm<C, DK, 3 * C, false, true>(stage,
@@ -615,80 +694,30 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                 dk[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(y);
             }
         });
-    // per-row dot products: 4 lanes per row, each a contiguous quarter of it (16-byte loads of the
-    // fp32 workspace rows); padded rows contribute nothing (their q, k, v are zero)
-    {
-        const int r = tid >> 2, part = tid & 3;
-        constexpr int QK4 = DK / 4, QV4 = DV / 4;
-        float tv = 0.f, tw = 0.f, qg = 0.f, kd = 0.f;
-        if (r < n) {
-            const float* x4 = rec + L::X4 + (size_t)r * DK + part * QK4;
-            const float* x0 = rec + L::X0 + (size_t)r * DK + part * QK4;
-            const float* x2 = rec + L::X2 + (size_t)r * DK + part * QK4;
-            const float* kdp = rec + L::KD + (size_t)r * DK + part * QK4;
-            const float* x3 = rec + L::X3 + (size_t)r * DV + part * QV4;
-            const T* kp = kc + (size_t)r * ks + part * QK4;
-            const T* qp = qc + (size_t)r * ks + part * QK4;
-            const T* vp = vc + (size_t)r * vs + part * QV4;
-#pragma unroll
-            for (int d = 0; d < QK4; d += 4) {
-                const f32x4 a4 = *(const f32x4*)(x4 + d), a0 = *(const f32x4*)(x0 + d);
-                const f32x4 a2 = *(const f32x4*)(x2 + d), b2 = *(const f32x4*)(kdp + d);
-                const f32x4 kv = ld4(kp + d), qv = ld4(qp + d);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    tw = fmaf(a4[u], kv[u], tw);
-                    qg = fmaf(a0[u], qv[u], qg);
-                    kd = fmaf(a2[u], b2[u], kd);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < QV4; j += 4) {
-                const f32x4 a3 = *(const f32x4*)(x3 + j), vv = ld4(vp + j);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) tv = fmaf(a3[u], vv[u], tv);
-            }
-        }
-#pragma unroll
-        for (int o = 1; o < 4; o <<= 1) {
-            tv += __shfl_xor(tv, o, 4);
-            tw += __shfl_xor(tw, o, 4);
-            qg += __shfl_xor(qg, o, 4);
-            kd += __shfl_xor(kd, o, 4);
-        }
-        if (part == 0) {
-            const float er = eg[r];
-            rowv[3][r] = rowv[2][r] + tv + er * tw;                                         // dbeta
-            rowv[4][r] = rowv[0][r] - rowv[1][r] + bs[r] * er * tw + er * qg - kd;          // dg (less the last-row terms)
-            rowv[5][r] = kd;
-        }
-    }
-    // e^{g_last} <dS_out, S_in>
-    {
-        float acc = 0.f;
-#pragma unroll 4
-        for (int i = tid * 4; i < DV * DK; i += NT * 4) {
-            const f32x4 a = *(const f32x4*)(dSo + i), b = *(const f32x4*)(Sin + i);
-            acc = fmaf(a[0], b[0], fmaf(a[1], b[1], fmaf(a[2], b[2], fmaf(a[3], b[3], acc))));
-        }
-        red[tid] = acc;
+    __syncthreads();  // every row sum is in place
+    // dbeta_r = sum_s dA_rs E_rs k_r.k_s + X3_r . v_r + e^{g_r} X4_r . k_r
+    // dg_r = rowsum(dA o A) - colsum(dA o A + dP o P) + dq_r . q_r + beta_r e^{g_r} X4_r . k_r - dKD_r . KD_r
+    //        (dq_r . q_r = e^{g_r} dQG_r . q_r + rowsum(dP o P); the last row also takes the chunk terms)
+    if (tid < C) {
+        const int r = tid;
+        const float er = eg[r], tw = rowv[4][r], kd = ekd[r] * rowv[5][r];
+        red[r] = rowv[2][r] + rowv[3][r] + er * tw;
+        red[C + r] = bs[r] * rowv[2][r] - rowv[1][r] + rowv[0][r] + bs[r] * er * tw - kd;
+        red[2 * C + r] = kd;
     }
     __syncthreads();
-    for (int o = NT / 2; o >= 1; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
     if (tid == 0) {
-        float kdsum = 0.f;
-        for (int r = 0; r < C; ++r) kdsum += rowv[5][r];
-        rowv[4][n - 1] += kdsum + expf(glast) * red[0];
+        float kdsum = 0.f, dss = 0.f;
+        for (int r = 0; r < C; ++r) kdsum += red[2 * C + r];
+        for (int i = 0; i < DV / RW; ++i) dss += rec[L::DSS + i];  // <dS_out, S_in> by row slice (reverse walk)
+        red[C + n - 1] += kdsum + expf(glast) * dss;
         // d ln(alpha_s) = sum_{r >= s} dg_r, over the real rows
         float run = 0.f;
         for (int s = n - 1; s >= 0; --s) {
-            run += rowv[4][s];
+            run += red[C + s];
             const size_t t = ((size_t)P.b * Tlen + P.t0 + s) * H + P.h;
             dalpha[t] = run / alpha[t];
-            dbeta[t] = rowv[3][s];
+            dbeta[t] = red[s];
         }
     }
 }
