@@ -226,19 +226,46 @@ __device__ __forceinline__ ChunkPos chunk_pos(int Tlen, int H, int NC) {
 // prep: g, A, Tinv, W, U, KD per chunk
 // ---------------------------------------------------------------------------------------------
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, const T* __restrict__ v,
-                                                   const float* __restrict__ alpha, const float* __restrict__ beta,
-                                                   float* __restrict__ ws, int Tlen, int H, int NC) {
+__global__ __launch_bounds__(NT, 2) void gdn_bwd_prep(const T* __restrict__ k, const T* __restrict__ v,
+                                                      const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                      float* __restrict__ ws, int Tlen, int H, int NC) {
     using L = WsLay<DK, DV>;
-    __shared__ float stage[STAGE_FLOATS];
-    __shared__ float Am[C * LD64], Tm[C * LD64];
+    // The chunk's K and V rows are read once, with 16-byte loads issued before anything else, and
+    // every product takes them from LDS (rows padded by 16 bytes); A lives in the products' staging
+    // buffer between its product and the inverse.
+    constexpr int EK = 16 / (int)sizeof(T), LDK = DK + EK, LDV = DV + EK;
+    constexpr int NKL = C * DK / EK / NT, NVL = C * DV / EK / NT;
+    static_assert(NKL * EK * NT == C * DK && NVL * EK * NT == C * DV, "tile copy split");
+    constexpr int LT = C + 4;  // row stride of A and Tinv (16-byte rows)
+    static_assert((size_t)C * LT <= STAGE_FLOATS, "A in the staging buffer");
+    __shared__ __align__(16) float stage[STAGE_FLOATS];
+    __shared__ __align__(16) T Kt[C * LDK];
+    __shared__ __align__(16) T Vt[C * LDV];
+    __shared__ __align__(16) float Tm[C * LT];
     __shared__ float gs[C], bs[C], g2[C], bsg[C], ekd[C];
+    float* Am = stage;
     const ChunkPos P = chunk_pos(Tlen, H, NC);
     float* rec = ws + P.cid * L::PER;
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h;
-    const int tid = (int)threadIdx.x;
+    const int tid = (int)threadIdx.x, n = P.n;
+    const size_t ks = (size_t)H * DK, vs = (size_t)H * DV;
+    const T* kc = k + tok0 * DK;
+    const T* vc = v + tok0 * DV;
+    f32x4 kr[NKL], vr[NVL];  // 16-byte carriers (raw bits of EK elements)
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+        const int i = (tid + m * NT) * EK, r = i / DK, d = i % DK;
+        kr[m] = kZero4;
+        if (r < n) __builtin_memcpy(&kr[m], kc + (size_t)r * ks + d, 16);
+    }
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) {
+        const int i = (tid + m * NT) * EK, r = i / DV, d = i % DV;
+        vr[m] = kZero4;
+        if (r < n) __builtin_memcpy(&vr[m], vc + (size_t)r * vs + d, 16);
+    }
     if (tid < 64) {
-        const bool ok = tid < P.n;
+        const bool ok = tid < n;
         float la = ok ? logf(alpha[tok0 + (size_t)tid * H]) : 0.0f;
         bs[tid] = ok ? beta[tok0 + (size_t)tid * H] : 0.0f;
 #pragma unroll
@@ -249,51 +276,98 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep(const T* __restrict__ k, cons
         gs[tid] = la;
         rec[L::G + tid] = la;
         // exponentials of the gates once per row (base 2 on the hardware unit)
-        const float l2 = la * kLog2e, gl2 = __shfl(la, P.n - 1, 64) * kLog2e;
+        const float l2 = la * kLog2e, gl2 = __shfl(la, n - 1, 64) * kLog2e;
         g2[tid] = l2;
         bsg[tid] = bs[tid] * fast_exp2(l2);
         ekd[tid] = fast_exp2(gl2 - l2);
     }
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+        const int i = (tid + m * NT) * EK;
+        __builtin_memcpy(Kt + (i / DK) * LDK + i % DK, &kr[m], 16);
+    }
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) {
+        const int i = (tid + m * NT) * EK;
+        __builtin_memcpy(Vt + (i / DV) * LDV + i % DV, &vr[m], 16);
+    }
     __syncthreads();
-    const int n = P.n;
-    const size_t ks = (size_t)H * DK, vs = (size_t)H * DV;
-    const T* kc = k + tok0 * DK;
-    const T* vc = v + tok0 * DV;
-    auto krow4 = [&](int r, int d) { return r < n ? ld4(kc + (size_t)r * ks + d) : kZero4; };
+    auto krow4 = [&](int r, int d) { return ld4(Kt + r * LDK + d); };
     // A = strict_lower(diag(beta) (K K^T) o E)
     tgemm<C, C, DK, true, false>(stage, krow4, [&](int d, int s) { return krow4(s, d); },
                                  [&](int r, int s, float x) {
-                                     Am[r * LD64 + s] = s < r ? bs[r] * fast_exp2(g2[r] - g2[s]) * x : 0.0f;
+                                     Am[r * LT + s] = s < r ? bs[r] * fast_exp2(g2[r] - g2[s]) * x : 0.0f;
                                  });
     __syncthreads();
-    // Tinv = (I + A)^{-1}, column j by forward substitution: T[r][j] = [r == j] - sum_{j<=s<r} A[r][s] T[s][j];
-    // four lanes per column (adjacent lanes of one wave) split the sum over s and combine it
+    // Tinv = (I + A)^{-1} (unit lower triangular) in 16 x 16 blocks.  Diagonal blocks: forward
+    // substitution in registers, one lane per (block, column) of wave 0, while the other waves clear
+    // the upper blocks.  Off-diagonal blocks by distance d = i - j = 1, 2, 3 (one wave each):
+    //     T_ij = -T_ii sum_{m = j}^{i - 1} A_im T_mj
+    // on fp32 MFMA; in step e the lanes of group G supply k slot 4 G + e of both operands, and the
+    // second product takes the first one's accumulator as its B operand in the same slot order.
     {
-        const int j = tid >> 2, part = tid & 3;
-        for (int r = 0; r < C; ++r) {
-            float x = 0.f;
-            for (int s = j + part; s < r; s += 4) x = fmaf(Am[r * LD64 + s], Tm[s * LD64 + j], x);
-            x += __shfl_xor(x, 1, 4);
-            x += __shfl_xor(x, 2, 4);
-            if (part == 0) Tm[r * LD64 + j] = r < j ? 0.0f : (r == j ? 1.0f : -x);
-            __syncthreads();  // row r is read by the other lanes of its column from row r + 1 on
+        const int lane = tid & 63, w = tid >> 6, G = lane >> 4, l16 = lane & 15;
+        if (w == 0) {
+            const int o = 16 * G, col = l16;
+            float a[16][16];
+#pragma unroll
+            for (int r = 1; r < 16; ++r)
+#pragma unroll
+                for (int s4 = 0; s4 < 16; s4 += 4)
+                    if (s4 < r) {
+                        const f32x4 x = *(const f32x4*)&Am[(o + r) * LT + o + s4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) a[r][s4 + u] = x[u];
+                    }
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == col ? 1.0f : 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc = fmaf(-a[r][s2], x[s2], acc);
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tm[(o + r) * LT + o + col] = x[r];
+        } else {
+            for (int i = tid - 64; i < 6 * 256; i += NT - 64) {
+                const int u = i >> 8, e = i & 255;
+                const int bi = u < 3 ? 0 : u < 5 ? 1 : 2, bj = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+                Tm[(16 * bi + (e >> 4)) * LT + 16 * bj + (e & 15)] = 0.0f;
+            }
+        }
+        __syncthreads();
+        for (int d = 1; d < 4; ++d) {
+            if (w < 4 - d) {
+                const int j = w, i = w + d;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int m = j; m < i; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Am[(16 * i + l16) * LT + 16 * m + 4 * G + e],
+                                                                   Tm[(16 * m + 4 * G + e) * LT + 16 * j + l16], acc, 0, 0, 0);
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[(16 * i + l16) * LT + 16 * i + 4 * G + e], acc[e], y, 0, 0, 0);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) Tm[(16 * i + 4 * G + x) * LT + 16 * j + l16] = -y[x];
+            }
+            __syncthreads();
         }
     }
-    __syncthreads();
-    for (int i = tid; i < C * C; i += NT) rec[L::TI + i] = Tm[(i / C) * LD64 + (i % C)];
+    for (int i = 4 * tid; i < C * C; i += 4 * NT) *(f32x4*)(rec + L::TI + i) = *(const f32x4*)&Tm[(i / C) * LT + i % C];
     // W = Tinv diag(beta e^g) K,  U = Tinv diag(beta) V
-    auto trow4 = [&](int r, int s) { return gather4([&](int u) { return Tm[r * LD64 + s + u]; }); };
+    auto trow4 = [&](int r, int s) { return *(const f32x4*)&Tm[r * LT + s]; };
     tgemm<C, DK, C, true, true>(stage, trow4, [&](int s, int d) { return bsg[s] * krow4(s, d); },
                                 [&](int r, int d, float x) { rec[L::W + (size_t)r * DK + d] = x; });
-    tgemm<C, DV, C, true, true>(stage, trow4,
-                                [&](int s, int d) { return s < n ? bs[s] * ld4(vc + (size_t)s * vs + d) : kZero4; },
+    tgemm<C, DV, C, true, true>(stage, trow4, [&](int s, int d) { return bs[s] * ld4(Vt + s * LDV + d); },
                                 [&](int r, int d, float x) { rec[L::U + (size_t)r * DV + d] = x; });
-    const float glast = gs[n - 1];
     for (int i = 4 * tid; i < C * DK; i += 4 * NT) {
         const int r = i / DK, d = i % DK;
         *(f32x4*)(rec + L::KD + i) = ekd[r] * krow4(r, d);
     }
-    if (tid == 0) rec[L::EGL] = expf(glast);
+    if (tid == 0) rec[L::EGL] = expf(gs[n - 1]);
 }
 
 // ---------------------------------------------------------------------------------------------
