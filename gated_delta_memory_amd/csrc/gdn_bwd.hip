@@ -190,8 +190,8 @@ struct WsLay {
                             E = DL + (size_t)C * DV, F = E + (size_t)C * DV, DDL = F + (size_t)DV * DK,
                             DSO = DDL + (size_t)C * DV, X1 = DSO + (size_t)DV * DK,
                             X2 = X1 + (size_t)C * DK, X4 = X2 + (size_t)C * DK,
-                            NQK = X4 + (size_t)C * DK, NKK = NQK + C * C, NDP = NKK + C * C, NDT = NDP + C * C,
-                            NZ = NDT + C * C, DSS = NZ + C * C,  // DSS: <dS_out, S_in> per row slice of the walk
+                            NQK = X4 + (size_t)C * DK, NKK = NQK + C * C,
+                            DSS = NKK + C * C,  // DSS: <dS_out, S_in> per row slice of the walk
                             PER = DSS + 4;                       // floats per chunk
 };
 
@@ -613,15 +613,17 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                                    float* __restrict__ dalpha, float* __restrict__ dbeta,
                                                    float* __restrict__ ws, int Tlen, int H, int NC) {
     using L = WsLay<DK, DV>;
-    // The 64 x 64 intermediates live in this chunk's workspace (cached; the workgroup's working set is
-    // small) rather than LDS, so that two workgroups fit on a CU.
     __shared__ float stage[STAGE_FLOATS];
     __shared__ float gs[C], bs[C], rowv[6][C], red[NT], g2[C], eg[C], bsg[C], ekd[C];
     const ChunkPos P = chunk_pos(Tlen, H, NC);
     float* rec = ws + P.cid * L::PER;
     constexpr int LD64 = C;  // row stride of the workspace 64 x 64 arrays
     const float* Tm = rec + L::TI;
-    float *QK = rec + L::NQK, *KK = rec + L::NKK, *dP = rec + L::NDP, *dT = rec + L::NDT, *Zm = rec + L::NZ;
+    float *QK = rec + L::NQK, *KK = rec + L::NKK;
+    // dP, dTinv (later dA) and Z (later M) are read and rewritten several times each: they stay in LDS
+    // (rows of C + 4 floats), the rest of the chunk's intermediates go through the workspace.
+    constexpr int LN = C + 4;
+    __shared__ __align__(16) float dP[C * LN], dT[C * LN], Zm[C * LN];
     const int tid = (int)threadIdx.x, n = P.n;
     if (tid < C) {
         gs[tid] = rec[L::G + tid];
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                          else KK[(r - C) * LD64 + s] = x;
                                      });
     tgemm<C, C, DV, true, false>(stage, orow4, [&](int j, int s) { return ld4(rec + L::DL + (size_t)s * DV + j); },
-                                 [&](int r, int s, float x) { dP[r * LD64 + s] = s <= r ? x : 0.0f; });
+                                 [&](int r, int s, float x) { dP[r * LN + s] = s <= r ? x : 0.0f; });
     // dTinv = dDelta (diag(beta) V)^T + dW (diag(beta e^g) K)^T
     tgemm<C, C, DV + DK, true, false>(
         stage,
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
             return j < DV ? ld4(rec + L::DDL + (size_t)r * DV + j) : ld4(rec + L::X1 + (size_t)r * DK + j - DV);
         },
         [&](int j, int s) { return j < DV ? bs[s] * vrow4(s, j) : bsg[s] * krow4(s, j - DV); },
-        [&](int r, int s, float x) { dT[r * LD64 + s] = x; });
+        [&](int r, int s, float x) { dT[r * LN + s] = x; });
     // X3 = Tinv^T dDelta: dv = beta o X3, and X3_r . v_r
     tgemm_blk<C, DV, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
                                      [&](int s, int j) { return ld4(rec + L::DDL + (size_t)s * DV + j); },
@@ -703,12 +705,12 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                          put_rows(4, rt0, rowdot(acc, rt0, kel));
                                      });
     // Z = dTinv Tinv^T, then dA = -strict_lower(Tinv^T Z) (into dT)
-    tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return ld4(dT + r * LD64 + s); },
+    tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return ld4(dT + r * LN + s); },
                                 [&](int s, int c2) { return ld4(Tm + c2 * LD64 + s); },
-                                [&](int r, int c2, float x) { Zm[r * LD64 + c2] = x; });
+                                [&](int r, int c2, float x) { Zm[r * LN + c2] = x; });
     tgemm<C, C, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
-                                [&](int s, int c2) { return ld4(Zm + s * LD64 + c2); },
-                                [&](int r, int c2, float x) { dT[r * LD64 + c2] = c2 < r ? -x : 0.0f; });
+                                [&](int s, int c2) { return ld4(Zm + s * LN + c2); },
+                                [&](int r, int c2, float x) { dT[r * LN + c2] = c2 < r ? -x : 0.0f; });
     __syncthreads();
     // column sums over the n x n terms, rowv[1] = colsum(dA o A + dP o P), and
     // rowv[2] = sum_s dA_rs E_rs k_r.k_s (so rowsum(dA o A) = beta_r rowv[2]; rowsum(dP o P) is part
@@ -722,10 +724,10 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         for (int m = 0; m < C / 4; ++m) {
             const int r = w0 + 4 * m;
             const float e = sc <= r ? fast_exp2(g2[r] - g2[sc]) : 0.0f;  // never exp of the upper triangle
-            const float dA = dT[r * LD64 + sc], kk = KK[r * LD64 + sc];
+            const float dA = dT[r * LN + sc], kk = KK[r * LD64 + sc];
             const float pP = sc <= r ? QK[r * LD64 + sc] * e : 0.0f;
             const float dae = dA * e * kk;
-            col += fmaf(dae, bs[r], dP[r * LD64 + sc] * pP);
+            col += fmaf(dae, bs[r], dP[r * LN + sc] * pP);
             const float r2 = wave_sum(dae);
             if (sc == 0) rowv[2][r] = r2;
         }
@@ -739,13 +741,13 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     for (int i = tid; i < C * C; i += NT) {
         const int r = i / C, s = i % C;
         const float e = s <= r ? fast_exp2(g2[r] - g2[s]) : 0.0f;
-        dP[r * LD64 + s] *= e;
-        Zm[r * LD64 + s] = dT[r * LD64 + s] * bs[r] * e;
+        dP[r * LN + s] *= e;
+        Zm[r * LN + s] = dT[r * LN + s] * bs[r] * e;
     }
     __syncthreads();
     // dq = e^g o dQG + (dP o E) K = [diag(e^g) dO | dP o E] [S_in; K]  (dQG = dO S_in), and dq_r . q_r
     tgemm_blk<C, DK, DV + C, true, true>(
-        stage, [&](int r, int kk) { return kk < DV ? eg[r] * orow4(r, kk) : ld4(dP + r * LD64 + kk - DV); },
+        stage, [&](int r, int kk) { return kk < DV ? eg[r] * orow4(r, kk) : ld4(dP + r * LN + kk - DV); },
         [&](int kk, int d) { return kk < DV ? ld4(Sin + (size_t)kk * DK + d) : krow4(kk - DV, d); },
         [&](const auto& acc, int rt0, int ct0) {
             each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
@@ -757,9 +759,9 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     const float glast = gs[n - 1];
     tgemm<C, DK, 3 * C, false, true>(stage,
         [&](int r, int kk) {
-            return kk < C       ? ld4(dP + kk * LD64 + r)
-                   : kk < 2 * C ? gather4([&](int u) { return Zm[(r + u) * LD64 + kk - C]; })
-                                : ld4(Zm + (kk - 2 * C) * LD64 + r);
+            return kk < C       ? ld4(dP + kk * LN + r)
+                   : kk < 2 * C ? gather4([&](int u) { return Zm[(r + u) * LN + kk - C]; })
+                                : ld4(Zm + (kk - 2 * C) * LN + r);
         },
         [&](int kk, int d) { return kk < C ? qrow4(kk, d) : krow4(kk % C, d); },
         [&](int r, int d, float x) {
