@@ -10,6 +10,8 @@
  *  - Tensor arguments are DEVICE pointers owned by the caller; the library never
  *    allocates, frees or retains them.  Arrays are dense and row-major with the last
  *    index fastest.  `stream` is a hipStream_t (NULL = the default stream).
+ *  - Every tensor and workspace pointer is 16-byte aligned (any hipMalloc or torch
+ *    allocation is): the kernels move rows in 8- and 16-byte pieces.  Not checked.
  *  - Calls are asynchronous on `stream`: the library performs no host synchronisation,
  *    no allocation and keeps no state between calls (thread-safe; concurrent calls on
  *    different streams must use different workspaces).
@@ -125,7 +127,7 @@ int atma_gdn_fwd_varlen(const void* q, const void* k, const void* v, const float
  *   Dk, Dv in {64, 128}; chunk == 64; dt == ATMA_BF16 or ATMA_F32.  All outputs are written,
  *   not accumulated.  alpha must be > 0 (the gradient divides by it).
  *   workspace at least atma_gdn_bwd_workspace_bytes(...) bytes (per chunk: the recomputed
- *   chunk operands, the chunk's input state and its gradient; about 400 KB per chunk at
+ *   chunk operands, the chunk's input state and its gradient; about 520 KB per chunk at
  *   Dk = Dv = 128).
  * ------------------------------------------------------------------------------- */
 int atma_gdn_bwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
