@@ -255,6 +255,25 @@ def secondary(torch, atma, workloads):
                      "polar_mfma_frac": round(fl / (tq.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del p, o_p
         torch.cuda.empty_cache()
+    # Canon prologue (depthwise causal convolution, 4 taps, residual, per-head unit norm) on the
+    # query projection of the 8/2-head, D = 128 layout at the 2K shape: algorithmic bytes are one
+    # read of x and one write of y (bf16), the taps and the carried state are negligible
+    B, T, Cq, K = 8, 2048, 8 * 128, 4
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn(B, T, Cq, device="cuda", generator=gen).to(torch.bfloat16)
+    wc = torch.randn(K, Cq, device="cuda", generator=gen) * 0.5
+    st = torch.zeros(B, K - 1, Cq, device="cuda", dtype=torch.bfloat16)
+    yc = torch.empty_like(x)
+    tc = Timer(torch)
+    for it in range(21):
+        (tc if it else (lambda f: f()))(lambda: atma.atma_canon(x, wc, st, residual=True, heads=8, update_state=False,
+                                                                y=yc))
+    torch.cuda.synchronize()
+    cb = 2 * B * T * Cq * 2
+    res["canon_q_d128_b8_t2k"] = {"canon_us": round(tc.mean_ms() * 1e3, 2), "bytes": cb,
+                                  "hbm_frac": round(cb / (tc.mean_ms() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del x, wc, st, yc
+    torch.cuda.empty_cache()
     # training step of the Polar core (training forward + backward) at the 2K layer shapes; the
     # backward's algorithmic work is the usual five products per visible (query, key) pair
     # (S recomputed, dP, dV, dK, dQ): 10 D flop per pair per head
