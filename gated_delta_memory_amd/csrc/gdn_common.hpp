@@ -16,20 +16,28 @@ struct TileRegs {
     static constexpr int NVEC = ROWS * COLS / VEC;
     static constexpr int PER = (NVEC + NT - 1) / NT;
     u32x4 r[PER];
-    // STREAM: non-temporal loads, for data no later kernel reads
+    int nr;  // rows < nr are real; the rest are stored as zero
+    // STREAM: non-temporal loads, for data no later kernel reads.  Every load is issued without a
+    // branch (rows at and past nrows >= 1 re-read row nrows - 1) and nothing reads the registers
+    // until the stores, which write those rows as zero: all the loads are in flight together.
     template <bool STREAM = false>
     __device__ __forceinline__ void load(const T* g, size_t ld, int nrows) {
+        nr = nrows;
 #pragma unroll
         for (int m = 0; m < PER; ++m) {
             const int i = threadIdx.x + m * NT;
             const int row = i / (COLS / VEC), cv = i % (COLS / VEC);
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (i < NVEC && row < nrows) {
-                const u32x4* src = (const u32x4*)(g + (size_t)row * ld + cv * VEC);
-                if constexpr (STREAM) x = __builtin_nontemporal_load(src);
-                else x = *src;
+            const u32x4* src = (const u32x4*)(g + (size_t)min(row, nrows - 1) * ld + cv * VEC);
+            if constexpr (NVEC % NT == 0) {  // every thread has PER pieces: no branch at all
+                if constexpr (STREAM) r[m] = __builtin_nontemporal_load(src);
+                else r[m] = *src;
+            } else {
+                r[m] = u32x4{0u, 0u, 0u, 0u};
+                if (i < NVEC) {
+                    if constexpr (STREAM) r[m] = __builtin_nontemporal_load(src);
+                    else r[m] = *src;
+                }
             }
-            r[m] = x;
         }
     }
     template <int LDS_LD>
@@ -39,7 +47,7 @@ struct TileRegs {
             const int i = threadIdx.x + m * NT;
             if (i < NVEC) {
                 const int row = i / (COLS / VEC), cv = i % (COLS / VEC);
-                *(u32x4*)(s + row * LDS_LD + cv * VEC) = r[m];
+                *(u32x4*)(s + row * LDS_LD + cv * VEC) = row < nr ? r[m] : u32x4{0u, 0u, 0u, 0u};
             }
         }
     }
@@ -51,7 +59,8 @@ struct TileRegs {
             const int i = threadIdx.x + m * NT;
             if (i < NVEC) {
                 const int row = i / (COLS / VEC), cv = i % (COLS / VEC);
-                const T* e = (const T*)&r[m];
+                const u32x4 v = row < nr ? r[m] : u32x4{0u, 0u, 0u, 0u};
+                const T* e = (const T*)&v;
 #pragma unroll
                 for (int x = 0; x < VEC; ++x) s[(cv * VEC + x) * LDS_LD + row] = e[x];
             }

@@ -184,17 +184,24 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
     char* rb = rg.rb + cid * L::RB;
 
     // ---- A: K into LDS, cumulative log decay; V's load starts here and lands after W --------
+    // (the gates are requested right behind the tiles, so that all of them share one trip to memory)
     TileRegs<bf16, C, DV> vr;
+    float a_in = 1.0f, b_in = 0.0f;
     {
         TileRegs<bf16, C, DK> kr;
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
         vr.template load<true>(v + tok0 * DV, (size_t)H * DV, n);
+        if (w == 0) {
+            const size_t gi = tok0 + (size_t)min(lane, n - 1) * H;  // rows past n re-read row n-1, then discarded
+            a_in = alpha[gi];
+            b_in = beta[gi];
+        }
         kr.template store<LDK>(sm.Ks);
     }
     if (w == 0) {
         const bool ok = lane < n;
-        float la = ok ? __logf(alpha[tok0 + (size_t)lane * H]) : 0.0f;
-        const float be = ok ? beta[tok0 + (size_t)lane * H] : 0.0f;
+        float la = ok ? __logf(a_in) : 0.0f;
+        const float be = ok ? b_in : 0.0f;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(la, o, 64);
