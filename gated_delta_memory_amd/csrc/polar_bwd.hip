@@ -366,20 +366,25 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
 }
 
 // ---------------------------------------------------------------------------------------------
-// dkv: 128 keys per workgroup, query blocks of 64 (every head of the group) through two stages
+// dkv: 128 keys per workgroup, query blocks of 64 (every head of the group) through two stages.
+// MODE 0 forms dK and dV together.  At head width 128 their accumulators and fragments need more
+// than half a SIMD's registers (one wave per SIMD, and one workgroup per CU at the usual grid
+// sizes), so one launch runs a dV role (MODE 1: S and dV) in its first half of workgroups and a
+// dK role (MODE 2: S, dP and dK) in its second half: each fits two waves per SIMD, and a CU holds
+// one workgroup of each.  Every product is the same in all modes, so the results are bitwise equal.
 // ---------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v, const bf16* __restrict__ dsg,
-                                                       const float* __restrict__ rec, bf16* __restrict__ dk,
-                                                       bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
+constexpr int dkv_stage_bytes() { return 2 * BShape<D>::TILE + NREC * BB * 4; }  // Q tile | dS tile | row scalars [5][64]
+
+template <int D, int MODE>
+__device__ __forceinline__ void dkv_body(int wg, int nwg, char* g_st0, char* g_st1, const bf16* __restrict__ q,
+                                         const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                         const bf16* __restrict__ dsg, const float* __restrict__ rec,
+                                         bf16* __restrict__ dk, bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
     using SH = BShape<D>;
     constexpr int NKS = SH::NKS, NDT = SH::NDT, ROWB = SH::ROWB;
-    constexpr int STAGE = 2 * SH::TILE + NREC * BB * 4;  // Q tile | dS tile | row scalars [5][64]
-    __shared__ __align__(16) char g_st0[STAGE];
-    __shared__ __align__(16) char g_st1[STAGE];
     const int nkt = (T + BKT - 1) / BKT;
-    const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
+    const int per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
     const int item = xcd * per + min(xcd, extra) + (wg >> 3);
     const int bk = item / nkt;
     const int j = item - bk * nkt;  // key tile; tile 0 streams the most query blocks and goes first
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16*
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             kf[ks] = *(const bf16x8*)(k + e0 + 16 * ks);
-            vf[ks] = *(const bf16x8*)(v + e0 + 16 * ks);
+            if constexpr (MODE != 1) vf[ks] = *(const bf16x8*)(v + e0 + 16 * ks);
         }
     }
     const int r0 = (int)threadIdx.x / SH::CPR, pc = (int)threadIdx.x % SH::CPR;
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16*
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 s = mfma32(*(const bf16x8*)(Qs + of.koff[ks] + qt * 32 * ROWB), kf[ks], s);
-                dp = mfma32(*(const bf16x8*)(Ss + of.koff[ks] + qt * 32 * ROWB), vf[ks], dp);
+                if constexpr (MODE != 1) dp = mfma32(*(const bf16x8*)(Ss + of.koff[ks] + qt * 32 * ROWB), vf[ks], dp);
             }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -462,15 +467,19 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16*
                     float p = fast_exp2(fmaf(s[x], rc[hf][z], -rl[hf][z]));
                     if (edge) p = (q0 + ql + 8 * hf + z < key) ? 0.0f : p;
                     pf[e] = (bf16)p;
-                    lf[e] = (bf16)(p * fmaf(rt[hf][z], dp[x], fmaf(rb[hf][z], p, ra[hf][z])));
+                    if constexpr (MODE != 1) lf[e] = (bf16)(p * fmaf(rt[hf][z], dp[x], fmaf(rb[hf][z], p, ra[hf][z])));
                 }
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const int base = (32 * qt + 16 * st) * ROWB;
-                    const bf16x4 slo = tr_read(Ss, base + of.tlo[dt]), shi = tr_read(Ss, base + of.thi[dt]);
-                    dva[dt] = mfma32(__builtin_shufflevector(slo, shi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dva[dt]);
-                    const bf16x4 qlo = tr_read(Qs, base + of.tlo[dt]), qhi = tr_read(Qs, base + of.thi[dt]);
-                    dka[dt] = mfma32(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), lf, dka[dt]);
+                    if constexpr (MODE != 2) {
+                        const bf16x4 slo = tr_read(Ss, base + of.tlo[dt]), shi = tr_read(Ss, base + of.thi[dt]);
+                        dva[dt] = mfma32(__builtin_shufflevector(slo, shi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dva[dt]);
+                    }
+                    if constexpr (MODE != 1) {
+                        const bf16x4 qlo = tr_read(Qs, base + of.tlo[dt]), qhi = tr_read(Qs, base + of.thi[dt]);
+                        dka[dt] = mfma32(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), lf, dka[dt]);
+                    }
                 }
             }
         }
@@ -501,10 +510,33 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16*
                     yk[x] = (bf16)dka[dt][4 * g + x];
                     yv[x] = (bf16)dva[dt][4 * g + x];
                 }
-                *(bf16x4*)(dk + e0 + 32 * dt + 8 * g + 4 * G2) = yk;
-                *(bf16x4*)(dv + e0 + 32 * dt + 8 * g + 4 * G2) = yv;
+                if constexpr (MODE != 1) *(bf16x4*)(dk + e0 + 32 * dt + 8 * g + 4 * G2) = yk;
+                if constexpr (MODE != 2) *(bf16x4*)(dv + e0 + 32 * dt + 8 * g + 4 * G2) = yv;
             }
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                       const bf16* __restrict__ v, const bf16* __restrict__ dsg,
+                                                       const float* __restrict__ rec, bf16* __restrict__ dk,
+                                                       bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
+    __shared__ __align__(16) char g_st0[dkv_stage_bytes<D>()];
+    __shared__ __align__(16) char g_st1[dkv_stage_bytes<D>()];
+    dkv_body<D, 0>((int)blockIdx.x, (int)gridDim.x, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
+}
+
+// grid 2 nk: workgroups [0, nk) take the dV role, [nk, 2 nk) the dK role of the same key tiles
+template <int D>
+__global__ __launch_bounds__(NT, 2) void polar_bwd_dkv_split(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                             const bf16* __restrict__ v, const bf16* __restrict__ dsg,
+                                                             const float* __restrict__ rec, bf16* __restrict__ dk,
+                                                             bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
+    __shared__ __align__(16) char g_st0[dkv_stage_bytes<D>()];
+    __shared__ __align__(16) char g_st1[dkv_stage_bytes<D>()];
+    const int nk = (int)gridDim.x / 2, wg = (int)blockIdx.x;
+    if (wg < nk) dkv_body<D, 1>(wg, nk, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
+    else dkv_body<D, 2>(wg - nk, nk, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -612,7 +644,7 @@ hipError_t launch_polar_bwd(const PolarBwdArgs& a, hipStream_t stream) {
     const long long nq = (long long)((a.T + BQ - 1) / BQ) * a.Hq * a.B;
     const long long nk = (long long)((a.T + BKT - 1) / BKT) * a.Hkv * a.B;
     const long long prep_threads = (long long)a.B * a.T * a.Hq * (a.D / 8);
-    if (nq > 0x7fffffffLL || nk > 0x7fffffffLL || prep_threads / NT > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (nq > 0x7fffffffLL || 2 * nk > 0x7fffffffLL || prep_threads / NT > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define ATMA_PB_LAUNCH(DD)                                                                                        \
     do {                                                                                                          \
         hipLaunchKernelGGL(polar_bwd_prep<DD>, dim3((unsigned)((prep_threads + NT - 1) / NT)), dim3(NT), 0,       \
@@ -623,9 +655,14 @@ hipError_t launch_polar_bwd(const PolarBwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((polar_bwd_dq<DD, false>), dim3((unsigned)nq), dim3(NT), 0, stream, (const bf16*)a.q,  \
                            (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.r0, a.p, w.rec, \
                            w.part, (bf16*)a.dq, w.dtr, a.T, Tp, a.Hq, a.Hkv);                                      \
-        hipLaunchKernelGGL(polar_bwd_dkv<DD>, dim3((unsigned)nk), dim3(NT), 0, stream, (const bf16*)a.q,          \
-                           (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.rec,            \
-                           (bf16*)a.dk, (bf16*)a.dv, a.T, Tp, a.Hq, a.Hkv);                                        \
+        if (DD == 64)                                                                                             \
+            hipLaunchKernelGGL(polar_bwd_dkv<DD>, dim3((unsigned)nk), dim3(NT), 0, stream, (const bf16*)a.q,      \
+                               (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.rec,        \
+                               (bf16*)a.dk, (bf16*)a.dv, a.T, Tp, a.Hq, a.Hkv);                                    \
+        else                                                                                                      \
+            hipLaunchKernelGGL(polar_bwd_dkv_split<DD>, dim3((unsigned)(2 * nk)), dim3(NT), 0, stream,            \
+                               (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg,          \
+                               (const float*)w.rec, (bf16*)a.dk, (bf16*)a.dv, a.T, Tp, a.Hq, a.Hkv);               \
         hipLaunchKernelGGL(polar_bwd_params_partial<DD>, dim3(a.Hq * PCH), dim3(NT), 0, stream,                   \
                            (const bf16*)w.dsg, (const float*)w.part, (const float*)w.dtr, w.ppart, a.B, a.T, a.Hq); \
         hipLaunchKernelGGL(polar_bwd_params_final<DD>, dim3(a.Hq), dim3(NT), 0, stream, (const float*)w.ppart,    \
