@@ -384,9 +384,10 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_prep(const T* __restrict__ k, c
 // 64 lanes of a read hit 64 different banks.
 // ---------------------------------------------------------------------------------------------
 constexpr int RW = 32;
+constexpr int NTW = 512, NWW = NTW / 64;  // threads and waves of a walk workgroup (two waves per SIMD)
 
 template <int DK, int DV, bool BACK>
-__global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0, float* __restrict__ sfinal,
+__global__ __launch_bounds__(NTW) void gdn_bwd_walk(const float* __restrict__ s0, float* __restrict__ sfinal,
                                                    float* __restrict__ ws, int H, int NC) {
     using L = WsLay<DK, DV>;
     constexpr int LA = DK + 4, LB = DK + 16, LS = DK + 4, LX = RW + 16;
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
     constexpr size_t OFF_XO = BACK ? L::DDL : L::DL;
     constexpr size_t OFF_SO = BACK ? L::DSO : L::SIN;
     constexpr float SG1 = BACK ? 1.0f : -1.0f, SG2 = BACK ? -1.0f : 1.0f;
-    constexpr int NA = C * DK / 4 / NT, NX = C * RW / 4 / NT, NF = RW * DK / 4 / NT;
+    constexpr int NA = C * DK / 4 / NTW, NX = C * RW / 4 / NTW, NF = RW * DK / 4 / NTW;
     static_assert(NA >= 1 && NX >= 1 && NF >= 1, "split");
     __shared__ __align__(16) float As[C * LA];
     __shared__ __align__(16) float Bs[C * LB];
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
     const int lane = tid & 63, w = tid >> 6, G = lane >> 4, c16 = lane & 15;
     const size_t bh = (size_t)(item / (DV / RW));
     // state rows in, zero when absent
-    for (int q = tid; q < RW * DK / 4; q += NT) {
+    for (int q = tid; q < RW * DK / 4; q += NTW) {
         const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (s0) x = *(const f32x4*)(s0 + (bh * DV + row0 + i) * DK + d4);
@@ -419,16 +420,17 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
     }
     f32x4 ra[NA], rb[NA], rx[NX], rf[NF], rs[NF];
     float regl;
-    __shared__ float wred[4];
-    // part p of 4 of a chunk's operands (part 0 also takes the small ones): the parts are issued
-    // between the quarters of the first product, so the loads drain while the MFMAs run instead
+    __shared__ float wred[NWW];
+    // part p of NP of a chunk's operands (part 0 also takes the small ones): the parts are issued
+    // between the k ranges of the first product, so the loads drain while the MFMAs run instead
     // of stalling the waves at issue
-    static_assert(NA % 4 == 0, "fetch split");
+    constexpr int NP = NA >= 4 ? 4 : NA;
+    static_assert(NA % NP == 0 && NP >= 2 && DK % (4 * NP) == 0, "fetch split");
     auto fetch_part = [&](int c, int p) {
         const float* rec = ws + (bh * NC + c) * L::PER;
 #pragma unroll
-        for (int m = p * (NA / 4); m < (p + 1) * (NA / 4); ++m) {
-            const int q = tid + m * NT, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+        for (int m = p * (NA / NP); m < (p + 1) * (NA / NP); ++m) {
+            const int q = tid + m * NTW, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
             ra[m] = *(const f32x4*)(rec + OFF_A + (size_t)r * DK + d4);
             rb[m] = *(const f32x4*)(rec + OFF_B + (size_t)r * DK + d4);
         }
@@ -436,27 +438,27 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
             if (p == 1)
 #pragma unroll
                 for (int m = 0; m < NF; ++m) {
-                    const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                    const int q = tid + m * NTW, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
                     rs[m] = *(const f32x4*)(rec + L::SIN + (size_t)(row0 + i) * DK + d4);
                 }
         }
         if (p != 0) return;
 #pragma unroll
         for (int m = 0; m < NX; ++m) {
-            const int q = tid + m * NT, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
+            const int q = tid + m * NTW, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
             rx[m] = *(const f32x4*)(rec + OFF_X + (size_t)r * DV + row0 + c4);
         }
         if constexpr (BACK) {
 #pragma unroll
             for (int m = 0; m < NF; ++m) {
-                const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                const int q = tid + m * NTW, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
                 rf[m] = *(const f32x4*)(rec + L::F + (size_t)(row0 + i) * DK + d4);
             }
         }
         regl = rec[L::EGL];
     };
 #pragma unroll
-    for (int p = 0; p < 4; ++p) fetch_part(BACK ? NC - 1 : 0, p);
+    for (int p = 0; p < NP; ++p) fetch_part(BACK ? NC - 1 : 0, p);
     for (int it = 0; it < NC; ++it) {
         const int c = BACK ? NC - 1 - it : it;
         float* rec = ws + (bh * NC + c) * L::PER;
@@ -468,20 +470,20 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
         // operands of this chunk into LDS; the state (S_in or dS_out) out to the workspace
 #pragma unroll
         for (int m = 0; m < NA; ++m) {
-            const int q = tid + m * NT, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            const int q = tid + m * NTW, r = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
             *(f32x4*)(As + r * LA + d4) = ra[m];
             *(f32x4*)(Bs + r * LB + d4) = rb[m];
         }
 #pragma unroll
         for (int m = 0; m < NX; ++m) {
-            const int q = tid + m * NT, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
+            const int q = tid + m * NTW, r = q / (RW / 4), c4 = (q % (RW / 4)) * 4;
             *(f32x4*)(Xs + r * LX + c4) = rx[m];
         }
         if constexpr (BACK) {  // dS_out out, and this slice's share of <dS_out, S_in>
             float dot = 0.f;
 #pragma unroll
             for (int m = 0; m < NF; ++m) {
-                const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+                const int q = tid + m * NTW, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
                 const f32x4 x = *(const f32x4*)(St + i * LS + d4);
                 *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = x;
                 dot = fmaf(x[0], rs[m][0], fmaf(x[1], rs[m][1], fmaf(x[2], rs[m][2], fmaf(x[3], rs[m][3], dot))));
@@ -489,45 +491,46 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
             dot = wave_sum(dot);
             if (lane == 0) wred[w] = dot;
         } else {
-            for (int q = tid; q < RW * DK / 4; q += NT) {
+            for (int q = tid; q < RW * DK / 4; q += NTW) {
                 const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
                 *(f32x4*)(rec + OFF_SO + (size_t)(row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
             }
         }
         __syncthreads();
-        if (BACK && tid == 0) rec[L::DSS + row0 / RW] = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-        // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns rows 16 w .. 16 w + 15, both column tiles;
-        // the next chunk's operands are requested a quarter at a time between the k quarters
+        if (BACK && tid == 0) {
+            float dss = 0.f;
+#pragma unroll
+            for (int i = 0; i < NWW; ++i) dss += wred[i];
+            rec[L::DSS + row0 / RW] = dss;
+        }
+        // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns the 16 x 16 tile (rows 16 (w % 4),
+        // columns 16 (w / 4)); the next chunk's operands are requested a part at a time between the
+        // k ranges
+        static_assert(C / 16 * (RW / 16) == NWW, "one tile per wave");
         {
-            f32x4 acc[RW / 16];
+            const int rt = w % (C / 16), yt = w / (C / 16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int y = 0; y < RW / 16; ++y) acc[y] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < NP; ++p) {
                 if (it + 1 < NC) fetch_part(BACK ? c - 1 : c + 1, p);
 #pragma unroll
-                for (int k = p * (DK / 4); k < (p + 1) * (DK / 4); k += 4) {
-                    const float a = As[(16 * w + c16) * LA + k + G];
-#pragma unroll
-                    for (int y = 0; y < RW / 16; ++y)
-                        acc[y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, St[(16 * y + c16) * LS + k + G], acc[y], 0, 0, 0);
-                }
+                for (int k = p * (DK / NP); k < (p + 1) * (DK / NP); k += 4)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(16 * rt + c16) * LA + k + G],
+                                                               St[(16 * yt + c16) * LS + k + G], acc, 0, 0, 0);
             }
 #pragma unroll
-            for (int y = 0; y < RW / 16; ++y)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * w + 4 * G + v, i = 16 * y + c16;
-                    const float x = Xs[r * LX + i] + SG1 * acc[y][v];
-                    Xs[r * LX + i] = x;
-                    rec[OFF_XO + (size_t)r * DV + row0 + i] = x;
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * rt + 4 * G + v, i = 16 * yt + c16;
+                const float x = Xs[r * LX + i] + SG1 * acc[v];
+                Xs[r * LX + i] = x;
+                rec[OFF_XO + (size_t)r * DV + row0 + i] = x;
+            }
         }
         __syncthreads();
         // St = e^{g_last} St (+ F rows)
 #pragma unroll
         for (int m = 0; m < NF; ++m) {
-            const int q = tid + m * NT, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
+            const int q = tid + m * NTW, i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
             f32x4 x = *(const f32x4*)(St + i * LS + d4);
 #pragma unroll
             for (int u = 0; u < 4; ++u) x[u] = BACK ? fmaf(egl, x[u], fcur[m][u]) : egl * x[u];
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
         __syncthreads();
         // St[i][d] += SG2 * sum_r X[r][i] B[r][d]: wave w owns column tiles of one row tile
         {
-            constexpr int DT = DK / 16 / (4 / (RW / 16));  // column tiles per wave
+            constexpr int DT = DK / 16 / (NWW / (RW / 16));  // column tiles per wave
             const int yt = w % (RW / 16), d0 = (w / (RW / 16)) * DT;
             f32x4 acc[DT];
 #pragma unroll
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_walk(const float* __restrict__ s0,
     }
     __syncthreads();
     if (sfinal)
-        for (int q = tid; q < RW * DK / 4; q += NT) {
+        for (int q = tid; q < RW * DK / 4; q += NTW) {
             const int i = q / (DK / 4), d4 = (q % (DK / 4)) * 4;
             *(f32x4*)(sfinal + (bh * DV + row0 + i) * DK + d4) = *(const f32x4*)(St + i * LS + d4);
         }
@@ -817,10 +820,10 @@ static void launch_bwd_typed(const GdnBwdArgs& a, hipStream_t s) {
     const dim3 gc(NC, a.H, a.B), gr((unsigned)(DV / RW) * a.H * a.B);
     hipLaunchKernelGGL((gdn_bwd_prep<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.k, (const T*)a.v, a.alpha, a.beta,
                        ws, a.T, a.H, NC);
-    hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, false>), gr, dim3(NT), 0, s, a.init_state, nullptr, ws, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, false>), gr, dim3(NTW), 0, s, a.init_state, nullptr, ws, a.H, NC);
     hipLaunchKernelGGL((gdn_bwd_pre<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.q, (const T*)a.k, (const T*)a.dO, ws,
                        a.T, a.H, NC);
-    hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, true>), gr, dim3(NT), 0, s, a.dS_final, a.d_init, ws, a.H, NC);
+    hipLaunchKernelGGL((gdn_bwd_walk<DK, DV, true>), gr, dim3(NTW), 0, s, a.dS_final, a.d_init, ws, a.H, NC);
     hipLaunchKernelGGL((gdn_bwd_post<T, DK, DV>), gc, dim3(NT), 0, s, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                        a.alpha, a.beta, (const T*)a.dO, (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dalpha, a.dbeta, ws, a.T,
                        a.H, NC);
