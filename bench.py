@@ -402,6 +402,20 @@ def secondary(torch, atma, workloads):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w):
     """The fp64 oracle, as it stands, on this host's cores: full memory recurrence and full causal
     Polar attention for the workload's sequences (same shapes, same seed recipe)."""
@@ -424,6 +438,7 @@ def cpu_baseline(w):
     used = max(oracle.threads_used(cores, nseq * w.gdn_H), oracle.threads_used(cores, nseq * w.T * w.polar_Hq))
     del np
     return {"value": round(nseq * w.T / dt, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "seconds": round(dt, 2),
             "sample": f"{nseq} of {w.B} sequences of {w.name} (T={w.T}): full fp64 memory recurrence "
                       f"({w.gdn_H} heads x d={w.gdn_D}) + full causal Polar attention ({w.polar_Hq} heads x d=64)"}

@@ -52,7 +52,8 @@ def _load() -> ctypes.CDLL:
     P = ctypes.POINTER(PolarParams)
     sig = {
         "atma_gdn_fwd": ([vp] * 8 + [i] * 7 + [vp, sz, vp], i),
-        "atma_gdn_fwd_workspace_bytes": ([i] * 7, sz),
+        "atma_gdn_fwd_workspace_bytes": ([i] * 6, sz),
+        "atma_gdn_fwd_workspace_bytes_dtype": ([i] * 7, sz),
         "atma_gdn_fwd_varlen": ([vp] * 6 + [i, i] + [vp] * 3 + [i] * 6 + [vp, sz, vp], i),
         "atma_gdn_decode_step": ([vp] * 7 + [i] * 5 + [vp], i),
         "atma_polar_attn_fwd": ([vp, vp, vp, P, vp, vp, vp] + [i] * 6 + [vp, sz, vp], i),
@@ -129,12 +130,33 @@ def _f32(t, name):
         raise TypeError(f"{name} must be float32")
 
 
+def _expect(t, name, shape, dtype=None, optional=False):
+    """Checks that tensor ``t`` (a buffer the library will read or write) has exactly ``shape``
+    and, when given, ``dtype``; None passes only when ``optional``.  Every buffer handed to the
+    C ABI goes through here or an equivalent check, so no kernel can run past a buffer's end."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 # ------------------------------------------------------------------------------------
 # gated-delta memory
 # ------------------------------------------------------------------------------------
-def atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk=CHUNK, dtype=torch.bfloat16) -> int:
-    return int(lib.atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk,
-                                                ATMA_BF16 if dtype == torch.bfloat16 else ATMA_F32))
+def atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk=CHUNK, dtype=None) -> int:
+    """Workspace bytes of atma_gdn_fwd: for either dtype when ``dtype`` is None, else for that one."""
+    if dtype is None:
+        return int(lib.atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk))
+    return int(lib.atma_gdn_fwd_workspace_bytes_dtype(B, T, H, Dk, Dv, chunk,
+                                                      ATMA_BF16 if dtype == torch.bfloat16 else ATMA_F32))
 
 
 def atma_gdn_fwd(q, k, v, alpha, beta, init_state=None, *, o=None, final_state=None, workspace=None,
@@ -147,18 +169,21 @@ def atma_gdn_fwd(q, k, v, alpha, beta, init_state=None, *, o=None, final_state=N
         raise ValueError("inconsistent shapes")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
-    _f32(alpha, "alpha"), _f32(beta, "beta"), _f32(init_state, "init_state")
+    _f32(alpha, "alpha"), _f32(beta, "beta")
+    _expect(init_state, "init_state", (B, H, Dv, Dk), torch.float32, optional=True)
     if o is None:
         o = torch.empty(B, T, H, Dv, dtype=q.dtype, device=q.device)
     if final_state is None and want_final:
         final_state = torch.empty(B, H, Dv, Dk, dtype=torch.float32, device=q.device)
+    _expect(o, "o", (B, T, H, Dv), q.dtype)
+    _expect(final_state, "final_state", (B, H, Dv, Dk), torch.float32, optional=True)
     need = atma_gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, CHUNK, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(q, k, v, alpha, beta, init_state, o, final_state, workspace)
     st = lib.atma_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(init_state), _ptr(o),
                           _ptr(final_state), B, T, H, Dk, Dv, CHUNK, _dtype_code(q), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream(stream))
+                          _nbytes(workspace), _stream(stream))
     _check("atma_gdn_fwd", st)
     return o, final_state
 
@@ -177,18 +202,21 @@ def atma_gdn_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, max_seqlen, init_state
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be an int32 vector of nseq + 1 offsets")
     nseq = cu_seqlens.numel() - 1
-    _f32(alpha, "alpha"), _f32(beta, "beta"), _f32(init_state, "init_state")
+    _f32(alpha, "alpha"), _f32(beta, "beta")
+    _expect(init_state, "init_state", (nseq, H, Dv, Dk), torch.float32, optional=True)
     if o is None:
         o = torch.empty(total, H, Dv, dtype=q.dtype, device=q.device)
     if final_state is None and want_final:
         final_state = torch.empty(nseq, H, Dv, Dk, dtype=torch.float32, device=q.device)
+    _expect(o, "o", (total, H, Dv), q.dtype)
+    _expect(final_state, "final_state", (nseq, H, Dv, Dk), torch.float32, optional=True)
     need = atma_gdn_fwd_workspace_bytes(nseq, max_seqlen, H, Dk, Dv, CHUNK, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(q, k, v, alpha, beta, cu_seqlens, init_state, o, final_state, workspace)
     st = lib.atma_gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), nseq,
                                  int(max_seqlen), _ptr(init_state), _ptr(o), _ptr(final_state), total, H, Dk, Dv,
-                                 CHUNK, _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 CHUNK, _dtype_code(q), _ptr(workspace), _nbytes(workspace),
                                  _stream(stream))
     _check("atma_gdn_fwd_varlen", st)
     return o, final_state
@@ -199,11 +227,14 @@ def atma_gdn_decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
     fp32 (updated in place).  Returns o [B,H,Dv]."""
     B, H, Dk = q.shape
     Dv = v.shape[-1]
-    if state.shape != (B, H, Dv, Dk):
-        raise ValueError("state shape mismatch")
-    _f32(alpha, "alpha"), _f32(beta, "beta"), _f32(state, "state")
+    _expect(k, "k", (B, H, Dk), q.dtype)
+    _expect(v, "v", (B, H, Dv), q.dtype)
+    _expect(alpha, "alpha", (B, H), torch.float32)
+    _expect(beta, "beta", (B, H), torch.float32)
+    _expect(state, "state", (B, H, Dv, Dk), torch.float32)
     if o is None:
         o = torch.empty(B, H, Dv, dtype=q.dtype, device=q.device)
+    _expect(o, "o", (B, H, Dv), q.dtype)
     _dev(q, k, v, alpha, beta, state, o)
     st = lib.atma_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
                                   B, H, Dk, Dv, _dtype_code(q), _stream(stream))
@@ -222,8 +253,11 @@ def atma_gdn_bwd(q, k, v, alpha, beta, do, *, init_state=None, dS_final=None, wa
         raise ValueError("inconsistent shapes")
     if alpha.shape != (B, T, H) or beta.shape != (B, T, H):
         raise ValueError("alpha / beta must be [B, T, H]")
-    for t, n in ((alpha, "alpha"), (beta, "beta"), (init_state, "init_state"), (dS_final, "dS_final")):
-        _f32(t, n)
+    if k.dtype != q.dtype or v.dtype != q.dtype or do.dtype != q.dtype:
+        raise TypeError("q, k, v and do must share a dtype")
+    _f32(alpha, "alpha"), _f32(beta, "beta")
+    _expect(init_state, "init_state", (B, H, Dv, Dk), torch.float32, optional=True)
+    _expect(dS_final, "dS_final", (B, H, Dv, Dk), torch.float32, optional=True)
     dt = _dtype_code(q)
     f = dict(dtype=torch.float32, device=q.device)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
@@ -236,7 +270,7 @@ def atma_gdn_bwd(q, k, v, alpha, beta, do, *, init_state=None, dS_final=None, wa
     st = lib.atma_gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(init_state), _ptr(do),
                           _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
                           _ptr(out["dbeta"]), _ptr(out["dinit"]), B, T, H, Dk, Dv, 64, dt, _ptr(workspace),
-                          workspace.numel(), _stream(stream))
+                          _nbytes(workspace), _stream(stream))
     _check("atma_gdn_bwd", st)
     return out
 
@@ -245,13 +279,13 @@ def atma_gdn_bwd(q, k, v, alpha, beta, do, *, init_state=None, dS_final=None, wa
 # Polar attention# ------------------------------------------------------------------------------------
 # Polar attention
 # ------------------------------------------------------------------------------------
-def polar_params_struct(params: dict) -> PolarParams:
+def polar_params_struct(params: dict, Hq: int, D: int) -> PolarParams:
     """Pack a dict of per-head fp32 device tensors (temp_raw, null_slope_raw, null_bias,
     mag_beta [Hq]; v_null [Hq, D]; eps float) into the C struct."""
-    for name in ("temp_raw", "null_slope_raw", "null_bias", "mag_beta", "v_null"):
-        t = params[name]
-        _dev(t)
-        _f32(t, name)
+    names = ("temp_raw", "null_slope_raw", "null_bias", "mag_beta", "v_null")
+    for name in names:
+        _expect(params[name], name, (Hq, D) if name == "v_null" else (Hq,), torch.float32)
+    _dev(*(params[name] for name in names))
     return PolarParams(params["temp_raw"].data_ptr(), params["null_slope_raw"].data_ptr(),
                        params["null_bias"].data_ptr(), params["mag_beta"].data_ptr(),
                        params["v_null"].data_ptr(), float(params.get("eps", 1e-12)))
@@ -262,16 +296,19 @@ def atma_polar_attn_fwd(q, k, v, params, *, o=None, mu_out=None, meff_out=None, 
     (mu / meff are [B,Hq,T] fp32 when requested or passed in, else None)."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
-        raise ValueError("inconsistent shapes")
+    _expect(k, "k", (B, T, Hkv, D), q.dtype)
+    _expect(v, "v", (B, T, Hkv, D), q.dtype)
     if o is None:
         o = torch.empty_like(q)
     if want_mu and mu_out is None:
         mu_out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
     if want_mu and meff_out is None:
         meff_out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _expect(o, "o", (B, T, Hq, D), q.dtype)
+    _expect(mu_out, "mu_out", (B, Hq, T), torch.float32, optional=True)
+    _expect(meff_out, "meff_out", (B, Hq, T), torch.float32, optional=True)
+    p = polar_params_struct(params, Hq, D)
     _dev(q, k, v, o, mu_out, meff_out)
-    p = polar_params_struct(params)
     st = lib.atma_polar_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(o), _ptr(mu_out),
                                  _ptr(meff_out), B, T, Hq, Hkv, D, _dtype_code(q), None, 0, _stream(stream))
     _check("atma_polar_attn_fwd", st)
@@ -284,14 +321,14 @@ def atma_polar_attn_fwd_train(q, k, v, params, *, stream=None):
     ``atma_polar_attn_bwd`` reads."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
-        raise ValueError("inconsistent shapes")
+    _expect(k, "k", (B, T, Hkv, D), q.dtype)
+    _expect(v, "v", (B, T, Hkv, D), q.dtype)
     o = torch.empty_like(q)
     mu = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
     stats = torch.empty(B, Hq, T, 4, dtype=torch.float32, device=q.device)
     dirn = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    p = polar_params_struct(params, Hq, D)
     _dev(q, k, v)
-    p = polar_params_struct(params)
     st = lib.atma_polar_attn_fwd_train(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(o), _ptr(mu), _ptr(stats),
                                        _ptr(dirn), B, T, Hq, Hkv, D, _dtype_code(q), _stream(stream))
     _check("atma_polar_attn_fwd_train", st)
@@ -305,26 +342,33 @@ def atma_polar_attn_bwd(q, k, v, params, mu, stats, dirn, do, *, out=None, works
     that dict's tensors."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    if k.shape != (B, T, Hkv, D) or v.shape != k.shape or do.shape != q.shape:
-        raise ValueError("inconsistent shapes")
-    if mu.shape != (B, Hq, T) or stats.shape != (B, Hq, T, 4) or dirn.shape != (B, T, Hq, D):
-        raise ValueError("mu / stats / dir do not match the training forward's shapes")
+    _expect(k, "k", (B, T, Hkv, D), q.dtype)
+    _expect(v, "v", (B, T, Hkv, D), q.dtype)
+    _expect(do, "do", (B, T, Hq, D), q.dtype)
+    _expect(mu, "mu", (B, Hq, T), torch.float32)
+    _expect(stats, "stats", (B, Hq, T, 4), torch.float32)
+    _expect(dirn, "dir", (B, T, Hq, D), torch.float32)
     if out is None:
         f = dict(dtype=torch.float32, device=q.device)
         out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
                "d_temp_raw": torch.empty(Hq, **f), "d_null_slope_raw": torch.empty(Hq, **f),
                "d_null_bias": torch.empty(Hq, **f), "d_mag_beta": torch.empty(Hq, **f),
                "d_v_null": torch.empty(Hq, D, **f)}
+    f32 = torch.float32
+    for n, shape, dt in (("dq", (B, T, Hq, D), q.dtype), ("dk", (B, T, Hkv, D), q.dtype),
+                         ("dv", (B, T, Hkv, D), q.dtype), ("d_temp_raw", (Hq,), f32), ("d_null_slope_raw", (Hq,), f32),
+                         ("d_null_bias", (Hq,), f32), ("d_mag_beta", (Hq,), f32), ("d_v_null", (Hq, D), f32)):
+        _expect(out.get(n), "out[" + n + "]", shape, dt)
     if workspace is None:
         workspace = torch.empty(lib.atma_polar_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8,
                                 device=q.device)
+    p = polar_params_struct(params, Hq, D)
     _dev(q, k, v, mu, stats, dirn, do, workspace, *out.values())
-    p = polar_params_struct(params)
     g = PolarParamGrads(out["d_temp_raw"].data_ptr(), out["d_null_slope_raw"].data_ptr(),
                         out["d_null_bias"].data_ptr(), out["d_mag_beta"].data_ptr(), out["d_v_null"].data_ptr())
     st = lib.atma_polar_attn_bwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(mu), _ptr(stats), _ptr(dirn),
                                  _ptr(do), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), ctypes.byref(g), B, T,
-                                 Hq, Hkv, D, _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(stream))
+                                 Hq, Hkv, D, _dtype_code(q), _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check("atma_polar_attn_bwd", st)
     return out
 
@@ -334,19 +378,20 @@ def atma_polar_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, params, *, o=Non
     [nseq+1] on the device.  Returns (o [total,Hq,D], mu [Hq,total] or None, meff [Hq,total] or None)."""
     total, Hq, D = q.shape
     Hkv = k.shape[1]
-    if k.shape != (total, Hkv, D) or v.shape != k.shape:
-        raise ValueError("inconsistent packed shapes")
+    _expect(k, "k", (total, Hkv, D), q.dtype)
+    _expect(v, "v", (total, Hkv, D), q.dtype)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be an int32 vector of nseq + 1 offsets")
     nseq = cu_seqlens.numel() - 1
     if o is None:
         o = torch.empty_like(q)
+    _expect(o, "o", (total, Hq, D), q.dtype)
     mu = meff = None
     if want_mu:
         mu = torch.empty(Hq, total, dtype=torch.float32, device=q.device)
         meff = torch.empty(Hq, total, dtype=torch.float32, device=q.device)
+    p = polar_params_struct(params, Hq, D)
     _dev(q, k, v, cu_seqlens, o, mu, meff)
-    p = polar_params_struct(params)
     st = lib.atma_polar_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, int(max_seqlen),
                                         ctypes.byref(p), _ptr(o), _ptr(mu), _ptr(meff), total, Hq, Hkv, D,
                                         _dtype_code(q), _stream(stream))
@@ -364,20 +409,22 @@ def atma_polar_attn_decode(q, k_cache, v_cache, cache_len, params, *, o=None, mu
     (the new token already written at slot cache_len-1).  Returns (o [B,Hq,D], mu [B,Hq] or None)."""
     B, Hq, D = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
-    if k_cache.shape != (B, Lmax, Hkv, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("inconsistent cache shapes")
+    _expect(k_cache, "k_cache", (B, Lmax, Hkv, D), q.dtype)
+    _expect(v_cache, "v_cache", (B, Lmax, Hkv, D), q.dtype)
     if o is None:
         o = torch.empty_like(q)
     if want_mu and mu_out is None:
         mu_out = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    _expect(o, "o", (B, Hq, D), q.dtype)
+    _expect(mu_out, "mu_out", (B, Hq), torch.float32, optional=True)
     need = atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p = polar_params_struct(params, Hq, D)
     _dev(q, k_cache, v_cache, o, mu_out, workspace)
-    p = polar_params_struct(params)
     st = lib.atma_polar_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len), Lmax, ctypes.byref(p),
                                     _ptr(o), _ptr(mu_out), B, Hq, Hkv, D, _dtype_code(q), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream))
+                                    _nbytes(workspace), _stream(stream))
     _check("atma_polar_attn_decode", st)
     return o, mu_out
 
@@ -389,23 +436,24 @@ def atma_polar_attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len
     Returns (o [B,Hq,D], mu [B,Hq] or None)."""
     B, Hq, D = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
-    if k_cache.shape != (B, Lmax, Hkv, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("inconsistent cache shapes")
-    if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,):
-        raise ValueError("cache_lens must be an int32 tensor of shape [B]")
+    _expect(k_cache, "k_cache", (B, Lmax, Hkv, D), q.dtype)
+    _expect(v_cache, "v_cache", (B, Lmax, Hkv, D), q.dtype)
+    _expect(cache_lens, "cache_lens", (B,), torch.int32)
     if o is None:
         o = torch.empty_like(q)
     if want_mu and mu_out is None:
         mu_out = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    _expect(o, "o", (B, Hq, D), q.dtype)
+    _expect(mu_out, "mu_out", (B, Hq), torch.float32, optional=True)
     need = atma_polar_attn_decode_workspace_bytes(B, Hq, max_cache_len, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p = polar_params_struct(params, Hq, D)
     _dev(q, k_cache, v_cache, cache_lens, o, mu_out, workspace)
-    p = polar_params_struct(params)
     st = lib.atma_polar_attn_decode_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
                                            int(max_cache_len), Lmax, ctypes.byref(p), _ptr(o), _ptr(mu_out), B, Hq,
                                            Hkv, D, _dtype_code(q), _ptr(workspace),
-                                           workspace.numel() * workspace.element_size(), _stream(stream))
+                                           _nbytes(workspace), _stream(stream))
     _check("atma_polar_attn_decode_varlen", st)
     return o, mu_out
 
@@ -415,6 +463,7 @@ def atma_rope(x, theta=10000.0, pos0=0, *, out=None, stream=None):
     B, T, H, D = x.shape
     if out is None:
         out = torch.empty_like(x)
+    _expect(out, "out", (B, T, H, D), x.dtype)
     _dev(x, out)
     st = lib.atma_rope(_ptr(x), _ptr(out), B, T, H, D, int(pos0), float(theta), _dtype_code(x), _stream(stream))
     _check("atma_rope", st)
@@ -425,15 +474,16 @@ def atma_softmax_attn_fwd(q, k, v, rope_theta=0.0, *, o=None, workspace=None, st
     """NoPE (rope_theta=0) or RoPE causal softmax attention.  q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
-        raise ValueError("inconsistent shapes")
+    _expect(k, "k", (B, T, Hkv, D), q.dtype)
+    _expect(v, "v", (B, T, Hkv, D), q.dtype)
     if o is None:
         o = torch.empty_like(q)
+    _expect(o, "o", (B, T, Hq, D), q.dtype)
     need = int(lib.atma_softmax_attn_workspace_bytes(B, T, Hq, Hkv, D, float(rope_theta)))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _dev(q, k, v, o, workspace)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wsb = 0 if workspace is None else _nbytes(workspace)
     st = lib.atma_softmax_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, Hq, Hkv, D, float(rope_theta),
                                    _dtype_code(q), _ptr(workspace), wsb, _stream(stream))
     _check("atma_softmax_attn_fwd", st)
@@ -444,17 +494,18 @@ def atma_softmax_attn_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0, *, 
     """Decode row of the NoPE / RoPE core; for RoPE the cache holds rotated keys (atma_rope)."""
     B, Hq, D = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
-    if k_cache.shape != (B, Lmax, Hkv, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("inconsistent cache shapes")
+    _expect(k_cache, "k_cache", (B, Lmax, Hkv, D), q.dtype)
+    _expect(v_cache, "v_cache", (B, Lmax, Hkv, D), q.dtype)
     if o is None:
         o = torch.empty_like(q)
+    _expect(o, "o", (B, Hq, D), q.dtype)
     need = atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(q, k_cache, v_cache, o, workspace)
     st = lib.atma_softmax_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len), Lmax, float(rope_theta),
                                       _ptr(o), B, Hq, Hkv, D, _dtype_code(q), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), _stream(stream))
+                                      _nbytes(workspace), _stream(stream))
     _check("atma_softmax_attn_decode", st)
     return o
 
@@ -464,11 +515,11 @@ def atma_canon(x, w, state=None, *, residual=False, heads=0, eps=1e-6, update_st
     place with the last K-1 inputs when ``update_state``).  Returns y [B,T,C]."""
     B, T, C = x.shape
     K = w.shape[0]
-    if w.shape != (K, C) or (state is not None and state.shape != (B, K - 1, C)):
-        raise ValueError("inconsistent shapes")
-    _f32(w, "w")
+    _expect(w, "w", (K, C), torch.float32)
+    _expect(state, "state", (B, K - 1, C), x.dtype, optional=True)
     if y is None:
         y = torch.empty_like(x)
+    _expect(y, "y", (B, T, C), x.dtype)
     _dev(x, w, state, y)
     st = lib.atma_canon(_ptr(x), _ptr(w), _ptr(state), _ptr(state) if update_state else None, _ptr(y), B, T, C, K,
                         int(bool(residual)), int(heads), float(eps), _dtype_code(x), _stream(stream))

@@ -54,10 +54,16 @@ const char* atma_status_string(int status) {
 
 int atma_version(void) { return 100; }
 
-size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt) {
+size_t atma_gdn_fwd_workspace_bytes_dtype(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt) {
     if (!pos(B) || !pos(T) || !pos(H) || !head_width_ok(Dk) || !head_width_ok(Dv) || chunk != 64) return 0;
     if (dt != ATMA_BF16 && dt != ATMA_F32) return 0;
     return atma::gdn_fwd_workspace_bytes(B, T, H, Dk, Dv, dt == ATMA_BF16);
+}
+
+size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk) {
+    const size_t a = atma_gdn_fwd_workspace_bytes_dtype(B, T, H, Dk, Dv, chunk, ATMA_BF16);
+    const size_t b = atma_gdn_fwd_workspace_bytes_dtype(B, T, H, Dk, Dv, chunk, ATMA_F32);
+    return a > b ? a : b;
 }
 
 int atma_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,

@@ -28,6 +28,8 @@
  *    numbers, never out-of-bounds accesses.
  *  - Numerics: bf16 operands with fp32 accumulation and fp32 statistics; the memory
  *    state is fp32 in HBM and in registers.  Outputs are written in the input dtype.
+ *    Exception: the bf16 memory prefill stages its chunk operands in fp16 (11-bit mantissa,
+ *    range below 2^15; see atma_gdn_fwd).
  *    The memory backward computes in fp32 throughout; the Polar backward contracts on
  *    bf16 MFMA like the forward.  Parameter and gate gradients are fp32.
  */
@@ -81,14 +83,25 @@ typedef struct {
  *   o           [B, T, H, Dv]  dtype `dt`  (output)
  *   final_state [B, H, Dv, Dk] fp32 (output), or NULL; may alias init_state
  *   Dk, Dv in {64, 128}; chunk == 64; dt == ATMA_BF16 or ATMA_F32.
- *   workspace   device buffer of at least atma_gdn_fwd_workspace_bytes(...) bytes,
- *               contents ignored on entry and undefined on exit.
+ *   workspace   device buffer of at least atma_gdn_fwd_workspace_bytes(...) bytes (or the
+ *               smaller atma_gdn_fwd_workspace_bytes_dtype(..., dt)), contents ignored on entry
+ *               and undefined on exit.
+ * Range (bf16 inputs): the bf16 path stages its chunk operands (the UT-transformed keys and
+ * values, the entering state and the chunk's state correction) as fp16 MFMA operands, which hold
+ * magnitudes below 2^15 = 32768.  Values |v| and state entries must stay below that (inputs of
+ * unit-norm keys and queries with |v| ~ 1 use about 2^-15 of the range); beyond it the fp16
+ * staging overflows and o and final_state hold inf or NaN.  Not checked (the values live on the
+ * device).  The fp32 path has no such limit.
  * ------------------------------------------------------------------------------- */
 int atma_gdn_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                  const float* init_state, void* o, float* final_state, int B, int T, int H, int Dk,
                  int Dv, int chunk, atma_dtype dt, void* workspace, size_t ws_bytes, void* stream);
 
-size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt);
+/* Workspace bytes atma_gdn_fwd needs for either input dtype (the larger of the two). */
+size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk);
+
+/* Workspace bytes atma_gdn_fwd needs for inputs of dtype `dt` (0 for unsupported arguments). */
+size_t atma_gdn_fwd_workspace_bytes_dtype(int B, int T, int H, int Dk, int Dv, int chunk, atma_dtype dt);
 
 /* ---------------------------------------------------------------------------------
  * Gated-delta memory, chunked prefill of a packed batch: nseq sequences of different
@@ -101,10 +114,11 @@ size_t atma_gdn_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chu
  *                <= total_T
  *   init_state   [nseq, H, Dv, Dk] fp32 or NULL (zeros);  final_state [nseq, H, Dv, Dk] or NULL
  *   chunk == 64, dt == ATMA_BF16, Dk and Dv in {64, 128}.
- *   workspace at least atma_gdn_fwd_workspace_bytes(nseq, max_seqlen, H, Dk, Dv, chunk,
- *   ATMA_BF16) bytes.  The offsets are read on the device: a sequence whose bounds are not
- *   inside [0, total_T], decrease, or exceed max_seqlen is skipped (its rows of o and its final
- *   state are left unwritten); no access leaves the buffers.
+ *   workspace at least atma_gdn_fwd_workspace_bytes_dtype(nseq, max_seqlen, H, Dk, Dv, chunk,
+ *   ATMA_BF16) bytes.  The fp16 staging range of atma_gdn_fwd applies.  The offsets are read on
+ *   the device: a sequence whose bounds are not inside [0, total_T], decrease, or exceed
+ *   max_seqlen is skipped (its rows of o and its final state are left unwritten); no access
+ *   leaves the buffers.
  * ------------------------------------------------------------------------------- */
 int atma_gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
                         const float* beta, const int* cu_seqlens, int nseq, int max_seqlen,

@@ -79,8 +79,8 @@ def _declare(lib):
     lib.oracle_polar_decode.argtypes = [i, i, i, i, l, l] + [_dp] * 3 + [_dp] * 5 + [d] + [_dp] * 4 + [i]
     lib.oracle_threads_used.argtypes = [i, l]
     lib.oracle_rope.argtypes = [i, i, i, i, l, d, i, _dp, _dp]
-    lib.oracle_softmax_attn.argtypes = [i, i, i, i, i, d, i, _dp, _dp, _dp, _dp, i]
-    lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, i, _dp, _dp, _dp, _dp]
+    lib.oracle_softmax_attn.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _dp, _dp, d, i]
+    lib.oracle_softmax_decode.argtypes = [i, i, i, i, l, l, d, _dp, _dp, _dp, _dp]
     lib.oracle_canon.argtypes = [i, i, i, i, i, i, d, _dp, _dp, _dp, _dp]
     lib.oracle_gdn_bwd.argtypes = [i, i, i, i, i] + [_dp] * 6 + [_dp, _dp] + [_dp] * 6 + [i]
     lib.oracle_polar_bwd.argtypes = [i, i, i, i, i] + [_dp] * 3 + [_dp] * 5 + [d, _dp] + [_dp] * 9 + [i]
@@ -218,28 +218,32 @@ def rope(x, theta=10000.0, pos0=0, bf16=False):
     return y
 
 
-def softmax_attn(q, k, v, rope_theta=0.0, rotated_bf16=False, threads=0):
-    """Causal softmax attention (NoPE; RoPE when rope_theta > 0, the rotated q and k rounded
-    to bf16 values when ``rotated_bf16``).  q [B,T,Hq,D], k/v [B,T,Hkv,D].  Returns o [B,T,Hq,D]."""
+def softmax_attn(q, k, v, rope_theta=0.0, tol_lambda=None, threads=0):
+    """Causal softmax attention (NoPE; RoPE with the exact rotation when rope_theta > 0).
+    q [B,T,Hq,D], k/v [B,T,Hkv,D].  Returns o [B,T,Hq,D]; with ``tol_lambda`` also, per output
+    element, the probabilistic tolerance (Hoeffding, ``tol_lambda`` standard deviations of the
+    first-order effect; see oracle.c) for rounding each element of the rotated q and k to the
+    nearest bf16 value."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     assert k.shape == (B, T, Hkv, D) and v.shape == (B, T, Hkv, D)
     o = np.zeros((B, T, Hq, D))
-    assert _load().oracle_softmax_attn(B, T, Hq, Hkv, D, float(rope_theta), int(rotated_bf16), _ptr(q), _ptr(k),
-                                       _ptr(v), _ptr(o), int(threads)) == 0
-    return o
+    tol = np.zeros((B, T, Hq, D)) if tol_lambda is not None else None
+    assert _load().oracle_softmax_attn(B, T, Hq, Hkv, D, float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       _ptr(tol), float(tol_lambda or 0.0), int(threads)) == 0
+    return (o, tol) if tol_lambda is not None else o
 
 
-def softmax_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0, rotated_keys_bf16=False):
-    """q [B,Hq,D], caches [B,Lmax,Hkv,D] with unrotated keys (their rotation rounded to bf16
-    values when ``rotated_keys_bf16``).  Returns o [B,Hq,D]."""
+def softmax_decode(q, k_cache, v_cache, cache_len, rope_theta=0.0):
+    """q [B,Hq,D], caches [B,Lmax,Hkv,D] used as given; for RoPE (rope_theta > 0) the cache holds
+    keys already rotated to their slot positions and only the query is rotated.  Returns o [B,Hq,D]."""
     q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
     B, Hq, D = q.shape
     Lmax, Hkv = kc.shape[1], kc.shape[2]
     o = np.zeros((B, Hq, D))
-    assert _load().oracle_softmax_decode(B, Hq, Hkv, D, int(cache_len), Lmax, float(rope_theta),
-                                         int(rotated_keys_bf16), _ptr(q), _ptr(kc), _ptr(vc), _ptr(o)) == 0
+    assert _load().oracle_softmax_decode(B, Hq, Hkv, D, int(cache_len), Lmax, float(rope_theta), _ptr(q), _ptr(kc),
+                                         _ptr(vc), _ptr(o)) == 0
     return o
 
 

@@ -504,9 +504,8 @@ int oracle_polar_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax
  *     the angle pos * theta^(-2p/D), pos being the token's position (rotary position
  *     embedding of Su et al.; theta = 10000 in the usual setting). */
 
-/* Round to the nearest bf16 value (ties to even), through fp32 as a bf16 pipeline rounds:
- * RoPE's rotated q and k are bf16 operands in any bf16 attention (and bf16 in a RoPE KV cache),
- * so the control core is defined on the rounded rotation when `quant` is set. */
+/* Round to the nearest bf16 value (ties to even), through fp32 as a bf16 pipeline rounds.
+ * atma_rope writes bf16: its output is the exact rotation rounded once by this function. */
 static double round_bf16(double x) {
     float f = (float)x;
     uint32_t u;
@@ -565,12 +564,57 @@ static void softmax_row(const double* qi, const double* K, const double* V, size
         for (int e = 0; e < D; ++e) o[e] += w[j] / z * V[j * vs + e];
 }
 
+/* Rounding tolerance of one softmax row whose query and keys are rounded element by element to
+ * the nearest bf16 value (what a bf16 attention kernel does to the rotated q and k of the RoPE
+ * core), by probabilistic rounding error analysis (Higham and Mary, "A new approach to
+ * probabilistic rounding error analysis", SIAM J. Sci. Comput. 41 (2019)): the relative rounding
+ * errors eta of the elements are modelled as independent, mean zero, |eta| <= u = 2^-8 (the unit
+ * roundoff of bf16, which keeps 8 significant bits).
+ *   To first order, q_e -> q_e (1 + eta_e) and k_je -> k_je (1 + eta'_je) move logit j by
+ *       d_j = sum_e (eta_e + eta'_je) q_e k_je / sqrt(D),
+ *   the weights by w_j (d_j - sum_k w_k d_k), and output element x by
+ *       dO_x = sum_j w_j d_j c_jx,   c_jx = v_jx - o_x   (the sum_k w_k d_k part cancels),
+ *            = (1/sqrt(D)) [ sum_e eta_e A_ex + sum_{j,e} eta'_je B_jex ],
+ *   A_ex = q_e sum_j w_j k_je c_jx,   B_jex = q_e k_je w_j c_jx.
+ *   Hoeffding's inequality for a sum of independent terms a_i eta_i, |eta_i| <= u, gives
+ *       P(|dO_x| >= lambda u sqrt(sum a_i^2) / sqrt(D)) <= 2 exp(-lambda^2 / 2),
+ *   so tol_x = lambda u sqrt(sum_e A_ex^2 + sum_j w_j^2 c_jx^2 sum_e (q_e k_je)^2) / sqrt(D).
+ * qi, K (stride ks), V (stride vs) as softmax_row; w the row's weights from softmax_row
+ * (renormalised here); tol [D] receives the tolerance for the given lambda. */
+static void rounding_tolerance(const double* qi, const double* K, const double* V, size_t ks, size_t vs, long n,
+                               int D, const double* o, const double* w, double lambda, double* tol) {
+    const double u = 1.0 / 256.0;
+    double z = 0.0;
+    for (long j = 0; j < n; ++j) z += w[j];
+    double* M = (double*)calloc((size_t)D * D, sizeof(double));  /* M[x][e] = sum_j w_j k_je c_jx */
+    double* sb = (double*)calloc((size_t)D, sizeof(double));     /* sum_j w_j^2 c_jx^2 sum_e (q_e k_je)^2 */
+    for (long j = 0; j < n; ++j) {
+        const double wj = w[j] / z;
+        double a2 = 0.0;
+        for (int e = 0; e < D; ++e) a2 += (qi[e] * K[j * ks + e]) * (qi[e] * K[j * ks + e]);
+        for (int x = 0; x < D; ++x) {
+            const double c = V[j * vs + x] - o[x];
+            sb[x] += wj * wj * c * c * a2;
+            double* Mx = M + (size_t)x * D;
+            for (int e = 0; e < D; ++e) Mx[e] += wj * c * K[j * ks + e];
+        }
+    }
+    for (int x = 0; x < D; ++x) {
+        double sa = 0.0;
+        for (int e = 0; e < D; ++e) sa += (qi[e] * M[(size_t)x * D + e]) * (qi[e] * M[(size_t)x * D + e]);
+        tol[x] = lambda * u * sqrt((sa + sb[x]) / (double)D);
+    }
+    free(M);
+    free(sb);
+}
+
 typedef struct {
     int B, T, Hq, Hkv, D;
     const double *q, *k, *v;
     double theta;
-    int quant;
     double* o;
+    double* tol;    /* NULL, or the rounding tolerance of every output element (see above) */
+    double lambda;
 } softmax_ctx;
 
 /* task = b * Hq + h: every query row of one (batch, query head) */
@@ -584,56 +628,52 @@ static void softmax_task(long task, void* p) {
     for (size_t j = 0; j < T; ++j) {
         memcpy(K + j * D, c->k + ((b * T + j) * c->Hkv + hk) * D, sizeof(double) * D);
         if (c->theta > 0.0) rope_vec(K + j * D, D, (double)j, c->theta);
-        for (int e = 0; c->theta > 0.0 && c->quant && e < D; ++e) K[j * D + e] = round_bf16(K[j * D + e]);
     }
     const double* V = c->v + ((size_t)b * T * c->Hkv + hk) * D;
     for (size_t i = 0; i < T; ++i) {
         memcpy(qi, c->q + ((b * T + i) * c->Hq + h) * D, sizeof(double) * D);
         if (c->theta > 0.0) rope_vec(qi, D, (double)i, c->theta);
-        for (int e = 0; c->theta > 0.0 && c->quant && e < D; ++e) qi[e] = round_bf16(qi[e]);
-        softmax_row(qi, K, V, D, (size_t)c->Hkv * D, (long)i + 1, D, c->o + ((b * T + i) * c->Hq + h) * D, w);
+        double* oi = c->o + ((b * T + i) * c->Hq + h) * D;
+        softmax_row(qi, K, V, D, (size_t)c->Hkv * D, (long)i + 1, D, oi, w);
+        if (c->tol) rounding_tolerance(qi, K, V, D, (size_t)c->Hkv * D, (long)i + 1, D, oi, w, c->lambda,
+                                       c->tol + ((b * T + i) * c->Hq + h) * D);
     }
     free(K);
     free(w);
     free(qi);
 }
 
-/* Causal softmax attention, NoPE (theta <= 0) or RoPE (theta > 0), all rows; with quant the
- * rotated q and k are rounded to bf16 before the scores.
- *   q [B, T, Hq, D];  k, v [B, T, Hkv, D];  o [B, T, Hq, D]. */
-int oracle_softmax_attn(int B, int T, int Hq, int Hkv, int D, double theta, int quant, const double* q,
-                        const double* k, const double* v, double* o, int nthreads) {
+/* Causal softmax attention, NoPE (theta <= 0) or RoPE (theta > 0, exact rotation), all rows.
+ *   q [B, T, Hq, D];  k, v [B, T, Hkv, D];  o [B, T, Hq, D];
+ *   tol [B, T, Hq, D] or NULL: for every output element, the tolerance (rounding_tolerance, with
+ *   the given lambda) for rounding each element of the rotated q and k to the nearest bf16 value. */
+int oracle_softmax_attn(int B, int T, int Hq, int Hkv, int D, double theta, const double* q,
+                        const double* k, const double* v, double* o, double* tol, double lambda, int nthreads) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || Hq % Hkv || !q || !k || !v || !o) return -1;
-    softmax_ctx c = {B, T, Hq, Hkv, D, q, k, v, theta, quant, o};
+    softmax_ctx c = {B, T, Hq, Hkv, D, q, k, v, theta, o, tol, lambda};
     run_tasks(softmax_task, &c, (long)B * Hq, nthreads);
     return 0;
 }
 
 /* Decode row of the same cores: the query at position cache_len - 1 against cache slots
- * 0..cache_len-1, whose keys are given unrotated (position = slot); with quant the rotated
- * keys are rounded to bf16 (a RoPE KV cache holds them in bf16), the query is not.
+ * 0..cache_len-1, used as given.  For RoPE (theta > 0) the cache holds keys already rotated to
+ * their slot positions (a RoPE KV cache is filled with rotated keys), and only the query is
+ * rotated here.
  *   q [B, Hq, D];  k_cache, v_cache [B, Lmax, Hkv, D];  o [B, Hq, D]. */
-int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax, double theta, int quant,
+int oracle_softmax_decode(int B, int Hq, int Hkv, int D, long cache_len, long Lmax, double theta,
                           const double* q, const double* kc, const double* vc, double* o) {
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || Hq % Hkv || cache_len < 1 || cache_len > Lmax) return -1;
     if (!q || !kc || !vc || !o) return -1;
-    double* K = (double*)malloc(sizeof(double) * (size_t)cache_len * D);
     double* w = (double*)malloc(sizeof(double) * (size_t)cache_len);
     double* qi = (double*)malloc(sizeof(double) * D);
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < Hq; ++h) {
             const int hk = h / (Hq / Hkv);
-            for (long j = 0; j < cache_len; ++j) {
-                memcpy(K + j * D, kc + (((size_t)b * Lmax + j) * Hkv + hk) * D, sizeof(double) * D);
-                if (theta > 0.0) rope_vec(K + j * D, D, (double)j, theta);
-                for (int e = 0; theta > 0.0 && quant && e < D; ++e) K[j * D + e] = round_bf16(K[j * D + e]);
-            }
             memcpy(qi, q + ((size_t)b * Hq + h) * D, sizeof(double) * D);
             if (theta > 0.0) rope_vec(qi, D, (double)(cache_len - 1), theta);
-            softmax_row(qi, K, vc + ((size_t)b * Lmax * Hkv + hk) * D, D, (size_t)Hkv * D, cache_len, D,
-                        o + ((size_t)b * Hq + h) * D, w);
+            softmax_row(qi, kc + ((size_t)b * Lmax * Hkv + hk) * D, vc + ((size_t)b * Lmax * Hkv + hk) * D,
+                        (size_t)Hkv * D, (size_t)Hkv * D, cache_len, D, o + ((size_t)b * Hq + h) * D, w);
         }
-    free(K);
     free(w);
     free(qi);
     return 0;

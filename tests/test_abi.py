@@ -26,13 +26,18 @@ def test_status_strings_and_version():
 
 
 def test_workspace_queries():
-    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, g.ATMA_F32) > 0
+    assert g.lib.atma_gdn_fwd_workspace_bytes_dtype(1, 256, 1, 64, 64, 64, g.ATMA_F32) > 0
     # bf16 records are smaller than fp32 ones; a ragged tail still gets a full chunk record
-    a = g.lib.atma_gdn_fwd_workspace_bytes(2, 100, 3, 128, 128, 64, g.ATMA_BF16)
-    b = g.lib.atma_gdn_fwd_workspace_bytes(2, 128, 3, 128, 128, 64, g.ATMA_BF16)
+    a = g.lib.atma_gdn_fwd_workspace_bytes_dtype(2, 100, 3, 128, 128, 64, g.ATMA_BF16)
+    b = g.lib.atma_gdn_fwd_workspace_bytes_dtype(2, 128, 3, 128, 128, 64, g.ATMA_BF16)
     assert a == b > 0
-    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, g.ATMA_BF16) == 0  # unsupported width
-    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 64, 64, 32, g.ATMA_BF16) == 0  # unsupported chunk
+    assert g.lib.atma_gdn_fwd_workspace_bytes_dtype(1, 256, 1, 96, 64, 64, g.ATMA_BF16) == 0  # unsupported width
+    assert g.lib.atma_gdn_fwd_workspace_bytes_dtype(1, 256, 1, 64, 64, 32, g.ATMA_BF16) == 0  # unsupported chunk
+    # the six-argument query covers either dtype (the larger need)
+    for args in ((1, 256, 1, 64, 64, 64), (2, 100, 3, 128, 128, 64), (1, 70000, 8, 128, 64, 64)):
+        both = [g.lib.atma_gdn_fwd_workspace_bytes_dtype(*args, dt) for dt in (g.ATMA_BF16, g.ATMA_F32)]
+        assert g.lib.atma_gdn_fwd_workspace_bytes(*args) == max(both) > 0
+    assert g.lib.atma_gdn_fwd_workspace_bytes(1, 256, 1, 96, 64, 64) == 0
     assert g.lib.atma_polar_attn_workspace_bytes(1, 1024, 16, 64) == 0
     assert g.lib.atma_polar_attn_decode_workspace_bytes(1, 16, 262144, 64) > 0
     assert g.lib.atma_polar_attn_decode_workspace_bytes(1, 16, 0, 64) == 0
@@ -57,7 +62,7 @@ def test_gdn_fwd_validation():
     assert _gdn(B=70000, T=70000) == g.ATMA_ERR_SHAPE          # element count overflow
     assert _gdn(ws=NULL) == g.ATMA_ERR_WORKSPACE
     assert _gdn(wsb=1) == g.ATMA_ERR_WORKSPACE                  # too small
-    need = g.lib.atma_gdn_fwd_workspace_bytes(1, 8, 1, 64, 64, 64, g.ATMA_BF16)
+    need = g.lib.atma_gdn_fwd_workspace_bytes_dtype(1, 8, 1, 64, 64, 64, g.ATMA_BF16)
     assert _gdn(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
 
 
@@ -80,7 +85,7 @@ def test_gdn_fwd_varlen_validation():
     assert _gdnv(Dk=96) == g.ATMA_ERR_UNSUPPORTED
     assert _gdnv(chunk=32) == g.ATMA_ERR_UNSUPPORTED
     assert _gdnv(ws=NULL) == g.ATMA_ERR_WORKSPACE
-    need = g.lib.atma_gdn_fwd_workspace_bytes(2, 8, 1, 64, 64, 64, g.ATMA_BF16)
+    need = g.lib.atma_gdn_fwd_workspace_bytes_dtype(2, 8, 1, 64, 64, 64, g.ATMA_BF16)
     assert _gdnv(wsb=need - 1) == g.ATMA_ERR_WORKSPACE
 
 
@@ -272,3 +277,77 @@ def test_binding_rejects_host_tensors():
     with pytest.raises((ValueError, RuntimeError)):
         g.atma_gdn_fwd(q, q, q, a, a, workspace=torch.zeros(1, dtype=torch.uint8), o=q.clone(),
                        final_state=torch.zeros(1, 1, 64, 64))
+
+
+# ---- the Python binding rejects malformed buffers before reaching the C ABI -------------------
+# These run on CPU tensors: the shape and dtype checks come before the device check, so each
+# call below raises on the host, naming the offending buffer, and nothing is launched.
+import torch  # noqa: E402
+
+
+def _polar_params(Hq, D):
+    return {"temp_raw": torch.zeros(Hq), "null_slope_raw": torch.zeros(Hq), "null_bias": torch.zeros(Hq),
+            "mag_beta": torch.zeros(Hq), "v_null": torch.zeros(Hq, D), "eps": 1e-12}
+
+
+def _raises(fn, match):
+    with pytest.raises((ValueError, TypeError), match=match):
+        fn()
+
+
+def test_binding_checks_memory_buffers():
+    bf = torch.bfloat16
+    B, T, H, D = 2, 8, 2, 64
+    q = torch.zeros(B, T, H, D, dtype=bf)
+    a = torch.zeros(B, T, H)
+    _raises(lambda: g.atma_gdn_fwd(q, q, q, a, a, torch.zeros(B, H, D, D + 1)), "init_state")
+    _raises(lambda: g.atma_gdn_fwd(q, q, q, a, a, torch.zeros(B, H, D, D, dtype=torch.float64)), "init_state")
+    _raises(lambda: g.atma_gdn_fwd(q, q, q, a, a, o=torch.zeros(B, T, H, D)), "o has dtype")
+    _raises(lambda: g.atma_gdn_fwd(q, q, q, a, a, o=torch.zeros(B, T, H, D - 1, dtype=bf)), "o has shape")
+    _raises(lambda: g.atma_gdn_fwd(q, q, q, a, a, final_state=torch.zeros(B, H, D, D - 8)), "final_state")
+    st = torch.zeros(B, H, D, D)
+    qd, ad = torch.zeros(B, H, D, dtype=bf), torch.zeros(B, H)
+    _raises(lambda: g.atma_gdn_decode_step(qd, torch.zeros(B, H + 1, D, dtype=bf), qd, ad, ad, st), "k has shape")
+    _raises(lambda: g.atma_gdn_decode_step(qd, qd, torch.zeros(B, H, D), ad, ad, st), "v has dtype")
+    _raises(lambda: g.atma_gdn_decode_step(qd, qd, qd, torch.zeros(B, H + 1), ad, st), "alpha")
+    _raises(lambda: g.atma_gdn_decode_step(qd, qd, qd, ad, torch.zeros(B), st), "beta")
+    _raises(lambda: g.atma_gdn_decode_step(qd, qd, qd, ad, ad, st, o=torch.zeros(B, H, 2 * D, dtype=bf)), "o has")
+    _raises(lambda: g.atma_gdn_bwd(q, q, q, a, a, torch.zeros(B, T, H, D)), "share a dtype")
+    _raises(lambda: g.atma_gdn_bwd(q, q, q, a, a, q, init_state=torch.zeros(B, H, D, 1)), "init_state")
+    _raises(lambda: g.atma_gdn_bwd(q, q, q, a, a, q, dS_final=torch.zeros(1, H, D, D)), "dS_final")
+
+
+def test_binding_checks_polar_buffers():
+    bf = torch.bfloat16
+    B, T, Hq, Hkv, D = 2, 8, 4, 2, 64
+    q, kv = torch.zeros(B, T, Hq, D, dtype=bf), torch.zeros(B, T, Hkv, D, dtype=bf)
+    p = _polar_params(Hq, D)
+    _raises(lambda: g.atma_polar_attn_fwd(q, kv, kv, _polar_params(Hq - 1, D)), "temp_raw")
+    bad = dict(p, v_null=torch.zeros(Hq, D // 2))
+    _raises(lambda: g.atma_polar_attn_fwd(q, kv, kv, bad), "v_null")
+    _raises(lambda: g.atma_polar_attn_fwd(q, kv, kv, p, o=torch.zeros(B, T, Hq, D)), "o has dtype")
+    _raises(lambda: g.atma_polar_attn_fwd(q, kv, kv, p, mu_out=torch.zeros(B, T, Hq)), "mu_out")
+    _raises(lambda: g.atma_polar_attn_fwd(q, kv, kv, p, meff_out=torch.zeros(B, Hq, T, dtype=bf)), "meff_out")
+    _raises(lambda: g.atma_polar_attn_fwd(q, kv, torch.zeros(B, T, Hkv, D), p), "v has dtype")
+    mu, stats, dirn = torch.zeros(B, Hq, T), torch.zeros(B, Hq, T, 4), torch.zeros(B, T, Hq, D)
+    _raises(lambda: g.atma_polar_attn_bwd(q, kv, kv, p, mu, stats, dirn, torch.zeros(B, T, Hq, D)), "do has dtype")
+    _raises(lambda: g.atma_polar_attn_bwd(q, kv, kv, p, mu.double(), stats, dirn, q), "mu has dtype")
+    _raises(lambda: g.atma_polar_attn_bwd(q, kv, kv, p, mu, stats.to(bf), dirn, q), "stats has dtype")
+    _raises(lambda: g.atma_polar_attn_bwd(q, kv, kv, p, mu, stats, dirn.to(bf), q), "dir has dtype")
+    outs = {"dq": torch.zeros_like(q), "dk": torch.zeros_like(kv), "dv": torch.zeros_like(kv),
+            "d_temp_raw": torch.zeros(Hq), "d_null_slope_raw": torch.zeros(Hq), "d_null_bias": torch.zeros(Hq),
+            "d_mag_beta": torch.zeros(Hq), "d_v_null": torch.zeros(Hq, D + 1)}
+    _raises(lambda: g.atma_polar_attn_bwd(q, kv, kv, p, mu, stats, dirn, q, out=outs), "d_v_null")
+    L = 16
+    qd, kc = torch.zeros(B, Hq, D, dtype=bf), torch.zeros(B, L, Hkv, D, dtype=bf)
+    _raises(lambda: g.atma_polar_attn_decode(qd, kc, torch.zeros(B, L + 1, Hkv, D, dtype=bf), L, p), "v_cache")
+    _raises(lambda: g.atma_polar_attn_decode(qd, kc, kc, L, p, o=torch.zeros(B, Hq, D)), "o has dtype")
+    _raises(lambda: g.atma_polar_attn_decode(qd, kc, kc, L, p, mu_out=torch.zeros(B, Hq + 1)), "mu_out")
+    lens = torch.full((B,), L, dtype=torch.int32)
+    _raises(lambda: g.atma_polar_attn_decode_varlen(qd, kc, kc, lens.long(), L, p), "cache_lens")
+    _raises(lambda: g.atma_softmax_attn_fwd(q, kv, kv, o=torch.zeros(B, T, Hq, D - 8, dtype=bf)), "o has shape")
+    _raises(lambda: g.atma_rope(q, out=torch.zeros(B, T, Hq, D)), "out has dtype")
+    x, w = torch.zeros(B, T, 128, dtype=bf), torch.zeros(4, 128)
+    _raises(lambda: g.atma_canon(x, w.double()), "w has dtype")
+    _raises(lambda: g.atma_canon(x, w, torch.zeros(B, 4, 128, dtype=bf)), "state has shape")
+    _raises(lambda: g.atma_canon(x, w, y=torch.zeros(B, T, 128)), "y has dtype")

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from parity import note, rel_err_fro, rel_err_max, to_np
+from parity import GDN_GRADS, gdn_grad_errors, gdn_grad_failures, note, rel_err_fro, rel_err_max, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -43,16 +43,10 @@ def _check(atma, B, T, H, Dk, Dv, dtype, init, final, seed):
                           init_state=cu(S0), dS_final=cu(dSf), want_dinit=True)
     torch.cuda.synchronize()
     ref = oracle.gdn_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], do, init_state=S0, dS_final=dSf)
-    tol_io = 1e-4 if dtype == "f32" else 4e-3
-    msg, bad = [], {}
-    for n, gn in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dalpha", "dalpha"), ("dbeta", "dbeta"),
-                  ("dinit", "dinit")):
-        em, ef = rel_err_max(to_np(g[gn]), ref[n]), rel_err_fro(to_np(g[gn]), ref[n])
-        msg.append(f"{n}={em:.1e}/{ef:.1e}")
-        tol = tol_io if n in ("dq", "dk", "dv") else 1e-4
-        if not (em <= tol and ef <= tol):
-            bad[n] = (em, ef)
-    note(f"  gdn bwd B{B} T{T} H{H} Dk{Dk} Dv{Dv} {dtype}: " + " ".join(msg))
+    errs = gdn_grad_errors({n: to_np(g[n]) for n in GDN_GRADS}, ref)
+    note(f"  gdn bwd B{B} T{T} H{H} Dk{Dk} Dv{Dv} {dtype}: " +
+         " ".join(f"{n}={e[0]:.1e}/{e[1]:.1e}" for n, e in errs.items()))
+    bad = gdn_grad_failures(errs, dtype)
     assert not bad, bad
 
 

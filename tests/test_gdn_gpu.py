@@ -29,6 +29,7 @@ def _run_and_check(atma, inp, dtype, init=None, tag=""):
     init_d = None if init is None else init.cuda()
     o, S = atma.atma_gdn_fwd(q, k, v, a, b, init_d)
     torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()  # every element written
     ro, rS = oracle.gdn_sequential(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], init_state=init)
     eo, eS = out_err(to_np(o), ro, dtype), rel_err(to_np(S), rS)
     note(f"  gdn {tag} dtype={dtype} err_o={eo:.3e} err_S={eS:.3e}")

@@ -5,8 +5,13 @@ Section 3.1), checked against what mathematics and a library routine fix:
 * RoPE rotates each adjacent pair: a D=2 unit vector at position m becomes (cos m, sin m);
   pair norms are preserved; pair p turns by theta^(-2p/D) per position (the textbook
   frequencies); scores depend only on the position difference (shift invariance);
-* the decode row equals the last row of the causal forward, with and without RoPE;
-* identical keys give the plain mean of the values.
+* the decode row equals the last row of the causal forward, with and without RoPE (the decode
+  cache holding keys already rotated to their slots);
+* identical keys give the plain mean of the values;
+* the probabilistic tolerance for rounding the rotated q and k to bf16 (7 standard deviations of
+  the first-order effect) covers the actual rounding and random perturbations of the same size,
+  is zero where no rounding can matter, and is not vacuous: the actual rounding reaches a fixed
+  share of it, and it scales with the rounding unit.
 """
 import math
 
@@ -95,7 +100,8 @@ def test_softmax_decode_is_last_row(theta):
     q, k, v = rng.standard_normal((B, T, Hq, D)), rng.standard_normal((B, T, Hkv, D)), rng.standard_normal(
         (B, T, Hkv, D))
     full = oracle.softmax_attn(q, k, v, rope_theta=theta)
-    kc = np.concatenate([k, rng.standard_normal((B, 7, Hkv, D))], axis=1)  # slots past cache_len unused
+    kr = oracle.rope(k, theta) if theta > 0 else k  # a RoPE cache holds rotated keys
+    kc = np.concatenate([kr, rng.standard_normal((B, 7, Hkv, D))], axis=1)  # slots past cache_len unused
     vc = np.concatenate([v, rng.standard_normal((B, 7, Hkv, D))], axis=1)
     dec = oracle.softmax_decode(q[:, T - 1], kc, vc, T, rope_theta=theta)
     assert np.abs(dec - full[:, T - 1]).max() < 1e-13
@@ -112,13 +118,70 @@ def test_identical_keys_give_mean_of_values():
 
 
 def test_rotated_bf16_rounding_matches_torch():
-    """The bf16 rounding of the rotation equals torch's fp64 -> bf16 conversion, and the core
-    with rounded rotations is the NoPE core on those rounded values."""
+    """oracle.rope(..., bf16=True) -- the definition of atma_rope's bf16 output -- is the exact
+    rotation rounded once as torch rounds fp64 -> bf16, over 262144 values at large positions and
+    magnitudes from 2^-20 to 2^20."""
     rng = np.random.default_rng(6)
-    x = rng.standard_normal((2, 40, 3, 16)) * 3.0
-    ref = torch.from_numpy(oracle.rope(x, 10000.0, pos0=77)).to(torch.bfloat16).double().numpy()
-    assert np.array_equal(oracle.rope(x, 10000.0, pos0=77, bf16=True), ref)
-    q, k, v = x[:, :, :2], x[:, :, 2:], rng.standard_normal((2, 40, 1, 16))
-    o = oracle.softmax_attn(q, k, v, rope_theta=10000.0, rotated_bf16=True)
-    o2 = oracle.softmax_attn(oracle.rope(q, bf16=True), oracle.rope(k, bf16=True), v)
-    assert np.abs(o - o2).max() < 1e-13
+    x = rng.standard_normal((2, 512, 4, 64)) * np.exp2(rng.integers(-20, 21, size=(2, 512, 4, 64)))
+    for pos0 in (0, 77, 262000):
+        y = oracle.rope(x, 10000.0, pos0=pos0)
+        ref = torch.from_numpy(y).to(torch.float32).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(oracle.rope(x, 10000.0, pos0=pos0, bf16=True), ref)
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(torch.bfloat16).double().numpy()
+
+
+LAMBDA = 7.0
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,qscale,theta", [(1, 400, 2, 1, 64, 1.0, 10000.0), (2, 90, 4, 2, 16, 4.0, 500.0),
+                                                        (1, 300, 1, 1, 128, 2.0, 10000.0)])
+def test_rope_rounding_tolerance_covers_rounding(B, T, Hq, Hkv, D, qscale, theta):
+    """Rounding every rotated q and k element to bf16 (what a bf16 attention kernel consumes) moves
+    each output element by less than the tolerance; so do random perturbations of the rotated
+    operands within the same relative size 2^-8 (bf16's unit roundoff).  The actual rounding reaches at least a fifth of
+    the tolerance somewhere (it is not vacuous)."""
+    rng = np.random.default_rng(T + D)
+    q = rng.standard_normal((B, T, Hq, D)) * qscale
+    k, v = rng.standard_normal((B, T, Hkv, D)), rng.standard_normal((B, T, Hkv, D))
+    o, tol = oracle.softmax_attn(q, k, v, rope_theta=theta, tol_lambda=LAMBDA)
+    assert np.all(tol >= 0)
+    rq, rk = oracle.rope(q, theta), oracle.rope(k, theta)
+    moved = np.abs(oracle.softmax_attn(_bf16(rq), _bf16(rk), v) - o)
+    assert np.all(moved <= tol + 1e-15)
+    assert np.max(moved[:, 1:] / tol[:, 1:]) > 0.2
+    for _ in range(3):
+        pq = rq * (1 + rng.uniform(-1, 1, rq.shape) / 256)
+        pk = rk * (1 + rng.uniform(-1, 1, rk.shape) / 256)
+        assert np.all(np.abs(oracle.softmax_attn(pq, pk, v) - o) <= tol + 1e-15)
+
+
+def test_rope_rounding_tolerance_zero_and_linear():
+    """A single visible key leaves nothing to move (the first row of a causal sequence equals its
+    value row whatever the logits), so the tolerance is zero there; it is linear in lambda; and
+    for a two-key row it is lambda u sqrt(sum_j w_j^2 (v_j - o)^2 sum_e (q_e k_je)^2 +
+    sum_e (q_e sum_j w_j k_je (v_j - o))^2) / sqrt(D), checked against perturbing each rotated
+    element alone by u and summing the squared first-order responses (finite differences)."""
+    rng = np.random.default_rng(11)
+    D, u = 8, 2.0 ** -8
+    q, k, v = (rng.standard_normal((1, 2, 1, D)) for _ in range(3))
+    o, tol = oracle.softmax_attn(q, k, v, tol_lambda=LAMBDA)
+    _, tol2 = oracle.softmax_attn(q, k, v, tol_lambda=2 * LAMBDA)
+    assert np.all(tol[0, 0] == 0.0)
+    assert np.allclose(tol2, 2 * tol, rtol=1e-12)
+    # finite-difference responses of row 1 to each element of q_1, k_0, k_1 scaled by (1 + u)
+    resp = []
+    for which, j in (("q", 1), ("k", 0), ("k", 1)):
+        for e in range(D):
+            qq, kk = q.copy(), k.copy()
+            if which == "q":
+                qq[0, j, 0, e] *= 1 + 1e-6
+            else:
+                kk[0, j, 0, e] *= 1 + 1e-6
+            resp.append((oracle.softmax_attn(qq, kk, v)[0, 1, 0] - o[0, 1, 0]) / 1e-6 * u)
+    resp = np.array(resp)
+    # q_1 is shared by both logits: its responses are the A terms; the key terms are the B terms
+    expect = LAMBDA * np.sqrt(np.sum(resp ** 2, axis=0))
+    assert np.allclose(tol[0, 1, 0], expect, rtol=1e-4)

@@ -43,8 +43,13 @@ MUTANTS = {
     "rope_reflect": ("x[2 * p + 1] = a * s + b * c;", "x[2 * p + 1] = -a * s + b * c;"),
     "rope_half_frequency": ("pos * pow(theta, -2.0 * p / D);", "pos * pow(theta, -1.0 * p / D);"),
     "softmax_no_scale": ("w[j] = d * scale;", "w[j] = d;"),
-    "softmax_sees_next_key": ("(long)i + 1, D, c->o + ((b * T + i) * c->Hq + h) * D, w);",
-                              "(long)(i + 1 < T ? i + 2 : i + 1), D, c->o + ((b * T + i) * c->Hq + h) * D, w);"),
+    "softmax_sees_next_key": ("softmax_row(qi, K, V, D, (size_t)c->Hkv * D, (long)i + 1, D, oi, w);",
+                              "softmax_row(qi, K, V, D, (size_t)c->Hkv * D, (long)(i + 1 < T ? i + 2 : i + 1), D, oi, w);"),
+    "tolerance_drops_query_term": ("tol[x] = lambda * u * sqrt((sa + sb[x]) / (double)D);",
+                                   "tol[x] = lambda * u * sqrt(sb[x] / (double)D);"),
+    "tolerance_no_sqrt_d": ("tol[x] = lambda * u * sqrt((sa + sb[x]) / (double)D);",
+                            "tol[x] = lambda * u * sqrt(sa + sb[x]);"),
+    "tolerance_unnormalised_weights": ("const double wj = w[j] / z;", "const double wj = w[j];"),
     "canon_anticausal": ("const long s = t - j;", "const long s = t + j < T ? t + j : t - j;"),
     "canon_state_offset": ("xv = state[((size_t)b * (K - 1) + (K - 1 + s)) * C + c];",
                            "xv = state[((size_t)b * (K - 1) + (K - 2 + s >= 0 ? K - 2 + s : 0)) * C + c];"),

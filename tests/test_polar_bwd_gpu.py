@@ -26,21 +26,10 @@ import torch
 
 import oracle
 import workloads
-from parity import note, rel_err_fro, rel_err_max, to_np
+from parity import (POLAR_BWD_TOL_FRO as TOL_FRO, POLAR_BWD_TOL_MAX as TOL_MAX, POLAR_GRADS, note,
+                    polar_grad_errors, polar_grad_failures, rel_err_fro, rel_err_max, to_np)
 
 pytestmark = pytest.mark.gpu
-
-TOL_MAX, TOL_FRO = 2e-2, 1e-2
-SCALAR_PARAMS = ("d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta")
-
-
-def sum_err(got, ref, mag):
-    """max over heads of |gpu - oracle| / (sum of the magnitudes of its terms): a parameter
-    gradient is a sum over all B T rows whose terms cancel (by 15-20 times on these inputs), and
-    its rounding error scales with the magnitude of the terms, not with the sum.  For the
-    temperature each row's term is itself a sum over keys of bf16-rounded logit gradients times
-    q.k, taken term by term."""
-    return float(np.max(np.abs(to_np(got) - ref) / np.maximum(mag, 1e-30)))
 
 
 @pytest.fixture(scope="module")
@@ -76,14 +65,10 @@ def _check(atma, B, T, Hq, Hkv, D, seed, eps=None):
     if eps is not None:
         cp["eps"] = eps
     ref = oracle.polar_bwd(inp["q"], inp["k"], inp["v"], cp, do)
-    names = ("dq", "dk", "dv", "d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta", "d_v_null")
-    emax = {n: rel_err_max(to_np(g[n]), ref[n]) for n in names}
-    efro = {n: rel_err_fro(to_np(g[n]), ref[n]) for n in names}
-    for n in SCALAR_PARAMS:  # sums over every row: judged against the sum of the rows' magnitudes
-        emax[n] = efro[n] = sum_err(g[n], ref[n], ref["abs_" + n])
+    errs = polar_grad_errors({n: to_np(g[n]) for n in POLAR_GRADS}, ref)
     note(f"  polar bwd B{B} T{T} Hq{Hq} Hkv{Hkv} D{D}: " +
-         " ".join(f"{n}={emax[n]:.1e}/{efro[n]:.1e}" for n in names))
-    bad = {n: (emax[n], efro[n]) for n in names if not (emax[n] <= TOL_MAX and efro[n] <= TOL_FRO)}
+         " ".join(f"{n}={e[0]:.1e}/{e[1]:.1e}" for n, e in errs.items()))
+    bad = polar_grad_failures(errs)
     assert not bad, bad
     return o, mu
 
@@ -112,12 +97,10 @@ def test_polar_bwd_needle_keys(atma):
     _, _, g = _run(atma, inp, do)
     cp = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp["params"].items()}
     ref = oracle.polar_bwd(inp["q"], inp["k"], inp["v"], cp, do)
-    for n in ("dq", "dk", "dv", "d_temp_raw", "d_null_slope_raw", "d_null_bias", "d_mag_beta", "d_v_null"):
-        em, ef = rel_err_max(to_np(g[n]), ref[n]), rel_err_fro(to_np(g[n]), ref[n])
-        if n in SCALAR_PARAMS:
-            em = ef = sum_err(g[n], ref[n], ref["abs_" + n])
-        note(f"  polar bwd needles {n}: {em:.1e}/{ef:.1e}")
-        assert em <= TOL_MAX and ef <= TOL_FRO, (n, em, ef)
+    errs = polar_grad_errors({n: to_np(g[n]) for n in POLAR_GRADS}, ref)
+    note("  polar bwd needles: " + " ".join(f"{n}={e[0]:.1e}/{e[1]:.1e}" for n, e in errs.items()))
+    bad = polar_grad_failures(errs)
+    assert not bad, bad
 
 
 def test_polar_bwd_clamped_normaliser(atma):

@@ -37,6 +37,8 @@ def _check_prefill(atma, inp, rows=None, tag=""):
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
     o, mu, meff = atma.atma_polar_attn_fwd(q, k, v, _dev_params(inp["params"]), want_mu=True)
     torch.cuda.synchronize()
+    for t in (o, mu, meff):  # every element written (the buffers start as NaN in GPU tests)
+        assert torch.isfinite(t.float()).all()
     ref = oracle.polar_fwd(inp["q"], inp["k"], inp["v"], _cpu_params(inp["params"]), rows=rows)
     idx = slice(None) if rows is None else rows
     go = to_np(o)[:, idx]
