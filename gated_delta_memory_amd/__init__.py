@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "atma_polar_attn_fwd_varlen": ([vp, vp, vp, vp, i, i, P, vp, vp, vp] + [i] * 5 + [vp], i),
         "atma_polar_attn_decode": ([vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_polar_attn_decode_workspace_bytes": ([i] * 4, sz),
+        "atma_polar_attn_decode_noalloc": ([vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp], i),
         "atma_polar_attn_decode_varlen": ([vp, vp, vp, vp, i, i, P, vp, vp] + [i] * 5 + [vp, sz, vp], i),
         "atma_rope": ([vp, vp] + [i] * 5 + [f, i, vp], i),
         "atma_softmax_attn_fwd": ([vp] * 4 + [i] * 5 + [f, i, vp, sz, vp], i),
@@ -426,6 +427,25 @@ def atma_polar_attn_decode(q, k_cache, v_cache, cache_len, params, *, o=None, mu
                                     _ptr(o), _ptr(mu_out), B, Hq, Hkv, D, _dtype_code(q), _ptr(workspace),
                                     _nbytes(workspace), _stream(stream))
     _check("atma_polar_attn_decode", st)
+    return o, mu_out
+
+
+def atma_polar_attn_decode_noalloc(q, k_cache, v_cache, cache_len, params, *, o, mu_out=None, stream=None):
+    """Decode one token like atma_polar_attn_decode, with no workspace and no allocation: the
+    caller passes o [B,Hq,D] (and optionally mu_out [B,Hq] fp32); the split records live in the
+    library's fixed 16 MiB per-device array.  Returns (o, mu_out)."""
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _expect(k_cache, "k_cache", (B, Lmax, Hkv, D), q.dtype)
+    _expect(v_cache, "v_cache", (B, Lmax, Hkv, D), q.dtype)
+    _expect(o, "o", (B, Hq, D), q.dtype)
+    _expect(mu_out, "mu_out", (B, Hq), torch.float32, optional=True)
+    p = polar_params_struct(params, Hq, D)
+    _dev(q, k_cache, v_cache, o, mu_out)
+    st = lib.atma_polar_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len), Lmax,
+                                            ctypes.byref(p), _ptr(o), _ptr(mu_out), B, Hq, Hkv, D, _dtype_code(q),
+                                            _stream(stream))
+    _check("atma_polar_attn_decode_noalloc", st)
     return o, mu_out
 
 

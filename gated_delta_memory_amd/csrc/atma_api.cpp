@@ -234,6 +234,22 @@ int atma_polar_attn_decode(const void* q, const void* k_cache, const void* v_cac
     return launched(atma::launch_polar_decode(a, (hipStream_t)stream));
 }
 
+int atma_polar_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, int cache_len, int Lmax,
+                                   const atma_polar_params* p, void* o, float* mu_out, int B, int Hq, int Hkv, int D,
+                                   atma_dtype dt, void* stream) {
+    if (!q || !k_cache || !v_cache || !o) return ATMA_ERR_NULL;
+    const int pc = check_params(p);
+    if (pc != ATMA_OK) return pc;
+    if (!pos(B) || !pos(Hq) || !pos(Hkv) || !pos(D) || !pos(cache_len) || !pos(Lmax)) return ATMA_ERR_SHAPE;
+    if (cache_len > Lmax || Hq % Hkv != 0) return ATMA_ERR_SHAPE;
+    if (dt != ATMA_BF16 || !atma::polar_decode_supported(Hq, Hkv, D)) return ATMA_ERR_UNSUPPORTED;
+    if (!fits(Lmax, Hkv, D, 1) || !fits(B, Hq, D, 1) || Hq > 65535 || B > 65535) return ATMA_ERR_SHAPE;
+    if (atma::polar_decode_workspace_bytes(B, Hq, cache_len, D) > atma::polar_decode_scratch_bytes())
+        return ATMA_ERR_WORKSPACE;
+    atma::PolarDecodeArgs a{q, k_cache, v_cache, dev_params(p), o, mu_out, cache_len, Lmax, B, Hq, Hkv, D, nullptr};
+    return launched(atma::launch_polar_decode_noalloc(a, (hipStream_t)stream));
+}
+
 int atma_polar_attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, const int* cache_lens,
                                   int max_cache_len, int Lmax, const atma_polar_params* p, void* o, float* mu_out,
                                   int B, int Hq, int Hkv, int D, atma_dtype dt, void* workspace, size_t ws_bytes,

@@ -126,6 +126,10 @@ size_t polar_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
 // Hkv * D <= 2048, Hq/Hkv in {1,2,4,8}.
 bool polar_decode_supported(int Hq, int Hkv, int D);
 hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream);
+// The same launches with the split records in the library's fixed per-device array
+// (a.workspace ignored); fails when they need more than polar_decode_scratch_bytes().
+size_t polar_decode_scratch_bytes();
+hipError_t launch_polar_decode_noalloc(PolarDecodeArgs a, hipStream_t stream);
 
 // Sets the dynamic-LDS limit of a kernel once per process.
 template <typename K>

@@ -22,6 +22,9 @@
 // With SOFTMAX set the kernels are the decode row of the NoPE / RoPE control cores: logits
 // q.k / sqrt(D), no temperature, no null, output Sv / L; for RoPE the query is rotated to
 // position cache_len - 1 (angle in fp64) and the cached keys are expected already rotated.
+#include <atomic>
+#include <mutex>
+
 #include "atma_device.hpp"
 #include "launch.hpp"
 
@@ -330,6 +333,53 @@ hipError_t launch_polar_decode(const PolarDecodeArgs& a, hipStream_t stream) {
 #undef ATMA_PD_GQ
 #undef ATMA_PD_CASE
     return hipGetLastError();
+}
+
+// ---- allocation-free decode ---------------------------------------------------------------
+// Callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that
+// forbid allocation) get the split records in a fixed array of device memory instead of a
+// workspace: 16 MiB, one copy per GPU the library runs on, held until the process ends.  The
+// partial kernel writes every record the combine kernel reads, so nothing needs clearing between
+// calls; calls that overlap on one GPU (different streams) share the array and race.
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per device.  In host code the
+// array's name is only a stand-in for the symbol; the kernels receive this address instead.
+hipError_t scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* addr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!addr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        addr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!addr) {
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch_addr[dev].store(addr, std::memory_order_release);
+        }
+    }
+    *out = addr;
+    return hipSuccess;
+}
+}  // namespace
+
+size_t polar_decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_polar_decode_noalloc(PolarDecodeArgs a, hipStream_t stream) {
+    if (polar_decode_workspace_bytes(a.B, a.Hq, a.cache_len, a.D) > kScratchBytes) return hipErrorInvalidValue;
+    void* addr = nullptr;
+    const hipError_t e = scratch_address(&addr);
+    if (e != hipSuccess) return e;
+    a.workspace = addr;
+    return launch_polar_decode(a, stream);
 }
 
 bool polar_decode_supported(int Hq, int Hkv, int D) {

@@ -275,6 +275,25 @@ int atma_polar_attn_decode(const void* q, const void* k_cache, const void* v_cac
 size_t atma_polar_attn_decode_workspace_bytes(int B, int Hq, int cache_len, int D);
 
 /* ---------------------------------------------------------------------------------
+ * Polar attention, one decode step that allocates nothing and takes no workspace: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same operation, arguments and results as
+ * atma_polar_attn_decode (bitwise: the same kernels and split grid), with the split records in
+ * a fixed array of device memory inside the library: 16 MiB, one copy per GPU the library runs
+ * on, held until the process ends.
+ *   Limit: atma_polar_attn_decode_workspace_bytes(B, Hq, cache_len, D) <= 16 MiB (for example
+ *   B * Hq * (D + 4) * 4 * splits with at most 512 splits in all; every B up to 512 fits at
+ *   Hq * (D + 4) <= 8192); larger calls return ATMA_ERR_WORKSPACE without launching.
+ *   The stream must belong to the current device.  Every call on one GPU shares that GPU's array
+ *   (each call overwrites what it reads, nothing is carried between calls), so calls that overlap
+ *   on one GPU -- on different streams or from different threads -- race and must be ordered by
+ *   the caller.  The first call on a device looks the array up (no allocation).
+ * ------------------------------------------------------------------------------- */
+int atma_polar_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, int cache_len,
+                                   int Lmax, const atma_polar_params* p, void* o, float* mu_out, int B, int Hq,
+                                   int Hkv, int D, atma_dtype dt, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Polar attention, one decode step for a batch of sequences with different cache lengths
  * (heterogeneous serving batches).  Same operation as atma_polar_attn_decode with
  * n = cache_lens[b] for sequence b.
