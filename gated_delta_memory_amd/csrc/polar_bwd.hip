@@ -15,19 +15,23 @@
 //   sum_i dnu_i sqrt(ln(n_i + 1)) sigmoid(null_slope_raw), dnull_bias = sum_i dnu_i,
 //   dmag_beta = sum_i dmu_i (1 - mu_i^2) ln(1 + m_eff,i), dv_null = sum_i w_0,i ds_i.
 // The weights are recomputed, so no T x T matrix is stored: w_ij = exp2(cq_i (q_i . k_j) - lse2_i)
-// with cq_i = t_i log2(e) / sqrt(D).  The row sums the backward needs (partition, R, Q2 and
-// sum_j w_ij ds_i . v_j inside Sigma) are taken again in a statistics pass over the same bf16
-// operands, so that they describe exactly the weights and the dP the gradient kernels form:
-// then sum_j dl_ij + dl_0 = Sigma (1 - R - w_0) vanishes to fp32 rounding.  Reusing the forward's
-// statistics instead (accumulated from bf16-rounded weights) leaves a residue of a few 2^-9 in
-// that sum, which dq_i = sum_j dl_ij k_j, a sum that largely cancels, amplifies several times.
+// with cq_i = t_i log2(e) / sqrt(D).  The row sums the backward needs come from the training
+// forward: its real mass R and squared mass Q2 are sums of the fp32 weights exp2(cq_i (q_i . k_j)
+// - M) it forms from the same bf16 operands on the same MFMA (origin M, rescaled to lse2 at the
+// end), i.e. of the weights recomputed here up to fp32 rounding, and the value sum is s = den c
+// from its direction.  So Sigma = dR R + 2 dQ2 Q2 + ds . s is formed per row before any pass over
+// the keys.  The logit gradients of a row then sum to sum_j dl_ij + dl_0 = ds . (s' - s), s' the
+// value sum of the recomputed fp32 weights, where the forward's s took its weights rounded to
+// bf16: a residue of about 2^-9 |ds| |v| / sqrt(n_eff) per row, the size of the other bf16
+// roundings.  (Masses summed from the bf16-rounded weights would add (dR - Sigma)(R' - R), which
+// the large mass terms dR, growing with m_eff, would carry into dq_i = sum_j dl_ij k_j, a sum that
+// largely cancels.)
 //
-// Kernels (one call = six launches):
-//   prep    one row per D/8 lanes: ds (bf16) and per-row {forward lse2, dm_eff, ds . v_null, dbeta};
-//   stats   the dq layout below with only S^T and dP^T: per query the sums of w, w^2 and w dP over
-//           its keys, then the row scalars {cq, lse2, t a / sqrt(D), t b / sqrt(D), t / sqrt(D)} laid
-//           out [B, Hq, 5, Tp] (Tp = T rounded up to 64; padding rows get a log partition of +inf so
-//           their weights are exactly zero) and the per-row parameter partials;
+// Kernels (one call = five launches):
+//   prep    one row per D/8 lanes: ds (bf16) and the row scalars {cq, lse2, t a / sqrt(D),
+//           t b / sqrt(D), t / sqrt(D)} laid out [B, Hq, 5, Tp] (Tp = T rounded up to 64; padding
+//           rows get a log partition of +inf so their weights are exactly zero), and the per-row
+//           parameter partials;
 //   dq      a workgroup per 128-query tile (4 waves x 32 queries) streams 64-key blocks of K and V
 //           through two LDS stages, as the forward does: S^T = K Q^T and dP^T = V dS^T on
 //           v_mfma_f32_32x32x16_bf16 (a lane holds 16 keys of one query column, so every row
@@ -113,22 +117,39 @@ struct Offsets {
 };
 
 // ---------------------------------------------------------------------------------------------
-// prep: one row (b, i, h) per CH = D / 8 lanes, 8 elements per lane
+// prep: one row (b, i, h) per CH = D / 8 lanes, 8 elements per lane; rows i of [T, Tp) are the
+// padding rows of the streamed query blocks.  Writes ds (bf16) and the row scalars the gradient
+// kernels read, {cq, lse2, t a / sqrt(D), t b / sqrt(D), t / sqrt(D)} in [B, Hq, 5, Tp], from the
+// training forward's statistics: its real mass R and squared mass Q2 are sums of the same fp32
+// weights the gradient kernels recompute from the same operands, and its direction gives the value
+// sum s = den c, so Sigma = dR R + 2 dQ2 Q2 + ds . s needs no pass over the keys.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(NT) void polar_bwd_prep(const bf16* __restrict__ dO, const float* __restrict__ dir,
                                                      const float* __restrict__ stats, const float* __restrict__ mu_in,
-                                                     PolarParamsDev prm, bf16* __restrict__ dsg, float* __restrict__ rowin,
-                                                     int B, int T, int Hq) {
+                                                     PolarParamsDev prm, bf16* __restrict__ dsg, float* __restrict__ rec,
+                                                     float* __restrict__ part, int B, int T, int Tp, int Hq) {
+    using SH = BShape<D>;
     constexpr int CH = D / 8;
     const size_t gid = (size_t)blockIdx.x * NT + threadIdx.x;
     const int ci = (int)(gid % CH);
     const size_t rid = gid / CH;
     const int h = (int)(rid % Hq);
-    const int i = (int)((rid / Hq) % T);
-    const int b = (int)(rid / ((size_t)Hq * T));
+    const int i = (int)((rid / Hq) % Tp);
+    const int b = (int)(rid / ((size_t)Hq * Tp));
     if (b >= B) return;
     const size_t bh = (size_t)b * Hq + h;
+    float* rr = rec + bh * NREC * Tp + i;
+    if (i >= T) {  // padding row: zero weight (log partition +inf), zero gradient
+        if (ci == 0) {
+            rr[0] = 1.0f;
+            rr[(size_t)Tp] = INFINITY;
+            rr[(size_t)2 * Tp] = 0.0f;
+            rr[(size_t)3 * Tp] = 0.0f;
+            rr[(size_t)4 * Tp] = 0.0f;
+        }
+        return;
+    }
     const size_t e0 = (((size_t)b * T + i) * Hq + h) * D + ci * 8;
     const bf16x8 gb = *(const bf16x8*)(dO + e0);
     const f32x4 c0 = *(const f32x4*)(dir + e0), c1 = *(const f32x4*)(dir + e0 + 4);
@@ -142,7 +163,7 @@ __global__ __launch_bounds__(NT) void polar_bwd_prep(const bf16* __restrict__ dO
         vn[e] = vn0[e]; vn[e + 4] = vn1[e];
     }
     const f32x4 st = *(const f32x4*)(stats + (bh * T + i) * 4);
-    const float R = st[1], Q2 = st[2], dens = st[3];
+    const float lse2 = st[0], R = st[1], Q2 = st[2], dens = st[3];
     const float mu = mu_in[bh * T + i];
     const bool clamped = dens < 0.0f;
     const float den = fabsf(dens);
@@ -151,36 +172,52 @@ __global__ __launch_bounds__(NT) void polar_bwd_prep(const bf16* __restrict__ dO
     for (int e = 0; e < 8; ++e) dmu += g[e] * c[e];
 #pragma unroll
     for (int o = CH / 2; o >= 1; o >>= 1) dmu += __shfl_xor(dmu, o, CH);
-    // ds is rounded to bf16 once and every later use (dP on MFMA, ds . v_null here) takes the
-    // rounded value
-    float dsv = 0.f;
+    // ds is rounded to bf16 once and every later use (dP on MFMA, ds . v_null and ds . c here)
+    // takes the rounded value
+    float dsv = 0.f, dsc = 0.f;
     const float sc = mu / den, pr = clamped ? 0.0f : dmu;
     bf16x8 dsb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         dsb[e] = (bf16)(sc * (g[e] - pr * c[e]));
         dsv += (float)dsb[e] * vn[e];
+        dsc += (float)dsb[e] * c[e];
     }
 #pragma unroll
-    for (int o = CH / 2; o >= 1; o >>= 1) dsv += __shfl_xor(dsv, o, CH);
+    for (int o = CH / 2; o >= 1; o >>= 1) {
+        dsv += __shfl_xor(dsv, o, CH);
+        dsc += __shfl_xor(dsc, o, CH);
+    }
     *(bf16x8*)(dsg + e0) = dsb;
     if (ci != 0) return;
+    const float n = (float)(i + 1);
+    const float t = 1.0f + softplus(prm.temp_raw[h]) * logf(n);
+    const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf(n + 1.0f));
     const float me = R * R * R / Q2;
     const float om = 1.0f - mu * mu;
-    const f32x4 rr = {st[0], dmu * om * prm.mag_beta[h] / (1.0f + me), dsv, dmu * om * log1pf(me)};
-    *(f32x4*)(rowin + (bh * T + i) * 4) = rr;
+    const float dme = dmu * om * prm.mag_beta[h] / (1.0f + me);
+    const float dR = 3.0f * dme * me / R, dQ2 = -dme * me / Q2;
+    const float wn = 1.0f - R;  // the null weight
+    const float Sig = dR * R + 2.0f * dQ2 * Q2 + den * dsc;
+    const float tqr = t * SH::kInvSqrtD;
+    rr[0] = t * kLog2e * SH::kInvSqrtD;  // cq, as the forward forms it
+    rr[(size_t)Tp] = lse2;
+    rr[(size_t)2 * Tp] = tqr * (dR - Sig);
+    rr[(size_t)3 * Tp] = tqr * (2.0f * dQ2);
+    rr[(size_t)4 * Tp] = tqr;
+    const float dl0 = wn * (dsv - Sig);
+    const f32x4 pp = {dl0 * nu, dl0 * t, dmu * om * log1pf(me), wn};
+    *(f32x4*)(part + (bh * T + i) * 4) = pp;
 }
 
 // ---------------------------------------------------------------------------------------------
 // dq: 128 queries per workgroup, key blocks of 64 through two LDS stages
 // ---------------------------------------------------------------------------------------------
-template <int D, bool STATS>
+template <int D>
 __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                       const bf16* __restrict__ v, const bf16* __restrict__ dsg,
-                                                      const float* __restrict__ rowin, PolarParamsDev prm,
-                                                      float* __restrict__ rec, float* __restrict__ part,
-                                                      bf16* __restrict__ dq, float* __restrict__ dtr, int T, int Tp,
-                                                      int Hq, int Hkv) {
+                                                      const float* __restrict__ rec, bf16* __restrict__ dq,
+                                                      float* __restrict__ dtr, int T, int Tp, int Hq, int Hkv) {
     using SH = BShape<D>;
     constexpr int NKS = SH::NKS, NDT = SH::NDT, ROWB = SH::ROWB;
     __shared__ __align__(16) char g_kv0[2 * SH::TILE];
@@ -214,16 +251,9 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
     const Offsets<D> of(lane);
 
     const int q0 = qt * BQ, qw0 = q0 + w * 32, qi = qw0 + l32, qc = min(qi, T - 1);
-    float cq, lse2, ap = 0.f, bp = 0.f, tq = 0.f;
-    f32x4 rin = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (STATS) {  // t_i exactly as the forward forms it
-        rin = *(const f32x4*)(rowin + ((size_t)bh * T + qc) * 4);
-        cq = (1.0f + softplus(prm.temp_raw[h]) * logf((float)(qc + 1))) * kLog2e * SH::kInvSqrtD;
-        lse2 = rin[0];
-    } else {
-        const float* rr = rec + (size_t)bh * NREC * Tp + qc;
-        cq = rr[0]; lse2 = rr[(size_t)Tp]; ap = rr[(size_t)2 * Tp]; bp = rr[(size_t)3 * Tp]; tq = rr[(size_t)4 * Tp];
-    }
+    const float* rr = rec + (size_t)bh * NREC * Tp + qc;
+    const float cq = rr[0], lse2 = rr[(size_t)Tp], ap = rr[(size_t)2 * Tp], bp = rr[(size_t)3 * Tp],
+                tq = rr[(size_t)4 * Tp];
     bf16x8 qf[NKS], sf[NKS];
     {
         const size_t e0 = ((size_t)b * T + qc) * qstride + (size_t)h * D + 8 * G2;
@@ -233,10 +263,9 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
             sf[ks] = *(const bf16x8*)(dsg + e0 + 16 * ks);
         }
     }
-    f32x16 acc[STATS ? 1 : NDT];  // dQ^T[d = 32 dt + 8 (x / 4) + 4 G2 + x % 4][qi]
+    f32x16 acc[NDT];  // dQ^T[d = 32 dt + 8 (x / 4) + 4 G2 + x % 4][qi]
 #pragma unroll
-    for (int dt = 0; dt < (STATS ? 1 : NDT); ++dt) acc[dt] = f32x16{};
-    float a1 = 0.f, a2 = 0.f, a3 = 0.f;  // sums over keys of w, w^2, w dP (statistics pass)
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
     const int nkb = (min(T, q0 + BQ) + BB - 1) / BB;
 
     auto block = [&](int kb, const char* Ks) {
@@ -252,22 +281,6 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
                 s[kt] = mfma32(*(const bf16x8*)(Ks + of.koff[ks] + kt * 32 * ROWB), qf[ks], s[kt]);
                 dp[kt] = mfma32(*(const bf16x8*)(Vs + of.koff[ks] + kt * 32 * ROWB), sf[ks], dp[kt]);
             }
-        if constexpr (STATS) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    float p = fast_exp2(fmaf(s[kt][x], cq, -lse2));
-                    if (edge) {
-                        const int key = key0 + 32 * kt + 8 * (x >> 2) + 4 * G2 + (x & 3);
-                        p = (key > qi || key >= T) ? 0.0f : p;
-                    }
-                    a1 += p;
-                    a2 = fmaf(p, p, a2);
-                    a3 = fmaf(p, dp[kt][x], a3);
-                }
-            return;
-        }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -306,42 +319,6 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
         block(kb + 1, g_kv1);
     }
 
-    if constexpr (STATS) {
-        // the weights of this row as the gradient kernels form them: partition Zb (relative to the
-        // forward's lse2), real mass, squared mass, sum_j w_j dP_j, and the null weight
-        a1 = pair_sum(a1);  // lanes l and l ^ 32 share a query
-        a2 = pair_sum(a2);
-        a3 = pair_sum(a3);
-        if (G2 != 0 || qi >= Tp) return;
-        float* rr = rec + (size_t)bh * NREC * Tp + qi;
-        if (qi >= T) {  // padding row of the streamed query blocks: zero weight, zero gradient
-            rr[0] = 1.0f;
-            rr[(size_t)Tp] = INFINITY;
-            rr[(size_t)2 * Tp] = 0.0f;
-            rr[(size_t)3 * Tp] = 0.0f;
-            rr[(size_t)4 * Tp] = 0.0f;
-            return;
-        }
-        const float t = 1.0f + softplus(prm.temp_raw[h]) * logf((float)(qi + 1));
-        const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf((float)(qi + 1) + 1.0f));
-        const float e0 = fast_exp2(t * nu * kLog2e - lse2);
-        const float inv = 1.0f / (a1 + e0);
-        const float R = a1 * inv, Q2 = a2 * inv * inv, wn = e0 * inv;
-        const float me = R * R * R / Q2;
-        const float dme = rin[1], dsv = rin[2];
-        const float dR = 3.0f * dme * me / R, dQ2 = -dme * me / Q2;
-        const float Sig = dR * R + 2.0f * dQ2 * Q2 + a3 * inv + wn * dsv;
-        const float tqr = t * SH::kInvSqrtD;
-        rr[0] = cq;
-        rr[(size_t)Tp] = lse2 + fast_log2(a1 + e0);
-        rr[(size_t)2 * Tp] = tqr * (dR - Sig);
-        rr[(size_t)3 * Tp] = tqr * (2.0f * dQ2);
-        rr[(size_t)4 * Tp] = tqr;
-        const float dl0 = wn * (dsv - Sig);
-        const f32x4 pp = {dl0 * nu, dl0 * t, rin[3], wn};
-        *(f32x4*)(part + ((size_t)bh * T + qi) * 4) = pp;
-        return;
-    }
     // dq row, and the temperature's share of this row: q . dq / t (dq already carries t / sqrt(D))
     if (qi < T) {
         const size_t e0 = ((size_t)b * T + qi) * qstride + (size_t)h * D;
@@ -609,7 +586,7 @@ __global__ __launch_bounds__(NT) void polar_bwd_params_final(const float* __rest
 
 struct BwdWs {
     bf16* dsg;
-    float *rec, *part, *dtr, *r0, *ppart;
+    float *rec, *part, *dtr, *ppart;
 };
 BwdWs carve(void* ws, int B, int T, int Hq, int D) {
     const size_t Tp = (size_t)(T + BB - 1) / BB * BB;
@@ -623,8 +600,6 @@ BwdWs carve(void* ws, int B, int T, int Hq, int D) {
     p += ((size_t)B * Hq * T * 16 + 255) / 256 * 256;
     w.dtr = (float*)p;
     p += ((size_t)B * Hq * T * 4 + 255) / 256 * 256;
-    w.r0 = (float*)p;
-    p += ((size_t)B * Hq * T * 16 + 255) / 256 * 256;
     w.ppart = (float*)p;
     return w;
 }
@@ -635,7 +610,7 @@ size_t polar_bwd_workspace_bytes(int B, int T, int Hq, int D) {
     const size_t Tp = (size_t)(T + BB - 1) / BB * BB;
     return ((size_t)B * T * Hq * D * 2 + 255) / 256 * 256 + ((size_t)B * Hq * NREC * Tp * 4 + 255) / 256 * 256 +
            ((size_t)B * Hq * T * 16 + 255) / 256 * 256 + ((size_t)B * Hq * T * 4 + 255) / 256 * 256 +
-           ((size_t)B * Hq * T * 16 + 255) / 256 * 256 + (size_t)Hq * PCH * (4 + D) * 4;
+           (size_t)Hq * PCH * (4 + D) * 4;
 }
 
 hipError_t launch_polar_bwd(const PolarBwdArgs& a, hipStream_t stream) {
@@ -643,18 +618,16 @@ hipError_t launch_polar_bwd(const PolarBwdArgs& a, hipStream_t stream) {
     const int Tp = (a.T + BB - 1) / BB * BB;
     const long long nq = (long long)((a.T + BQ - 1) / BQ) * a.Hq * a.B;
     const long long nk = (long long)((a.T + BKT - 1) / BKT) * a.Hkv * a.B;
-    const long long prep_threads = (long long)a.B * a.T * a.Hq * (a.D / 8);
+    const long long prep_threads = (long long)a.B * Tp * a.Hq * (a.D / 8);
     if (nq > 0x7fffffffLL || 2 * nk > 0x7fffffffLL || prep_threads / NT > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define ATMA_PB_LAUNCH(DD)                                                                                        \
     do {                                                                                                          \
         hipLaunchKernelGGL(polar_bwd_prep<DD>, dim3((unsigned)((prep_threads + NT - 1) / NT)), dim3(NT), 0,       \
-                           stream, (const bf16*)a.dO, a.dir, a.stats, a.mu, a.p, w.dsg, w.r0, a.B, a.T, a.Hq);     \
-        hipLaunchKernelGGL((polar_bwd_dq<DD, true>), dim3((unsigned)nq), dim3(NT), 0, stream, (const bf16*)a.q,   \
-                           (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.r0, a.p, w.rec, \
-                           w.part, (bf16*)a.dq, w.dtr, a.T, Tp, a.Hq, a.Hkv);                                      \
-        hipLaunchKernelGGL((polar_bwd_dq<DD, false>), dim3((unsigned)nq), dim3(NT), 0, stream, (const bf16*)a.q,  \
-                           (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.r0, a.p, w.rec, \
-                           w.part, (bf16*)a.dq, w.dtr, a.T, Tp, a.Hq, a.Hkv);                                      \
+                           stream, (const bf16*)a.dO, a.dir, a.stats, a.mu, a.p, w.dsg, w.rec, w.part, a.B, a.T,   \
+                           Tp, a.Hq);                                                                              \
+        hipLaunchKernelGGL(polar_bwd_dq<DD>, dim3((unsigned)nq), dim3(NT), 0, stream, (const bf16*)a.q,           \
+                           (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.rec,            \
+                           (bf16*)a.dq, w.dtr, a.T, Tp, a.Hq, a.Hkv);                                              \
         if (DD == 64)                                                                                             \
             hipLaunchKernelGGL(polar_bwd_dkv<DD>, dim3((unsigned)nk), dim3(NT), 0, stream, (const bf16*)a.q,      \
                                (const bf16*)a.k, (const bf16*)a.v, (const bf16*)w.dsg, (const float*)w.rec,        \

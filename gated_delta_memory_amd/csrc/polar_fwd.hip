@@ -26,8 +26,10 @@
 //     lanes that share a query are combined with v_permlane32_swap);
 //   * the same registers, cast to bf16, are the B operand of O^T = V^T P^T; the V^T
 //     fragments come straight from the row-major V tile with ds_read_b64_tr_b16;
-//   * L and Q2 are accumulated from the bf16 weights with v_dot2_f32_bf16, so they use
-//     exactly the weights the value sum uses;
+//   * L and Q2 are accumulated from the fp32 weights (before their rounding to bf16 for the value
+//     product), which are exactly the weights the backward recomputes from the same operands, so
+//     the backward can take its row statistics from this pass (the control cores, which have no
+//     backward, sum the bf16 weights with v_dot2_f32_bf16);
 //   * a workgroup computes two query tiles of one (batch, head), the k-th heaviest and the
 //     k-th lightest, so all workgroups stream the same number of key blocks (causal balance);
 //     the tiles of one (batch, head) go to one XCD so their K/V stream is shared in its L2.
@@ -270,8 +272,14 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
                     const float p0 = fast_exp2(fmaf(s[kt][8 * st + e], cq, -m_used));
                     const float p1 = fast_exp2(fmaf(s[kt][8 * st + e + 1], cq, -m_used));
                     const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    ls = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(bf16)1.0f, (bf16)1.0f}, ls, false);
-                    if constexpr (POLAR) qs = __builtin_amdgcn_fdot2_f32_bf16(pp, pp, qs, false);
+                    if constexpr (POLAR) {  // the fp32 weights, as the backward recomputes them
+                        ls += p0;
+                        ls += p1;
+                        qs = fmaf(p0, p0, qs);
+                        qs = fmaf(p1, p1, qs);
+                    } else {
+                        ls = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(bf16)1.0f, (bf16)1.0f}, ls, false);
+                    }
                     pf[e] = pp[0];
                     pf[e + 1] = pp[1];
                 }
