@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tokens/sec gated-delta+Polar fwd at T=2K/64K/256K; % MFMA or HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_MFMA_TFLOPS = 157.3
 
 
 def polar_flops(B, T, Hq, D=64):
@@ -37,6 +38,17 @@ def gdn_bytes(B, T, H, D=128, es=2):
     # q, k, v read + o written (es bytes each) and alpha, beta (fp32) per token and head,
     # plus the final fp32 state
     return B * H * T * (4 * D * es + 8) + B * H * D * D * 4
+
+
+def gdn_fwd_flops(B, T, H, D=128, C=64):
+    # chunked forward's products per token and head: C(3 Dk + 2 Dv) + 6 Dk Dv + C^2/3 (Dk = Dv = D;
+    # triangular halves counted once)
+    return B * H * T * (C * 5 * D + 6 * D * D + C * C / 3)
+
+
+def gdn_bwd_flops(B, T, H, D=128, C=64):
+    # every forward product has two operand gradients of its own size: twice the forward
+    return 2 * gdn_fwd_flops(B, T, H, D, C)
 
 
 def decode_bytes(B, L, Hkv=16, D=64, H=8, Dg=128):
@@ -53,6 +65,8 @@ MEASURED_TRAFFIC = {
     "polar_fwd_kernel": {"sha": "cb022c8c60206c91", "bytes": 161031574},
     # layer_b8_t2k, prep + carry + out (one segment at this shape)
     "atma_gdn_fwd (prep+carry+out)": {"sha": "1b9dd2ec90e1eba6", "bytes": 577296374},
+    # layer_b8_t2k backward: prep + both walks + pre + post (profiles/gdn_bwd_layer_b8_t2k.txt)
+    "atma_gdn_bwd (all kernels)": {"sha": "a156336d3424ad46", "bytes": 3665200000},
 }
 
 
@@ -65,6 +79,7 @@ def _sources_sha(names):
 
 
 KERNEL_SOURCES = {"polar_fwd_kernel": ["polar_fwd.hip", "atma_device.hpp"],
+                  "atma_gdn_bwd (all kernels)": ["gdn_bwd.hip", "gdn_common.hpp", "atma_device.hpp"],
                   "atma_gdn_fwd (prep+carry+out)": ["gdn_fwd.hip", "gdn_fwd_bf16.hip", "gdn_common.hpp",
                                                     "atma_device.hpp"]}
 
@@ -111,6 +126,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true", help="skip the 64K prefill and 256K decode lines")
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma-separated secondary sections to run (default: all): " + ", ".join(SECTIONS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB three times (counter calibration)")
@@ -215,190 +232,232 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_secondary:
-        out["secondary"] = secondary(torch, atma, workloads)
+        out["secondary"] = secondary(torch, atma, workloads, sections=args.sections.split(","))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 
 
-def secondary(torch, atma, workloads):
+SECTIONS = ("cores", "polar_d128", "canon", "polar_train", "gdn_train", "prefill_64k", "prefill_256k", "decode")
+
+
+def secondary(torch, atma, workloads, sections=SECTIONS):
     res = {}
-    # the matched control cores (NoPE / RoPE causal softmax attention) beside Polar, 2K layer shape
-    w = workloads.WORKLOADS["layer_b8_t2k"]
-    p = workloads.make_workload(w, device="cuda")["polar"]
-    o_p = torch.empty_like(p["q"])
-    ws_r = torch.empty(int(atma.lib.atma_softmax_attn_workspace_bytes(w.B, w.T, w.polar_Hq, w.polar_Hkv, 64,
-                                                                       10000.0)), dtype=torch.uint8, device="cuda")
-    tpo, tno, tro = Timer(torch), Timer(torch), Timer(torch)
-    for it in range(21):
-        (tpo if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
-        (tno if it else (lambda f: f()))(lambda: atma.atma_softmax_attn_fwd(p["q"], p["k"], p["v"], 0.0, o=o_p))
-        (tro if it else (lambda f: f()))(lambda: atma.atma_softmax_attn_fwd(p["q"], p["k"], p["v"], 10000.0, o=o_p,
-                                                                            workspace=ws_r))
-    torch.cuda.synchronize()
-    pf = polar_flops(w.B, w.T, w.polar_Hq)
-    res["cores_" + w.name] = {"polar_ms": round(tpo.mean_ms(), 4), "nope_ms": round(tno.mean_ms(), 4),
-                              "rope_ms": round(tro.mean_ms(), 4),
-                              "nope_mfma_frac": round(pf / (tno.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    del p, o_p, ws_r
-    torch.cuda.empty_cache()
-    # the real model's attention layout: 8 query / 2 kv heads at head width 128
-    for (B, T, name, reps) in ((8, 2048, "polar_d128_gqa_b8_t2k", 21), (1, 65536, "polar_d128_gqa_b1_t64k", 4)):
-        p = workloads.make_polar_inputs(B, T, 8, 2, 128, device="cuda")
+
+    def want(name):
+        return name in sections
+
+    if want("cores"):
+        # the matched control cores (NoPE / RoPE causal softmax attention) beside Polar, 2K layer shape
+        w = workloads.WORKLOADS["layer_b8_t2k"]
+        p = workloads.make_workload(w, device="cuda")["polar"]
         o_p = torch.empty_like(p["q"])
-        tq = Timer(torch)
-        for it in range(reps):
-            (tq if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+        ws_r = torch.empty(int(atma.lib.atma_softmax_attn_workspace_bytes(w.B, w.T, w.polar_Hq, w.polar_Hkv, 64,
+                                                                           10000.0)), dtype=torch.uint8, device="cuda")
+        tpo, tno, tro = Timer(torch), Timer(torch), Timer(torch)
+        for it in range(21):
+            (tpo if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+            (tno if it else (lambda f: f()))(lambda: atma.atma_softmax_attn_fwd(p["q"], p["k"], p["v"], 0.0, o=o_p))
+            (tro if it else (lambda f: f()))(lambda: atma.atma_softmax_attn_fwd(p["q"], p["k"], p["v"], 10000.0, o=o_p,
+                                                                                workspace=ws_r))
         torch.cuda.synchronize()
-        fl = 4 * 128 * B * 8 * T * (T + 1) / 2
-        res[name] = {"polar_ms": round(tq.mean_ms(), 4),
-                     "polar_mfma_frac": round(fl / (tq.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del p, o_p
+        pf = polar_flops(w.B, w.T, w.polar_Hq)
+        res["cores_" + w.name] = {"polar_ms": round(tpo.mean_ms(), 4), "nope_ms": round(tno.mean_ms(), 4),
+                                  "rope_ms": round(tro.mean_ms(), 4),
+                                  "nope_mfma_frac": round(pf / (tno.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del p, o_p, ws_r
         torch.cuda.empty_cache()
-    # Canon prologue (depthwise causal convolution, 4 taps, residual, per-head unit norm) on the
-    # query projection of the 8/2-head, D = 128 layout at the 2K shape: algorithmic bytes are one
-    # read of x and one write of y (bf16), the taps and the carried state are negligible
-    B, T, Cq, K = 8, 2048, 8 * 128, 4
-    gen = torch.Generator(device="cuda").manual_seed(5)
-    x = torch.randn(B, T, Cq, device="cuda", generator=gen).to(torch.bfloat16)
-    wc = torch.randn(K, Cq, device="cuda", generator=gen) * 0.5
-    st = torch.zeros(B, K - 1, Cq, device="cuda", dtype=torch.bfloat16)
-    yc = torch.empty_like(x)
-    tc = Timer(torch)
-    for it in range(21):
-        (tc if it else (lambda f: f()))(lambda: atma.atma_canon(x, wc, st, residual=True, heads=8, update_state=False,
-                                                                y=yc))
-    torch.cuda.synchronize()
-    cb = 2 * B * T * Cq * 2
-    res["canon_q_d128_b8_t2k"] = {"canon_us": round(tc.mean_ms() * 1e3, 2), "bytes": cb,
-                                  "hbm_frac": round(cb / (tc.mean_ms() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del x, wc, st, yc
-    torch.cuda.empty_cache()
-    # training step of the Polar core (training forward + backward) at the 2K layer shapes; the
-    # backward's algorithmic work is the usual five products per visible (query, key) pair
-    # (S recomputed, dP, dV, dK, dQ): 10 D flop per pair per head
-    for (B, T, Hq, Hkv, D, name) in ((8, 2048, 16, 16, 64, "polar_train_layer_b8_t2k"),
-                                     (8, 2048, 8, 2, 128, "polar_train_d128_gqa_b8_t2k")):
-        p = workloads.make_polar_inputs(B, T, Hq, Hkv, D, device="cuda")
-        do = torch.randn(B, T, Hq, D, device="cuda").to(torch.bfloat16)
-        f = dict(dtype=torch.float32, device="cuda")
-        gout = {"dq": torch.empty_like(p["q"]), "dk": torch.empty_like(p["k"]), "dv": torch.empty_like(p["v"]),
-                "d_temp_raw": torch.empty(Hq, **f), "d_null_slope_raw": torch.empty(Hq, **f),
-                "d_null_bias": torch.empty(Hq, **f), "d_mag_beta": torch.empty(Hq, **f),
-                "d_v_null": torch.empty(Hq, D, **f)}
-        ws_b = torch.empty(int(atma.lib.atma_polar_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)), dtype=torch.uint8,
+    if want("polar_d128"):
+        # the real model's attention layout: 8 query / 2 kv heads at head width 128
+        for (B, T, name, reps) in ((8, 2048, "polar_d128_gqa_b8_t2k", 21), (1, 65536, "polar_d128_gqa_b1_t64k", 4)):
+            p = workloads.make_polar_inputs(B, T, 8, 2, 128, device="cuda")
+            o_p = torch.empty_like(p["q"])
+            tq = Timer(torch)
+            for it in range(reps):
+                (tq if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
+            torch.cuda.synchronize()
+            fl = 4 * 128 * B * 8 * T * (T + 1) / 2
+            res[name] = {"polar_ms": round(tq.mean_ms(), 4),
+                         "polar_mfma_frac": round(fl / (tq.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del p, o_p
+            torch.cuda.empty_cache()
+    if want("canon"):
+        # Canon prologue (depthwise causal convolution, 4 taps, residual, per-head unit norm) on the
+        # query projection of the 8/2-head, D = 128 layout at the 2K shape: algorithmic bytes are one
+        # read of x and one write of y (bf16), the taps and the carried state are negligible
+        B, T, Cq, K = 8, 2048, 8 * 128, 4
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        x = torch.randn(B, T, Cq, device="cuda", generator=gen).to(torch.bfloat16)
+        wc = torch.randn(K, Cq, device="cuda", generator=gen) * 0.5
+        st = torch.zeros(B, K - 1, Cq, device="cuda", dtype=torch.bfloat16)
+        yc = torch.empty_like(x)
+        tc = Timer(torch)
+        for it in range(21):
+            (tc if it else (lambda f: f()))(lambda: atma.atma_canon(x, wc, st, residual=True, heads=8, update_state=False,
+                                                                    y=yc))
+        torch.cuda.synchronize()
+        cb = 2 * B * T * Cq * 2
+        res["canon_q_d128_b8_t2k"] = {"canon_us": round(tc.mean_ms() * 1e3, 2), "bytes": cb,
+                                      "hbm_frac": round(cb / (tc.mean_ms() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del x, wc, st, yc
+        torch.cuda.empty_cache()
+    if want("polar_train"):
+        # training step of the Polar core (training forward + backward) at the 2K layer shapes; the
+        # backward's algorithmic work is the usual five products per visible (query, key) pair
+        # (S recomputed, dP, dV, dK, dQ): 10 D flop per pair per head
+        for (B, T, Hq, Hkv, D, name) in ((8, 2048, 16, 16, 64, "polar_train_layer_b8_t2k"),
+                                         (8, 2048, 8, 2, 128, "polar_train_d128_gqa_b8_t2k")):
+            p = workloads.make_polar_inputs(B, T, Hq, Hkv, D, device="cuda")
+            do = torch.randn(B, T, Hq, D, device="cuda").to(torch.bfloat16)
+            f = dict(dtype=torch.float32, device="cuda")
+            gout = {"dq": torch.empty_like(p["q"]), "dk": torch.empty_like(p["k"]), "dv": torch.empty_like(p["v"]),
+                    "d_temp_raw": torch.empty(Hq, **f), "d_null_slope_raw": torch.empty(Hq, **f),
+                    "d_null_bias": torch.empty(Hq, **f), "d_mag_beta": torch.empty(Hq, **f),
+                    "d_v_null": torch.empty(Hq, D, **f)}
+            ws_b = torch.empty(int(atma.lib.atma_polar_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)), dtype=torch.uint8,
+                               device="cuda")
+            fw = {}
+            tf, tb = Timer(torch), Timer(torch)
+
+            def fwd_train():
+                fw["o"], fw["mu"], fw["st"], fw["dir"] = atma.atma_polar_attn_fwd_train(p["q"], p["k"], p["v"],
+                                                                                        p["params"])
+
+            def bwd():
+                atma.atma_polar_attn_bwd(p["q"], p["k"], p["v"], p["params"], fw["mu"], fw["st"], fw["dir"], do,
+                                         out=gout, workspace=ws_b)
+
+            for it in range(11):
+                (tf if it else (lambda fn: fn()))(fwd_train)
+                (tb if it else (lambda fn: fn()))(bwd)
+            torch.cuda.synchronize()
+            pairs = B * Hq * T * (T + 1) / 2
+            res[name] = {"fwd_train_ms": round(tf.mean_ms(), 4), "bwd_ms": round(tb.mean_ms(), 4),
+                         "bwd_TFLOPs": round(10 * D * pairs / (tb.mean_ms() * 1e-3) / 1e12, 2),
+                         "bwd_mfma_frac": round(10 * D * pairs / (tb.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "tokens_per_s": round(B * T / ((tf.mean_ms() + tb.mean_ms()) * 1e-3), 1)}
+            del p, do, gout, ws_b, fw
+            torch.cuda.empty_cache()
+    if want("gdn_train"):
+        # memory backward at the 2K layer shape (B=8, H=8, d=128, bf16 inputs, fp32 arithmetic)
+        w = workloads.WORKLOADS["layer_b8_t2k"]
+        g = workloads.make_workload(w, device="cuda")["gdn"]
+        do = torch.randn_like(g["v"])
+        ws_gb = torch.empty(int(atma.lib.atma_gdn_bwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D, 64, 1)),
+                            dtype=torch.uint8, device="cuda")
+        tgb = Timer(torch)
+        for it in range(6):
+            (tgb if it else (lambda fn: fn()))(lambda: atma.atma_gdn_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], do,
+                                                                         workspace=ws_gb))
+        torch.cuda.synchronize()
+        bf = gdn_bwd_flops(w.B, w.T, w.gdn_H, w.gdn_D)
+        tf = bf / (tgb.mean_ms() * 1e-3) / 1e12
+        res["gdn_train_" + w.name] = {
+            "bwd_ms": round(tgb.mean_ms(), 4), "workspace_MB": round(ws_gb.numel() / 2 ** 20, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "traffic": measured_traffic("atma_gdn_bwd (all kernels)"),
+                         "per_launch": f"{bf:.4e} flop = 2 x B*H*T*(C(3D+2D) + 6D^2 + C^2/3), B={w.B} T={w.T} "
+                                       f"H={w.gdn_H} D={w.gdn_D} C=64 (twice the chunked forward's products)"}}
+        del g, do, ws_gb
+        torch.cuda.empty_cache()
+    if want("prefill_64k"):
+        # 64K prefill
+        w = workloads.WORKLOADS["prefill_b1_t64k"]
+        inp = workloads.make_workload(w, device="cuda")
+        g, p = inp["gdn"], inp["polar"]
+        o_g = torch.empty_like(g["v"])
+        ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
                            device="cuda")
-        fw = {}
-        tf, tb = Timer(torch), Timer(torch)
-
-        def fwd_train():
-            fw["o"], fw["mu"], fw["st"], fw["dir"] = atma.atma_polar_attn_fwd_train(p["q"], p["k"], p["v"],
-                                                                                    p["params"])
-
-        def bwd():
-            atma.atma_polar_attn_bwd(p["q"], p["k"], p["v"], p["params"], fw["mu"], fw["st"], fw["dir"], do,
-                                     out=gout, workspace=ws_b)
-
-        for it in range(11):
-            (tf if it else (lambda fn: fn()))(fwd_train)
-            (tb if it else (lambda fn: fn()))(bwd)
+        S_g = torch.empty(w.B, w.gdn_H, w.gdn_D, w.gdn_D, device="cuda")
+        o_p = torch.empty_like(p["q"])
+        tg, tp = Timer(torch), Timer(torch)
+        for it in range(4):
+            (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
+                                                                      o=o_g, final_state=S_g, workspace=ws_g))
+            (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
         torch.cuda.synchronize()
-        pairs = B * Hq * T * (T + 1) / 2
-        res[name] = {"fwd_train_ms": round(tf.mean_ms(), 4), "bwd_ms": round(tb.mean_ms(), 4),
-                     "bwd_TFLOPs": round(10 * D * pairs / (tb.mean_ms() * 1e-3) / 1e12, 2),
-                     "bwd_mfma_frac": round(10 * D * pairs / (tb.mean_ms() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "tokens_per_s": round(B * T / ((tf.mean_ms() + tb.mean_ms()) * 1e-3), 1)}
-        del p, do, gout, ws_b, fw
+        gm, pm = tg.mean_ms(), tp.mean_ms()
+        pf = polar_flops(w.B, w.T, w.polar_Hq)
+        res[w.name] = {"tokens_per_s": round(w.B * w.T / ((gm + pm) * 1e-3), 1), "gdn_ms": round(gm, 3),
+                       "polar_ms": round(pm, 3), "polar_mfma_frac": round(pf / (pm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "gdn_hbm_frac": round(gdn_bytes(w.B, w.T, w.gdn_H) / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del inp, g, p, o_g, ws_g, S_g, o_p
         torch.cuda.empty_cache()
-    # memory backward at the 2K layer shape (B=8, H=8, d=128, bf16 inputs, fp32 arithmetic)
-    w = workloads.WORKLOADS["layer_b8_t2k"]
-    g = workloads.make_workload(w, device="cuda")["gdn"]
-    do = torch.randn_like(g["v"])
-    ws_gb = torch.empty(int(atma.lib.atma_gdn_bwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D, 64, 1)),
-                        dtype=torch.uint8, device="cuda")
-    tgb = Timer(torch)
-    for it in range(6):
-        (tgb if it else (lambda fn: fn()))(lambda: atma.atma_gdn_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], do,
-                                                                     workspace=ws_gb))
-    torch.cuda.synchronize()
-    res["gdn_train_" + w.name] = {"bwd_ms": round(tgb.mean_ms(), 4),
-                                  "workspace_MB": round(ws_gb.numel() / 2 ** 20, 1)}
-    del g, do, ws_gb
-    torch.cuda.empty_cache()
-    # 64K prefill
-    w = workloads.WORKLOADS["prefill_b1_t64k"]
-    inp = workloads.make_workload(w, device="cuda")
-    g, p = inp["gdn"], inp["polar"]
-    o_g = torch.empty_like(g["v"])
-    ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
-                       device="cuda")
-    S_g = torch.empty(w.B, w.gdn_H, w.gdn_D, w.gdn_D, device="cuda")
-    o_p = torch.empty_like(p["q"])
-    tg, tp = Timer(torch), Timer(torch)
-    for it in range(4):
-        (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
-                                                                  o=o_g, final_state=S_g, workspace=ws_g))
-        (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
-    torch.cuda.synchronize()
-    gm, pm = tg.mean_ms(), tp.mean_ms()
-    pf = polar_flops(w.B, w.T, w.polar_Hq)
-    res[w.name] = {"tokens_per_s": round(w.B * w.T / ((gm + pm) * 1e-3), 1), "gdn_ms": round(gm, 3),
-                   "polar_ms": round(pm, 3), "polar_mfma_frac": round(pf / (pm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                   "gdn_hbm_frac": round(gdn_bytes(w.B, w.T, w.gdn_H) / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del inp, g, p, o_g, ws_g, S_g, o_p
-    torch.cuda.empty_cache()
-    # 256K prefill, once (one warm-up, one timed call of each)
-    w = workloads.WORKLOADS["prefill_b1_t256k"]
-    inp = workloads.make_workload(w, device="cuda")
-    g, p = inp["gdn"], inp["polar"]
-    o_g = torch.empty_like(g["v"])
-    ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
-                       device="cuda")
-    S_g = torch.empty(w.B, w.gdn_H, w.gdn_D, w.gdn_D, device="cuda")
-    o_p = torch.empty_like(p["q"])
-    tg, tp = Timer(torch), Timer(torch)
-    for it in range(2):
-        (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
-                                                                  o=o_g, final_state=S_g, workspace=ws_g))
-        (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
-    torch.cuda.synchronize()
-    gm, pm = tg.mean_ms(), tp.mean_ms()
-    pf = polar_flops(w.B, w.T, w.polar_Hq)
-    res[w.name] = {"tokens_per_s": round(w.B * w.T / ((gm + pm) * 1e-3), 1), "gdn_ms": round(gm, 3),
-                   "polar_ms": round(pm, 3), "polar_mfma_frac": round(pf / (pm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                   "gdn_hbm_frac": round(gdn_bytes(w.B, w.T, w.gdn_H) / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del inp, g, p, o_g, ws_g, S_g, o_p
-    torch.cuda.empty_cache()
-    # 256K decode, batch 1 and 16; two state / query buffers alternate so caches cannot serve them
-    L = workloads.DECODE_CONTEXT
-    for B in (1, 16):
-        d = workloads.make_decode_inputs(B, L, device="cuda")
-        ws = torch.empty(atma.atma_polar_attn_decode_workspace_bytes(B, 16, L), dtype=torch.uint8, device="cuda")
-        gd = d["gdn"]
-        states = [gd["state"].clone(), gd["state"].clone()]
-        qs = [d["q"], d["q"].clone()]
-        od = torch.empty_like(d["q"])
-        og = torch.empty(B, 8, 128, dtype=torch.bfloat16, device="cuda")
-        tpd, tgd = Timer(torch), Timer(torch)
-        for it in range(23):
-            i = it & 1
-            fp = lambda: atma.atma_polar_attn_decode(qs[i], d["k_cache"], d["v_cache"], L, d["params"], o=od,
-                                                     workspace=ws)
-            fg = lambda: atma.atma_gdn_decode_step(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], states[i],
-                                                   o=og)
-            if it < 3:
-                fp(), fg()
-            else:
-                tpd(fp)
-                tgd(fg)
+    if want("prefill_256k"):
+        # 256K prefill, once (one warm-up, one timed call of each)
+        w = workloads.WORKLOADS["prefill_b1_t256k"]
+        inp = workloads.make_workload(w, device="cuda")
+        g, p = inp["gdn"], inp["polar"]
+        o_g = torch.empty_like(g["v"])
+        ws_g = torch.empty(atma.atma_gdn_fwd_workspace_bytes(w.B, w.T, w.gdn_H, w.gdn_D, w.gdn_D), dtype=torch.uint8,
+                           device="cuda")
+        S_g = torch.empty(w.B, w.gdn_H, w.gdn_D, w.gdn_D, device="cuda")
+        o_p = torch.empty_like(p["q"])
+        tg, tp = Timer(torch), Timer(torch)
+        for it in range(2):
+            (tg if it else (lambda f: f()))(lambda: atma.atma_gdn_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"],
+                                                                      o=o_g, final_state=S_g, workspace=ws_g))
+            (tp if it else (lambda f: f()))(lambda: atma.atma_polar_attn_fwd(p["q"], p["k"], p["v"], p["params"], o=o_p))
         torch.cuda.synchronize()
-        pm, gm = tpd.mean_ms(), tgd.mean_ms()
-        byts = decode_bytes(B, L)
-        res[f"decode_262k_b{B}"] = {"tokens_per_s": round(B / ((pm + gm) * 1e-3), 1), "polar_us": round(pm * 1e3, 1),
-                                    "gdn_us": round(gm * 1e3, 1),
-                                    "hbm_frac": round(byts / ((pm + gm) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        del d, ws, states, qs, od, og
+        gm, pm = tg.mean_ms(), tp.mean_ms()
+        pf = polar_flops(w.B, w.T, w.polar_Hq)
+        res[w.name] = {"tokens_per_s": round(w.B * w.T / ((gm + pm) * 1e-3), 1), "gdn_ms": round(gm, 3),
+                       "polar_ms": round(pm, 3), "polar_mfma_frac": round(pf / (pm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "gdn_hbm_frac": round(gdn_bytes(w.B, w.T, w.gdn_H) / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del inp, g, p, o_g, ws_g, S_g, o_p
         torch.cuda.empty_cache()
+    if want("decode"):
+        # 256K decode, batch 1 and 16; two state / query buffers alternate so caches cannot serve them
+        L = workloads.DECODE_CONTEXT
+        for B in (1, 16):
+            d = workloads.make_decode_inputs(B, L, device="cuda")
+            ws = torch.empty(atma.atma_polar_attn_decode_workspace_bytes(B, 16, L), dtype=torch.uint8, device="cuda")
+            gd = d["gdn"]
+            states = [gd["state"].clone(), gd["state"].clone()]
+            qs = [d["q"], d["q"].clone()]
+            od = torch.empty_like(d["q"])
+            og = torch.empty(B, 8, 128, dtype=torch.bfloat16, device="cuda")
+            tpd, tgd = Timer(torch), Timer(torch)
+            for it in range(23):
+                i = it & 1
+                fp = lambda: atma.atma_polar_attn_decode(qs[i], d["k_cache"], d["v_cache"], L, d["params"], o=od,
+                                                         workspace=ws)
+                fg = lambda: atma.atma_gdn_decode_step(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], states[i],
+                                                       o=og)
+                if it < 3:
+                    fp(), fg()
+                else:
+                    tpd(fp)
+                    tgd(fg)
+            torch.cuda.synchronize()
+            pm, gm = tpd.mean_ms(), tgd.mean_ms()
+            # the same step with the memory step on a second stream (default priority), overlapping
+            # the Polar decode: the step's time is then the longer of the two
+            side, main_s = torch.cuda.Stream(), torch.cuda.current_stream()
+            t2 = Timer(torch)
+            for it in range(23):
+                i = it & 1
+
+                def step2():
+                    side.wait_stream(main_s)
+                    atma.atma_gdn_decode_step(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], states[i], o=og,
+                                              stream=side)
+                    atma.atma_polar_attn_decode(qs[i], d["k_cache"], d["v_cache"], L, d["params"], o=od, workspace=ws)
+                    main_s.wait_stream(side)
+
+                (t2 if it >= 3 else (lambda f: f()))(step2)
+            torch.cuda.synchronize()
+            sm = t2.mean_ms()
+            byts = decode_bytes(B, L)
+            res[f"decode_262k_b{B}"] = {"tokens_per_s": round(B / ((pm + gm) * 1e-3), 1), "polar_us": round(pm * 1e3, 1),
+                                        "gdn_us": round(gm * 1e3, 1),
+                                        "hbm_frac": round(byts / ((pm + gm) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                        "two_streams": {"step_us": round(sm * 1e3, 1),
+                                                        "tokens_per_s": round(B / (sm * 1e-3), 1),
+                                                        "hbm_frac": round(byts / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+            del d, ws, states, qs, od, og
+            torch.cuda.empty_cache()
     return res
 
 
