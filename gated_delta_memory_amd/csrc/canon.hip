@@ -5,7 +5,8 @@
 // unit-norm queries and keys).  One thread per (run of TR = 8 tokens, 8-channel chunk): it slides
 // down its run with the K-1 previous inputs in registers, so every input row is read once (plus
 // a K-1 row halo per run), with 16-byte loads along the channel axis; fp32 weights and
-// accumulation, bf16 output.  The chunks of a run are consecutive lanes, so a head's norm is a
+// accumulation, bf16 output.  The run's rows are loaded and y is stored non-temporally (each is
+// touched once), so the L2 keeps the K-1 halo rows the next run re-reads.  The chunks of a run are consecutive lanes, so a head's norm is a
 // reduction over D / 8 adjacent lanes, all at the same token.
 // A second kernel then writes the new state (the last K-1 inputs); one thread owns all K-1
 // slots of its channels, so the state may be updated in place.
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(NT) void canon_kernel(const bf16* __restrict__ x, c
 #pragma unroll
     for (int i = 0; i < TR; ++i) {
         raw[i] = u32x4{0u, 0u, 0u, 0u};
-        if (t0 + i < T) raw[i] = *(const u32x4*)(x + ((size_t)b * T + t0 + i) * C + 8 * ch);
+        if (t0 + i < T) raw[i] = __builtin_nontemporal_load((const u32x4*)(x + ((size_t)b * T + t0 + i) * C + 8 * ch));
     }
 #pragma unroll
     for (int i = 0; i < TR; ++i) {
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(NT) void canon_kernel(const bf16* __restrict__ x, c
                 const bf16x2 pr = {(bf16)acc[2 * x2], (bf16)acc[2 * x2 + 1]};
                 out[x2] = __builtin_bit_cast(unsigned, pr);
             }
-            *(u32x4*)(y + ((size_t)b * T + t) * C + 8 * ch) = out;
+            __builtin_nontemporal_store(out, (u32x4*)(y + ((size_t)b * T + t) * C + 8 * ch));
         }
 #pragma unroll
         for (int j = K - 1; j >= 1; --j)

@@ -353,16 +353,21 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
 template <int D>
 constexpr int dkv_stage_bytes() { return 2 * BShape<D>::TILE + NREC * BB * 4; }  // Q tile | dS tile | row scalars [5][64]
 
+// Workgroup wg of nwg runs on XCD wg % 8; renumber so that every XCD receives a contiguous range
+// of work items (the tiles of one (batch, kv head) then share an XCD's L2).
+__device__ __forceinline__ int xcd_item(int wg, int nwg) {
+    const int per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
+    return xcd * per + min(xcd, extra) + (wg >> 3);
+}
+
 template <int D, int MODE>
-__device__ __forceinline__ void dkv_body(int wg, int nwg, char* g_st0, char* g_st1, const bf16* __restrict__ q,
+__device__ __forceinline__ void dkv_body(int item, char* g_st0, char* g_st1, const bf16* __restrict__ q,
                                          const bf16* __restrict__ k, const bf16* __restrict__ v,
                                          const bf16* __restrict__ dsg, const float* __restrict__ rec,
                                          bf16* __restrict__ dk, bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
     using SH = BShape<D>;
     constexpr int NKS = SH::NKS, NDT = SH::NDT, ROWB = SH::ROWB;
     const int nkt = (T + BKT - 1) / BKT;
-    const int per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
-    const int item = xcd * per + min(xcd, extra) + (wg >> 3);
     const int bk = item / nkt;
     const int j = item - bk * nkt;  // key tile; tile 0 streams the most query blocks and goes first
     const int hk = bk % Hkv, b = bk / Hkv;
@@ -500,10 +505,12 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void polar_bwd_dkv(const bf16*
                                                        bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
     __shared__ __align__(16) char g_st0[dkv_stage_bytes<D>()];
     __shared__ __align__(16) char g_st1[dkv_stage_bytes<D>()];
-    dkv_body<D, 0>((int)blockIdx.x, (int)gridDim.x, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
+    dkv_body<D, 0>(xcd_item((int)blockIdx.x, (int)gridDim.x), g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq,
+                   Hkv);
 }
 
-// grid 2 nk: workgroups [0, nk) take the dV role, [nk, 2 nk) the dK role of the same key tiles
+// grid 2 nk: work item 2 j is the dV role of key tile j and item 2 j + 1 its dK role, so the
+// two roles of a tile (which stream the same query blocks) sit side by side on one XCD
 template <int D>
 __global__ __launch_bounds__(NT, 2) void polar_bwd_dkv_split(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, const bf16* __restrict__ dsg,
@@ -511,9 +518,9 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dkv_split(const bf16* __restr
                                                              bf16* __restrict__ dv, int T, int Tp, int Hq, int Hkv) {
     __shared__ __align__(16) char g_st0[dkv_stage_bytes<D>()];
     __shared__ __align__(16) char g_st1[dkv_stage_bytes<D>()];
-    const int nk = (int)gridDim.x / 2, wg = (int)blockIdx.x;
-    if (wg < nk) dkv_body<D, 1>(wg, nk, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
-    else dkv_body<D, 2>(wg - nk, nk, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
+    const int it = xcd_item((int)blockIdx.x, (int)gridDim.x);
+    if ((it & 1) == 0) dkv_body<D, 1>(it >> 1, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
+    else dkv_body<D, 2>(it >> 1, g_st0, g_st1, q, k, v, dsg, rec, dk, dv, T, Tp, Hq, Hkv);
 }
 
 // ---------------------------------------------------------------------------------------------

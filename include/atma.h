@@ -46,7 +46,7 @@ typedef enum {
     ATMA_OK = 0,
     ATMA_ERR_NULL = -1,        /* a required pointer is NULL                                  */
     ATMA_ERR_SHAPE = -2,       /* a size is < 1, inconsistent, or too large                   */
-    ATMA_ERR_UNSUPPORTED = -3, /* a head width, chunk or dtype this build has no kernel for   */
+    ATMA_ERR_UNSUPPORTED = -3, /* a head width, chunk or dtype the library has no kernel for  */
     ATMA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the matching *_workspace_bytes */
     ATMA_ERR_LAUNCH = -5       /* the HIP runtime reported an error after launch              */
 } atma_status;
@@ -177,7 +177,7 @@ int atma_gdn_decode_step(const void* q, const void* k, const void* v, const floa
  *   o        [B, T, Hq, D]  dtype `dt` (output)
  *   mu_out   [B, Hq, T] fp32 (output) or NULL;  meff_out [B, Hq, T] fp32 or NULL
  *   D in {64, 128} and dt == ATMA_BF16; workspace may be NULL when
- *   atma_polar_attn_workspace_bytes returns 0 (it does for this build).
+ *   atma_polar_attn_workspace_bytes returns 0 (it does in this version).
  * ------------------------------------------------------------------------------- */
 int atma_polar_attn_fwd(const void* q, const void* k, const void* v, const atma_polar_params* p,
                         void* o, float* mu_out, float* meff_out, int B, int T, int Hq, int Hkv, int D,
