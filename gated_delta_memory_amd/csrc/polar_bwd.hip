@@ -22,8 +22,8 @@
 // from its direction.  So Sigma = dR R + 2 dQ2 Q2 + ds . s is formed per row before any pass over
 // the keys.  The logit gradients of a row then sum to sum_j dl_ij + dl_0 = ds . (s' - s), s' the
 // value sum of the recomputed fp32 weights, where the forward's s took its weights rounded to
-// bf16: a residue of about 2^-9 |ds| |v| / sqrt(n_eff) per row, the size of the other bf16
-// roundings.  (Masses summed from the bf16-rounded weights would add (dR - Sigma)(R' - R), which
+// bf16: a residue of about u |ds| |v| / sqrt(n_eff) per row (u = 2^-8, the bf16 unit roundoff),
+// the size of the other bf16 roundings.  (Masses summed from the bf16-rounded weights would add (dR - Sigma)(R' - R), which
 // the large mass terms dR, growing with m_eff, would carry into dq_i = sum_j dl_ij k_j, a sum that
 // largely cancels.)
 //
@@ -117,7 +117,7 @@ struct Offsets {
 };
 
 // ---------------------------------------------------------------------------------------------
-// prep: one row (b, i, h) per CH = D / 8 lanes, 8 elements per lane; rows i of [T, Tp) are the
+// prep: one row (b, h, i) per CH = D / 8 lanes, 8 elements per lane; rows i of [T, Tp) are the
 // padding rows of the streamed query blocks.  Writes ds (bf16) and the row scalars the gradient
 // kernels read, {cq, lse2, t a / sqrt(D), t b / sqrt(D), t / sqrt(D)} in [B, Hq, 5, Tp], from the
 // training forward's statistics: its real mass R and squared mass Q2 are sums of the same fp32
@@ -131,14 +131,17 @@ __global__ __launch_bounds__(NT) void polar_bwd_prep(const bf16* __restrict__ dO
                                                      float* __restrict__ part, int B, int T, int Tp, int Hq) {
     using SH = BShape<D>;
     constexpr int CH = D / 8;
+    // rows in (batch, head, position) order, position fastest: the per-row scalars (read and
+    // written in [B, Hq, ...] layouts) are then contiguous across a workgroup, and every row of
+    // dO, the direction and ds is still whole cache lines
     const size_t gid = (size_t)blockIdx.x * NT + threadIdx.x;
     const int ci = (int)(gid % CH);
     const size_t rid = gid / CH;
-    const int h = (int)(rid % Hq);
-    const int i = (int)((rid / Hq) % Tp);
-    const int b = (int)(rid / ((size_t)Hq * Tp));
+    const int i = (int)(rid % Tp);
+    const size_t bh = rid / Tp;
+    const int h = (int)(bh % Hq);
+    const int b = (int)(bh / Hq);
     if (b >= B) return;
-    const size_t bh = (size_t)b * Hq + h;
     float* rr = rec + bh * NREC * Tp + i;
     if (i >= T) {  // padding row: zero weight (log partition +inf), zero gradient
         if (ci == 0) {
