@@ -740,28 +740,24 @@ __global__ __launch_bounds__(NT) void gdn_seg_scan(Regions rg, const float* init
 // =========================================================================================
 // output
 // =========================================================================================
-// The output kernel forms QG = diag(e^g) Q and P = lower_incl((Q K^T) o E) itself from the
+// The output kernel forms P = lower_incl((Q K^T) o E) and QG = diag(e^{g}) Q itself from the
 // bf16 inputs (its MFMA operands in fp16, fragment-major in LDS), then
-// O = QG S_in^T + P Delta with the S_in^T and Delta fragments the carry wrote.
+// O = QG S_in^T + P Delta with the S_in^T and Delta fragments the carry wrote.  The K tile's
+// space takes QG once P is built, and the Q tile's space takes the output staging once QG is
+// built, so three workgroups fit a CU.
 template <int DK, int DV>
 struct OutSmem {
     static constexpr int LDQ = DK + 8, LDO = DV + 8;
-    static constexpr int QK_BYTES = 2 * C * LDQ * 2;
-    static constexpr int OS_BYTES = C * LDO * 2;
-    union {
-        struct {
-            bf16 Qs[C * LDQ];
-            bf16 Ks[C * LDQ];
-        } in;
-        bf16 Os[C * LDO];  // output staging, once QG and P are built
-    } u;
-    char qg[C * DK * 2];  // QG, fragment-major fp16
-    char pm[C * C * 2];   // P, fragment-major fp16
+    static constexpr int A_BYTES = C * LDQ * 2 > C * LDO * 2 ? C * LDQ * 2 : C * LDO * 2;
+    static constexpr int B_BYTES = C * LDQ * 2 > C * DK * 2 ? C * LDQ * 2 : C * DK * 2;
+    __align__(16) char ra[A_BYTES];  // Q tile (bf16, row stride LDQ), then the output staging (LDO)
+    __align__(16) char rb[B_BYTES];  // K tile (bf16, row stride LDQ), then QG (fragment-major fp16)
+    __align__(16) char pm[C * C * 2];  // P, fragment-major fp16
     float Gs[C];
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, const bf16* __restrict__ k, Regions rg,
+__global__ __launch_bounds__(NT, 3) void gdn_out_h(const bf16* __restrict__ q, const bf16* __restrict__ k, Regions rg,
                                                    bf16* __restrict__ o, int Tmax, int H, const int* __restrict__ cu,
                                                    int total) {
     using L = Lay<DK, DV>;
@@ -778,27 +774,37 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id()), G = lane >> 4, l16 = lane & 15;
     const size_t cid = ((size_t)b * H + h) * NC + c;
     const size_t tok0 = (seq0 + t0) * H + h;
+    // this wave's S_in^T and Delta fragments (n-tiles nt = w + 4 m of 16 state rows: carry slice
+    // nt / 4, wave nt % 4), requested with the tiles so their trip to memory overlaps P and QG
+    constexpr int NTW = DV / 64;
+    Frag<half> sf[NTW][DK / 32], df[NTW][2];
+    {
+        const char* sfc = rg.sf + cid * L::SF;
+        const char* dfc = rg.df + cid * L::DF;
+#pragma unroll
+        for (int m = 0; m < NTW; ++m) {
+            const int sl = m, wp = w;
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                sf[m][kb].v = __builtin_nontemporal_load(
+                    (const f16x8*)(sfc + (size_t)sl * (DK / 32) * 4096 + ((kb * 4 + wp) * 64 + lane) * 16));
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                df[m][kb].v = __builtin_nontemporal_load(
+                    (const f16x8*)(dfc + (size_t)sl * 2 * 4096 + ((kb * 4 + wp) * 64 + lane) * 16));
+        }
+    }
     {
         TileRegs<bf16, C, DK> qr, kr;
         qr.template load<true>(q + tok0 * DK, (size_t)H * DK, n);
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
         if (threadIdx.x < C) sm.Gs[threadIdx.x] = ((const float*)(rg.rb + cid * L::RB))[threadIdx.x];
-        qr.template store<LDQ>(sm.u.in.Qs);
-        kr.template store<LDQ>(sm.u.in.Ks);
+        qr.template store<LDQ>((bf16*)sm.ra);
+        kr.template store<LDQ>((bf16*)sm.rb);
     }
     __syncthreads();
-    // QG = diag(e^g) Q
-#pragma unroll
-    for (int id = threadIdx.x; id < C * DK / 8; id += NT) {
-        const int r = id / (DK / 8), cc = id % (DK / 8);
-        const float e = __expf(sm.Gs[r]);
-        const bf16x8 x = *(const bf16x8*)&sm.u.in.Qs[r * LDQ + 8 * cc];
-        f16x8 y;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) y[t] = (half)((float)x[t] * e);
-        *(f16x4*)(sm.qg + fm_off<DK>(r, 8 * cc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
-        *(f16x4*)(sm.qg + fm_off<DK>(r, 8 * cc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
-    }
+    const bf16* Qs = (const bf16*)sm.ra;
+    const bf16* Ks = (const bf16*)sm.rb;
     // P tiles (i, j): the ten on or below the diagonal from Q K^T, the six above it zero
     for (int ti = w; ti < 16; ti += 4) {
         int i, j;
@@ -817,8 +823,8 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
             Frag<bf16> a[DK / 32], bk[DK / 32];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                load_frag_rows(bk[kb], sm.u.in.Ks, LDQ, 16 * j + l16, 32 * kb);
-                load_frag_rows(a[kb], sm.u.in.Qs, LDQ, 16 * i + l16, 32 * kb);
+                load_frag_rows(bk[kb], Ks, LDQ, 16 * j + l16, 32 * kb);
+                load_frag_rows(a[kb], Qs, LDQ, 16 * i + l16, 32 * kb);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -832,21 +838,25 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
             *(half*)(sm.pm + fm_off<C>(r, s2)) = (half)((s2 <= r) ? e * qk[x] : 0.0f);
         }
     }
-    __syncthreads();  // QG and P ready; the input tiles are dead and the output staging reuses them
-    const char* sQ = sm.qg;
+    __syncthreads();  // P ready; the K tile is dead and QG takes its place
+    // QG = diag(e^g) Q
+#pragma unroll
+    for (int id = threadIdx.x; id < C * DK / 8; id += NT) {
+        const int r = id / (DK / 8), cc = id % (DK / 8);
+        const float e = __expf(sm.Gs[r]);
+        const bf16x8 x = *(const bf16x8*)&Qs[r * LDQ + 8 * cc];
+        f16x8 y;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) y[t] = (half)((float)x[t] * e);
+        *(f16x4*)(sm.rb + fm_off<DK>(r, 8 * cc)) = __builtin_shufflevector(y, y, 0, 1, 2, 3);
+        *(f16x4*)(sm.rb + fm_off<DK>(r, 8 * cc + 4)) = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+    }
+    __syncthreads();  // QG ready; the Q tile is dead and the output staging takes its place
+    const char* sQ = sm.rb;
     const char* sP = sm.pm;
-    const char* sfc = rg.sf + cid * L::SF;
-    const char* dfc = rg.df + cid * L::DF;
-    // n-tiles of 16 state rows: carry slice sl, wave w' -> n-tile 4 sl + w'
 #pragma unroll
-    for (int nt = w; nt < DV / 16; nt += 4) {
-        const int sl = nt >> 2, wp = nt & 3;
-        Frag<half> sf[DK / 32], df[2];
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb)
-            sf[kb].v = __builtin_nontemporal_load((const f16x8*)(sfc + (size_t)sl * (DK / 32) * 4096 + ((kb * 4 + wp) * 64 + lane) * 16));
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) df[kb].v = __builtin_nontemporal_load((const f16x8*)(dfc + (size_t)sl * 2 * 4096 + ((kb * 4 + wp) * 64 + lane) * 16));
+    for (int m = 0; m < NTW; ++m) {
+        const int nt = 4 * m + w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x4 acc = {0, 0, 0, 0};
@@ -854,23 +864,23 @@ __global__ __launch_bounds__(NT, 2) void gdn_out_h(const bf16* __restrict__ q, c
             for (int kb = 0; kb < DK / 32; ++kb) {
                 Frag<half> a;
                 a.v = fm_frag<DK>(sQ, i, kb);
-                mma(acc, a, sf[kb]);
+                mma(acc, a, sf[m][kb]);
             }
 #pragma unroll
             for (int kb = 0; kb < (i < 2 ? 1 : 2); ++kb) {
                 Frag<half> a;
                 a.v = fm_frag<C>(sP, i, kb);
-                mma(acc, a, df[kb]);
+                mma(acc, a, df[m][kb]);
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) sm.u.Os[(16 * i + 4 * G + x) * LDO + 16 * nt + l16] = (bf16)acc[x];
+            for (int x = 0; x < 4; ++x) ((bf16*)sm.ra)[(16 * i + 4 * G + x) * LDO + 16 * nt + l16] = (bf16)acc[x];
         }
     }
     __syncthreads();
     for (int id = threadIdx.x; id < C * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cc = id % (DV / 8);
         if (r < n)
-            __builtin_nontemporal_store(*(const u32x4*)&sm.u.Os[r * LDO + 8 * cc],
+            __builtin_nontemporal_store(*(const u32x4*)((const bf16*)sm.ra + r * LDO + 8 * cc),
                                         (u32x4*)(o + ((seq0 + t0 + r) * H + h) * DV + 8 * cc));
     }
 }
