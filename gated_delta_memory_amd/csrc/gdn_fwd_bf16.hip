@@ -435,16 +435,20 @@ __shared__ __align__(16) char g_stage0[kStageMax];
 __shared__ __align__(16) char g_stage1[kStageMax];
 __shared__ __align__(16) char g_stage2[kStageMax];
 
-template <int DK, int DV, bool STORE>
+// NW waves per workgroup (4, or 2 for grids too small to fill the GPU: 16 NW state rows per
+// workgroup either way one 16-row band per wave); wave w of the workgroup is wave wq of the
+// 64-row record slice sl (U slices, S_in^T and Delta fragments are laid out per 64 rows).
+template <int DK, int DV, bool STORE, int NW>
 struct Carry {
     using L = Lay<DK, DV>;
-    static constexpr int RBK = L::RBK, NKT = DK / 16;
+    static constexpr int RBK = L::RBK, NKT = DK / 16, NTC = 64 * NW;
     static constexpr int NCH = (int)L::STAGE / 16;  // 16-byte copies per chunk
-    static constexpr int TPT = NCH / NT;             // tile copies per thread per chunk
+    static constexpr int TPT = NCH / NTC;            // tile copies per thread per chunk
     static constexpr int DPT = TPT + 1;              // all copies per thread per chunk (+ e^{g_last})
     static constexpr int SPT = STORE ? DK / 32 + 2 : 0;  // fragment stores per thread per chunk
     static_assert(L::STAGE + 1024 <= kStageMax, "stage too large");
-    static_assert(NCH % NT == 0, "stage must be a whole number of copy rounds");
+    static_assert(NCH % NTC == 0, "stage must be a whole number of copy rounds");
+    static_assert(DPT + SPT < 64, "vmcnt range");
 
     const char* ra0;   // this (batch, head)'s first chunk record
     char* sf0;
@@ -452,6 +456,7 @@ struct Carry {
     const float* egl;
     int sl;       // U slice copied with each chunk
     float ukeep;  // 1 for real state rows, 0 for the identity rows of a segment summary
+    int wq;       // this wave within the 64-row slice
 
     // Starts the copy of chunk c into `dst`.  The chunk's e^{g_last} is copied into the
     // stage too (every lane copies the same word, so all threads issue the same operations)
@@ -466,16 +471,16 @@ struct Carry {
         gdn::lds_dma4((const void*)(egl + c), 0u, gdn::lds_addr(dst) + (unsigned)(L::STAGE + w * 256));
 #pragma unroll
         for (int m = 0; m < TPT; ++m) {
-            const unsigned ch = (unsigned)(m * NT) + threadIdx.x;
+            const unsigned ch = (unsigned)(m * NTC) + threadIdx.x;
             const unsigned off = ch * 16 < (unsigned)L::A_U
                                      ? ch * 16
                                      : (unsigned)(L::A_U + sl * L::USLICE) + (ch * 16 - (unsigned)L::A_U);
-            gdn::lds_dma16((const void*)src, off, lds + (unsigned)(m * NT * 16));
+            gdn::lds_dma16((const void*)src, off, lds + (unsigned)(m * NTC * 16));
         }
     }
 
     __device__ __forceinline__ void step(int c, const char* sW, f32x4* st) const {
-        const int lane = lane_id(), w = wave_id();
+        const int lane = lane_id(), w = wq;
         const char* sK = sW + L::A_KDT;
         const char* sU = sW + L::A_U;
         // All LDS operands of the chunk are requested in two batches ahead of their MFMAs
@@ -558,12 +563,12 @@ struct Carry {
 // fragments for the output kernel and, in the last segment, the final state.
 // !STORE (segment summary): (Dv + Dk) / 64 slices; real rows start from zero, the Dk extra
 // rows start from the identity with U ignored; the end state goes to the summary region.
-template <int DK, int DV, bool STORE>
-__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
+template <int DK, int DV, bool STORE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
     Regions rg, const float* init_state, float* final_state, int Tmax, int H, int nseg, int seglen,
     const int* __restrict__ cu, int total) {
     using L = Lay<DK, DV>;
-    using K = Carry<DK, DV, STORE>;
+    using K = Carry<DK, DV, STORE, NW>;
     constexpr int NKT = DK / 16;
     // slices of one (b, h, segment) on one XCD (workgroup i runs on XCD i % 8)
     const int nsl = (int)gridDim.x, nwg = nsl * (int)gridDim.y * (int)gridDim.z;
@@ -572,7 +577,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     const int item = xcd * per + min(xcd, extra) + (wgi >> 3);
     const int sl = item % nsl, yy = (item / nsl) % (int)gridDim.y, b = item / (nsl * (int)gridDim.y);
     const int h = yy / nseg, sg = yy % nseg;
-    const int lane = lane_id(), w = wave_id(), G = lane >> 4, l16 = lane & 15;
+    const int lane = lane_id(), G = lane >> 4, l16 = lane & 15;
+    const int wq = (sl % (4 / NW)) * NW + wave_id();  // wave within the 64-row slice
+    const int sl64 = sl / (4 / NW);                     // 64-row slice
     size_t seq0;
     int Tlen;
     if (!gdn::seq_bounds(cu, b, Tmax, total, seq0, Tlen)) return;
@@ -581,10 +588,10 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     const int cb = sg * seglen, n = min(NC - cb, seglen);  // this segment's chunks (<= 0: none)
     const size_t bh = (size_t)b * H + h;
     const size_t c0 = bh * NCs + cb;
-    const bool real = sl < DV / 64;
-    const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, real ? sl : 0,
-              real ? 1.0f : 0.0f};
-    const int row = sl * 64 + 16 * w + l16;  // state row held by this lane's accumulators
+    const bool real = sl64 < DV / 64;
+    const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, real ? sl64 : 0,
+              real ? 1.0f : 0.0f, wq};
+    const int row = sl64 * 64 + 16 * wq + l16;  // state row held by this lane's accumulators
 
     f32x4 st[NKT];  // st[t][x] = S[row][16 t + 4 G + x]
     if constexpr (STORE) {
@@ -903,14 +910,26 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gdn_prep_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), prep_smem, stream, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, rg, a.T, a.H, a.cu, a.total);
+    // Carry workgroups hold 64 state rows with four waves, or 32 rows with two when four-wave
+    // workgroups would leave more than half of the 256 CUs idle (one workgroup per CU: the LDS
+    // stages fill it), so that the carry's LDS reads are spread over twice the CUs.
+    const long long units = (long long)a.H * nseg * a.B;
     if (nseg > 1) {
-        hipLaunchKernelGGL((gdn_carry_h<DK, DV, false>), dim3((DV + DK) / 64, a.H * nseg, a.B), dim3(NT), 0, stream,
-                           rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
+        if (units * ((DV + DK) / 64) * 2 <= 256)
+            hipLaunchKernelGGL((gdn_carry_h<DK, DV, false, 2>), dim3((DV + DK) / 32, a.H * nseg, a.B), dim3(128), 0,
+                               stream, rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
+        else
+            hipLaunchKernelGGL((gdn_carry_h<DK, DV, false, 4>), dim3((DV + DK) / 64, a.H * nseg, a.B), dim3(NT), 0,
+                               stream, rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
         hipLaunchKernelGGL((gdn_seg_scan<DK, DV>), dim3(DV / 16, a.H, a.B), dim3(NT), scan_smem, stream, rg,
                            a.init_state, a.H, nseg);
     }
-    hipLaunchKernelGGL((gdn_carry_h<DK, DV, true>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream, rg,
-                       a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
+    if (units * (DV / 64) * 2 <= 256)
+        hipLaunchKernelGGL((gdn_carry_h<DK, DV, true, 2>), dim3(DV / 32, a.H * nseg, a.B), dim3(128), 0, stream, rg,
+                           a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
+    else
+        hipLaunchKernelGGL((gdn_carry_h<DK, DV, true, 4>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream, rg,
+                           a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
     hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, (const bf16*)a.q,
                        (const bf16*)a.k, rg, (bf16*)a.o, a.T, a.H, a.cu, a.total);
     return hipGetLastError();
