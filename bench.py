@@ -67,7 +67,7 @@ MEASURED_TRAFFIC = {
     # layer_b8_t2k: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch (profiles/polar_fwd_layer_b8_t2k.txt)
     "polar_fwd_kernel": {"sha": "1ab4ae80aae8fa5a", "bytes": 161005056},
     # layer_b8_t2k, prep + carry + out (one segment at this shape)
-    "atma_gdn_fwd (prep+carry+out)": {"sha": "1b9dd2ec90e1eba6", "bytes": 577296374},
+    "atma_gdn_fwd (prep+carry+out)": {"sha": "90b61ba8b0248e5f", "bytes": 577324085},
     # layer_b8_t2k backward: prep + both walks + pre + post (profiles/gdn_bwd_layer_b8_t2k.txt)
     "atma_gdn_bwd (all kernels)": {"sha": "a156336d3424ad46", "bytes": 3665200000},
 }
