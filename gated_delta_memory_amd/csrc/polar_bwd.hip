@@ -193,9 +193,12 @@ __global__ __launch_bounds__(NT) void polar_bwd_prep(const bf16* __restrict__ dO
     }
     *(bf16x8*)(dsg + e0) = dsb;
     if (ci != 0) return;
+    // t and nu exactly as the forward forms them (cq below is its cq; its null logit t nu).  The
+    // masses stay IEEE divisions: on null-dominated rows R^3 underflows and Q2 can be subnormal,
+    // where a hardware reciprocal (subnormals flushed) would turn 0 / Q2 into 0 * inf.
     const float n = (float)(i + 1);
     const float t = 1.0f + softplus(prm.temp_raw[h]) * logf(n);
-    const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * sqrtf(logf(n + 1.0f));
+    const float nu = prm.null_bias[h] + softplus(prm.null_slope_raw[h]) * __builtin_sqrtf(__logf(n + 1.0f));
     const float me = R * R * R / Q2;
     const float om = 1.0f - mu * mu;
     const float dme = dmu * om * prm.mag_beta[h] / (1.0f + me);
