@@ -193,7 +193,8 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
         voff[dt] = swz_v<D>(4 * G2 + (i16 >> 2), dcol >> 3) + ((dcol & 7) << 1);
     }
 
-  auto tile = [&](int qt) {
+  // `after`: key blocks this workgroup streams after this tile (its second tile, when paired)
+  auto tile = [&](int qt, int after) {
     const int q0 = qt * BQ;
     const int qw0 = q0 + w * QW;
     const int qi = qw0 + l32;  // this lane's query
@@ -300,10 +301,21 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
     // two-stage pipeline: the copy of block kb + 1 overlaps the computation of block kb.  The
     // loop is unrolled by two so each stage is a fixed LDS address and every fragment read
     // takes its offset as an immediate.
+    // Wave priority by the work the workgroup has left: a SIMD serves its co-resident waves
+    // unevenly, so equal work does not end at equal times; letting the waves with more blocks to go
+    // issue first makes the workgroups of a CU finish together (at the 2K layer ~7% sooner).
+    auto prio = [&](int kb) {
+        const int rem = nkb - kb + after;
+        if (rem > 24) __builtin_amdgcn_s_setprio(3);
+        else if (rem > 16) __builtin_amdgcn_s_setprio(2);
+        else if (rem > 8) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+    };
     issue(0, g_kv0);
     for (int kb = 0; kb < nkb; kb += 2) {
         wait_vmcnt<0>();
         lds_barrier();
+        prio(kb);
         if (kb + 1 < nkb) issue(kb + 1, g_kv1);
         block(kb, g_kv0);
         if (kb + 1 >= nkb) break;
@@ -401,10 +413,11 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
     }
   };
 
-    tile(nqt - 1 - pr);
-    if (paired && pr != nqt - 1 - pr) {
+    const int second = (paired && pr != nqt - 1 - pr) ? (min(T, pr * BQ + BQ) + BK - 1) / BK : 0;
+    tile(nqt - 1 - pr, second);
+    if (second) {
         lds_barrier();  // every wave is done with the stages before they are refilled
-        tile(pr);
+        tile(pr, 0);
     }
 }
 
