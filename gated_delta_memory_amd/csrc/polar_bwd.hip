@@ -91,6 +91,17 @@ __device__ __forceinline__ bf16x4 tr_read(const char* lds_base, int byte_off) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// Wave priority by the share of the largest workload a workgroup still has to stream (rem of maxw
+// blocks): a SIMD serves its co-resident waves unevenly, and letting the waves with more work to
+// go issue first makes co-resident workgroups finish together.
+__device__ __forceinline__ void prio_by_work(int rem, int maxw) {
+    const int l = 4 * rem / (maxw + 1);
+    if (l >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (l == 2) __builtin_amdgcn_s_setprio(2);
+    else if (l == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -312,10 +323,12 @@ __global__ __launch_bounds__(NT, 2) void polar_bwd_dq(const bf16* __restrict__ q
             }
     };
 
+    const int maxw = (T + BB - 1) / BB;  // key blocks of the heaviest query tile
     issue(0, g_kv0);
     for (int kb = 0; kb < nkb; kb += 2) {
         wait_vmcnt<0>();
         lds_barrier();
+        prio_by_work(nkb - kb, maxw);
         if (kb + 1 < nkb) issue(kb + 1, g_kv1);
         block(kb, g_kv0);
         if (kb + 1 >= nkb) break;
@@ -477,6 +490,7 @@ __device__ __forceinline__ void dkv_body(int item, char* g_st0, char* g_st1, con
     for (int it = 0; it < nit; it += 2) {
         wait_vmcnt<0>();
         lds_barrier();
+        prio_by_work(nit - it, G * nqb);  // the heaviest key tile streams G nqb query blocks
         if (it + 1 < nit) issue(it + 1, g_st1);
         block(it, g_st0);
         if (it + 1 >= nit) break;
