@@ -11,7 +11,8 @@
 //   gdn_prep_h  (parallel over chunks) - A, Tinv (fp32), W and U from an fp32-accurate
 //               hi/lo bf16 split of Tinv, and KD^T; writes them as fp16 tiles already in
 //               the carry's MFMA-fragment order, plus the chunk's g for the output kernel.
-//               It needs neither Q nor P, so its LDS (K, later V; A; Tinv) fits three
+//               It needs neither Q nor P, and A and Tinv share one 64 x 64 tile (A
+//               transposed above the diagonal, Tinv below), so its LDS fits four
 //               workgroups per CU.
 //   gdn_carry_h (one workgroup per 64 state rows of a (batch, head), walks the chunks)
 //               keeps S^T in fp32 MFMA accumulators; per chunk it only forms Delta and the
@@ -138,12 +139,17 @@ template <int DK, int DV>
 struct PrepSmem {
     static constexpr int LDK = (DK > DV ? DK : DV) + 8, LDX = LDK, LDA = C + 4;
     bf16 Ks[C * LDK];   // K, then V once W is formed
-    float Am[C * LDA];  // A, later the W staging tile
-    float Tm[C * LDA];  // P staging, then Tinv, then the U staging tile
+    // AT[r][c]: Tinv[r][c] for c <= r (its diagonal blocks in full, zeros above the diagonal
+    // included) and A[c][r] for c < r outside the diagonal blocks (A is strictly lower, so its
+    // transpose fits above the diagonal; A's diagonal blocks are read once, by the inverse of
+    // those blocks, before Tinv's overwrite them).  Later the W staging tile, then the U
+    // staging tile.
+    float AT[C * LDA];
     float Gs[C];  // g_r = sum_{s <= r} ln alpha_s
     float Bs[C];  // beta_r
     float Es[C];  // beta_r e^{g_r}
 };
+static_assert(sizeof(float) * 64 * 68 >= 64 * 128 * 2, "the staging tiles fit the A / Tinv tile");
 
 // B fragment (kmap order over the chunk positions) of a row-major bf16 LDS tile, columns
 // 16 ct .. 16 ct + 15, by two transpose reads.
@@ -160,7 +166,7 @@ __device__ __forceinline__ Frag<bf16> bfrag_tr(const bf16* tile, int ld, int ct,
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(NT, 4) void gdn_prep_h(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                     const bf16* __restrict__ v, const float* __restrict__ alpha,
                                                     const float* __restrict__ beta, Regions rg, int Tmax, int H,
                                                     const int* __restrict__ cu, int total) {
@@ -183,14 +189,12 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
     char* ra = rg.ra + cid * L::RA;
     char* rb = rg.rb + cid * L::RB;
 
-    // ---- A: K into LDS, cumulative log decay; V's load starts here and lands after W --------
-    // (the gates are requested right behind the tiles, so that all of them share one trip to memory)
-    TileRegs<bf16, C, DV> vr;
+    // ---- A: K into LDS, cumulative log decay ------------------------------------------------
+    // (the gates are requested right behind the tile, so that they share one trip to memory)
     float a_in = 1.0f, b_in = 0.0f;
     {
         TileRegs<bf16, C, DK> kr;
         kr.load(k + tok0 * DK, (size_t)H * DK, n);
-        vr.template load<true>(v + tok0 * DV, (size_t)H * DV, n);
         if (w == 0) {
             const size_t gi = tok0 + (size_t)min(lane, n - 1) * H;  // rows past n re-read row n-1, then discarded
             a_in = alpha[gi];
@@ -215,23 +219,17 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
     }
     __syncthreads();
 
-    // ---- B: A = strict_lower(diag(beta) (K K^T) o E) in fp32 ----------------------------------
-    for (int ti = w; ti < 16; ti += 4) {
-        int i, j;
-        if (ti < 10) {
-            i = (ti >= 6) ? 3 : (ti >= 3) ? 2 : (ti >= 1) ? 1 : 0;
-            j = ti - i * (i + 1) / 2;
-        } else {
-            const int u = ti - 10;  // the six strictly upper tiles
-            i = (u < 3) ? 0 : (u < 5) ? 1 : 2;
-            j = (u < 3) ? u + 1 : (u < 5) ? u - 1 : 3;
-        }
-        // gate values of this lane's rows r = 16 i + 4 G + x and column s = 16 j + l16
+    // ---- B: A = strict_lower(diag(beta) (K K^T) o E) in fp32, stored transposed --------------
+    // (the ten tiles on or below the diagonal; lane (G, l16) holds rows r = 16 i + 4 G + x of
+    // column s = 16 j + l16, which are consecutive in A^T)
+    for (int ti = w; ti < 10; ti += 4) {
+        const int i = (ti >= 6) ? 3 : (ti >= 3) ? 2 : (ti >= 1) ? 1 : 0;
+        const int j = ti - i * (i + 1) / 2;
         const f32x4 gr = *(const f32x4*)&sm.Gs[16 * i + 4 * G];
         const f32x4 br = *(const f32x4*)&sm.Bs[16 * i + 4 * G];
         const float gs = sm.Gs[16 * j + l16];
         f32x4 kk = {0, 0, 0, 0};
-        if (ti < 10) {
+        {
             // every fragment of the tile is requested before the first MFMA waits on one
             Frag<bf16> a[DK / 32], bk[DK / 32];
 #pragma unroll
@@ -244,14 +242,19 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
             for (int kb = 0; kb < DK / 32; ++kb) mma(kk, a[kb], bk[kb]);
         }
         const int s = 16 * j + l16;
+        f32x4 y;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * i + 4 * G + x;
             // g_r - g_s <= 0 wherever the mask keeps the entry (s < r)
             const float e = __expf(fminf(gr[x] - gs, 0.0f));
-            sm.Am[r * LDA + s] = (s < r) ? br[x] * e * kk[x] : 0.0f;
+            y[x] = (s < r) ? br[x] * e * kk[x] : 0.0f;
         }
+        *(f32x4*)&sm.AT[s * LDA + 16 * i + 4 * G] = y;
     }
+    // V's load starts here (after the A tiles' fragments are dead) and lands after W is formed
+    TileRegs<bf16, C, DV> vr;
+    vr.template load<true>(v + tok0 * DV, (size_t)H * DV, n);
 
     // ---- C: KD^T, straight to the records ----------------------------------------------------
     {
@@ -279,36 +282,30 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
 
     // ---- D: Tinv = (I + A)^{-1} -----------------------------------------------------------
     if (w == 0) {
-        // 16x16 diagonal blocks: lane (blk, col) solves column `col` of block `blk`
+        // 16x16 diagonal blocks: lane (blk, col) solves column `col` of block `blk` by forward
+        // substitution, a column of A at a time (a row of A^T: x[r] -= A[r][s] x[s], r > s, for
+        // s = 0, 1, ..., so every x[r] takes its terms in the order of s)
         const int blk = lane >> 4, col = l16, o = 16 * blk;
-        float a[16][16];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-#pragma unroll
-            for (int s4 = 0; s4 < 16; s4 += 4) {
-                if (s4 < r) {
-                    const f32x4 x = *(const f32x4*)&sm.Am[(o + r) * LDA + o + s4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) a[r][s4 + u] = x[u];
-                }
-            }
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == col) ? 1.0f : 0.0f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int s2 = 0; s2 < r; ++s2) acc -= a[r][s2] * x[s2];
-            x[r] = acc;
-        }
+        for (int s2 = 0; s2 < 15; ++s2) {
+            float acol[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Tm[(o + r) * LDA + o + col] = x[r];
-    } else {
-        for (int i = threadIdx.x - 64; i < 6 * 256; i += NT - 64) {
-            const int u = i >> 8, e = i & 255;
-            const int bi = (u < 3) ? 0 : (u < 5) ? 1 : 2;
-            const int bj = (u < 3) ? u + 1 : (u < 5) ? u - 1 : 3;
-            sm.Tm[(16 * bi + (e >> 4)) * LDA + 16 * bj + (e & 15)] = 0.0f;
+            for (int r4 = 0; r4 < 16; r4 += 4) {
+                if (r4 + 3 > s2) {
+                    const f32x4 v4 = *(const f32x4*)&sm.AT[(o + s2) * LDA + o + r4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acol[r4 + u] = v4[u];
+                }
+            }
+#pragma unroll
+            for (int r = s2 + 1; r < 16; ++r) x[r] -= acol[r] * x[s2];
         }
+        // the whole block, zeros above its diagonal included (after every read of the block)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.AT[(o + r) * LDA + o + col] = x[r];
     }
     __syncthreads();
     for (int d = 1; d < 4; ++d) {
@@ -318,19 +315,19 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
             for (int m = j; m < i; ++m) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float av = sm.Am[(16 * i + l16) * LDA + 16 * m + 4 * G + e];
-                    const float bv = sm.Tm[(16 * m + 4 * G + e) * LDA + 16 * j + l16];
+                    const float av = sm.AT[(16 * m + 4 * G + e) * LDA + 16 * i + l16];  // A[16 i + l16][16 m + 4 G + e]
+                    const float bv = sm.AT[(16 * m + 4 * G + e) * LDA + 16 * j + l16];  // Tinv, block (m, j), m >= j
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
                 }
             }
             f32x4 y = {0, 0, 0, 0};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float av = sm.Tm[(16 * i + l16) * LDA + 16 * i + 4 * G + e];
+                const float av = sm.AT[(16 * i + l16) * LDA + 16 * i + 4 * G + e];
                 y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, acc[e], y, 0, 0, 0);
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) sm.Tm[(16 * i + 4 * G + x) * LDA + 16 * j + l16] = -y[x];
+            for (int x = 0; x < 4; ++x) sm.AT[(16 * i + 4 * G + x) * LDA + 16 * j + l16] = -y[x];
         }
         __syncthreads();
     }
@@ -347,7 +344,8 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int s0 = 32 * kb + 16 * hh + 4 * G;
-                tv[hh] = *(const f32x4*)&sm.Tm[(16 * i + l16) * LDA + s0];
+                // blocks above the diagonal hold A: Tinv is zero there
+                tv[hh] = 2 * kb + hh > i ? f32x4{0, 0, 0, 0} : *(const f32x4*)&sm.AT[(16 * i + l16) * LDA + s0];
                 bv[hh] = *(const f32x4*)&sm.Bs[s0];
                 ev[hh] = *(const f32x4*)&sm.Es[s0];
             }
@@ -363,22 +361,24 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
                 ul[kb].set(e, tu - (float)hu);
             }
         }
-        __syncthreads();  // Tinv consumed: Am and Tm become staging tiles
-        char* wstage = (char*)sm.Am;
-        char* ustage = (char*)sm.Tm;
-        // B fragments are requested four column tiles at a time before their MFMAs (one LDS
-        // round trip per group, 32 registers of fragments)
+        __syncthreads();  // Tinv consumed: AT becomes the W staging tile, then the U staging tile
+        char* wstage = (char*)sm.AT;
+        char* ustage = (char*)sm.AT;
+        // B fragments are requested a group of column tiles at a time before their MFMAs (one
+        // LDS round trip per group): two tiles for W, while V's tile is in flight in registers,
+        // four for U
         Frag<bf16> bx[4][2];
+        constexpr int GW = 2;
 #pragma unroll
-        for (int c0 = 0; c0 < DK / 16; c0 += 4) {
+        for (int c0 = 0; c0 < DK / 16; c0 += GW) {
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+            for (int ct = 0; ct < GW; ++ct)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
                     if (kb < nkb) bx[ct][kb] = bfrag_tr(sm.Ks, LDK, c0 + ct, kb);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
+            for (int ct = 0; ct < GW; ++ct) {
                 f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
@@ -392,9 +392,10 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
                     *(half*)(wstage + fm_off<DK>(16 * i + 4 * G + x, 16 * (c0 + ct) + l16)) = (half)acc[x];
             }
         }
-        __syncthreads();  // every wave is done with K: V takes its place
+        __syncthreads();  // W staged, every wave is done with K: W goes out and V takes K's place
+        copy_out(ra + L::A_W, wstage, C * DK * 2);
         vr.template store<LDX>(sm.Ks);
-        __syncthreads();
+        __syncthreads();  // W has left the staging tile
 #pragma unroll
         for (int c0 = 0; c0 < DV / 16; c0 += 4) {
 #pragma unroll
@@ -420,7 +421,6 @@ __global__ __launch_bounds__(NT, 3) void gdn_prep_h(const bf16* __restrict__ q, 
             }
         }
         __syncthreads();
-        copy_out(ra + L::A_W, wstage, C * DK * 2);
         copy_out(ra + L::A_U, ustage, C * DV * 2);
     }
 }

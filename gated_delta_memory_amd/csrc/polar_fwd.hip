@@ -125,6 +125,10 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
     // Two K/V stages, one LDS object each (the copy into one stage overlaps the reads of the other).
     __shared__ __align__(16) char g_kv0[2 * SH::TILE];
     __shared__ __align__(16) char g_kv1[2 * SH::TILE];
+    // per-head constants of the finalisation: v_null[0..D), softplus(null slope), null bias,
+    // magnitude beta.  Read from LDS when a tile finalises: global loads there would expose a
+    // round trip to memory per tile (the loop leaves nothing to overlap them with).
+    __shared__ __align__(16) float g_par[D + 4];
     const int nqt_grid = (Tmax + BQ - 1) / BQ;
     const int per_bh = paired ? (nqt_grid + 1) / 2 : nqt_grid;
     const int nwg = (int)gridDim.x, wg = (int)blockIdx.x, per = nwg >> 3, extra = nwg & 7, xcd = wg & 7;
@@ -151,9 +155,6 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());  // wave-uniform
     const int l32 = lane & 31, G2 = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
     const float a_t = POLAR ? softplus(prm.temp_raw[h]) : 0.0f;
-    // per-head constants of the finalisation
-    const float s_nu = POLAR ? softplus(prm.null_slope_raw[h]) : 0.0f;
-    const float nbias = POLAR ? prm.null_bias[h] : 0.0f, mbeta = POLAR ? prm.mag_beta[h] : 0.0f;
     const size_t qstride = (size_t)Hq * D;
     const size_t kvstride = (size_t)Hkv * D;
     const unsigned rowbytes = (unsigned)(kvstride * 2);
@@ -193,14 +194,20 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
         voff[dt] = swz_v<D>(4 * G2 + (i16 >> 2), dcol >> 3) + ((dcol & 7) << 1);
     }
 
-  // `after`: key blocks this workgroup streams after this tile (its second tile, when paired)
-  auto tile = [&](int qt, int after) {
+  // `after`: key blocks this workgroup streams after this tile (its second tile, when paired);
+  // `first`: the workgroup's first tile (it fills g_par)
+  auto tile = [&](int qt, int after, bool first) {
     const int q0 = qt * BQ;
     const int qw0 = q0 + w * QW;
     const int qi = qw0 + l32;  // this lane's query
     const float cq = POLAR ? (1.0f + a_t * logf((float)(qi + 1))) * kLog2e * SH::kInvSqrtD  // t_i log2(e) / sqrt(D)
                            : kLog2e * SH::kInvSqrtD;
 
+    // the finalisation constants are requested with the tile's first loads (stored after them)
+    float pv = 0.0f;
+    const int tp = (int)threadIdx.x;
+    if (POLAR && first && tp < D + 3)
+        pv = tp < D ? prm.v_null[h * D + tp] : tp == D ? prm.null_slope_raw[h] : tp == D + 1 ? prm.null_bias[h] : prm.mag_beta[h];
     // Q^T fragments (B operand): lane supplies Q[qi][16 ks + 8 G2 + e]
     bf16x8 qf[NKS];
     {
@@ -315,6 +322,10 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
         else __builtin_amdgcn_s_setprio(0);
     };
     issue(0, g_kv0);
+    if (POLAR && first) {  // visible to every wave after the loop's first barrier
+        __builtin_amdgcn_sched_barrier(0);
+        if (tp < D + 3) g_par[tp] = tp == D ? softplus(pv) : pv;
+    }
     for (int kb = 0; kb < nkb; kb += 2) {
         wait_vmcnt<0>();
         lds_barrier();
@@ -349,6 +360,7 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
     const float Q2 = pair_sum((q2sum[0] + q2sum[1]) + (q2sum[2] + q2sum[3]));
     // the row scalars with the hardware's log, exp, square root and reciprocal (errors of a few
     // fp32 ulps, far below the bf16 output's rounding; the IEEE library forms cost ~3% at 2K)
+    const float s_nu = g_par[D], nbias = g_par[D + 1], mbeta = g_par[D + 2];
     const float n = (float)(qi + 1);
     const float t = 1.0f + a_t * __logf(n);
     const float nu = nbias + s_nu * __builtin_sqrtf(__logf(n + 1.0f));
@@ -368,11 +380,14 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-            const int d = 32 * dt + 8 * (x >> 2) + 4 * G2 + (x & 3);
-            const float sv = (oacc[dt][x] * f + pn * prm.v_null[h * D + d]) * invZ;
-            oacc[dt][x] = sv;
-            nrm2 += sv * sv;
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 vn = *(const f32x4*)&g_par[32 * dt + 8 * g + 4 * G2];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float sv = (oacc[dt][4 * g + x] * f + pn * vn[x]) * invZ;
+                oacc[dt][4 * g + x] = sv;
+                nrm2 += sv * sv;
+            }
         }
     nrm2 = pair_sum(nrm2);
     const float scale = mu * __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(nrm2), prm.eps));
@@ -417,10 +432,10 @@ __global__ __launch_bounds__(NT, Shape<D>::OCC) void polar_fwd_kernel(const bf16
   };
 
     const int second = (paired && pr != nqt - 1 - pr) ? (min(T, pr * BQ + BQ) + BK - 1) / BK : 0;
-    tile(nqt - 1 - pr, second);
+    tile(nqt - 1 - pr, second, true);
     if (second) {
         lds_barrier();  // every wave is done with the stages before they are refilled
-        tile(pr, 0);
+        tile(pr, 0, false);
     }
 }
 
