@@ -180,6 +180,33 @@ __device__ __forceinline__ f32x4 rowdot(const f32x4 (&acc)[1][CT], int rt0, F f)
     return part;
 }
 
+// The values f(r, c) that rowdot or an epilogue pairs with this lane's accumulator elements of a
+// product with one 16-row tile per wave (M = 64, so wave w owns row tile w), requested before the
+// product so that their trip to memory overlaps its MFMAs: pre[y][v] = f(16 w + 4 (lane / 16) + v,
+// 16 y + lane % 16).
+template <int CT, class F>
+__device__ __forceinline__ void prefetch_rows(f32x4 (&pre)[CT], F f) {
+    const int lane = (int)threadIdx.x & 63, G = lane >> 4, c16 = lane & 15, rt0 = (int)threadIdx.x >> 6;
+#pragma unroll
+    for (int y = 0; y < CT; ++y)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pre[y][v] = f(16 * rt0 + 4 * G + v, 16 * y + c16);
+}
+// rowdot with the factors already in registers (the same sums in the same order).
+template <int CT>
+__device__ __forceinline__ f32x4 rowdot_pre(const f32x4 (&acc)[1][CT], const f32x4 (&pre)[CT]) {
+    f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int y = 0; y < CT; ++y)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[v] = fmaf(acc[0][y][v], pre[y][v], part[v]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[v] += __shfl_xor(part[v], o, 16);
+    return part;
+}
+
 constexpr size_t STAGE_FLOATS = (size_t)KS * (128 + 16) * 2;  // sA + sB for the largest shapes (M, N <= 128)
 
 // Per-chunk fp32 workspace arrays, chunk id cid = (b H + h) NC + c.
@@ -659,6 +686,9 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
 #pragma unroll
             for (int v = 0; v < 4; ++v) rowv[slot][16 * rt0 + G4 + v] = part[v];
     };
+    // the k elements of X2_r . k_r and X4_r . k_r, in flight during the first products
+    f32x4 kpre[DK / 16];
+    prefetch_rows(kpre, kel);
     // X1 = dW = -dDelta S_in
     tgemm<C, DK, DV, true, true>(stage, [&](int r, int i) { return ld4(rec + L::DDL + (size_t)r * DV + i); },
                                  [&](int i, int d) { return ld4(Sin + (size_t)i * DK + d); },
@@ -670,7 +700,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                          each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
                                              rec[L::X2 + (size_t)r * DK + d] = x;
                                          });
-                                         put_rows(5, rt0, rowdot(acc, rt0, kel));
+                                         put_rows(5, rt0, rowdot_pre(acc, kpre));
                                      });
     // Q K^T and K K^T (raw), dP = lower_incl(dO Delta^T)
     tgemm<2 * C, C, DK, true, false>(stage, [&](int r, int d) { return r < C ? qrow4(r, d) : krow4(r - C, d); },
@@ -681,6 +711,9 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                      });
     tgemm<C, C, DV, true, false>(stage, orow4, [&](int j, int s) { return ld4(rec + L::DL + (size_t)s * DV + j); },
                                  [&](int r, int s, float x) { dP[r * LN + s] = s <= r ? x : 0.0f; });
+    // the v elements of X3_r . v_r, in flight during dTinv
+    f32x4 vpre[DV / 16];
+    prefetch_rows(vpre, vel);
     // dTinv = dDelta (diag(beta) V)^T + dW (diag(beta e^g) K)^T
     tgemm<C, C, DV + DK, true, false>(
         stage,
@@ -696,7 +729,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                          each_elem(acc, rt0, ct0, [&](int r, int j, float x) {
                                              if (r < n) dv[(size_t)r * vs + j + tok0 * DV] = from_f32<T>(bs[r] * x);
                                          });
-                                         put_rows(3, rt0, rowdot(acc, rt0, vel));
+                                         put_rows(3, rt0, rowdot_pre(acc, vpre));
                                      });
     // X4 = Tinv^T dW (kept for dk), and X4_r . k_r
     tgemm_blk<C, DK, C, false, true>(stage, [&](int r, int s) { return ld4(Tm + s * LD64 + r); },
@@ -705,8 +738,11 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                          each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
                                              rec[L::X4 + (size_t)r * DK + d] = x;
                                          });
-                                         put_rows(4, rt0, rowdot(acc, rt0, kel));
+                                         put_rows(4, rt0, rowdot_pre(acc, kpre));
                                      });
+    // the q elements of dq_r . q_r, in flight from here to the dq product
+    f32x4 qpre[DK / 16];
+    prefetch_rows(qpre, qel);
     // Z = dTinv Tinv^T, then dA = -strict_lower(Tinv^T Z) (into dT)
     tgemm<C, C, C, true, false>(stage, [&](int r, int s) { return ld4(dT + r * LN + s); },
                                 [&](int s, int c2) { return ld4(Tm + c2 * LD64 + s); },
@@ -723,12 +759,18 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     {
         const int sc = tid & (C - 1), w0 = tid >> 6;
         float col = 0.f;
+        float kkv[C / 4], qkv[C / 4];  // every workspace value of the loop, requested before it starts
+#pragma unroll
+        for (int m = 0; m < C / 4; ++m) {
+            kkv[m] = KK[(w0 + 4 * m) * LD64 + sc];
+            qkv[m] = QK[(w0 + 4 * m) * LD64 + sc];
+        }
 #pragma unroll 4
         for (int m = 0; m < C / 4; ++m) {
             const int r = w0 + 4 * m;
             const float e = sc <= r ? fast_exp2(g2[r] - g2[sc]) : 0.0f;  // never exp of the upper triangle
-            const float dA = dT[r * LN + sc], kk = KK[r * LD64 + sc];
-            const float pP = sc <= r ? QK[r * LD64 + sc] * e : 0.0f;
+            const float dA = dT[r * LN + sc], kk = kkv[m];
+            const float pP = sc <= r ? qkv[m] * e : 0.0f;
             const float dae = dA * e * kk;
             col += fmaf(dae, bs[r], dP[r * LN + sc] * pP);
             const float r2 = wave_sum(dae);
@@ -748,6 +790,11 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         Zm[r * LN + s] = dT[r * LN + s] * bs[r] * e;
     }
     __syncthreads();
+    // X4 and dKD for dk's epilogue (the elements this lane itself stored: the same row and column
+    // tiles), in flight during the dq product
+    f32x4 x4pre[DK / 16], x2pre[DK / 16];
+    prefetch_rows(x4pre, [&](int r, int d) { return rec[L::X4 + (size_t)r * DK + d]; });
+    prefetch_rows(x2pre, [&](int r, int d) { return rec[L::X2 + (size_t)r * DK + d]; });
     // dq = e^g o dQG + (dP o E) K = [diag(e^g) dO | dP o E] [S_in; K]  (dQG = dO S_in), and dq_r . q_r
     tgemm_blk<C, DK, DV + C, true, true>(
         stage, [&](int r, int kk) { return kk < DV ? eg[r] * orow4(r, kk) : ld4(dP + r * LN + kk - DV); },
@@ -756,22 +803,29 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
             each_elem(acc, rt0, ct0, [&](int r, int d, float x) {
                 if (r < n) dq[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(x);
             });
-            put_rows(0, rt0, rowdot(acc, rt0, qel));
+            put_rows(0, rt0, rowdot_pre(acc, qpre));
         });
     // dk = beta e^g o X4 + e^{g_last - g} o dKD + [(dP o E)^T | M | M^T] [Q; K; K]
     const float glast = gs[n - 1];
-    tgemm<C, DK, 3 * C, false, true>(stage,
+    tgemm_blk<C, DK, 3 * C, false, true>(stage,
         [&](int r, int kk) {
             return kk < C       ? ld4(dP + kk * LN + r)
                    : kk < 2 * C ? gather4([&](int u) { return Zm[(r + u) * LN + kk - C]; })
                                 : ld4(Zm + (kk - 2 * C) * LN + r);
         },
         [&](int kk, int d) { return kk < C ? qrow4(kk, d) : krow4(kk % C, d); },
-        [&](int r, int d, float x) {
-            if (r < n) {
-                const float y = bsg[r] * rec[L::X4 + (size_t)r * DK + d] + ekd[r] * rec[L::X2 + (size_t)r * DK + d] + x;
-                dk[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(y);
-            }
+        [&](const auto& acc, int rt0, int ct0) {
+            constexpr int CTK = DK / 16;
+#pragma unroll
+            for (int y = 0; y < CTK; ++y)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * rt0 + G4 + v, d = 16 * (ct0 + y) + c16;
+                    if (r < n) {
+                        const float val = bsg[r] * x4pre[y][v] + ekd[r] * x2pre[y][v] + acc[0][y][v];
+                        dk[tok0 * DK + (size_t)r * ks + d] = from_f32<T>(val);
+                    }
+                }
         });
     __syncthreads();  // every row sum is in place
     // dbeta_r = sum_s dA_rs E_rs k_r.k_s + X3_r . v_r + e^{g_r} X4_r . k_r
@@ -785,18 +839,22 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
         red[2 * C + r] = kd;
     }
     __syncthreads();
-    if (tid == 0) {
-        float kdsum = 0.f, dss = 0.f;
-        for (int r = 0; r < C; ++r) kdsum += red[2 * C + r];
-        for (int i = 0; i < DV / RW; ++i) dss += rec[L::DSS + i];  // <dS_out, S_in> by row slice (reverse walk)
-        red[C + n - 1] += kdsum + expf(glast) * dss;
-        // d ln(alpha_s) = sum_{r >= s} dg_r, over the real rows
-        float run = 0.f;
-        for (int s = n - 1; s >= 0; --s) {
-            run += red[C + s];
-            const size_t t = ((size_t)P.b * Tlen + P.t0 + s) * H + P.h;
-            dalpha[t] = run / alpha[t];
-            dbeta[t] = red[s];
+    if (tid < C) {  // wave 0, lane = row
+        const int r = tid;
+        const float kdsum = wave_sum(red[2 * C + r]);
+        const float dss = wave_sum(r < DV / RW ? rec[L::DSS + r] : 0.0f);  // <dS_out, S_in> by row slice (reverse walk)
+        float x = r < n ? red[C + r] : 0.0f;
+        if (r == n - 1) x += kdsum + expf(glast) * dss;
+        // d ln(alpha_s) = sum_{r >= s} dg_r over the real rows: a suffix scan across the wave
+#pragma unroll
+        for (int o = 1; o < C; o <<= 1) {
+            const float y = __shfl_down(x, o, 64);
+            if (r + o < C) x += y;
+        }
+        if (r < n) {
+            const size_t t = ((size_t)P.b * Tlen + P.t0 + r) * H + P.h;
+            dalpha[t] = x / alpha[t];
+            dbeta[t] = red[r];
         }
     }
 }
