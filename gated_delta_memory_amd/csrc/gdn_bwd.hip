@@ -616,10 +616,12 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *oc = dO + tok0 * DV;
-    auto qrow4 = [&](int r, int d) { return r < n ? ld4(qc + (size_t)r * ks + d) : kZero4; };
-    auto orow4 = [&](int r, int j) { return r < n ? ld4(oc + (size_t)r * vs + j) : kZero4; };
+    // rows past n read row n - 1 and are zeroed after the load: no branch around the load, so the
+    // loads of a product's K slice are all in flight together
+    auto qrow4 = [&](int r, int d) { const f32x4 x = ld4(qc + (size_t)min(r, n - 1) * ks + d); return r < n ? x : kZero4; };
+    auto orow4 = [&](int r, int j) { const f32x4 x = ld4(oc + (size_t)min(r, n - 1) * vs + j); return r < n ? x : kZero4; };
     tgemm<C, C, DK, true, false>(stage, qrow4,
-                                 [&](int d, int s) { return s < n ? ld4(kc + (size_t)s * ks + d) : kZero4; },
+                                 [&](int d, int s) { const f32x4 x = ld4(kc + (size_t)min(s, n - 1) * ks + d); return s < n ? x : kZero4; },
                                  [&](int r, int s, float x) {
                                      Pm[r * LD64 + s] = s <= r ? x * fast_exp2(g2[r] - g2[s]) : 0.0f;
                                  });
@@ -667,16 +669,18 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
     __syncthreads();
     const size_t tok0 = ((size_t)P.b * Tlen + P.t0) * H + P.h, ks = (size_t)H * DK, vs = (size_t)H * DV;
     const T *qc = q + tok0 * DK, *kc = k + tok0 * DK, *vc = v + tok0 * DV, *oc = dO + tok0 * DV;
-    auto qrow4 = [&](int r, int d) { return r < n ? ld4(qc + (size_t)r * ks + d) : kZero4; };
-    auto krow4 = [&](int r, int d) { return r < n ? ld4(kc + (size_t)r * ks + d) : kZero4; };
-    auto vrow4 = [&](int r, int j) { return r < n ? ld4(vc + (size_t)r * vs + j) : kZero4; };
-    auto orow4 = [&](int r, int j) { return r < n ? ld4(oc + (size_t)r * vs + j) : kZero4; };
+    // rows past n read row n - 1 and are zeroed after the load: no branch around the load, so the
+    // loads of a product's K slice (and of a prefetch) are all in flight together
+    auto qrow4 = [&](int r, int d) { const f32x4 x = ld4(qc + (size_t)min(r, n - 1) * ks + d); return r < n ? x : kZero4; };
+    auto krow4 = [&](int r, int d) { const f32x4 x = ld4(kc + (size_t)min(r, n - 1) * ks + d); return r < n ? x : kZero4; };
+    auto vrow4 = [&](int r, int j) { const f32x4 x = ld4(vc + (size_t)min(r, n - 1) * vs + j); return r < n ? x : kZero4; };
+    auto orow4 = [&](int r, int j) { const f32x4 x = ld4(oc + (size_t)min(r, n - 1) * vs + j); return r < n ? x : kZero4; };
     const float* Sin = rec + L::SIN;
     const float* dSo = rec + L::DSO;
     // element loaders for the per-row dot products (rows past n read as zero)
-    auto qel = [&](int r, int d) { return r < n ? to_f32(qc[(size_t)r * ks + d]) : 0.0f; };
-    auto kel = [&](int r, int d) { return r < n ? to_f32(kc[(size_t)r * ks + d]) : 0.0f; };
-    auto vel = [&](int r, int j) { return r < n ? to_f32(vc[(size_t)r * vs + j]) : 0.0f; };
+    auto qel = [&](int r, int d) { const float x = to_f32(qc[(size_t)min(r, n - 1) * ks + d]); return r < n ? x : 0.0f; };
+    auto kel = [&](int r, int d) { const float x = to_f32(kc[(size_t)min(r, n - 1) * ks + d]); return r < n ? x : 0.0f; };
+    auto vel = [&](int r, int j) { const float x = to_f32(vc[(size_t)min(r, n - 1) * vs + j]); return r < n ? x : 0.0f; };
     // Per-row sums, each formed in the epilogue of the product that makes its left factor (so no
     // product is read back for them): rowv[0] = dq_r . q_r, [1] = colsum over the n x n terms,
     // [2] = sum_s dA_rs E_rs k_r . k_s, [3] = X3_r . v_r, [4] = X4_r . k_r, [5] = X2_r . k_r.
