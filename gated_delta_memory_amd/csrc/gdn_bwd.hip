@@ -20,9 +20,9 @@
 //            (+ sum_r dKD_r . KD_r + e^{g_last} <dS_out, S_in> on the last row of the chunk)
 //     d ln(alpha_s) = sum_{r >= s} dg_r within the chunk;  dalpha = d ln(alpha) / alpha.
 // Five kernels, all fp32 arithmetic (inputs bf16 or fp32, converted on load):
-//   prep   (parallel over chunks)  g, A, Tinv (forward substitution), W, U, KD
+//   prep   (parallel over chunks)  g, A, Tinv (forward substitution), W, U, KD; raw K K^T
 //   walk   (sequential over chunks, one workgroup per 32 state rows)  S_in and Delta per chunk
-//   pre    (parallel over chunks)  P^T dO and dO^T QG
+//   pre    (parallel over chunks)  P^T dO and dO^T QG; raw Q K^T
 //   walk   (sequential, reverse)   dS_out and dDelta per chunk, the gradient on the initial state
 //   post   (parallel over chunks)  every gradient above
 // Matrix products use one LDS-staged fp32 routine on v_mfma_f32_16x16x4_f32 (K in slices of 16).  Rows past the end of a ragged last chunk are zero (k = q = v = 0,
@@ -320,10 +320,11 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_prep(const T* __restrict__ k, c
     }
     __syncthreads();
     auto krow4 = [&](int r, int d) { return ld4(Kt + r * LDK + d); };
-    // A = strict_lower(diag(beta) (K K^T) o E)
+    // A = strict_lower(diag(beta) (K K^T) o E); the raw K K^T also goes to the workspace for post
     tgemm<C, C, DK, true, false>(stage, krow4, [&](int d, int s) { return krow4(s, d); },
                                  [&](int r, int s, float x) {
                                      Am[r * LT + s] = s < r ? bs[r] * fast_exp2(g2[r] - g2[s]) * x : 0.0f;
+                                     rec[L::NKK + r * C + s] = x;
                                  });
     __syncthreads();
     // Tinv = (I + A)^{-1} (unit lower triangular) in 16 x 16 blocks.  Diagonal blocks: forward
@@ -624,6 +625,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_pre(const T* __restrict__ q, const
                                  [&](int d, int s) { const f32x4 x = ld4(kc + (size_t)min(s, n - 1) * ks + d); return s < n ? x : kZero4; },
                                  [&](int r, int s, float x) {
                                      Pm[r * LD64 + s] = s <= r ? x * fast_exp2(g2[r] - g2[s]) : 0.0f;
+                                     rec[L::NQK + r * C + s] = x;  // raw Q K^T, for post
                                  });
     __syncthreads();
     tgemm<C, DV, C, false, true>(stage,
@@ -706,13 +708,7 @@ __global__ __launch_bounds__(NT, 2) void gdn_bwd_post(const T* __restrict__ q, c
                                          });
                                          put_rows(5, rt0, rowdot_pre(acc, kpre));
                                      });
-    // Q K^T and K K^T (raw), dP = lower_incl(dO Delta^T)
-    tgemm<2 * C, C, DK, true, false>(stage, [&](int r, int d) { return r < C ? qrow4(r, d) : krow4(r - C, d); },
-                                     [&](int d, int s) { return krow4(s, d); },
-                                     [&](int r, int s, float x) {
-                                         if (r < C) QK[r * LD64 + s] = x;
-                                         else KK[(r - C) * LD64 + s] = x;
-                                     });
+    // dP = lower_incl(dO Delta^T) (the raw Q K^T and K K^T are in the workspace, from pre and prep)
     tgemm<C, C, DV, true, false>(stage, orow4, [&](int j, int s) { return ld4(rec + L::DL + (size_t)s * DV + j); },
                                  [&](int r, int s, float x) { dP[r * LN + s] = s <= r ? x : 0.0f; });
     // the v elements of X3_r . v_r, in flight during dTinv
