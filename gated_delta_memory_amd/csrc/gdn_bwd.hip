@@ -415,7 +415,7 @@ constexpr int RW = 32;
 constexpr int NTW = 512, NWW = NTW / 64;  // threads and waves of a walk workgroup (two waves per SIMD)
 
 template <int DK, int DV, bool BACK>
-__global__ __launch_bounds__(NTW) void gdn_bwd_walk(const float* __restrict__ s0, float* __restrict__ sfinal,
+__global__ __launch_bounds__(NTW) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_bwd_walk(const float* __restrict__ s0, float* __restrict__ sfinal,
                                                    float* __restrict__ ws, int H, int NC) {
     using L = WsLay<DK, DV>;
     constexpr int LA = DK + 4, LB = DK + 16, LS = DK + 4, LX = RW + 16;
@@ -533,19 +533,33 @@ __global__ __launch_bounds__(NTW) void gdn_bwd_walk(const float* __restrict__ s0
         }
         // X[r][i] += SG1 * sum_d A[r][d] St[i][d]: wave w owns the 16 x 16 tile (rows 16 (w % 4),
         // columns 16 (w / 4)); the next chunk's operands are requested a part at a time between the
-        // k ranges
+        // k ranges.  Lane group G takes the quarter d in [G DK / 4, (G + 1) DK / 4) (MFMA step t
+        // sums d = G DK / 4 + t over the four groups), so every lane reads its A row and its S^T
+        // column as runs of four (16-byte LDS reads), and four accumulators (steps t mod 4) split
+        // the chain of dependent MFMAs.
         static_assert(C / 16 * (RW / 16) == NWW, "one tile per wave");
         {
             const int rt = w % (C / 16), yt = w / (C / 16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            constexpr int KQ = DK / 4;
+            static_assert(KQ % (4 * NP) == 0, "steps per part");
+            f32x4 acc4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const float* arow = As + (16 * rt + c16) * LA + G * KQ;
+            const float* srow = St + (16 * yt + c16) * LS + G * KQ;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 if (it + 1 < NC) fetch_part(BACK ? c - 1 : c + 1, p);
 #pragma unroll
-                for (int k = p * (DK / NP); k < (p + 1) * (DK / NP); k += 4)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(16 * rt + c16) * LA + k + G],
-                                                               St[(16 * yt + c16) * LS + k + G], acc, 0, 0, 0);
+                for (int t = p * (KQ / NP); t < (p + 1) * (KQ / NP); t += 4) {
+                    const f32x4 a4 = *(const f32x4*)(arow + t), s4 = *(const f32x4*)(srow + t);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc4[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[u], s4[u], acc4[u], 0, 0, 0);
+                }
             }
+            f32x4 acc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = (acc4[0][v] + acc4[1][v]) + (acc4[2][v] + acc4[3][v]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * rt + 4 * G + v, i = 16 * yt + c16;
@@ -569,22 +583,40 @@ __global__ __launch_bounds__(NTW) void gdn_bwd_walk(const float* __restrict__ s0
         {
             constexpr int DT = DK / 16 / (NWW / (RW / 16));  // column tiles per wave
             const int yt = w % (RW / 16), d0 = (w / (RW / 16)) * DT;
-            f32x4 acc[DT];
+            // the two halves of the chunk accumulate separately (twice the independent MFMA chains)
+            f32x4 acc[2][DT];
 #pragma unroll
-            for (int x = 0; x < DT; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int k = 0; k < C; k += 4) {
-                const float a = Xs[(k + G) * LX + 16 * yt + c16];
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int x = 0; x < DT; ++x)
-                    acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[(k + G) * LB + 16 * (d0 + x) + c16], acc[x], 0, 0, 0);
+                for (int x = 0; x < DT; ++x) acc[hf][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // operands of four k steps are read before their MFMAs (one LDS round trip per group)
+#pragma unroll
+            for (int k0 = 0; k0 < C / 2; k0 += 16) {
+                float a[2][4], b[2][4][DT];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int kk = k0 + 4 * j + hf * (C / 2);
+                        a[hf][j] = Xs[(kk + G) * LX + 16 * yt + c16];
+#pragma unroll
+                        for (int x = 0; x < DT; ++x) b[hf][j][x] = Bs[(kk + G) * LB + 16 * (d0 + x) + c16];
+                    }
+                __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its MFMAs
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int x = 0; x < DT; ++x)
+                            acc[hf][x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[hf][j], b[hf][j][x], acc[hf][x], 0, 0, 0);
             }
 #pragma unroll
             for (int x = 0; x < DT; ++x)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int i = 16 * yt + 4 * G + v, d = 16 * (d0 + x) + c16;
-                    St[i * LS + d] += SG2 * acc[x][v];
+                    St[i * LS + d] += SG2 * (acc[0][x][v] + acc[1][x][v]);
                 }
         }
     }
