@@ -452,6 +452,21 @@ __device__ __forceinline__ void dkv_body(int item, char* g_st0, char* g_st1, con
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 const int ql = 32 * qt + 16 * st + 4 * G2;  // queries ql + (e & 3) + 8 (e >> 2)
+                // the transposed dS and Q fragments of this step are requested before the weights
+                // are formed, so their LDS latency overlaps the exponentials
+                bf16x8 sfr[NDT], qfr[NDT];
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const int base = (32 * qt + 16 * st) * ROWB;
+                    if constexpr (MODE != 2) {
+                        const bf16x4 slo = tr_read(Ss, base + of.tlo[dt]), shi = tr_read(Ss, base + of.thi[dt]);
+                        sfr[dt] = __builtin_shufflevector(slo, shi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                    if constexpr (MODE != 1) {
+                        const bf16x4 qlo = tr_read(Qs, base + of.tlo[dt]), qhi = tr_read(Qs, base + of.thi[dt]);
+                        qfr[dt] = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                }
                 f32x4 rc[2], rl[2], ra[2], rb[2], rt[2];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
@@ -472,15 +487,8 @@ __device__ __forceinline__ void dkv_body(int item, char* g_st0, char* g_st1, con
                 }
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const int base = (32 * qt + 16 * st) * ROWB;
-                    if constexpr (MODE != 2) {
-                        const bf16x4 slo = tr_read(Ss, base + of.tlo[dt]), shi = tr_read(Ss, base + of.thi[dt]);
-                        dva[dt] = mfma32(__builtin_shufflevector(slo, shi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dva[dt]);
-                    }
-                    if constexpr (MODE != 1) {
-                        const bf16x4 qlo = tr_read(Qs, base + of.tlo[dt]), qhi = tr_read(Qs, base + of.thi[dt]);
-                        dka[dt] = mfma32(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), lf, dka[dt]);
-                    }
+                    if constexpr (MODE != 2) dva[dt] = mfma32(sfr[dt], pf, dva[dt]);
+                    if constexpr (MODE != 1) dka[dt] = mfma32(qfr[dt], lf, dka[dt]);
                 }
             }
         }
