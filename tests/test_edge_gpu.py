@@ -143,3 +143,12 @@ def test_gdn_values_near_fp16_staging_limit(atma):
     init = torch.randn(2, 2, 128, 128, generator=torch.Generator().manual_seed(510)) * 4096
     assert float(inp["v"].float().abs().max()) > 2 ** 14
     _gdn(atma, inp, "bf16", init, "v x 2^12")
+
+
+def test_binding_buffers_are_guarded(atma):
+    """The GPU tests' fixture hands the binding guarded, poisoned buffers (checked after each test)."""
+    inp = workloads.make_gdn_inputs(1, 70, 1, 64, 64, seed=9)
+    o, fs = atma.atma_gdn_fwd(*[inp[x].cuda() for x in ("q", "k", "v", "alpha", "beta")])
+    torch.cuda.synchronize()
+    assert len(atma.torch.guarded) >= 3  # o, the final state and the workspace
+    assert torch.isfinite(o.float()).all() and torch.isfinite(fs).all()
