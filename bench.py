@@ -65,11 +65,11 @@ def decode_bytes(B, L, Hkv=16, D=64, H=8, Dg=128):
 # counters were taken, so an edited kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # layer_b8_t2k: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch (profiles/polar_fwd_layer_b8_t2k.txt)
-    "polar_fwd_kernel": {"sha": "e5540cc82bc0cca1", "bytes": 185661989},
+    "polar_fwd_kernel": {"sha": "e5540cc82bc0cca1", "bytes": 185649366},
     # layer_b8_t2k, prep + carry + out (one segment at this shape)
-    "atma_gdn_fwd (prep+carry+out)": {"sha": "2901dc79a147defe", "bytes": 577335760},
+    "atma_gdn_fwd (prep+carry+out)": {"sha": "2901dc79a147defe", "bytes": 577338486},
     # layer_b8_t2k backward: prep + both walks + pre + post (profiles/gdn_bwd_layer_b8_t2k.txt)
-    "atma_gdn_bwd (all kernels)": {"sha": "435838d3e9475fec", "bytes": 3548965872},
+    "atma_gdn_bwd (all kernels)": {"sha": "435838d3e9475fec", "bytes": 3556505114},
 }
 
 
