@@ -80,6 +80,20 @@ def test_polar_layer_b8_t2k(atma):
     _check_prefill(atma, inp, rows=sample_rows(2048), tag="layer_b8_t2k")
 
 
+def test_polar_layer_b8_t2k_output_only(atma):
+    """The layer call without the optional mu / m_eff outputs (the form a layer step uses): the
+    same o, bit for bit, as the call that also writes them, and every element written."""
+    inp = workloads.make_workload("layer_b8_t2k")["polar"]
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    p = _dev_params(inp["params"])
+    o1, mu1, me1 = atma.atma_polar_attn_fwd(q, k, v, p)
+    o2, _, _ = atma.atma_polar_attn_fwd(q, k, v, p, want_mu=True)
+    torch.cuda.synchronize()
+    assert mu1 is None and me1 is None
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(o1, o2)
+
+
 def test_polar_prefill_b2_t16k_needle(atma):
     w = workloads.WORKLOADS["prefill_b2_t16k_needle"]
     inp = workloads.make_polar_inputs(w.B, w.T, w.polar_Hq, w.polar_Hkv, w.polar_D, needle_frac=w.needle_frac,
