@@ -28,7 +28,7 @@
 // largely cancels.)
 //
 // Kernels (one call = five launches):
-//   prep    one row per D/8 lanes: ds (bf16) and the row scalars {cq, lse2, t a / sqrt(D),
+//   prep    ds one row per D/8 lanes, then one row per lane: ds (bf16) and the row scalars {cq, lse2, t a / sqrt(D),
 //           t b / sqrt(D), t / sqrt(D)} laid out [B, Hq, 5, Tp] (Tp = T rounded up to 64; padding
 //           rows get a log partition of +inf so their weights are exactly zero), and the per-row
 //           parameter partials;
@@ -128,8 +128,9 @@ struct Offsets {
 };
 
 // ---------------------------------------------------------------------------------------------
-// prep: one row (b, h, i) per CH = D / 8 lanes, 8 elements per lane; rows i of [T, Tp) are the
-// padding rows of the streamed query blocks.  Writes ds (bf16) and the row scalars the gradient
+// prep: ds of one row (b, h, i) per CH = D / 8 lanes, 8 elements per lane, then the row scalars of
+// one row per lane; rows i of [T, Tp) are the padding rows of the streamed query blocks.  Writes
+// ds (bf16) and the row scalars the gradient
 // kernels read, {cq, lse2, t a / sqrt(D), t b / sqrt(D), t / sqrt(D)} in [B, Hq, 5, Tp], from the
 // training forward's statistics: its real mass R and squared mass Q2 are sums of the same fp32
 // weights the gradient kernels recompute from the same operands, and its direction gives the value
@@ -141,69 +142,83 @@ __global__ __launch_bounds__(NT) void polar_bwd_prep(const bf16* __restrict__ dO
                                                      PolarParamsDev prm, bf16* __restrict__ dsg, float* __restrict__ rec,
                                                      float* __restrict__ part, int B, int T, int Tp, int Hq) {
     using SH = BShape<D>;
-    constexpr int CH = D / 8;
-    // rows in (batch, head, position) order, position fastest: the per-row scalars (read and
-    // written in [B, Hq, ...] layouts) are then contiguous across a workgroup, and every row of
-    // dO, the direction and ds is still whole cache lines
-    const size_t gid = (size_t)blockIdx.x * NT + threadIdx.x;
-    const int ci = (int)(gid % CH);
-    const size_t rid = gid / CH;
-    const int i = (int)(rid % Tp);
-    const size_t bh = rid / Tp;
+    constexpr int CH = D / 8, NG = 64 / CH;
+    // A wave takes 64 consecutive positions of one (batch, head) (Tp is a multiple of 64): in step
+    // `it` each group of CH lanes forms ds for position i0 + NG it + g, and lane ci == it keeps
+    // that row's three sums; afterwards every lane finishes the row scalars of its own position
+    // i0 + NG ci + g, so the scalar tail runs on all 64 lanes instead of one lane per row, and the
+    // scalars of the wave's 64 positions are read and written as whole runs.
+    const size_t gw = ((size_t)blockIdx.x * NT + threadIdx.x) >> 6;
+    const size_t rid0 = gw * 64;
+    const size_t bh = rid0 / Tp;
+    if (bh >= (size_t)B * Hq) return;
+    const int i0 = (int)(rid0 - bh * Tp);
     const int h = (int)(bh % Hq);
     const int b = (int)(bh / Hq);
-    if (b >= B) return;
-    float* rr = rec + bh * NREC * Tp + i;
-    if (i >= T) {  // padding row: zero weight (log partition +inf), zero gradient
-        if (ci == 0) {
-            rr[0] = 1.0f;
-            rr[(size_t)Tp] = INFINITY;
-            rr[(size_t)2 * Tp] = 0.0f;
-            rr[(size_t)3 * Tp] = 0.0f;
-            rr[(size_t)4 * Tp] = 0.0f;
-        }
-        return;
-    }
-    const size_t e0 = (((size_t)b * T + i) * Hq + h) * D + ci * 8;
-    const bf16x8 gb = *(const bf16x8*)(dO + e0);
-    const f32x4 c0 = *(const f32x4*)(dir + e0), c1 = *(const f32x4*)(dir + e0 + 4);
+    const int lane = lane_id(), g = lane / CH, ci = lane % CH;
     const f32x4 vn0 = *(const f32x4*)(prm.v_null + (size_t)h * D + ci * 8);
     const f32x4 vn1 = *(const f32x4*)(prm.v_null + (size_t)h * D + ci * 8 + 4);
-    float g[8], c[8], vn[8];
+    float kdmu = 0.f, kdsv = 0.f, kdsc = 0.f;  // the sums of row i0 + NG ci + g
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        g[e] = (float)gb[e]; g[e + 4] = (float)gb[e + 4];
-        c[e] = c0[e]; c[e + 4] = c1[e];
-        vn[e] = vn0[e]; vn[e + 4] = vn1[e];
+    for (int it = 0; it < CH; ++it) {
+        const int i = i0 + NG * it + g;
+        const int ic = min(i, T - 1);  // padding rows re-read the last row; nothing of theirs is stored
+        const size_t e0 = (((size_t)b * T + ic) * Hq + h) * D + ci * 8;
+        const bf16x8 gb = *(const bf16x8*)(dO + e0);
+        const f32x4 c0 = *(const f32x4*)(dir + e0), c1 = *(const f32x4*)(dir + e0 + 4);
+        const float dens = stats[(bh * T + ic) * 4 + 3];
+        const float mu = mu_in[bh * T + ic];
+        float gg[8], c[8], vn[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gg[e] = (float)gb[e]; gg[e + 4] = (float)gb[e + 4];
+            c[e] = c0[e]; c[e + 4] = c1[e];
+            vn[e] = vn0[e]; vn[e + 4] = vn1[e];
+        }
+        const bool clamped = dens < 0.0f;
+        const float den = fabsf(dens);
+        float dmu = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dmu += gg[e] * c[e];
+#pragma unroll
+        for (int o = CH / 2; o >= 1; o >>= 1) dmu += __shfl_xor(dmu, o, CH);
+        // ds is rounded to bf16 once and every later use (dP on MFMA, ds . v_null and ds . c here)
+        // takes the rounded value
+        float dsv = 0.f, dsc = 0.f;
+        const float sc = mu / den, pr = clamped ? 0.0f : dmu;
+        bf16x8 dsb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dsb[e] = (bf16)(sc * (gg[e] - pr * c[e]));
+            dsv += (float)dsb[e] * vn[e];
+            dsc += (float)dsb[e] * c[e];
+        }
+#pragma unroll
+        for (int o = CH / 2; o >= 1; o >>= 1) {
+            dsv += __shfl_xor(dsv, o, CH);
+            dsc += __shfl_xor(dsc, o, CH);
+        }
+        if (i < T) *(bf16x8*)(dsg + e0) = dsb;
+        if (ci == it) {
+            kdmu = dmu;
+            kdsv = dsv;
+            kdsc = dsc;
+        }
+    }
+    const int i = i0 + NG * ci + g;
+    float* rr = rec + bh * NREC * Tp + i;
+    if (i >= T) {  // padding row: zero weight (log partition +inf), zero gradient
+        rr[0] = 1.0f;
+        rr[(size_t)Tp] = INFINITY;
+        rr[(size_t)2 * Tp] = 0.0f;
+        rr[(size_t)3 * Tp] = 0.0f;
+        rr[(size_t)4 * Tp] = 0.0f;
+        return;
     }
     const f32x4 st = *(const f32x4*)(stats + (bh * T + i) * 4);
-    const float lse2 = st[0], R = st[1], Q2 = st[2], dens = st[3];
+    const float lse2 = st[0], R = st[1], Q2 = st[2], den = fabsf(st[3]);
     const float mu = mu_in[bh * T + i];
-    const bool clamped = dens < 0.0f;
-    const float den = fabsf(dens);
-    float dmu = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dmu += g[e] * c[e];
-#pragma unroll
-    for (int o = CH / 2; o >= 1; o >>= 1) dmu += __shfl_xor(dmu, o, CH);
-    // ds is rounded to bf16 once and every later use (dP on MFMA, ds . v_null and ds . c here)
-    // takes the rounded value
-    float dsv = 0.f, dsc = 0.f;
-    const float sc = mu / den, pr = clamped ? 0.0f : dmu;
-    bf16x8 dsb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        dsb[e] = (bf16)(sc * (g[e] - pr * c[e]));
-        dsv += (float)dsb[e] * vn[e];
-        dsc += (float)dsb[e] * c[e];
-    }
-#pragma unroll
-    for (int o = CH / 2; o >= 1; o >>= 1) {
-        dsv += __shfl_xor(dsv, o, CH);
-        dsc += __shfl_xor(dsc, o, CH);
-    }
-    *(bf16x8*)(dsg + e0) = dsb;
-    if (ci != 0) return;
+    const float dmu = kdmu, dsv = kdsv, dsc = kdsc;
     // t and nu exactly as the forward forms them (cq below is its cq; its null logit t nu).  The
     // masses stay IEEE divisions: on null-dominated rows R^3 underflows and Q2 can be subnormal,
     // where a hardware reciprocal (subnormals flushed) would turn 0 / Q2 into 0 * inf.
@@ -653,7 +668,7 @@ hipError_t launch_polar_bwd(const PolarBwdArgs& a, hipStream_t stream) {
     const int Tp = (a.T + BB - 1) / BB * BB;
     const long long nq = (long long)((a.T + BQ - 1) / BQ) * a.Hq * a.B;
     const long long nk = (long long)((a.T + BKT - 1) / BKT) * a.Hkv * a.B;
-    const long long prep_threads = (long long)a.B * Tp * a.Hq * (a.D / 8);
+    const long long prep_threads = (long long)a.B * Tp * a.Hq;  // one lane per row (64 rows per wave)
     if (nq > 0x7fffffffLL || 2 * nk > 0x7fffffffLL || prep_threads / NT > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define ATMA_PB_LAUNCH(DD)                                                                                        \
     do {                                                                                                          \
