@@ -577,27 +577,65 @@ __global__ __launch_bounds__(NT) void polar_bwd_params_partial(const bf16* __res
                                                                const float* __restrict__ part,
                                                                const float* __restrict__ dtr,
                                                                float* __restrict__ ppart, int B, int T, int Hq) {
-    constexpr int CH = D / 8, RL = NT / CH;
+    constexpr int CH = D / 8, RL = NT / CH, U = 4;
     __shared__ float red[4][NT];
     __shared__ float vred[RL][D];
     const int h = (int)blockIdx.x / PCH, c = (int)blockIdx.x % PCH, tid = (int)threadIdx.x;
     const int ci = tid % CH, rl = tid / CH;
     const long rows = (long)B * T, r0 = rows * c / PCH, r1 = rows * (c + 1) / PCH;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (long r = r0 + rl; r < r1; r += RL) {
+    if (r1 <= r0) {  // fewer rows than workgroups: an empty range contributes zeros
+        float* out = ppart + ((size_t)h * PCH + c) * (4 + D);
+        if (tid < 4 + D) out[tid] = 0.0f;
+        return;
+    }
+    auto row_index = [&](long r) {  // row r of this head's B*T rows in the [B, Hq, T] layouts
         const int b = (int)(r / T), i = (int)(r - (long)b * T);
-        const size_t ri = ((size_t)b * Hq + h) * T + i;
-        const f32x4 p = *(const f32x4*)(part + ri * 4);
-        if (ci == 0) {
-            const float n = (float)(i + 1);
-            s0 += (dtr[ri] + p[0]) * logf(n);
-            s1 += p[1] * sqrtf(logf(n + 1.0f));
-            s2 += p[1];
-            s3 += p[2];
-        }
-        const bf16x8 d8 = *(const bf16x8*)(dsg + (((size_t)b * T + i) * Hq + h) * D + ci * 8);
+        return ((size_t)b * Hq + h) * T + i;
+    };
+    // the scalar parameters: one row per thread, U rows requested together (rows past the range
+    // re-read its first row and are skipped)
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (long rb = r0 + tid; rb < r1; rb += (long)U * NT) {
+        f32x4 p[U];
+        float dt[U];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(p[3], (float)d8[e], acc[e]);
+        for (int u = 0; u < U; ++u) {
+            const long r = rb + (long)u * NT;
+            const size_t ri = row_index(r < r1 ? r : r0);
+            p[u] = *(const f32x4*)(part + ri * 4);
+            dt[u] = dtr[ri];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long r = rb + (long)u * NT;
+            if (r < r1) {
+                const int i = (int)(r % T);
+                const float n = (float)(i + 1);
+                s0 += (dt[u] + p[u][0]) * logf(n);
+                s1 += p[u][1] * sqrtf(logf(n + 1.0f));
+                s2 += p[u][1];
+                s3 += p[u][2];
+            }
+        }
+    }
+    // v_null: CH lanes per row (8 value columns each), U rows requested together
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (long rb = r0 + rl; rb < r1; rb += (long)U * RL) {
+        bf16x8 d8[U];
+        float wn[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long r = rb + (long)u * RL;
+            const long rc = r < r1 ? r : r0;
+            const int b = (int)(rc / T), i = (int)(rc - (long)b * T);
+            const float x = part[row_index(rc) * 4 + 3];
+            wn[u] = r < r1 ? x : 0.0f;
+            d8[u] = *(const bf16x8*)(dsg + (((size_t)b * T + i) * Hq + h) * D + ci * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wn[u], (float)d8[u][e], acc[e]);
     }
     red[0][tid] = s0; red[1][tid] = s1; red[2][tid] = s2; red[3][tid] = s3;
 #pragma unroll
@@ -626,6 +664,7 @@ __global__ __launch_bounds__(NT) void polar_bwd_params_final(const float* __rest
     const int h = (int)blockIdx.x, tid = (int)threadIdx.x;
     if (tid >= 4 + D) return;
     float sum = 0.f;
+#pragma unroll 16
     for (int c = 0; c < PCH; ++c) sum += ppart[((size_t)h * PCH + c) * (4 + D) + tid];
     if (tid == 0) d_temp_raw[h] = sum * sigmoidf(prm.temp_raw[h]);
     else if (tid == 1) d_slope[h] = sum * sigmoidf(prm.null_slope_raw[h]);
