@@ -11,17 +11,20 @@
 //   gdn_prep_h  (parallel over chunks) - A, Tinv (fp32), W and U from an fp32-accurate
 //               hi/lo bf16 split of Tinv, and KD^T; writes them as fp16 tiles already in
 //               the carry's MFMA-fragment order, plus the chunk's g for the output kernel.
-//               It needs neither Q nor P, and A and Tinv share one 64 x 64 tile (A
-//               transposed above the diagonal, Tinv below), so its LDS fits four
-//               workgroups per CU.
+//               A and Tinv share one 64 x 64 tile (A transposed above the diagonal, Tinv
+//               below), so its LDS fits four workgroups per CU.  When the carry forms the
+//               output, prep also writes P and QG as fp16 fragments.
 //   gdn_carry_h (one workgroup per 64 state rows of a (batch, head), walks the chunks)
 //               keeps S^T in fp32 MFMA accumulators; per chunk it only forms Delta and the
 //               state update (32 MFMAs per wave), streaming W, KD^T and its U slice through
 //               three LDS stages with direct global->LDS copies issued two chunks ahead.
 //               It writes the fp16 operands it built anyway -- S_in^T and Delta, in MFMA
-//               fragment order -- for the output kernel.
-//   gdn_out_h   (parallel over chunks) - QG and P from the bf16 Q and K tiles, then
-//               O = QG S_in^T + P Delta, coalesced bf16 stores.
+//               fragment order -- for the output kernel; or, in its two-wave form (grids
+//               too small to fill the GPU), hands them through LDS to two output waves of
+//               the same workgroup, which form O = QG S_in^T + P Delta for its 32 columns
+//               while the carry goes on (no output kernel, no S_in^T / Delta records).
+//   gdn_out_h   (parallel over chunks, after the four-wave carry) - QG and P from the bf16
+//               Q and K tiles, then O = QG S_in^T + P Delta, coalesced bf16 stores.
 // Long sequences with few (batch, head) pairs leave most of the GPU idle during the carry, so
 // the sequence is cut into segments.  Per chunk the state map is affine in S,
 //     S_out = S_in A_c + B_c,  A_c = e^{g_last} I - W^T KD,  B_c = U^T KD,
@@ -51,6 +54,9 @@ using gdn::copy_out;
 //   SF : S_in^T fragments [DV/64][DK/32][4 waves][64 lanes] x 16 B
 //   DF : Delta fragments  [DV/64][2][4 waves][64 lanes] x 16 B
 //   EGL: e^{g_last} (fp32)
+// When the carry forms the output itself (see gdn_carry_h), SF and DF are not needed; instead
+//   RP : P fragments [4][2][64 lanes] x 16 B | QG fragments [4][DK/32][64 lanes] x 16 B
+//        (fragment-major fp16 A operands of O = QG S_in^T + P Delta, written by the prep kernel)
 template <int DK, int DV> struct Lay {
     static constexpr int RBK = DK * 2;  // bytes per W / QG row
     static constexpr size_t A_W = 0;
@@ -62,25 +68,38 @@ template <int DK, int DV> struct Lay {
     static constexpr size_t SF = (size_t)DV * DK * 2;
     static constexpr size_t DF = (size_t)C * DV * 2;
     static constexpr size_t STAGE = A_U + USLICE;  // bytes one carry workgroup streams per chunk
-    static size_t total(size_t nchunks) { return nchunks * (RA + RB + SF + DF + sizeof(float)); }  // + seg_bytes
+    static constexpr size_t P_OFF = 0, QG_OFF = (size_t)4 * 2 * 1024;
+    static constexpr size_t RP = QG_OFF + (size_t)4 * (DK / 32) * 1024;
+    static size_t total(size_t nchunks, bool fused) {  // + seg_bytes
+        return nchunks * (RA + RB + (fused ? RP : SF + DF) + sizeof(float));
+    }
 };
 
 struct Regions {
-    char *ra, *rb, *sf, *df;
+    char *ra, *rb, *sf, *df, *rp;  // sf, df without the fused output; rp with it
     float* egl;
     float* seg;  // segment summaries [B H][nseg][Dv + Dk rows][Dk]: B_seg rows, then A_seg rows
     float* sst;  // segment start states [B H][nseg][Dv][Dk]
 };
 template <int DK, int DV>
-Regions regions(void* ws, size_t nchunks, size_t nbh, int nseg) {
+Regions regions(void* ws, size_t nchunks, size_t nbh, int nseg, bool fused) {
     using L = Lay<DK, DV>;
     char* p = (char*)ws;
     Regions r;
     r.ra = p;
     r.rb = r.ra + nchunks * L::RA;
-    r.sf = r.rb + nchunks * L::RB;
-    r.df = r.sf + nchunks * L::SF;
-    r.egl = (float*)(r.df + nchunks * L::DF);
+    char* e = r.rb + nchunks * L::RB;
+    if (fused) {
+        r.sf = r.df = nullptr;
+        r.rp = e;
+        e += nchunks * L::RP;
+    } else {
+        r.rp = nullptr;
+        r.sf = e;
+        r.df = r.sf + nchunks * L::SF;
+        e = r.df + nchunks * L::DF;
+    }
+    r.egl = (float*)e;
     char* q = (char*)(r.egl + nchunks);
     q += (256 - (size_t)q % 256) % 256;
     r.seg = nseg > 1 ? (float*)q : nullptr;
@@ -111,6 +130,11 @@ int choose_nseg(int B, int T, int H, int Dk, int Dv) {
     const int len = (NC + best - 1) / best;
     return (NC + len - 1) / len;  // every segment non-empty
 }
+
+// Two-wave carry workgroups (32 state rows each) when four-wave ones would leave more than half
+// of the 256 CUs idle; those carry workgroups also form the output (a third wave), so the S_in^T
+// and Delta records never go through memory and there is no output kernel.
+bool small_carry(int B, int H, int nseg, int Dv) { return (long long)H * nseg * B * (Dv / 64) * 2 <= 256; }
 
 // ---- fragment-major tiles -----------------------------------------------------------------
 // An R x K fp16 MFMA A-operand tile is stored as its fragments, [R/16][K/32][64 lanes][8]:
@@ -280,6 +304,56 @@ __global__ __launch_bounds__(NT, 4) void gdn_prep_h(const bf16* __restrict__ q, 
     }
     __syncthreads();  // A complete
 
+    // ---- P and QG for a carry that forms the output (waves 1-3, while wave 0 solves the
+    // diagonal blocks below) -----------------------------------------------------------------
+    // QG = diag(e^g) Q and P = lower_incl((Q K^T) o E) as fragment-major fp16 A operands.  P is
+    // formed transposed, P^T = K Q^T, so that the accumulator of tile (jt, it) -- lane (l16, G)
+    // holding P[16 it + l16][16 jt + 4 G + x] -- is already half of the A fragment (it, jt / 2).
+    if (w != 0 && rg.rp) {
+        char* rp = rg.rp + cid * L::RP;
+        auto pq = [&](int it) {
+            const int r = 16 * it + l16;
+            const bf16* qrow = q + (tok0 + (size_t)min(r, n - 1) * H) * DK + 4 * G;  // rows past n: row n - 1
+            Frag<bf16> qf[DK / 32];
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const bf16x4 lo = *(const bf16x4*)(qrow + 32 * kb), hi = *(const bf16x4*)(qrow + 32 * kb + 16);
+                qf[kb].v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            const float gr = sm.Gs[r];
+            const float eg = __expf(gr);
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                f16x8 y;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = (half)((float)qf[kb].v[e] * eg);
+                __builtin_nontemporal_store(y, (f16x8*)(rp + L::QG_OFF + ((it * (DK / 32) + kb) * 64 + lane) * 16));
+            }
+            for (int jt = 0; jt <= it; ++jt) {
+                Frag<bf16> kf[DK / 32];
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) load_frag_rows(kf[kb], sm.Ks, LDK, 16 * jt + l16, 32 * kb);
+                f32x4 pt = {0, 0, 0, 0};
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) mma(pt, kf[kb], qf[kb]);
+                const f32x4 gs = *(const f32x4*)&sm.Gs[16 * jt + 4 * G];
+                f16x4 y;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int s2 = 16 * jt + 4 * G + x;
+                    const float e = __expf(fminf(gr - gs[x], 0.0f));  // g_r - g_s <= 0 where s <= r
+                    y[x] = (half)((s2 <= r) ? e * pt[x] : 0.0f);
+                }
+                __builtin_nontemporal_store(y, (f16x4*)(rp + L::P_OFF + ((it * 2 + (jt >> 1)) * 64 + lane) * 16 + (jt & 1) * 8));
+            }
+            if ((it & 1) == 0)  // tile it + 1 of the same fragment lies above the diagonal
+                __builtin_nontemporal_store(f16x4{0, 0, 0, 0},
+                                            (f16x4*)(rp + L::P_OFF + ((it * 2 + (it >> 1)) * 64 + lane) * 16 + 8));
+        };
+        pq(w);
+        if (w == 3) pq(0);
+    }
+
     // ---- D: Tinv = (I + A)^{-1} -----------------------------------------------------------
     if (w == 0) {
         // 16x16 diagonal blocks: lane (blk, col) solves column `col` of block `blk` by forward
@@ -434,18 +508,32 @@ constexpr int kStageMax = 40960 + 1024;  // tiles + e^{g_last} (one word per lan
 __shared__ __align__(16) char g_stage0[kStageMax];
 __shared__ __align__(16) char g_stage1[kStageMax];
 __shared__ __align__(16) char g_stage2[kStageMax];
+// Fused output (two carry waves and two output waves): each carry wave's S_in^T and Delta
+// fragments of a chunk, double-buffered, [2][2 waves][DK/32 + 2][64 lanes] x 16 B, and the output
+// waves' staging tile of 64 rows x 32 columns (bf16, rows padded to 40; 32 rows per output wave).
+constexpr int kHandMax = 2 * 2 * (128 / 32 + 2) * 1024;
+constexpr int kOLD = 40;
+__shared__ __align__(16) char g_hand[kHandMax];
+__shared__ __align__(16) bf16 g_ostage[C * kOLD];
+
+// byte offset of fragment `slot` of carry wave `wv` in hand-off buffer `buf` (this lane's 16 bytes)
+template <int DK>
+__device__ __forceinline__ int hand_off(int buf, int wv, int slot) {
+    return ((buf * 2 + wv) * (DK / 32 + 2) + slot) * 1024 + lane_id() * 16;
+}
 
 // NW waves per workgroup (4, or 2 for grids too small to fill the GPU: 16 NW state rows per
 // workgroup either way one 16-row band per wave); wave w of the workgroup is wave wq of the
 // 64-row record slice sl (U slices, S_in^T and Delta fragments are laid out per 64 rows).
-template <int DK, int DV, bool STORE, int NW>
+template <int DK, int DV, bool STORE, int NW, bool FUSE>
 struct Carry {
     using L = Lay<DK, DV>;
     static constexpr int RBK = L::RBK, NKT = DK / 16, NTC = 64 * NW;
     static constexpr int NCH = (int)L::STAGE / 16;  // 16-byte copies per chunk
     static constexpr int TPT = NCH / NTC;            // tile copies per thread per chunk
     static constexpr int DPT = TPT + 1;              // all copies per thread per chunk (+ e^{g_last})
-    static constexpr int SPT = STORE ? DK / 32 + 2 : 0;  // fragment stores per thread per chunk
+    static constexpr int SPT = STORE && !FUSE ? DK / 32 + 2 : 0;  // fragment stores per thread per chunk
+    static_assert(!FUSE || (STORE && NW == 2 && DK <= 128), "the fused output serves the two-wave carry");
     static_assert(L::STAGE + 1024 <= kStageMax, "stage too large");
     static_assert(NCH % NTC == 0, "stage must be a whole number of copy rounds");
     static_assert(DPT + SPT < 64, "vmcnt range");
@@ -502,7 +590,8 @@ struct Carry {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
             acc_to_frag(sf[kb], st[2 * kb], st[2 * kb + 1]);
-            if constexpr (STORE) __builtin_nontemporal_store(sf[kb].v, (f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16));
+            if constexpr (FUSE) *(f16x8*)(g_hand + hand_off<DK>(c & 1, wave_id(), kb)) = sf[kb].v;
+            else if constexpr (STORE) __builtin_nontemporal_store(sf[kb].v, (f16x8*)(sfo + ((kb * 4 + w) * 64 + lane) * 16));
         }
         f16x8 kf[NKT][2];
 #pragma unroll
@@ -531,7 +620,8 @@ struct Carry {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             acc_to_frag(df[kb], dl[2 * kb], dl[2 * kb + 1]);
-            if constexpr (STORE) __builtin_nontemporal_store(df[kb].v, (f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16));
+            if constexpr (FUSE) *(f16x8*)(g_hand + hand_off<DK>(c & 1, wave_id(), DK / 32 + kb)) = df[kb].v;
+            else if constexpr (STORE) __builtin_nontemporal_store(df[kb].v, (f16x8*)(dfo + ((kb * 4 + w) * 64 + lane) * 16));
         }
         // S_out^T = e^{g_last} S_in^T + KD^T Delta
 #pragma unroll
@@ -563,12 +653,104 @@ struct Carry {
 // fragments for the output kernel and, in the last segment, the final state.
 // !STORE (segment summary): (Dv + Dk) / 64 slices; real rows start from zero, the Dk extra
 // rows start from the identity with U ignored; the end state goes to the summary region.
-template <int DK, int DV, bool STORE, int NW>
-__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
-    Regions rg, const float* init_state, float* final_state, int Tmax, int H, int nseg, int seglen,
-    const int* __restrict__ cu, int total) {
+//
+// FUSE (two carry waves): two more waves form the output, rows 32 cw .. 32 cw + 31 each (cw = 0,
+// 1).  In the interval after the barrier that opens carry step c, output wave cw forms its rows of
+// chunk c - 1 from that chunk's S_in^T and Delta fragments, which the carry waves left in the LDS
+// hand-off buffer (c - 1) & 1 during step c - 1 and overwrite only in step c + 1, and from the P
+// and QG fragments prep wrote, requested three intervals ahead (three register sets, by chunk
+// index mod 3; plain loads, so the four workgroups of a (batch, head) share them in the L2); the carry waves pass one more barrier after their last step, so both sides pass
+// the same number.
+template <int DK, int DV, int CW>
+struct OutFrags {
+    static constexpr int NKB = DK / 32, NP = CW == 0 ? 2 : 4;  // P fragments (it, kb), kb < (it < 2 ? 1 : 2)
+    f16x8 pf[NP], qg[2][NKB];
+    __device__ __forceinline__ void request(const char* r) {
+        using L = Lay<DK, DV>;
+        const int lane = lane_id();
+#pragma unroll
+        for (int f = 0; f < NP; ++f) {
+            const int it = CW == 0 ? f : 2 + (f >> 1), kb = CW == 0 ? 0 : (f & 1);
+            pf[f] = *(const f16x8*)(r + L::P_OFF + ((it * 2 + kb) * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int il = 0; il < 2; ++il)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                qg[il][kb] = *(const f16x8*)(r + L::QG_OFF + (((2 * CW + il) * NKB + kb) * 64 + lane) * 16);
+    }
+};
+
+template <int DK, int DV, int CW>
+__device__ __forceinline__ void carry_output_chunk(const OutFrags<DK, DV, CW>& fr, int cc, bf16* __restrict__ o,
+                                                   size_t seq0, int tfirst, int Tlen, int H, int h, int col0) {
+    constexpr int NKB = DK / 32;
+    const int lane = lane_id(), G = lane >> 4, l16 = lane & 15, buf = cc & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // the two carry waves' 16 state rows = 16 output columns each
+        Frag<half> sf[NKB], df[2];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sf[kb].v = *(const f16x8*)(g_hand + hand_off<DK>(buf, j, kb));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) df[kb].v = *(const f16x8*)(g_hand + hand_off<DK>(buf, j, NKB + kb));
+#pragma unroll
+        for (int il = 0; il < 2; ++il) {
+            const int i = 2 * CW + il;
+            f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                Frag<half> a;
+                a.v = fr.qg[il][kb];
+                mma(acc, a, sf[kb]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < (CW == 0 ? 1 : 2); ++kb) {
+                Frag<half> a;
+                a.v = fr.pf[CW == 0 ? il : 2 * il + kb];
+                mma(acc, a, df[kb]);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) g_ostage[(16 * i + 4 * G + x) * kOLD + 16 * j + l16] = (bf16)acc[x];
+        }
+    }
+    // this wave's 32 rows of 32 columns (64 bytes each) out
+    const int t0 = tfirst + cc * C, nrow = min(C, Tlen - t0);
+#pragma unroll
+    for (int m = 2 * CW; m < 2 * CW + 2; ++m) {
+        const int r = (lane >> 2) + 16 * m, qd = lane & 3;
+        const u32x4 y = *(const u32x4*)&g_ostage[r * kOLD + 8 * qd];
+        if (r < nrow) __builtin_nontemporal_store(y, (u32x4*)(o + ((seq0 + t0 + r) * H + h) * DV + col0 + 8 * qd));
+    }
+}
+
+template <int DK, int DV, int CW>
+__device__ __forceinline__ void carry_output(const char* rp0, bf16* __restrict__ o, size_t seq0, int tfirst, int Tlen,
+                                             int H, int h, int col0, int n) {
     using L = Lay<DK, DV>;
-    using K = Carry<DK, DV, STORE, NW>;
+    OutFrags<DK, DV, CW> f0, f1, f2;  // chunks of index 0, 1, 2 mod 3
+    f0.request(rp0);
+    if (1 < n) f1.request(rp0 + L::RP);
+    for (int c = 0; c <= n; c += 3) {
+        gdn::lds_barrier();  // opens carry step c (or follows the last one)
+        if (c > 0) carry_output_chunk<DK, DV, CW>(f2, c - 1, o, seq0, tfirst, Tlen, H, h, col0);
+        if (c + 2 < n) f2.request(rp0 + (size_t)(c + 2) * L::RP);
+        if (c + 1 > n) break;
+        gdn::lds_barrier();
+        carry_output_chunk<DK, DV, CW>(f0, c, o, seq0, tfirst, Tlen, H, h, col0);
+        if (c + 3 < n) f0.request(rp0 + (size_t)(c + 3) * L::RP);
+        if (c + 2 > n) break;
+        gdn::lds_barrier();
+        carry_output_chunk<DK, DV, CW>(f1, c + 1, o, seq0, tfirst, Tlen, H, h, col0);
+        if (c + 4 < n) f1.request(rp0 + (size_t)(c + 4) * L::RP);
+    }
+}
+
+template <int DK, int DV, bool STORE, int NW, bool FUSE>
+__global__ __launch_bounds__(64 * (NW + (FUSE ? 2 : 0)), 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_carry_h(
+    Regions rg, const float* init_state, float* final_state, int Tmax, int H, int nseg, int seglen,
+    const int* __restrict__ cu, int total, bf16* __restrict__ o) {
+    using L = Lay<DK, DV>;
+    using K = Carry<DK, DV, STORE, NW, FUSE>;
     constexpr int NKT = DK / 16;
     // slices of one (b, h, segment) on one XCD (workgroup i runs on XCD i % 8)
     const int nsl = (int)gridDim.x, nwg = nsl * (int)gridDim.y * (int)gridDim.z;
@@ -588,6 +770,15 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1
     const int cb = sg * seglen, n = min(NC - cb, seglen);  // this segment's chunks (<= 0: none)
     const size_t bh = (size_t)b * H + h;
     const size_t c0 = bh * NCs + cb;
+    if constexpr (FUSE) {
+        if (wave_id() >= NW) {  // the output waves (uniform branches: whole waves)
+            if (n > 0) {
+                if (wave_id() == NW) carry_output<DK, DV, 0>(rg.rp + c0 * L::RP, o, seq0, cb * C, Tlen, H, h, 32 * sl, n);
+                else carry_output<DK, DV, 1>(rg.rp + c0 * L::RP, o, seq0, cb * C, Tlen, H, h, 32 * sl, n);
+            }
+            return;
+        }
+    }
     const bool real = sl64 < DV / 64;
     const K k{rg.ra + c0 * L::RA, rg.sf + c0 * L::SF, rg.df + c0 * L::DF, rg.egl + c0, real ? sl64 : 0,
               real ? 1.0f : 0.0f, wq};
@@ -652,6 +843,7 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1
         k.issue(min(c + 4, last), g_stage2);
         k.step(c + 2, g_stage0, st);
     }
+    if constexpr (FUSE) gdn::lds_barrier();  // the output waves read the last chunk's hand-off after it
     finish();
 }
 
@@ -898,7 +1090,8 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
     const size_t nbh = (size_t)a.B * a.H;
     const int nseg = choose_nseg(a.B, a.T, a.H, DK, DV);
     const int seglen = (NC + nseg - 1) / nseg;
-    const Regions rg = regions<DK, DV>(a.workspace, nbh * NC, nbh, nseg);
+    const bool fused = small_carry(a.B, a.H, nseg, DV);
+    const Regions rg = regions<DK, DV>(a.workspace, nbh * NC, nbh, nseg, fused);
     const size_t prep_smem = sizeof(PrepSmem<DK, DV>), out_smem = sizeof(OutSmem<DK, DV>);
     const size_t scan_smem = sizeof(ScanSmem<DK, DV>);
     static const hipError_t attr = [&] {
@@ -912,26 +1105,30 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
                        (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, rg, a.T, a.H, a.cu, a.total);
     // Carry workgroups hold 64 state rows with four waves, or 32 rows with two when four-wave
     // workgroups would leave more than half of the 256 CUs idle (one workgroup per CU: the LDS
-    // stages fill it), so that the carry's LDS reads are spread over twice the CUs.
+    // stages fill it), so that the carry's LDS reads are spread over twice the CUs.  The two-wave
+    // carry also forms the output (a third wave); after the four-wave carry the output kernel does.
     const long long units = (long long)a.H * nseg * a.B;
     if (nseg > 1) {
         if (units * ((DV + DK) / 64) * 2 <= 256)
-            hipLaunchKernelGGL((gdn_carry_h<DK, DV, false, 2>), dim3((DV + DK) / 32, a.H * nseg, a.B), dim3(128), 0,
-                               stream, rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
+            hipLaunchKernelGGL((gdn_carry_h<DK, DV, false, 2, false>), dim3((DV + DK) / 32, a.H * nseg, a.B), dim3(128),
+                               0, stream, rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total,
+                               nullptr);
         else
-            hipLaunchKernelGGL((gdn_carry_h<DK, DV, false, 4>), dim3((DV + DK) / 64, a.H * nseg, a.B), dim3(NT), 0,
-                               stream, rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
+            hipLaunchKernelGGL((gdn_carry_h<DK, DV, false, 4, false>), dim3((DV + DK) / 64, a.H * nseg, a.B), dim3(NT),
+                               0, stream, rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total,
+                               nullptr);
         hipLaunchKernelGGL((gdn_seg_scan<DK, DV>), dim3(DV / 16, a.H, a.B), dim3(NT), scan_smem, stream, rg,
                            a.init_state, a.H, nseg);
     }
-    if (units * (DV / 64) * 2 <= 256)
-        hipLaunchKernelGGL((gdn_carry_h<DK, DV, true, 2>), dim3(DV / 32, a.H * nseg, a.B), dim3(128), 0, stream, rg,
-                           a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
-    else
-        hipLaunchKernelGGL((gdn_carry_h<DK, DV, true, 4>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream, rg,
-                           a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total);
-    hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, (const bf16*)a.q,
-                       (const bf16*)a.k, rg, (bf16*)a.o, a.T, a.H, a.cu, a.total);
+    if (fused) {
+        hipLaunchKernelGGL((gdn_carry_h<DK, DV, true, 2, true>), dim3(DV / 32, a.H * nseg, a.B), dim3(256), 0, stream,
+                           rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total, (bf16*)a.o);
+    } else {
+        hipLaunchKernelGGL((gdn_carry_h<DK, DV, true, 4, false>), dim3(DV / 64, a.H * nseg, a.B), dim3(NT), 0, stream,
+                           rg, a.init_state, a.final_state, a.T, a.H, nseg, seglen, a.cu, a.total, nullptr);
+        hipLaunchKernelGGL((gdn_out_h<DK, DV>), dim3(NC, a.H, a.B), dim3(NT), out_smem, stream, (const bf16*)a.q,
+                           (const bf16*)a.k, rg, (bf16*)a.o, a.T, a.H, a.cu, a.total);
+    }
     return hipGetLastError();
 }
 
@@ -940,10 +1137,11 @@ hipError_t launch(const GdnFwdArgs& a, hipStream_t stream) {
 size_t gdn_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
     const size_t nbh = (size_t)B * H, nchunks = nbh * ((T + C - 1) / C);
     const int nseg = choose_nseg(B, T, H, Dk, Dv);
-    if (Dk == 64 && Dv == 64) return Lay<64, 64>::total(nchunks) + seg_bytes<64, 64>(nbh, nseg);
-    if (Dk == 64 && Dv == 128) return Lay<64, 128>::total(nchunks) + seg_bytes<64, 128>(nbh, nseg);
-    if (Dk == 128 && Dv == 64) return Lay<128, 64>::total(nchunks) + seg_bytes<128, 64>(nbh, nseg);
-    if (Dk == 128 && Dv == 128) return Lay<128, 128>::total(nchunks) + seg_bytes<128, 128>(nbh, nseg);
+    const bool fused = small_carry(B, H, nseg, Dv);
+    if (Dk == 64 && Dv == 64) return Lay<64, 64>::total(nchunks, fused) + seg_bytes<64, 64>(nbh, nseg);
+    if (Dk == 64 && Dv == 128) return Lay<64, 128>::total(nchunks, fused) + seg_bytes<64, 128>(nbh, nseg);
+    if (Dk == 128 && Dv == 64) return Lay<128, 64>::total(nchunks, fused) + seg_bytes<128, 64>(nbh, nseg);
+    if (Dk == 128 && Dv == 128) return Lay<128, 128>::total(nchunks, fused) + seg_bytes<128, 128>(nbh, nseg);
     return 0;
 }
 
