@@ -113,11 +113,11 @@ def _run_mutant(name, workdir):
 
 @pytest.fixture(scope="module")
 def mutant_results(tmp_path_factory):
-    """Every mutant built and evaluated up front, four at a time."""
+    """Every mutant built and evaluated up front, one process per CPU (at most 8)."""
     import concurrent.futures as cf
 
     work = tmp_path_factory.mktemp("strength")
-    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
         futs = {n: ex.submit(_run_mutant, n, work) for n in STRENGTH_MUTANTS}
         return {n: f.result() for n, f in futs.items()}
 

@@ -72,14 +72,16 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_planted_mistake(tmp_path, name):
+def _run_pins(name, workdir):
+    """Builds the mutant and runs every pin against it; returns (exit status, output tail)."""
     old, new = MUTANTS[name]
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
-    mutated = tmp_path / "oracle_mut.c"
+    d = workdir / name
+    d.mkdir()
+    mutated = d / "oracle_mut.c"
     mutated.write_text(src.replace(old, new))
-    lib = tmp_path / "liboracle_mut.so"
+    lib = d / "liboracle_mut.so"
     subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-D_POSIX_C_SOURCE=200809L", "-shared", "-o", str(lib),
                     str(mutated), "-lm", "-lpthread"], check=True)
     env = dict(os.environ, ATMA_ORACLE_LIB=str(lib))
@@ -89,5 +91,22 @@ def test_pins_catch_planted_mistake(tmp_path, name):
                         os.path.join(ROOT, "tests", "test_oracle_baseline.py"),
                         os.path.join(ROOT, "tests", "test_oracle_canon.py"),
                         os.path.join(ROOT, "tests", "test_oracle_grad.py")],
-                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=900)
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def pin_results(tmp_path_factory):
+    """Every mutant built and run against the pins up front, one process per CPU (at most 8)."""
+    import concurrent.futures as cf
+
+    work = tmp_path_factory.mktemp("mutants")
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        futs = {n: ex.submit(_run_pins, n, work) for n in sorted(MUTANTS)}
+        return {n: f.result() for n, f in futs.items()}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(pin_results, name):
+    rc, out = pin_results[name]
+    assert rc != 0, f"mutant {name} survived every pin:\n{out}"
