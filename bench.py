@@ -67,7 +67,7 @@ MEASURED_TRAFFIC = {
     # layer_b8_t2k: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch (profiles/polar_fwd_layer_b8_t2k.txt)
     "polar_fwd_kernel": {"sha": "e5540cc82bc0cca1", "bytes": 185649366},
     # layer_b8_t2k, prep + carry (one segment at this shape; the carry forms the output)
-    "atma_gdn_fwd (prep+carry+out)": {"sha": "e2dfe1ac7d327c8f", "bytes": 443968512},
+    "atma_gdn_fwd (prep+carry+out)": {"sha": "402753ebac569130", "bytes": 444711826},
     # layer_b8_t2k backward: prep + both walks + pre + post (profiles/gdn_bwd_layer_b8_t2k.txt)
     "atma_gdn_bwd (all kernels)": {"sha": "435838d3e9475fec", "bytes": 3556505114},
 }

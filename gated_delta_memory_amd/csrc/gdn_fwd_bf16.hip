@@ -238,7 +238,7 @@ __global__ __launch_bounds__(NT, 4) void gdn_prep_h(const bf16* __restrict__ q, 
         sm.Gs[lane] = la;
         sm.Bs[lane] = be;
         sm.Es[lane] = be * __expf(la);
-        __builtin_nontemporal_store(la, (float*)rb + lane);
+        ((float*)rb)[lane] = la;
         if (lane == C - 1) rg.egl[cid] = __expf(la);
     }
     __syncthreads();
@@ -306,6 +306,8 @@ __global__ __launch_bounds__(NT, 4) void gdn_prep_h(const bf16* __restrict__ q, 
 
     // ---- P and QG for a carry that forms the output (waves 1-3, while wave 0 solves the
     // diagonal blocks below) -----------------------------------------------------------------
+    // (plain stores, like W, KD^T and U: at the 2K layer the records of a call fit the last-level
+    // cache, from which the carry reads them back; streaming stores made the call 11% slower)
     // QG = diag(e^g) Q and P = lower_incl((Q K^T) o E) as fragment-major fp16 A operands.  P is
     // formed transposed, P^T = K Q^T, so that the accumulator of tile (jt, it) -- lane (l16, G)
     // holding P[16 it + l16][16 jt + 4 G + x] -- is already half of the A fragment (it, jt / 2).
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(NT, 4) void gdn_prep_h(const bf16* __restrict__ q, 
                 f16x8 y;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = (half)((float)qf[kb].v[e] * eg);
-                __builtin_nontemporal_store(y, (f16x8*)(rp + L::QG_OFF + ((it * (DK / 32) + kb) * 64 + lane) * 16));
+                *(f16x8*)(rp + L::QG_OFF + ((it * (DK / 32) + kb) * 64 + lane) * 16) = y;
             }
             for (int jt = 0; jt <= it; ++jt) {
                 Frag<bf16> kf[DK / 32];
@@ -344,11 +346,10 @@ __global__ __launch_bounds__(NT, 4) void gdn_prep_h(const bf16* __restrict__ q, 
                     const float e = __expf(fminf(gr - gs[x], 0.0f));  // g_r - g_s <= 0 where s <= r
                     y[x] = (half)((s2 <= r) ? e * pt[x] : 0.0f);
                 }
-                __builtin_nontemporal_store(y, (f16x4*)(rp + L::P_OFF + ((it * 2 + (jt >> 1)) * 64 + lane) * 16 + (jt & 1) * 8));
+                *(f16x4*)(rp + L::P_OFF + ((it * 2 + (jt >> 1)) * 64 + lane) * 16 + (jt & 1) * 8) = y;
             }
             if ((it & 1) == 0)  // tile it + 1 of the same fragment lies above the diagonal
-                __builtin_nontemporal_store(f16x4{0, 0, 0, 0},
-                                            (f16x4*)(rp + L::P_OFF + ((it * 2 + (it >> 1)) * 64 + lane) * 16 + 8));
+                *(f16x4*)(rp + L::P_OFF + ((it * 2 + (it >> 1)) * 64 + lane) * 16 + 8) = f16x4{0, 0, 0, 0};
         };
         pq(w);
         if (w == 3) pq(0);
